@@ -1,0 +1,16 @@
+"""Shared pytest configuration.
+
+Tests marked ``gpu`` need a real MI355X and call the HIP library through its
+C ABI; everything else runs on the CPU (oracle pins, host-side validation and
+the library's export table).
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")

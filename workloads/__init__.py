@@ -1,0 +1,227 @@
+"""Seeded synthetic workloads shared by the tests, the smoke check and the benchmark.
+
+This module holds inputs and network structure only: random arrays drawn in a
+fixed order from ``numpy.random.default_rng(seed)`` and layer lists that say
+which layer feeds which.  It contains none of the method's arithmetic (no
+convolution, normalisation, activation, resize or shape arithmetic), so the
+CPU oracle and the HIP library can both consume it without sharing code.
+
+The workloads stand in for data the source pages used but did not publish:
+MNIST digits ("Как я свертки ускорял", "Пациента на стол"), COCO frames
+("YOLO26N Inference Optimisation", "mAP caveat") and camera frames
+("A fused Ampere preprocess kernel", "The setup").  Convolution run time does
+not depend on the values, so uniform random inputs of the same shapes serve.
+
+Recipe (seed = 1000 + workload index unless a test passes its own):
+  activations     fp32, U(-1, 1) for the single depthwise layer, U(0, 1) elsewhere
+  frames          u8, uniform over 0..255, HWC RGB
+  conv weights    fp32, N(0, 1/fan_in) i.e. std = 1/sqrt((cin/groups)*kh*kw)
+  BN parameters   gamma U(0.5, 1.5), beta U(-0.1, 0.1), mean U(-0.1, 0.1),
+                  var U(0.5, 1.5), eps 1e-5
+  fc              weight N(0, 1/192), bias U(-0.1, 0.1)
+  draw order      input first, then per layer: weight, gamma, beta, mean, var
+                  (fc: weight, bias)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+EPS = 1e-5
+
+ACT_NONE, ACT_RELU, ACT_SILU = 0, 1, 2
+RES_NONE, RES_BEFORE_ACT, RES_AFTER_ACT = 0, 1, 2
+
+KIND_CONV, KIND_GAP, KIND_FC, KIND_PREPROC = 0, 1, 2, 3
+
+#: index meaning "the network input" in ``Layer.inp`` / ``Layer.res``
+NET_INPUT = -1
+#: index meaning "no residual" in ``Layer.res``
+NO_RES = -2
+
+#: per-channel normalisation used for the stem prologue (a common convention,
+#: not given by the pages: the caller supplies mean/std)
+PRE_MEAN = (0.485, 0.456, 0.406)
+PRE_STD = (0.229, 0.224, 0.225)
+
+
+@dataclass
+class Layer:
+    """One node of a layer list.  ``inp``/``res`` index earlier layers."""
+
+    kind: int
+    inp: int = NET_INPUT
+    res: int = NO_RES
+    cin: int = 0
+    cout: int = 0
+    k: int = 1
+    stride: int = 1
+    pad: int = 0
+    groups: int = 1
+    act: int = ACT_NONE
+    res_mode: int = RES_NONE
+    name: str = ""
+    params: Dict[str, np.ndarray] = field(default_factory=dict)
+    # prologue only
+    dst_h: int = 0
+    dst_w: int = 0
+    pre_mean: Tuple[float, float, float] = PRE_MEAN
+    pre_std: Tuple[float, float, float] = PRE_STD
+
+
+@dataclass
+class Workload:
+    name: str
+    x: np.ndarray                 # fp32 NCHW, or u8 NHWC when the first layer is the prologue
+    layers: List[Layer]
+
+
+def rng_for(index: int) -> np.random.Generator:
+    return np.random.default_rng(1000 + index)
+
+
+def draw_bn(rng: np.random.Generator, c: int) -> Dict[str, np.ndarray]:
+    f = np.float32
+    return {
+        "gamma": rng.uniform(0.5, 1.5, c).astype(f),
+        "beta": rng.uniform(-0.1, 0.1, c).astype(f),
+        "mean": rng.uniform(-0.1, 0.1, c).astype(f),
+        "var": rng.uniform(0.5, 1.5, c).astype(f),
+    }
+
+
+def conv_layer(rng: np.random.Generator, cin: int, cout: int, k: int, stride: int, pad: int,
+               groups: int = 1, act: int = ACT_RELU, res_mode: int = RES_NONE,
+               inp: int = NET_INPUT, res: int = NO_RES, name: str = "") -> Layer:
+    fan_in = (cin // groups) * k * k
+    w = rng.normal(0.0, 1.0 / np.sqrt(fan_in), (cout, cin // groups, k, k)).astype(np.float32)
+    p = {"w": w}
+    p.update(draw_bn(rng, cout))
+    return Layer(KIND_CONV, inp=inp, res=res, cin=cin, cout=cout, k=k, stride=stride, pad=pad,
+                 groups=groups, act=act, res_mode=res_mode, name=name, params=p)
+
+
+# --------------------------------------------------------------------------- configs
+def depthwise_single(seed_index: int = 0) -> Workload:
+    """Single depthwise 3x3 s1 p1 layer on [1,48,28,28], BN folded, ReLU."""
+    rng = rng_for(seed_index)
+    x = rng.uniform(-1.0, 1.0, (1, 48, 28, 28)).astype(np.float32)
+    layer = conv_layer(rng, 48, 48, 3, 1, 1, groups=48, act=ACT_RELU, name="dw48")
+    return Workload("dw3x3_48x28x28", x, [layer])
+
+
+def mnist_cnn(batch: int, seed_index: int = 1) -> Workload:
+    """The depthwise-separable MNIST CNN ("Как я свертки ускорял", "Пациента на стол").
+
+    conv1 3x3 1->48 + BN + ReLU; four blocks (48->96 s2, 96->96, 96->192 s2,
+    192->192), each dw3x3 + BN + ReLU -> pw1x1 + BN, plus a shortcut (1x1
+    stride-s conv + BN when the block changes stride or width, else identity),
+    added before the block's final ReLU; global average pool; fc 192->10.
+    """
+    rng = rng_for(seed_index)
+    x = rng.uniform(0.0, 1.0, (batch, 1, 28, 28)).astype(np.float32)
+    L: List[Layer] = [conv_layer(rng, 1, 48, 3, 1, 1, act=ACT_RELU, name="conv1")]
+    for bi, (cin, cout, s) in enumerate([(48, 96, 2), (96, 96, 1), (96, 192, 2), (192, 192, 1)]):
+        block_in = len(L) - 1
+        L.append(conv_layer(rng, cin, cin, 3, s, 1, groups=cin, act=ACT_RELU,
+                            inp=block_in, name=f"b{bi}.dw"))
+        dw_idx = len(L) - 1
+        if s != 1 or cin != cout:
+            L.append(conv_layer(rng, cin, cout, 1, s, 0, act=ACT_NONE, inp=block_in,
+                                name=f"b{bi}.skip"))
+            short = len(L) - 1
+        else:
+            short = block_in
+        L.append(conv_layer(rng, cin, cout, 1, 1, 0, act=ACT_RELU, res_mode=RES_BEFORE_ACT,
+                            inp=dw_idx, res=short, name=f"b{bi}.pw"))
+    last = len(L) - 1
+    L.append(Layer(KIND_GAP, inp=last, cin=192, cout=192, name="gap"))
+    fc_w = rng.normal(0.0, 1.0 / np.sqrt(192), (10, 192)).astype(np.float32)
+    fc_b = rng.uniform(-0.1, 0.1, 10).astype(np.float32)
+    L.append(Layer(KIND_FC, inp=len(L) - 1, cin=192, cout=10, name="fc",
+                   params={"w": fc_w, "b": fc_b}))
+    return Workload(f"mnist_dwsep_b{batch}", x, L)
+
+
+def _stem_layers(rng: np.random.Generator, first_inp: int) -> List[Layer]:
+    return [
+        conv_layer(rng, 3, 16, 3, 2, 1, act=ACT_SILU, inp=first_inp, name="stem1"),
+        conv_layer(rng, 16, 32, 3, 2, 1, act=ACT_SILU, inp=first_inp + 1, name="stem2"),
+    ]
+
+
+def detector_stem(seed_index: int = 2) -> Workload:
+    """[1,3,640,640] -> 3x3 s2 3->16 +BN+SiLU -> 3x3 s2 16->32 +BN+SiLU."""
+    rng = rng_for(seed_index)
+    x = rng.uniform(0.0, 1.0, (1, 3, 640, 640)).astype(np.float32)
+    return Workload("stem_640", x, _stem_layers(rng, NET_INPUT))
+
+
+#: the per-layer sweep of nano-detector shapes:
+#: (name, cin, h=w, cout, k, stride, groups, residual?)
+SWEEP = [
+    ("a_64x80_3x3", 64, 80, 64, 3, 1, 1, True),
+    ("b_64x80_3x3s2", 64, 80, 128, 3, 2, 1, False),
+    ("c_128x40_1x1", 128, 40, 128, 1, 1, 1, True),
+    ("d_128x40_3x3", 128, 40, 128, 3, 1, 1, True),
+    ("e_128x40_3x3s2", 128, 40, 256, 3, 2, 1, False),
+    ("f_256x20_1x1", 256, 20, 256, 1, 1, 1, True),
+    ("g_256x20_3x3", 256, 20, 256, 3, 1, 1, True),
+    ("h_64x13_dw3x3", 64, 13, 64, 3, 1, 64, True),
+]
+
+
+def sweep_layer(name: str, seed_index: int = 3, batch: int = 1) -> Workload:
+    """One layer of the sweep, alone: x U(0,1), SiLU, residual = the layer's own input
+    on the stride-1 equal-width layers (added after the activation)."""
+    names = [s[0] for s in SWEEP]
+    i = names.index(name)
+    rng = np.random.default_rng(1000 + seed_index + 100 * (i + 1))
+    _, cin, hw, cout, k, s, g, has_res = SWEEP[i]
+    x = rng.uniform(0.0, 1.0, (batch, cin, hw, hw)).astype(np.float32)
+    layer = conv_layer(rng, cin, cout, k, s, k // 2, groups=g, act=ACT_SILU,
+                       res_mode=RES_AFTER_ACT if has_res else RES_NONE,
+                       res=NET_INPUT if has_res else NO_RES, name=name)
+    return Workload(f"sweep_{name}", x, [layer])
+
+
+def detector_pipeline(batch: int, seed_index: int = 4) -> Workload:
+    """u8 frame [N,720,1280,3] -> fused resize/normalise/CHW to [N,3,640,640] ->
+    stem (3->16 s2, 16->32 s2) -> bridge 3x3 s2 32->64 -> sweep layers a..g in order,
+    each stride-1 equal-width layer adding its own input after the SiLU."""
+    rng = rng_for(seed_index)
+    x = rng.integers(0, 256, (batch, 720, 1280, 3), dtype=np.uint8)
+    L: List[Layer] = [Layer(KIND_PREPROC, inp=NET_INPUT, cin=3, cout=3, name="preprocess",
+                            dst_h=640, dst_w=640)]
+    L += _stem_layers(rng, 0)
+    L.append(conv_layer(rng, 32, 64, 3, 2, 1, act=ACT_SILU, inp=len(L) - 1, name="bridge"))
+    for (name, cin, hw, cout, k, s, g, has_res) in SWEEP[:7]:
+        prev = len(L) - 1
+        L.append(conv_layer(rng, cin, cout, k, s, k // 2, groups=g, act=ACT_SILU,
+                            res_mode=RES_AFTER_ACT if has_res else RES_NONE,
+                            inp=prev, res=prev if has_res else NO_RES, name=name))
+    return Workload(f"detector_640_b{batch}", x, L)
+
+
+def random_conv_case(seed: int, n: int, cin: int, h: int, w: int, cout: int, k: int,
+                     stride: int, pad: int, groups: int = 1, act: int = ACT_SILU,
+                     res_mode: int = RES_NONE, x_lo: float = -1.0) -> Tuple[np.ndarray, Layer]:
+    """A single-layer case for parity sweeps: x ~ U(x_lo, 1) of shape [n,cin,h,w]
+    and one seeded conv layer.  A residual, when the case has one, is drawn
+    separately by ``residual_for`` once the caller knows the output's shape."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(x_lo, 1.0, (n, cin, h, w)).astype(np.float32)
+    layer = conv_layer(rng, cin, cout, k, stride, pad, groups=groups, act=act, res_mode=res_mode)
+    return x, layer
+
+
+def residual_for(seed: int, shape: Tuple[int, ...]) -> np.ndarray:
+    """Independent U(-1,1) residual tensor for a parity case."""
+    return np.random.default_rng(seed + 7777).uniform(-1.0, 1.0, shape).astype(np.float32)
+
+
+def frame(seed: int, n: int, h: int, w: int) -> np.ndarray:
+    """u8 HWC RGB frames, uniform over 0..255."""
+    return np.random.default_rng(seed).integers(0, 256, (n, h, w, 3), dtype=np.uint8)
