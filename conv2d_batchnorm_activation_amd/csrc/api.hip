@@ -1,0 +1,586 @@
+// api.hip -- the C ABI of libcvx: host-side validation, per-shape planning and
+// the layer-list executor.  Every check runs on the host before anything is
+// enqueued; the only device work is the kernels in the k_*.hip files.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "cvx_internal.h"
+
+using namespace cvx;
+
+namespace {
+
+constexpr long kMaxElems = 0x7fffffffL;  // kernels index tensors with 32-bit element counts
+
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+inline Range span(const void* p, size_t bytes)
+{
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int out_extent(int in, int k, int stride, int pad)
+{
+    const int span_ = in + 2 * pad - k;
+    return span_ < 0 ? 0 : span_ / stride + 1;
+}
+
+cvx_status geom_from_desc(const cvx_conv_desc* d, ConvGeom* g)
+{
+    if (d == nullptr) return CVX_ERR_NULL;
+    if (d->act < CVX_ACT_NONE || d->act > CVX_ACT_SILU) return CVX_ERR_ARG;
+    if (d->res_mode < CVX_RES_NONE || d->res_mode > CVX_RES_AFTER_ACT) return CVX_ERR_ARG;
+    if (d->n < 1 || d->c_in < 1 || d->h < 1 || d->w < 1 || d->c_out < 1) return CVX_ERR_SHAPE;
+    if (d->kh < 1 || d->kw < 1 || d->stride < 1 || d->pad < 0 || d->groups < 1)
+        return CVX_ERR_SHAPE;
+    if (d->n > 65535) return CVX_ERR_SHAPE;
+    if (d->c_in % d->groups != 0 || d->c_out % d->groups != 0) return CVX_ERR_SHAPE;
+    if (d->kh != d->kw) return CVX_ERR_UNSUPPORTED;       // square windows only
+    if (d->kh > 7 || d->stride > 4) return CVX_ERR_UNSUPPORTED;
+    if (d->pad >= d->kh) return CVX_ERR_UNSUPPORTED;      // every output sees the image
+    const int oh = out_extent(d->h, d->kh, d->stride, d->pad);
+    const int ow = out_extent(d->w, d->kw, d->stride, d->pad);
+    if (oh < 1 || ow < 1) return CVX_ERR_SHAPE;
+    if ((long)d->n * d->c_in * d->h * d->w > kMaxElems) return CVX_ERR_SHAPE;
+    if ((long)d->n * d->c_out * oh * ow > kMaxElems) return CVX_ERR_SHAPE;
+    if ((long)d->c_out * (d->c_in / d->groups) * d->kh * d->kw > kMaxElems) return CVX_ERR_SHAPE;
+    *g = {d->n, d->c_in, d->h, d->w, d->c_out, d->kh, d->stride, d->pad, d->groups,
+          d->act, d->res_mode, oh, ow};
+    return CVX_OK;
+}
+
+// ------------------------------------------------------------------ planning
+// Kernel family and tile parameters per layer shape ("YOLO26N Inference
+// Optimisation", "Key observations" #1-#2 and "Improvements" #1, #3: one fixed
+// tile configuration cannot serve both the large-map stem and the
+// many-channel late layers, so a single dispatcher picks per shape).
+bool plan_depthwise(const ConvGeom& g, Plan* p)
+{
+    if (!(g.groups == g.cin && g.cin == g.cout && g.k == 3)) return false;
+    if (g.stride != 1 && g.stride != 2) return false;
+    const int pw = g.w + 2 * g.pad;
+    const int ohw = g.oh * g.ow;
+    const int planes = g.n * g.cout;
+    const size_t budget = 32 * 1024 / sizeof(float);  // floats of halo tile per workgroup
+    if (ohw <= 1024 && (size_t)((g.oh - 1) * g.stride + 3) * pw <= budget) {
+        // whole planes; several per workgroup when they are small
+        const int plane_tile = ((g.oh - 1) * g.stride + 3) * pw;
+        int ppb = std::max(1, 1024 / ohw);
+        ppb = std::min<int>(ppb, (int)(budget / plane_tile));
+        ppb = std::max(1, std::min(ppb, planes));
+        p->dw_ppb = ppb;
+        p->dw_toh = g.oh;
+    } else {
+        // bands of output rows of one plane
+        int toh = std::max(1, 1024 / g.ow);
+        while (toh > 1 && (size_t)((toh - 1) * g.stride + 3) * pw > budget) --toh;
+        if ((size_t)(2 * g.stride + 3) * pw > budget && toh == 1 && (size_t)3 * pw > budget)
+            return false;  // a single row does not fit the LDS budget
+        p->dw_ppb = 1;
+        p->dw_toh = std::min(toh, g.oh);
+    }
+    p->fam = FAM_DEPTHWISE;
+    p->ws_bytes = 0;
+    return true;
+}
+
+bool plan_igemm(const ConvGeom& g, Plan* p)
+{
+    if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
+    if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
+    GemmTile t;
+    t.bm = g.cout <= 32 ? 32 : 64;
+    t.bn = t.bm == 32 ? 128 : 64;
+    t.splitk = 1;
+    // as many channels per chunk as the LDS budget allows (even, <= 16)
+    t.ck = 16;
+    while (t.ck > 2 && igemm_lds_bytes(g, t) > kMaxLdsBytes) t.ck -= 2;
+    if (igemm_lds_bytes(g, t) > kMaxLdsBytes) return false;
+    // split the reduction when the tiles alone leave most compute units idle
+    const long tiles = (long)g.n * ((g.oh * g.ow + t.bn - 1) / t.bn) * ((g.cout + t.bm - 1) / t.bm);
+    const int nchunks = (g.cin + t.ck - 1) / t.ck;
+    if (tiles < 128 && nchunks >= 4) {
+        int sk = (int)std::min<long>(nchunks / 2, (256 + tiles - 1) / tiles);
+        t.splitk = std::max(1, std::min(sk, 8));
+    }
+    p->fam = FAM_IGEMM;
+    p->tile = t;
+    p->ws_bytes = t.splitk > 1 ? (size_t)t.splitk * g.n * g.cout * g.oh * g.ow * sizeof(float) : 0;
+    return true;
+}
+
+void plan_direct(const ConvGeom& g, Plan* p)
+{
+    const int cout_g = g.cout / g.groups;
+    p->fam = FAM_DIRECT;
+    p->direct_cob = cout_g >= 16 ? 16 : cout_g >= 8 ? 8 : cout_g >= 4 ? 4 : 1;
+    p->ws_bytes = 0;
+}
+
+cvx_status make_plan(const ConvGeom& g, Plan* p)
+{
+    *p = Plan{};
+    if (plan_depthwise(g, p)) return CVX_OK;
+    if (plan_igemm(g, p)) return CVX_OK;
+    plan_direct(g, p);
+    const int cout_g = g.cout / g.groups;
+    if ((long)g.groups * ((cout_g + p->direct_cob - 1) / p->direct_cob) > 65535)
+        return CVX_ERR_UNSUPPORTED;
+    return CVX_OK;
+}
+
+cvx_status launch_conv(const ConvGeom& g, const Plan& p, const float* x, const float* w,
+                       const float* scale, const float* bias, const float* res, float* y, void* ws,
+                       hipStream_t s)
+{
+    hipError_t e = hipSuccess;
+    switch (p.fam) {
+    case FAM_DEPTHWISE: e = launch_depthwise(g, p, x, w, scale, bias, res, y, s); break;
+    case FAM_DIRECT: e = launch_direct(g, p, x, w, scale, bias, res, y, s); break;
+    case FAM_IGEMM: e = launch_igemm(g, p, x, w, scale, bias, res, y, ws, s); break;
+    }
+    return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
+}
+
+size_t elems_in(const ConvGeom& g) { return (size_t)g.n * g.cin * g.h * g.w; }
+size_t elems_out(const ConvGeom& g) { return (size_t)g.n * g.cout * g.oh * g.ow; }
+size_t elems_w(const ConvGeom& g) { return (size_t)g.cout * (g.cin / g.groups) * g.k * g.k; }
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* cvx_status_str(cvx_status s)
+{
+    switch (s) {
+    case CVX_OK: return "ok";
+    case CVX_ERR_NULL: return "a required pointer is NULL";
+    case CVX_ERR_SHAPE: return "sizes are non-positive, inconsistent or too large";
+    case CVX_ERR_UNSUPPORTED: return "convolution not implemented by this library";
+    case CVX_ERR_ALIGN: return "a tensor pointer is not 4-byte aligned";
+    case CVX_ERR_ALIAS: return "the output overlaps an input";
+    case CVX_ERR_WORKSPACE: return "workspace missing or too small";
+    case CVX_ERR_HIP: return "HIP runtime error on launch";
+    case CVX_ERR_ARG: return "enum or index argument out of range";
+    default: return "unknown status";
+    }
+}
+
+const char* cvx_version(void) { return "cvx 0.1 gfx950"; }
+
+cvx_status cvx_conv_out_shape(const cvx_conv_desc* d, int* oh, int* ow)
+{
+    if (oh == nullptr || ow == nullptr) return CVX_ERR_NULL;
+    ConvGeom g;
+    cvx_status st = geom_from_desc(d, &g);
+    if (st != CVX_OK) return st;
+    Plan p;
+    st = make_plan(g, &p);
+    if (st != CVX_OK) return st;
+    *oh = g.oh;
+    *ow = g.ow;
+    return CVX_OK;
+}
+
+cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
+{
+    if (buf == nullptr || buf_len < 1) return CVX_ERR_NULL;
+    ConvGeom g;
+    cvx_status st = geom_from_desc(d, &g);
+    if (st != CVX_OK) return st;
+    Plan p;
+    st = make_plan(g, &p);
+    if (st != CVX_OK) return st;
+    switch (p.fam) {
+    case FAM_DEPTHWISE:
+        snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d kernel=cvx::k_depthwise3x3<%d>",
+                 g.stride, p.dw_ppb, p.dw_toh, g.stride);
+        break;
+    case FAM_DIRECT:
+        snprintf(buf, buf_len, "direct k%d s%d cob=%d kernel=cvx::k_direct<%d>", g.k, g.stride,
+                 p.direct_cob, p.direct_cob);
+        break;
+    case FAM_IGEMM: {
+        const int wm = p.tile.bm == 32 ? 1 : 2, wn = 4 / wm;
+        snprintf(buf, buf_len,
+                 "igemm_mfma k%d s%d bm=%d bn=%d ck=%d splitk=%d kernel=cvx::k_igemm<%d, %d, %d, %d, %d>",
+                 g.k, g.stride, p.tile.bm, p.tile.bn, p.tile.ck, p.tile.splitk, p.tile.bm, p.tile.bn,
+                 wm, wn, g.k);
+        break;
+    }
+    }
+    return CVX_OK;
+}
+
+size_t cvx_conv_workspace_bytes(const cvx_conv_desc* d)
+{
+    ConvGeom g;
+    if (geom_from_desc(d, &g) != CVX_OK) return 0;
+    Plan p;
+    if (make_plan(g, &p) != CVX_OK) return 0;
+    return p.ws_bytes;
+}
+
+cvx_status cvx_fold_bn(const float* gamma, const float* beta, const float* mean, const float* var,
+                       float eps, int c, float* scale, float* bias, void* stream)
+{
+    if (!gamma || !beta || !mean || !var || !scale || !bias) return CVX_ERR_NULL;
+    if (c < 1) return CVX_ERR_SHAPE;
+    if (!(eps > 0.0f)) return CVX_ERR_ARG;
+    for (const void* p : {(const void*)gamma, (const void*)beta, (const void*)mean,
+                          (const void*)var, (const void*)scale, (const void*)bias})
+        if (!aligned4(p)) return CVX_ERR_ALIGN;
+    const size_t b = (size_t)c * sizeof(float);
+    const Range outs[2] = {span(scale, b), span(bias, b)};
+    if (overlap(outs[0], outs[1])) return CVX_ERR_ALIAS;
+    for (const float* in : {gamma, beta, mean, var})
+        for (const Range& o : outs)
+            if (overlap(o, span(in, b))) return CVX_ERR_ALIAS;
+    hipError_t e = launch_fold_bn(gamma, beta, mean, var, eps, c, scale, bias,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
+}
+
+cvx_status cvx_conv_bn_act(const cvx_conv_desc* d, const float* x, const float* w,
+                           const float* scale, const float* bias, const float* residual, float* y,
+                           void* workspace, size_t ws_bytes, void* stream)
+{
+    ConvGeom g;
+    cvx_status st = geom_from_desc(d, &g);
+    if (st != CVX_OK) return st;
+    if (!x || !w || !scale || !bias || !y) return CVX_ERR_NULL;
+    if (g.res_mode != CVX_RES_NONE && residual == nullptr) return CVX_ERR_NULL;
+    const float* res = g.res_mode != CVX_RES_NONE ? residual : nullptr;
+    for (const void* p : {(const void*)x, (const void*)w, (const void*)scale, (const void*)bias,
+                          (const void*)y})
+        if (!aligned4(p)) return CVX_ERR_ALIGN;
+    if (res && !aligned4(res)) return CVX_ERR_ALIGN;
+    Plan p;
+    st = make_plan(g, &p);
+    if (st != CVX_OK) return st;
+    const Range yr = span(y, elems_out(g) * sizeof(float));
+    if (overlap(yr, span(x, elems_in(g) * sizeof(float))) ||
+        overlap(yr, span(w, elems_w(g) * sizeof(float))) ||
+        overlap(yr, span(scale, g.cout * sizeof(float))) ||
+        overlap(yr, span(bias, g.cout * sizeof(float))) ||
+        (res && overlap(yr, span(res, elems_out(g) * sizeof(float)))))
+        return CVX_ERR_ALIAS;
+    if (p.ws_bytes > 0) {
+        if (workspace == nullptr || ws_bytes < p.ws_bytes) return CVX_ERR_WORKSPACE;
+        if (!aligned4(workspace)) return CVX_ERR_ALIGN;
+        const Range wr = span(workspace, p.ws_bytes);
+        if (overlap(wr, yr) || overlap(wr, span(x, elems_in(g) * sizeof(float))) ||
+            overlap(wr, span(w, elems_w(g) * sizeof(float))) ||
+            (res && overlap(wr, span(res, elems_out(g) * sizeof(float)))))
+            return CVX_ERR_ALIAS;
+    }
+    return launch_conv(g, p, x, w, scale, bias, res, y, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+cvx_status cvx_preprocess_u8(const unsigned char* src, int n, int src_h, int src_w,
+                             long src_row_bytes, float* dst, int dst_h, int dst_w,
+                             const float* mean, const float* stdv, void* stream)
+{
+    if (!src || !dst || !mean || !stdv) return CVX_ERR_NULL;
+    if (n < 1 || n > 65535 || src_h < 1 || src_w < 1 || dst_h < 1 || dst_w < 1)
+        return CVX_ERR_SHAPE;
+    if (src_row_bytes < 3L * src_w) return CVX_ERR_SHAPE;
+    if ((long)n * 3 * dst_h * dst_w > kMaxElems) return CVX_ERR_SHAPE;
+    if (!aligned4(dst)) return CVX_ERR_ALIGN;
+    for (int c = 0; c < 3; ++c)
+        if (!(stdv[c] != 0.0f)) return CVX_ERR_ARG;
+    const size_t src_bytes = (size_t)n * src_h * src_row_bytes;
+    if (overlap(span(dst, (size_t)n * 3 * dst_h * dst_w * sizeof(float)), span(src, src_bytes)))
+        return CVX_ERR_ALIAS;
+    hipError_t e = launch_preprocess(src, n, src_h, src_w, src_row_bytes, dst, dst_h, dst_w, mean,
+                                     stdv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
+}
+
+cvx_status cvx_gap_fc(const float* x, int n, int c, int h, int w, const float* fc_w,
+                      const float* fc_b, int out_f, float* out, void* stream)
+{
+    if (!x || !fc_w || !fc_b || !out) return CVX_ERR_NULL;
+    if (n < 1 || n > 65535 || c < 1 || c > 4096 || h < 1 || w < 1 || out_f < 1)
+        return CVX_ERR_SHAPE;
+    if ((long)n * c * h * w > kMaxElems) return CVX_ERR_SHAPE;
+    for (const void* p : {(const void*)x, (const void*)fc_w, (const void*)fc_b, (const void*)out})
+        if (!aligned4(p)) return CVX_ERR_ALIGN;
+    const Range o = span(out, (size_t)n * out_f * sizeof(float));
+    if (overlap(o, span(x, (size_t)n * c * h * w * sizeof(float))) ||
+        overlap(o, span(fc_w, (size_t)out_f * c * sizeof(float))) ||
+        overlap(o, span(fc_b, (size_t)out_f * sizeof(float))))
+        return CVX_ERR_ALIAS;
+    hipError_t e = launch_gap_fc(x, n, c, h * w, fc_w, fc_b, out_f, out,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ============================================================ layer lists
+namespace {
+
+struct Shape {
+    int n, c, h, w;
+    size_t elems() const { return (size_t)n * c * h * w; }
+};
+
+struct NodePlan {
+    Shape in, out;
+    ConvGeom g;
+    Plan p;
+    bool fuse_next;      // GAP whose only reader is the following FC: run as one kernel
+    bool skipped;        // FC folded into the preceding GAP
+    int last_use;        // last layer index reading this output
+    size_t offset;       // workspace offset of the output (non-final layers)
+};
+
+struct ListPlan {
+    std::vector<NodePlan> nodes;
+    Shape input;
+    bool input_u8;
+    size_t act_bytes;    // activation region
+    size_t layer_ws;     // largest per-layer workspace (after the activations)
+    size_t total() const { return act_bytes + layer_ws; }
+};
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
+{
+    if (L == nullptr) return CVX_ERR_NULL;
+    if (nl < 1 || nl > 4096) return CVX_ERR_SHAPE;
+    lp->nodes.assign(nl, NodePlan{});
+    lp->input_u8 = L[0].kind == CVX_L_PREPROC;
+    bool have_input = false;
+    auto input_shape = [&](const Shape& s) -> bool {
+        if (!have_input) {
+            lp->input = s;
+            have_input = true;
+            return true;
+        }
+        return lp->input.n == s.n && lp->input.c == s.c && lp->input.h == s.h &&
+               lp->input.w == s.w;
+    };
+    for (int i = 0; i < nl; ++i) {
+        const cvx_layer& l = L[i];
+        NodePlan& np = lp->nodes[i];
+        np.last_use = i;
+        if (l.kind < CVX_L_CONV || l.kind > CVX_L_PREPROC) return CVX_ERR_ARG;
+        if (l.in < CVX_INPUT || l.in >= i) return CVX_ERR_ARG;
+        if (l.kind == CVX_L_PREPROC) {
+            if (i != 0 || l.in != CVX_INPUT) return CVX_ERR_ARG;
+            const cvx_conv_desc& d = l.conv;
+            if (d.n < 1 || d.n > 65535 || d.h < 1 || d.w < 1 || l.dst_h < 1 || l.dst_w < 1)
+                return CVX_ERR_SHAPE;
+            if ((long)d.n * 3 * l.dst_h * l.dst_w > kMaxElems) return CVX_ERR_SHAPE;
+            for (int c = 0; c < 3; ++c)
+                if (!(l.std[c] != 0.0f)) return CVX_ERR_ARG;
+            lp->input = {d.n, 3, d.h, d.w};  // u8 frames [n][h][w][3]
+            have_input = true;
+            np.in = lp->input;
+            np.out = {d.n, 3, l.dst_h, l.dst_w};
+            continue;
+        }
+        if (l.in == CVX_INPUT && lp->input_u8) return CVX_ERR_ARG;  // raw frames feed only layer 0
+        Shape in = l.in == CVX_INPUT ? Shape{l.conv.n, l.conv.c_in, l.conv.h, l.conv.w}
+                                     : lp->nodes[l.in].out;
+        if (l.in == CVX_INPUT && !input_shape(in)) return CVX_ERR_SHAPE;
+        if (l.in >= 0) lp->nodes[l.in].last_use = i;
+        np.in = in;
+        if (l.kind == CVX_L_CONV) {
+            const cvx_conv_desc& d = l.conv;
+            if (d.n != in.n || d.c_in != in.c || d.h != in.h || d.w != in.w) return CVX_ERR_SHAPE;
+            cvx_status st = geom_from_desc(&d, &np.g);
+            if (st != CVX_OK) return st;
+            st = make_plan(np.g, &np.p);
+            if (st != CVX_OK) return st;
+            if (!l.w || !l.scale || !l.bias) return CVX_ERR_NULL;
+            np.out = {d.n, d.c_out, np.g.oh, np.g.ow};
+            if (d.res_mode != CVX_RES_NONE) {
+                if (l.res < CVX_INPUT || l.res >= i) return CVX_ERR_ARG;
+                Shape r = l.res == CVX_INPUT ? lp->input : lp->nodes[l.res].out;
+                if (l.res == CVX_INPUT && (!have_input || lp->input_u8)) return CVX_ERR_ARG;
+                if (r.n != np.out.n || r.c != np.out.c || r.h != np.out.h || r.w != np.out.w)
+                    return CVX_ERR_SHAPE;
+                if (l.res >= 0) lp->nodes[l.res].last_use = i;
+            } else if (l.res != CVX_NO_RES) {
+                return CVX_ERR_ARG;
+            }
+        } else if (l.kind == CVX_L_GAP) {
+            if (l.conv.n != in.n || l.conv.c_in != in.c || l.conv.h != in.h || l.conv.w != in.w)
+                return CVX_ERR_SHAPE;
+            if (in.c > 4096) return CVX_ERR_SHAPE;
+            np.out = {in.n, in.c, 1, 1};
+        } else {  // FC
+            if (in.h != 1 || in.w != 1 || l.conv.n != in.n || l.conv.c_in != in.c)
+                return CVX_ERR_SHAPE;
+            if (l.conv.c_out < 1 || in.c > 4096) return CVX_ERR_SHAPE;
+            if (!l.w || !l.bias) return CVX_ERR_NULL;
+            np.out = {in.n, l.conv.c_out, 1, 1};
+        }
+    }
+    if (!have_input) return CVX_ERR_ARG;
+    // GAP immediately followed by its only reader, an FC: one kernel
+    for (int i = 0; i + 1 < nl; ++i) {
+        if (L[i].kind == CVX_L_GAP && L[i + 1].kind == CVX_L_FC && L[i + 1].in == i &&
+            lp->nodes[i].last_use == i + 1) {
+            lp->nodes[i].fuse_next = true;
+            lp->nodes[i + 1].skipped = true;
+        }
+    }
+    // first-fit placement of intermediate outputs over their live ranges
+    lp->act_bytes = 0;
+    lp->layer_ws = 0;
+    std::vector<int> placed;
+    for (int i = 0; i < nl - 1; ++i) {
+        NodePlan& np = lp->nodes[i];
+        if (np.fuse_next) {  // pooled vector never materialised
+            np.offset = 0;
+            continue;
+        }
+        const size_t sz = round_up(np.out.elems() * sizeof(float));
+        std::vector<std::pair<size_t, size_t>> busy;
+        for (int j : placed) {
+            const NodePlan& o = lp->nodes[j];
+            if (o.last_use >= i)  // live while layer i writes
+                busy.push_back({o.offset, o.offset + round_up(o.out.elems() * sizeof(float))});
+        }
+        std::sort(busy.begin(), busy.end());
+        size_t off = 0;
+        for (auto& b : busy) {
+            if (off + sz <= b.first) break;
+            off = std::max(off, b.second);
+        }
+        np.offset = off;
+        lp->act_bytes = std::max(lp->act_bytes, off + sz);
+        placed.push_back(i);
+    }
+    for (int i = 0; i < nl; ++i)
+        if (L[i].kind == CVX_L_CONV) lp->layer_ws = std::max(lp->layer_ws, lp->nodes[i].p.ws_bytes);
+    lp->act_bytes = round_up(lp->act_bytes);
+    return CVX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cvx_status cvx_forward_out_shape(const cvx_layer* layers, int n_layers, int out_shape[4])
+{
+    if (out_shape == nullptr) return CVX_ERR_NULL;
+    ListPlan lp;
+    cvx_status st = plan_list(layers, n_layers, &lp);
+    if (st != CVX_OK) return st;
+    const Shape& o = lp.nodes.back().out;
+    out_shape[0] = o.n;
+    out_shape[1] = o.c;
+    out_shape[2] = o.h;
+    out_shape[3] = o.w;
+    return CVX_OK;
+}
+
+size_t cvx_forward_workspace_bytes(const cvx_layer* layers, int n_layers, cvx_status* status)
+{
+    ListPlan lp;
+    cvx_status st = plan_list(layers, n_layers, &lp);
+    if (status) *status = st;
+    return st == CVX_OK ? lp.total() : 0;
+}
+
+cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input, float* output,
+                       void* workspace, size_t ws_bytes, void* stream)
+{
+    ListPlan lp;
+    cvx_status st = plan_list(layers, n_layers, &lp);
+    if (st != CVX_OK) return st;
+    if (!input || !output) return CVX_ERR_NULL;
+    if (!aligned4(output) || (!lp.input_u8 && !aligned4(input))) return CVX_ERR_ALIGN;
+    const size_t need = lp.total();
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return CVX_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return CVX_ERR_ALIGN;
+    }
+    const size_t in_bytes = lp.input_u8 ? (size_t)lp.input.n * lp.input.h * lp.input.w * 3
+                                        : lp.input.elems() * sizeof(float);
+    const Range out_r = span(output, lp.nodes.back().out.elems() * sizeof(float));
+    if (overlap(out_r, span(input, in_bytes))) return CVX_ERR_ALIAS;
+    if (need > 0 && (overlap(out_r, span(workspace, need)) ||
+                     overlap(span(input, in_bytes), span(workspace, need))))
+        return CVX_ERR_ALIAS;
+    for (int i = 0; i < n_layers; ++i) {
+        const cvx_layer& l = layers[i];
+        if (l.kind == CVX_L_CONV) {
+            for (const void* p : {(const void*)l.w, (const void*)l.scale, (const void*)l.bias})
+                if (!aligned4(p)) return CVX_ERR_ALIGN;
+            const NodePlan& np = lp.nodes[i];
+            // weights must not overlap anything the list writes
+            const Range wr = span(l.w, elems_w(np.g) * sizeof(float));
+            if (overlap(wr, out_r) || (need > 0 && overlap(wr, span(workspace, need))))
+                return CVX_ERR_ALIAS;
+        } else if (l.kind == CVX_L_FC) {
+            if (!aligned4(l.w) || !aligned4(l.bias)) return CVX_ERR_ALIGN;
+        }
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    auto out_ptr = [&](int i) -> float* {
+        return i == n_layers - 1 ? output : reinterpret_cast<float*>(ws + lp.nodes[i].offset);
+    };
+    auto in_ptr = [&](int i) -> const float* {
+        return i == CVX_INPUT ? static_cast<const float*>(input) : out_ptr(i);
+    };
+    void* layer_ws = ws ? ws + lp.act_bytes : nullptr;
+    for (int i = 0; i < n_layers; ++i) {
+        const cvx_layer& l = layers[i];
+        const NodePlan& np = lp.nodes[i];
+        if (np.skipped) continue;
+        hipError_t e = hipSuccess;
+        cvx_status cs = CVX_OK;
+        switch (l.kind) {
+        case CVX_L_PREPROC:
+            e = launch_preprocess(static_cast<const unsigned char*>(input), np.in.n, np.in.h,
+                                  np.in.w, 3L * np.in.w, out_ptr(i), l.dst_h, l.dst_w, l.mean,
+                                  l.std, s);
+            break;
+        case CVX_L_CONV: {
+            const float* res = l.conv.res_mode != CVX_RES_NONE ? in_ptr(l.res) : nullptr;
+            cs = launch_conv(np.g, np.p, in_ptr(l.in), l.w, l.scale, l.bias, res, out_ptr(i),
+                             layer_ws, s);
+            break;
+        }
+        case CVX_L_GAP:
+            if (np.fuse_next) {
+                const cvx_layer& fc = layers[i + 1];
+                e = launch_gap_fc(in_ptr(l.in), np.in.n, np.in.c, np.in.h * np.in.w, fc.w, fc.bias,
+                                  fc.conv.c_out, out_ptr(i + 1), s);
+            } else {
+                e = launch_gap_fc(in_ptr(l.in), np.in.n, np.in.c, np.in.h * np.in.w, nullptr,
+                                  nullptr, 0, out_ptr(i), s);
+            }
+            break;
+        case CVX_L_FC:
+            e = launch_gap_fc(in_ptr(l.in), np.in.n, np.in.c, 1, l.w, l.bias, l.conv.c_out,
+                              out_ptr(i), s);
+            break;
+        }
+        if (e != hipSuccess) return CVX_ERR_HIP;
+        if (cs != CVX_OK) return cs;
+    }
+    return CVX_OK;
+}
+
+}  // extern "C"

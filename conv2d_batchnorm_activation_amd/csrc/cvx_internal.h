@@ -1,0 +1,75 @@
+// cvx_internal.h -- declarations shared by the host dispatcher and the kernel
+// translation units of libcvx.  Not part of the public ABI (include/cvx.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "cvx.h"
+
+namespace cvx {
+
+// Kernel families.  The dispatcher picks one per layer shape.
+enum Family : int {
+    FAM_DEPTHWISE = 0,  // depthwise 3x3 direct kernel, LDS halo tile per plane
+    FAM_DIRECT = 1,     // direct VALU kernel (tiny c_in stems, grouped, large k)
+    FAM_IGEMM = 2,      // implicit GEMM on fp32 MFMA (dense 1x1 and 3x3)
+};
+
+// Geometry of one convolution, derived from a validated cvx_conv_desc.
+struct ConvGeom {
+    int n, cin, h, w, cout, k, stride, pad, groups, act, res_mode;
+    int oh, ow;
+};
+
+// Tile configuration for the implicit-GEMM family.
+struct GemmTile {
+    int bm, bn;       // output tile: bm output channels x bn output pixels
+    int ck;           // input channels staged per K chunk
+    int splitk;       // number of K slices (1 = no split); >1 uses the workspace
+};
+
+struct Plan {
+    Family fam;
+    GemmTile tile;     // FAM_IGEMM only
+    int dw_ppb;        // FAM_DEPTHWISE: planes per workgroup
+    int dw_toh;        // FAM_DEPTHWISE: output rows per workgroup
+    int direct_cob;    // FAM_DIRECT: output channels per thread
+    size_t ws_bytes;   // workspace the plan needs
+};
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are validated by the
+// caller; the launchers assume shapes match the kernels' grid assumptions.
+hipError_t launch_fold_bn(const float* gamma, const float* beta, const float* mean,
+                          const float* var, float eps, int c, float* scale, float* bias,
+                          hipStream_t s);
+
+hipError_t launch_depthwise(const ConvGeom& g, const Plan& p, const float* x, const float* w,
+                            const float* scale, const float* bias, const float* res, float* y,
+                            hipStream_t s);
+
+hipError_t launch_direct(const ConvGeom& g, const Plan& p, const float* x, const float* w,
+                         const float* scale, const float* bias, const float* res, float* y,
+                         hipStream_t s);
+
+hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const float* w,
+                        const float* scale, const float* bias, const float* res, float* y,
+                        void* ws, hipStream_t s);
+
+hipError_t launch_gap_fc(const float* x, int n, int c, int hw, const float* fc_w,
+                         const float* fc_b, int out_f, float* out, hipStream_t s);
+
+hipError_t launch_preprocess(const unsigned char* src, int n, int src_h, int src_w,
+                             long src_row_bytes, float* dst, int dst_h, int dst_w,
+                             const float mean[3], const float stdv[3], hipStream_t s);
+
+// igemm helpers used by the planner (defined next to the kernel).
+int igemm_rows_max(const ConvGeom& g, int bn);
+size_t igemm_lds_bytes(const ConvGeom& g, const GemmTile& t);
+bool igemm_tile_supported(const GemmTile& t);
+
+constexpr size_t kMaxLdsBytes = 64 * 1024;
+
+}  // namespace cvx

@@ -1,0 +1,221 @@
+/*
+ * cvx.h -- C ABI of libcvx: fused convolution + folded BatchNorm + activation
+ * for AMD MI355X (gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are fp32, dense and contiguous.  Activations are NCHW: element
+ *    (n, c, h, w) sits at n*C*H*W + c*H*W + h*W + w ("YOLO26N Inference
+ *    Optimisation", section "NHWC migration", "What NHWC is and why it matters").
+ *    Convolution weights are OIHW: [c_out][c_in/groups][kh][kw], the order the
+ *    MNIST page's PyTorch weights use ("Как я свертки ускорял", "Ускоряем скорость").
+ *  - Every tensor pointer is a DEVICE pointer (HBM), 4-byte aligned, unless the
+ *    argument says "host".  The caller owns all memory; the library borrows the
+ *    pointers until the work it enqueued has finished, keeps no reference and
+ *    never allocates device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    enqueued asynchronously; no call synchronises the device or the stream.
+ *  - Errors are returned as cvx_status codes.  All argument validation happens on
+ *    the host before anything is enqueued, so an error return means nothing was
+ *    launched (except CVX_ERR_HIP, which reports a failed launch).
+ *  - Calls are thread-safe: the library has no mutable global state.
+ */
+#ifndef CVX_H
+#define CVX_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbol (the library is built with hidden default visibility). */
+#define CVX_API __attribute__((visibility("default")))
+
+typedef int cvx_status;
+
+enum {
+    CVX_OK = 0,
+    CVX_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    CVX_ERR_SHAPE = -2,       /* sizes are non-positive, inconsistent or too large */
+    CVX_ERR_UNSUPPORTED = -3, /* valid convolution this library does not implement */
+    CVX_ERR_ALIGN = -4,       /* a tensor pointer is not 4-byte aligned            */
+    CVX_ERR_ALIAS = -5,       /* the output overlaps an input                      */
+    CVX_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required           */
+    CVX_ERR_HIP = -7,         /* the HIP runtime reported an error on launch       */
+    CVX_ERR_ARG = -8          /* an enum or index argument is out of range         */
+};
+
+/* Activation applied in the epilogue. ReLU = max(0, v) ("Как я свертки ускорял",
+ * "А теперь — хардкор на Metal", step 4); SiLU = v / (1 + exp(-v)) (the
+ * activation of the fused kernels in "YOLO26N Inference Optimisation",
+ * "nsys kernel-level breakdown"). */
+enum { CVX_ACT_NONE = 0, CVX_ACT_RELU = 1, CVX_ACT_SILU = 2 };
+
+/* Where the optional residual r is added, with z = scale*conv + bias:
+ *   CVX_RES_BEFORE_ACT: y = act(z + r)  -- the MNIST block adds its shortcut
+ *                       before the final ReLU ("Как я свертки ускорял",
+ *                       "Пациента на стол");
+ *   CVX_RES_AFTER_ACT : y = act(z) + r  -- the residual add that followed the
+ *                       fused conv+BN+SiLU kernel ("YOLO26N Inference
+ *                       Optimisation", "Improvements", #7, now in the epilogue). */
+enum { CVX_RES_NONE = 0, CVX_RES_BEFORE_ACT = 1, CVX_RES_AFTER_ACT = 2 };
+
+/* One convolution layer.  Output extent: oh = (h + 2*pad - kh)/stride + 1 (floor),
+ * likewise ow.  Supported: 1 <= kh, kw <= 7, 1 <= stride <= 4, 0 <= pad < k,
+ * groups dividing c_in and c_out; dilation 1.  n*c*h*w of every tensor must stay
+ * below 2^31 elements. */
+typedef struct cvx_conv_desc {
+    int n, c_in, h, w;   /* input  [n][c_in][h][w]                 */
+    int c_out, kh, kw;   /* weight [c_out][c_in/groups][kh][kw]    */
+    int stride, pad;     /* same in both spatial dimensions        */
+    int groups;          /* 1 = dense; c_in = c_out = groups: depthwise */
+    int act;             /* CVX_ACT_*                              */
+    int res_mode;        /* CVX_RES_*                              */
+} cvx_conv_desc;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+CVX_API const char *cvx_status_str(cvx_status s);
+
+/* Library version string, e.g. "cvx 0.1 gfx950" (static storage). */
+CVX_API const char *cvx_version(void);
+
+/* Host-only query: output extent of `d`.  Validates `d` exactly as
+ * cvx_conv_bn_act does (without pointers).  Touches no GPU. */
+CVX_API cvx_status cvx_conv_out_shape(const cvx_conv_desc *d, int *oh, int *ow);
+
+/* Host-only query: which kernel family and tile configuration the dispatcher
+ * selects for `d` ("YOLO26N Inference Optimisation", "Improvements", #1 and #3:
+ * one code path whose tile parameters are chosen per layer shape).  Writes a
+ * short NUL-terminated description into buf (at most buf_len bytes). */
+CVX_API cvx_status cvx_conv_plan(const cvx_conv_desc *d, char *buf, int buf_len);
+
+/* Workspace bytes cvx_conv_bn_act needs for `d` (0 when the selected kernel
+ * needs none).  Host-only. */
+CVX_API size_t cvx_conv_workspace_bytes(const cvx_conv_desc *d);
+
+/*
+ * cvx_fold_bn -- fold inference BatchNorm into a per-channel affine map:
+ *     scale[i] = gamma[i] / sqrt(var[i] + eps),  bias[i] = beta[i] - mean[i]*scale[i]
+ * so that BN(v) = scale*v + bias.  The BatchNorm form is (v - mean)/sqrt(var + eps)
+ * * gamma + beta ("Как я свертки ускорял", "А теперь — хардкор на Metal", step 4);
+ * folding it before inference is the "weight folding" of "YOLO26N Inference
+ * Optimisation", "Baseline benchmark".  Weights are left untouched: scale and bias
+ * are applied in the convolution epilogue.
+ *   gamma, beta, mean, var : device, [c] each, read only.
+ *   scale, bias            : device, [c] each, written.  Must not overlap the inputs.
+ *   eps > 0; c >= 1.
+ */
+CVX_API cvx_status cvx_fold_bn(const float *gamma, const float *beta, const float *mean,
+                       const float *var, float eps, int c, float *scale, float *bias,
+                       void *stream);
+
+/*
+ * cvx_conv_bn_act -- one fused layer:
+ *     z[n][co][oh][ow] = scale[co] * sum_{ci,i,j} x[n][g*Cg+ci][oh*s-p+i][ow*s-p+j]
+ *                                     * w[co][ci][i][j]  +  bias[co]
+ *     y = act(z [+ r]) [+ r]        (placement of r by d->res_mode)
+ * a zero-padded cross-correlation ("Как я свертки ускорял", "А теперь — хардкор на
+ * Metal", steps 2-5: window origin = output position * stride - pad, out-of-image
+ * taps read as zero, BN and the activation applied while the sum is still in
+ * registers, one store per output), in one launch per layer (or two when the
+ * selected plan splits the reduction; then the workspace holds the partial sums).
+ *   d        : host, layer description.
+ *   x        : device [n][c_in][h][w].
+ *   w        : device [c_out][c_in/groups][kh][kw].
+ *   scale,bias: device [c_out] (from cvx_fold_bn).
+ *   residual : device [n][c_out][oh][ow]; required iff d->res_mode != CVX_RES_NONE,
+ *              may equal x (read only) but must not overlap y.
+ *   y        : device [n][c_out][oh][ow]; must not overlap x, w, scale, bias, residual.
+ *              Only the n*c_out*oh*ow elements are written (no row padding).
+ *   workspace: device scratch of cvx_conv_workspace_bytes(d) bytes (may be NULL when
+ *              that is 0); contents on entry are ignored.
+ */
+CVX_API cvx_status cvx_conv_bn_act(const cvx_conv_desc *d, const float *x, const float *w,
+                           const float *scale, const float *bias, const float *residual,
+                           float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * cvx_preprocess_u8 -- stem prologue in one pass: u8 HWC RGB frames ->
+ * bilinear resize with half-pixel centres (source coordinate
+ * s = (d + 0.5) * src/dst - 0.5, clamped below at 0; the upper neighbour clamped
+ * to the last row/column) -> v/255 -> (v - mean[c]) / std[c] -> fp32 CHW.
+ * The u8 frame is read once and the fp32 tensor written once; interpolated values
+ * are not rounded back to u8 ("A fused Ampere preprocess kernel", "The theory"
+ * and "My notes from Day 7": the resize is the half-pixel bilinear function).
+ *   src          : device, n frames, frame b at src + b*src_h*src_row_bytes,
+ *                  pixel (y, x) channel c at + y*src_row_bytes + 3*x + c.
+ *   src_row_bytes: >= 3*src_w.
+ *   dst          : device [n][3][dst_h][dst_w].
+ *   mean, std    : HOST arrays of 3 floats; std[c] != 0.
+ */
+CVX_API cvx_status cvx_preprocess_u8(const unsigned char *src, int n, int src_h, int src_w,
+                             long src_row_bytes, float *dst, int dst_h, int dst_w,
+                             const float *mean, const float *std, void *stream);
+
+/*
+ * cvx_gap_fc -- classifier tail: v[b][c] = mean over the h*w plane of x[b][c];
+ * out[b][o] = sum_c fc_w[o][c] * v[b][c] + fc_b[o] ("Как я свертки ускорял",
+ * "Пациента на стол": average pool to 1x1, flatten, Linear).  One launch.
+ *   x: device [n][c][h][w]; fc_w: device [out_f][c]; fc_b: device [out_f];
+ *   out: device [n][out_f], must not overlap the inputs.
+ */
+CVX_API cvx_status cvx_gap_fc(const float *x, int n, int c, int h, int w, const float *fc_w,
+                      const float *fc_b, int out_f, float *out, void *stream);
+
+/* ---------------------------------------------------------------- layer lists */
+enum {
+    CVX_L_CONV = 0,    /* cvx_conv_bn_act                                    */
+    CVX_L_GAP = 1,     /* global average pool: [n][c][h][w] -> [n][c][1][1]   */
+    CVX_L_FC = 2,      /* fc on [n][c][1][1] -> [n][c_out][1][1] (w, bias)   */
+    CVX_L_PREPROC = 3  /* cvx_preprocess_u8; only as layer 0 on the raw input */
+};
+
+#define CVX_INPUT (-1)  /* `in` / `res` index meaning the network input */
+#define CVX_NO_RES (-2) /* `res` index meaning no residual               */
+
+typedef struct cvx_layer {
+    int kind;              /* CVX_L_*                                              */
+    int in;                /* index of the layer whose output this reads; CVX_INPUT */
+    int res;               /* residual source index, CVX_INPUT, or CVX_NO_RES       */
+    cvx_conv_desc conv;    /* CONV: full description; GAP: n, c_in, h, w;
+                              FC: n, c_in (in features), c_out; PREPROC: n, and
+                              h, w = source frame height and width                */
+    const float *w;        /* CONV: OIHW weights; FC: [c_out][c_in] (device)       */
+    const float *scale;    /* CONV: folded scale [c_out] (device)                  */
+    const float *bias;     /* CONV: folded bias [c_out]; FC: bias [c_out] (device) */
+    int dst_h, dst_w;      /* PREPROC: output extent                               */
+    float mean[3], std[3]; /* PREPROC: per-channel normalisation (by value)        */
+} cvx_layer;
+
+/* Output shape [n][c][h][w] of the last layer of a list (host only; validates
+ * the whole list: every `in`/`res` index must name an earlier layer or the
+ * input, shapes must chain, residual shapes must equal output shapes). */
+CVX_API cvx_status cvx_forward_out_shape(const cvx_layer *layers, int n_layers, int out_shape[4]);
+
+/* Workspace bytes cvx_forward needs: intermediate activations (each 256-byte
+ * aligned, reused once no later layer reads them) plus the largest per-layer
+ * workspace.  Host only.  Returns 0 and sets *status on an invalid list when
+ * status != NULL. */
+CVX_API size_t cvx_forward_workspace_bytes(const cvx_layer *layers, int n_layers, cvx_status *status);
+
+/*
+ * cvx_forward -- run an ordered layer list on one stream, with no host
+ * synchronisation: layer i reads the output of layer `in` (and the residual from
+ * layer `res`), so a list expresses chains and the MNIST block's shortcut.  The
+ * last layer writes `output`; the others write into `workspace`.  This is the
+ * whole-network launch sequence the pages replay per inference ("YOLO26N
+ * Inference Optimisation", "Baseline benchmark" and "nsys kernel-level
+ * breakdown": kernels, not copies, take the time).
+ *   input : device; fp32 NCHW, or u8 NHWC frames when layer 0 is CVX_L_PREPROC.
+ *   output: device, shape from cvx_forward_out_shape; must not overlap input/workspace.
+ *   workspace: device, >= cvx_forward_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+CVX_API cvx_status cvx_forward(const cvx_layer *layers, int n_layers, const void *input, float *output,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CVX_H */

@@ -1,0 +1,253 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/cvx.h declares, and rejects bad arguments on the host before launching
+anything (the error paths return before any HIP call, so they run here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as wl
+from conv2d_batchnorm_activation_amd import cvx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cvx.h")
+
+# fake, never dereferenced device addresses (validation fails before any launch)
+X = 0x10000000
+W = 0x20000000
+S = 0x30000000
+B = 0x30001000
+Y = 0x40000000
+R = 0x50000000
+WS = 0x60000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CVX_API\s+[\w\s\*]*?\b(cvx_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert len(decl) >= 12
+    assert sorted(cvx.EXPORTS) == decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(cvx._LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in cvx.cvx_version()
+    for code in range(-8, 1):
+        assert cvx.cvx_status_str(code)
+    assert cvx.cvx_status_str(-99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(n=1, c_in=64, h=80, w=80, c_out=64, k=3, stride=1, pad=1, groups=1,
+                act=cvx.CVX_ACT_SILU, res_mode=cvx.CVX_RES_NONE)
+    base.update(kw)
+    return cvx.make_desc(**base)
+
+
+def _call(d, x=X, w=W, s=S, b=B, r=None, y=Y, ws=None, ws_bytes=0):
+    return cvx.lib.cvx_conv_bn_act(ctypes.byref(d), x, w, s, b, r, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("h,k,s,p,expect", [
+    (80, 3, 1, 1, 80), (80, 3, 2, 1, 40), (40, 3, 2, 1, 20), (13, 3, 1, 1, 13), (28, 1, 2, 0, 14),
+    (7, 3, 2, 1, 4), (640, 3, 2, 1, 320), (5, 5, 2, 2, 3), (9, 7, 3, 3, 3), (4, 3, 1, 0, 2),
+])
+def test_out_shape(h, k, s, p, expect):
+    assert cvx.cvx_conv_out_shape(_desc(h=h, w=h + 1 if h > 4 else h, k=k, stride=s, pad=p)) == \
+        (expect, (h + 1 + 2 * p - k) // s + 1 if h > 4 else expect)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=0), -2), (dict(c_in=0), -2), (dict(h=-1), -2), (dict(c_out=0), -2),
+    (dict(stride=0), -2), (dict(pad=-1), -2), (dict(groups=0), -2),
+    (dict(groups=3), -2),                         # 64 % 3 != 0
+    (dict(k=9), -3), (dict(stride=5), -3), (dict(pad=3), -3),
+    (dict(h=1, w=1, pad=0), -2),                  # window larger than the image
+    (dict(act=3), -8), (dict(res_mode=7), -8), (dict(act=-1), -8),
+    (dict(n=70000), -2),
+    (dict(n=4096, c_in=1024, h=1024, w=1024), -2),  # > 2^31 elements
+])
+def test_invalid_descriptors_rejected(bad, code):
+    d = _desc(**bad)
+    oh, ow = ctypes.c_int(), ctypes.c_int()
+    assert cvx.lib.cvx_conv_out_shape(ctypes.byref(d), ctypes.byref(oh), ctypes.byref(ow)) == code
+    assert _call(d) == code
+
+
+def test_non_square_kernel_rejected():
+    d = _desc()
+    d.kw = 1
+    assert _call(d) == -3
+
+
+def test_null_pointers_rejected():
+    d = _desc()
+    assert cvx.lib.cvx_conv_bn_act(None, X, W, S, B, None, Y, None, 0, None) == -1
+    for kw in (dict(x=None), dict(w=None), dict(s=None), dict(b=None), dict(y=None)):
+        assert _call(d, **kw) == -1
+    # residual required iff a residual mode is set
+    assert _call(_desc(res_mode=cvx.CVX_RES_AFTER_ACT)) == -1
+
+
+def test_misaligned_pointers_rejected():
+    d = _desc()
+    assert _call(d, x=X + 2) == -4
+    assert _call(d, y=Y + 1) == -4
+    assert _call(_desc(res_mode=cvx.CVX_RES_BEFORE_ACT), r=R + 2) == -4
+
+
+def test_aliasing_rejected():
+    d = _desc()
+    assert _call(d, y=X) == -5                      # y == x
+    assert _call(d, y=X + 4 * 64 * 80 * 80 - 4) == -5  # y starts in x's last element
+    assert _call(d, y=W + 8) == -5
+    assert _call(d, y=S - 4) == -5                  # y's tail covers scale
+    r = _desc(res_mode=cvx.CVX_RES_AFTER_ACT)
+    assert _call(r, r=Y + 4) == -5
+    # residual may equal x (read only), so that is not an aliasing error; a missing
+    # workspace is the next error this split-K shape reports
+    assert _call(r, r=X) == -6
+
+
+def test_workspace_checks():
+    d = _desc(c_in=256, h=20, w=20, c_out=256)      # split-K plan
+    need = cvx.cvx_conv_workspace_bytes(d)
+    assert need > 0
+    assert _call(d) == -6
+    assert _call(d, ws=WS, ws_bytes=need - 4) == -6
+    assert _call(d, ws=Y, ws_bytes=need) == -5      # workspace overlapping the output
+    assert cvx.cvx_conv_workspace_bytes(_desc(groups=64, c_in=64, c_out=64)) == 0
+
+
+def test_fold_bn_validation():
+    f = cvx.lib.cvx_fold_bn
+    assert f(None, X, X + 4096, X + 8192, 1e-5, 16, Y, Y + 4096, None) == -1
+    assert f(X, X + 4096, X + 8192, X + 12288, 1e-5, 0, Y, Y + 4096, None) == -2
+    assert f(X, X + 4096, X + 8192, X + 12288, 0.0, 16, Y, Y + 4096, None) == -8
+    assert f(X, X + 4096, X + 8192, X + 12288, 1e-5, 16, Y, Y + 32, None) == -5
+    assert f(X, X + 4096, X + 8192, X + 12288, 1e-5, 16, X + 4096, Y, None) == -5
+    assert f(X + 1, X + 4096, X + 8192, X + 12288, 1e-5, 16, Y, Y + 4096, None) == -4
+
+
+def test_preprocess_validation():
+    f = cvx.lib.cvx_preprocess_u8
+    m = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    s = (ctypes.c_float * 3)(0.2, 0.2, 0.2)
+    z = (ctypes.c_float * 3)(0.2, 0.0, 0.2)
+    assert f(None, 1, 720, 1280, 3840, Y, 640, 640, m, s, None) == -1
+    assert f(X, 1, 720, 1280, 3840, Y, 640, 640, None, s, None) == -1
+    assert f(X, 0, 720, 1280, 3840, Y, 640, 640, m, s, None) == -2
+    assert f(X, 1, 720, 1280, 3839, Y, 640, 640, m, s, None) == -2
+    assert f(X, 1, 720, 1280, 3840, Y + 2, 640, 640, m, s, None) == -4
+    assert f(X, 1, 720, 1280, 3840, Y, 640, 640, m, z, None) == -8
+    assert f(X, 1, 720, 1280, 3840, X + 100, 640, 640, m, s, None) == -5
+
+
+def test_gap_fc_validation():
+    f = cvx.lib.cvx_gap_fc
+    assert f(X, 1, 192, 7, 7, None, B, 10, Y, None) == -1
+    assert f(X, 1, 5000, 7, 7, W, B, 10, Y, None) == -2
+    assert f(X, 1, 192, 7, 7, W, B, 10, X + 8, None) == -5
+
+
+def _net_layers(wk):
+    """cvx_layer array for a workload, with fake parameter pointers (planning only)."""
+    shapes = []
+    out = []
+    for i, L in enumerate(wk.layers):
+        lay = cvx.cvx_layer()
+        lay.kind, lay.in_, lay.res = L.kind, L.inp, (L.res if L.res_mode else cvx.CVX_NO_RES)
+        s_in = wk.x.shape if L.inp == -1 else shapes[L.inp]
+        if L.kind == wl.KIND_PREPROC:
+            n, h, w, _ = s_in
+            lay.conv = cvx.cvx_conv_desc(n, 3, h, w, 3, 1, 1, 1, 0, 1, 0, 0)
+            lay.dst_h, lay.dst_w = L.dst_h, L.dst_w
+            lay.mean = (ctypes.c_float * 3)(*L.pre_mean)
+            lay.std = (ctypes.c_float * 3)(*L.pre_std)
+            o = (n, 3, L.dst_h, L.dst_w)
+        elif L.kind == wl.KIND_CONV:
+            n, c, h, w = s_in
+            d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode)
+            oh, ow = cvx.cvx_conv_out_shape(d)
+            lay.conv = d
+            lay.w, lay.scale, lay.bias = W + 0x100000 * i, S + 0x1000 * i, B + 0x1000 * i + 0x800
+            o = (n, L.cout, oh, ow)
+        elif L.kind == wl.KIND_GAP:
+            n, c, h, w = s_in
+            lay.conv = cvx.cvx_conv_desc(n, c, h, w, c, 1, 1, 1, 0, 1, 0, 0)
+            o = (n, c, 1, 1)
+        else:
+            n, c = s_in[:2]
+            lay.conv = cvx.cvx_conv_desc(n, c, 1, 1, L.cout, 1, 1, 1, 0, 1, 0, 0)
+            lay.w, lay.bias = W + 0x100000 * i, B + 0x1000 * i
+            o = (n, L.cout, 1, 1)
+        shapes.append(o)
+        out.append(lay)
+    return out, shapes
+
+
+@pytest.mark.parametrize("wk_fn,expect", [
+    (lambda: wl.mnist_cnn(1), (1, 10, 1, 1)),
+    (lambda: wl.mnist_cnn(256), (256, 10, 1, 1)),
+    (lambda: wl.detector_stem(), (1, 32, 160, 160)),
+    (lambda: wl.detector_pipeline(1), (1, 256, 20, 20)),
+    (lambda: wl.detector_pipeline(8), (8, 256, 20, 20)),
+])
+def test_forward_shapes_and_workspace(wk_fn, expect):
+    wk = wk_fn()
+    layers, shapes = _net_layers(wk)
+    assert cvx.cvx_forward_out_shape(layers) == expect
+    ws = cvx.cvx_forward_workspace_bytes(layers)
+    inter = [s for s in shapes[:-1]]
+    largest = max(4 * s[0] * s[1] * s[2] * s[3] for s in inter)
+    total = sum(4 * s[0] * s[1] * s[2] * s[3] for s in inter)
+    # liveness-based reuse: at least the largest intermediate, at most all of them
+    # (plus alignment) and any split-K partials
+    assert ws >= largest
+    assert ws <= total + 256 * len(inter) + max(
+        cvx.cvx_conv_workspace_bytes(l.conv) if l.kind == 0 else 0 for l in layers)
+
+
+def test_forward_list_validation():
+    wk = wl.mnist_cnn(1)
+    layers, _ = _net_layers(wk)
+    arr, n = cvx.layer_array(layers)
+    out = (ctypes.c_int * 4)()
+    # forward reference
+    bad = cvx.layer_array(layers)[0]
+    bad[3].in_ = 5
+    assert cvx.lib.cvx_forward_out_shape(bad, n, out) == -8
+    # residual of the wrong shape (block 0's pw reading conv1's output as shortcut)
+    bad = cvx.layer_array(layers)[0]
+    bad[3].res = 0
+    assert cvx.lib.cvx_forward_out_shape(bad, n, out) == -2
+    # shape chain broken
+    bad = cvx.layer_array(layers)[0]
+    bad[1].conv.c_in = 47
+    assert cvx.lib.cvx_forward_out_shape(bad, n, out) == -2
+    # unknown kind
+    bad = cvx.layer_array(layers)[0]
+    bad[2].kind = 9
+    assert cvx.lib.cvx_forward_out_shape(bad, n, out) == -8
+    # prologue anywhere but first
+    bad = cvx.layer_array(layers)[0]
+    bad[4].kind = cvx.CVX_L_PREPROC
+    assert cvx.lib.cvx_forward_out_shape(bad, n, out) == -8
+    # runtime checks
+    ws = cvx.cvx_forward_workspace_bytes(layers)
+    f = cvx.lib.cvx_forward
+    assert f(arr, n, X, Y, WS, ws - 4, None) == -6
+    assert f(arr, n, X, Y, WS + 16, ws, None) == -4   # workspace must be 256-byte aligned
+    assert f(arr, n, X, X, WS, ws, None) == -5        # output == input
+    assert f(arr, n, None, Y, WS, ws, None) == -1
+    assert f(arr, 0, X, Y, WS, ws, None) == -2

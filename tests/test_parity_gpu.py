@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs, element by element, |gpu - oracle| <= 1e-4*max(1,|oracle|).
+
+Covers every workload at full size (the detector pipeline at batch 8 on sampled
+images), a sweep of single layers spanning several tiles with ragged tails, the
+edge cases (odd and tile-misaligned widths, stride 2, tiny and single-pixel
+maps, batch > 1, every activation and residual placement, split reductions),
+NaN guard bands around outputs, and run-to-run determinism.
+"""
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import DEV, Guarded, check, dev, say
+
+pytestmark = pytest.mark.gpu
+
+from conv2d_batchnorm_activation_amd import cvx  # noqa: E402  (raises if libcvx is not built)
+from conv2d_batchnorm_activation_amd.net import Net  # noqa: E402
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_conv(x, L, residual=None, guard=True):
+    """One layer through cvx_fold_bn + cvx_conv_bn_act.  Returns (y, guards_ok)."""
+    n, c, h, w = x.shape
+    d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode)
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    p = L.params
+    xt, wt = dev(x), dev(p["w"])
+    g, b, m, v = (dev(p[k]) for k in ("gamma", "beta", "mean", "var"))
+    scale = torch.empty(L.cout, device=DEV)
+    bias = torch.empty(L.cout, device=DEV)
+    cvx.cvx_fold_bn(g, b, m, v, wl.EPS, scale, bias)
+    rt = dev(residual) if residual is not None else None
+    out = Guarded((n, L.cout, oh, ow))
+    nws = cvx.cvx_conv_workspace_bytes(d)
+    ws = torch.empty(max(nws, 4), dtype=torch.uint8, device=DEV)
+    cvx.cvx_conv_bn_act(d, xt, wt, scale, bias, rt, out.t, ws, nws)
+    torch.cuda.synchronize()
+    return out.t.cpu().numpy(), out.guards_intact()
+
+
+def oracle_conv(x, L, residual=None):
+    p = L.params
+    return oracle.conv_bn_act(x, p["w"], p["gamma"], p["beta"], p["mean"], p["var"], wl.EPS,
+                              L.stride, L.pad, L.groups, L.act, L.res_mode, residual)
+
+
+# ----------------------------------------------------------------------------- workloads
+def test_fold_bn_matches_oracle():
+    rng = np.random.default_rng(5)
+    bn = wl.draw_bn(rng, 257)
+    say("fold_bn c=257")
+    t = {k: dev(v) for k, v in bn.items()}
+    scale = torch.empty(257, device=DEV)
+    bias = torch.empty(257, device=DEV)
+    cvx.cvx_fold_bn(t["gamma"], t["beta"], t["mean"], t["var"], wl.EPS, scale, bias)
+    torch.cuda.synchronize()
+    s_ref, b_ref = oracle.fold_bn(bn["gamma"], bn["beta"], bn["mean"], bn["var"], wl.EPS)
+    check(scale.cpu().numpy(), s_ref, "scale")
+    check(bias.cpu().numpy(), b_ref, "bias")
+
+
+def test_single_depthwise_layer():
+    wk = wl.depthwise_single()
+    say(f"workload {wk.name}")
+    y, ok = gpu_conv(wk.x, wk.layers[0])
+    assert ok, "write outside the output"
+    check(y, oracle_conv(wk.x, wk.layers[0]), wk.name)
+
+
+@pytest.mark.parametrize("name", [s[0] for s in wl.SWEEP])
+def test_sweep_layer(name):
+    wk = wl.sweep_layer(name)
+    L = wk.layers[0]
+    r = wk.x if L.res_mode else None
+    say(f"sweep layer {name}")
+    y, ok = gpu_conv(wk.x, L, r)
+    assert ok, "write outside the output"
+    check(y, oracle_conv(wk.x, L, r), name)
+
+
+def _forward_check(wk, sample=None):
+    net = Net(wk.layers, wk.x.shape, device=DEV)
+    x = dev(wk.x)
+    say(f"forward {wk.name} ({len(wk.layers)} layers)")
+    y = net(x)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    if sample is None:
+        ref = oracle.forward(wk.layers, wk.x)
+        check(got, ref, wk.name)
+    else:
+        ref = oracle.forward(wk.layers, wk.x[sample])
+        check(got[sample], ref, f"{wk.name} images {sample}")
+    return net, got
+
+
+def test_detector_stem():
+    _forward_check(wl.detector_stem())
+
+
+@pytest.mark.parametrize("batch", [1, 256])
+def test_mnist_cnn(batch):
+    _forward_check(wl.mnist_cnn(batch))
+
+
+def test_detector_pipeline_b1():
+    _forward_check(wl.detector_pipeline(1))
+
+
+def test_detector_pipeline_b8_sampled():
+    # the oracle checks images 0 and 7 of the batch; every image is independent
+    _forward_check(wl.detector_pipeline(8), sample=[0, 7])
+
+
+def test_detector_pipeline_layer_isolated():
+    """Each layer of the chain against the oracle fed the GPU's own previous
+    output, so an error is pinned to one layer."""
+    wk = wl.detector_pipeline(1)
+    net = Net(wk.layers, wk.x.shape, device=DEV)
+    say("detector chain, layer by layer")
+    # prologue
+    pre = torch.empty(net.layer_io[0][1], device=DEV)
+    L0 = wk.layers[0]
+    cvx.cvx_preprocess_u8(dev(wk.x), pre, L0.pre_mean, L0.pre_std)
+    torch.cuda.synchronize()
+    cur = pre.cpu().numpy()
+    check(cur, oracle.preprocess(wk.x, L0.dst_h, L0.dst_w, L0.pre_mean, L0.pre_std), "preprocess")
+    for L in wk.layers[1:]:
+        say(f"  layer {L.name}")
+        r = cur if L.res_mode else None
+        y, ok = gpu_conv(cur, L, r)
+        assert ok, f"{L.name}: write outside the output"
+        check(y, oracle_conv(cur, L, r), L.name)
+        cur = y
+
+
+# ----------------------------------------------------------------------------- layer sweep
+# (seed, n, cin, h, w, cout, k, stride, pad, groups, act, res_mode)
+A, R, N_ = wl.ACT_SILU, wl.ACT_RELU, wl.ACT_NONE
+B4, AF = wl.RES_BEFORE_ACT, wl.RES_AFTER_ACT
+CASES = [
+    # implicit GEMM 3x3: ragged pixel tails, c_out not a multiple of the tile, odd c_in
+    (1, 1, 16, 17, 23, 40, 3, 1, 1, 1, A, 0),
+    (2, 2, 24, 20, 20, 72, 3, 1, 1, 1, R, AF),
+    (3, 1, 13, 31, 9, 33, 3, 2, 1, 1, A, 0),
+    (4, 3, 40, 14, 15, 64, 3, 2, 1, 1, N_, B4),
+    (5, 1, 96, 7, 7, 128, 3, 1, 1, 1, A, AF),
+    (6, 1, 8, 40, 40, 16, 3, 1, 1, 1, A, 0),       # OW = 40 (the page's overrun width)
+    (7, 1, 8, 20, 20, 16, 3, 1, 1, 1, A, AF),      # OW = 20
+    (8, 1, 32, 161, 33, 20, 3, 2, 1, 1, A, 0),     # wide odd map, stride 2
+    (9, 1, 512, 6, 6, 64, 3, 1, 1, 1, A, 0),       # long reduction, split
+    (10, 1, 64, 1, 1, 32, 3, 1, 1, 1, R, 0),       # single pixel
+    (11, 2, 16, 9, 11, 24, 3, 1, 0, 1, A, 0),      # no padding
+    # implicit GEMM 1x1
+    (20, 1, 48, 14, 14, 96, 1, 1, 0, 1, R, B4),
+    (21, 4, 48, 28, 28, 96, 1, 2, 0, 1, N_, 0),    # strided shortcut
+    (22, 1, 20, 13, 13, 37, 1, 1, 0, 1, A, AF),
+    (23, 1, 300, 5, 7, 70, 1, 1, 0, 1, A, 0),
+    (24, 1, 192, 1, 1, 10, 1, 1, 0, 1, N_, 0),
+    # depthwise 3x3
+    (30, 2, 48, 28, 28, 48, 3, 2, 1, 48, R, 0),
+    (31, 1, 64, 13, 13, 64, 3, 1, 1, 64, A, AF),
+    (32, 3, 7, 9, 31, 7, 3, 1, 1, 7, A, B4),
+    (33, 1, 4, 64, 300, 4, 3, 1, 1, 4, R, 0),      # band path (large plane)
+    (34, 1, 3, 97, 41, 3, 3, 2, 1, 3, A, AF),      # band path, stride 2, odd sizes
+    (35, 2, 5, 1, 1, 5, 3, 1, 1, 5, R, 0),
+    (36, 1, 6, 8, 8, 6, 3, 2, 0, 6, A, 0),         # no padding
+    # direct (tiny c_in, grouped, large kernels)
+    (40, 2, 3, 33, 47, 16, 3, 2, 1, 1, A, 0),
+    (41, 2, 1, 28, 28, 48, 3, 1, 1, 1, R, 0),
+    (42, 1, 8, 12, 12, 12, 3, 1, 1, 2, A, AF),     # grouped
+    (43, 1, 3, 23, 19, 10, 5, 2, 2, 1, A, 0),
+    (44, 1, 4, 16, 16, 8, 7, 1, 3, 1, N_, B4),
+    (45, 1, 2, 10, 10, 5, 3, 3, 1, 1, A, 0),       # stride 3
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
+def test_layer_sweep(case):
+    seed, n, cin, h, w, cout, k, s, p, g, act, rm = case
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, g, act, rm)
+    d = cvx.make_desc(n, cin, h, w, cout, k, s, p, g, act, rm)
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    r = wl.residual_for(seed, (n, cout, oh, ow)) if rm else None
+    say(f"case {case}: plan {cvx.cvx_conv_plan(d)}")
+    y, ok = gpu_conv(x, L, r)
+    assert ok, "write outside the output"
+    check(y, oracle_conv(x, L, r), f"case {seed}")
+
+
+@pytest.mark.parametrize("ow,cols", GOLDEN["tma_edge_overflow"]["cases"])
+def test_no_row_overrun_at_page_widths(ow, cols):
+    """Widths 40 and 20 are where a 16-wide unmasked tile overran into the next
+    row ("YOLO26N Inference Optimisation", "Bug fixed: TMA overflow").  Every
+    output row must hold exactly its own values, for each kernel family."""
+    for fam, (cin, cout, k, g) in {"igemm3": (64, 64, 3, 1), "igemm1": (64, 64, 1, 1),
+                                   "dw": (64, 64, 3, 64), "direct": (3, 16, 3, 1)}.items():
+        x, L = wl.random_conv_case(100 + ow, 1, cin, ow, ow, cout, k, 1, k // 2, g, wl.ACT_SILU)
+        say(f"overrun check OW={ow} {fam}")
+        y, ok = gpu_conv(x, L)
+        assert ok
+        check(y, oracle_conv(x, L), f"OW={ow} {fam}")
+
+
+def test_preprocess_sizes():
+    m, s = wl.PRE_MEAN, wl.PRE_STD
+    for (n, sh, sw, dh, dw) in [(1, 720, 1280, 640, 640), (2, 720, 1280, 480, 640),
+                                (1, 37, 53, 100, 71), (3, 9, 7, 9, 7), (1, 1, 1, 3, 5),
+                                (1, 480, 640, 333, 517)]:
+        src = wl.frame(sh * 7 + sw, n, sh, sw)
+        dst = Guarded((n, 3, dh, dw))
+        say(f"preprocess {n}x{sh}x{sw} -> {dh}x{dw}")
+        cvx.cvx_preprocess_u8(dev(src), dst.t, m, s)
+        torch.cuda.synchronize()
+        assert dst.guards_intact()
+        check(dst.t.cpu().numpy(), oracle.preprocess(src, dh, dw, m, s), f"pre {sh}x{sw}->{dh}x{dw}")
+
+
+def test_preprocess_padded_rows():
+    n, sh, sw, pitch = 2, 45, 61, 3 * 61 + 13
+    src = np.random.default_rng(77).integers(0, 256, (n, sh, pitch), dtype=np.uint8)
+    dense = np.ascontiguousarray(src[:, :, :3 * sw].reshape(n, sh, sw, 3))
+    dst = torch.empty((n, 3, 30, 40), device=DEV)
+    say("preprocess padded rows")
+    cvx.cvx_preprocess_u8(dev(dense), dst, wl.PRE_MEAN, wl.PRE_STD)  # dense reference run
+    t = dev(src)
+    rc = cvx.lib.cvx_preprocess_u8(t.data_ptr(), n, sh, sw, pitch, dst.data_ptr(), 30, 40,
+                                   (ctypes.c_float * 3)(*wl.PRE_MEAN),
+                                   (ctypes.c_float * 3)(*wl.PRE_STD),
+                                   torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    check(dst.cpu().numpy(), oracle.preprocess(dense, 30, 40, wl.PRE_MEAN, wl.PRE_STD), "pitch")
+
+
+def test_gap_fc():
+    rng = np.random.default_rng(3)
+    for (n, c, h, w, o) in [(1, 192, 7, 7, 10), (5, 33, 3, 5, 7), (2, 300, 1, 1, 64)]:
+        x = rng.uniform(-1, 1, (n, c, h, w)).astype(np.float32)
+        fw = rng.normal(0, 0.1, (o, c)).astype(np.float32)
+        fb = rng.uniform(-0.1, 0.1, o).astype(np.float32)
+        out = torch.empty((n, o), device=DEV)
+        say(f"gap_fc {n}x{c}x{h}x{w} -> {o}")
+        cvx.cvx_gap_fc(dev(x), dev(fw), dev(fb), out)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), oracle.fc(oracle.gap(x), fw, fb), "gap_fc")
+
+
+def test_deterministic_across_runs():
+    """Split reductions are summed in a fixed order: two runs are bit-identical."""
+    for name in ("g_256x20_3x3", "f_256x20_1x1", "a_64x80_3x3"):
+        wk = wl.sweep_layer(name)
+        L = wk.layers[0]
+        r = wk.x if L.res_mode else None
+        say(f"determinism {name}")
+        y1, _ = gpu_conv(wk.x, L, r)
+        y2, _ = gpu_conv(wk.x, L, r)
+        assert np.array_equal(y1, y2), name
+
+
+def test_forward_repeat_is_stable():
+    """The same forward twice on one stream gives bit-identical output (no
+    state carried between calls, workspace contents on entry ignored)."""
+    wk = wl.mnist_cnn(16)
+    net = Net(wk.layers, wk.x.shape, device=DEV)
+    x = dev(wk.x)
+    say("forward repeat mnist b16")
+    a = net(x).clone()
+    net.workspace.fill_(255)
+    b = net(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
