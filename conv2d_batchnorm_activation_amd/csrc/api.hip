@@ -2,9 +2,11 @@
 // the layer-list executor.  Every check runs on the host before anything is
 // enqueued; the only device work is the kernels in the k_*.hip files.
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "cvx_internal.h"
@@ -92,28 +94,66 @@ bool plan_depthwise(const ConvGeom& g, Plan* p)
     return true;
 }
 
+// Implicit-GEMM tile choice by a small cost model of one MI355X: 256 compute
+// units, one workgroup per unit per round, each unit retiring 256 fp32 MFMA
+// FLOP per clock; every chunk of input channels costs a fixed staging overhead,
+// every workgroup a fixed start-up latency, and a split reduction costs a
+// finishing pass over the partial sums.
 bool plan_igemm(const ConvGeom& g, Plan* p)
 {
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
-    GemmTile t;
-    t.bm = g.cout <= 32 ? 32 : 64;
-    t.bn = t.bm == 32 ? 128 : 64;
-    t.splitk = 1;
-    // as many channels per chunk as the LDS budget allows (even, <= 16)
-    t.ck = 16;
-    while (t.ck > 2 && igemm_lds_bytes(g, t) > kMaxLdsBytes) t.ck -= 2;
-    if (igemm_lds_bytes(g, t) > kMaxLdsBytes) return false;
-    // split the reduction when the tiles alone leave most compute units idle
-    const long tiles = (long)g.n * ((g.oh * g.ow + t.bn - 1) / t.bn) * ((g.cout + t.bm - 1) / t.bm);
-    const int nchunks = (g.cin + t.ck - 1) / t.ck;
-    if (tiles < 128 && nchunks >= 4) {
-        int sk = (int)std::min<long>(nchunks / 2, (256 + tiles - 1) / tiles);
-        t.splitk = std::max(1, std::min(sk, 8));
+    const double kCUs = 256.0, kFlopPerClk = 256.0, kChunkClk = 400.0, kStartClk = 3000.0,
+                 kLaunchClk = 4000.0, kBytesPerClk = 2000.0;
+    const int ck = igemm_chunk_channels();
+    const int nchunks = (g.cin + ck - 1) / ck;
+    const int kk = g.k * g.k;
+    double best = 1e300;
+    GemmTile bt{-1, 0, 0, 0, 1};
+    for (int tile = 0; tile < igemm_num_tiles(); ++tile) {
+        int bm, bn;
+        igemm_tile_shape(tile, &bm, &bn);
+        for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
+            if (!igemm_tile_fits(g, tile, tc, nullptr)) continue;
+            const double stage_clk = igemm_stage_floats(g, tile, tc) / 256.0 * 6.0;
+            const long tiles = (long)g.n * igemm_tiles_per_image(g, tile, tc) *
+                               ((g.cout + bm - 1) / bm);
+            for (int sk = 1; sk <= 8 && sk <= nchunks; ++sk) {
+                const int per = (nchunks + sk - 1) / sk;
+                if ((long)(sk - 1) * per >= nchunks) continue;  // an empty slice
+                if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
+                const long wgs = tiles * sk;
+                const double rounds = std::ceil(wgs / kCUs);
+                const double wg_clk = 2.0 * bm * bn * per * ck * kk / kFlopPerClk +
+                                      per * (kChunkClk + stage_clk) + kStartClk;
+                double cost = rounds * wg_clk;
+                if (sk > 1)
+                    cost += kLaunchClk +
+                            (double)g.n * g.cout * g.oh * g.ow * 4.0 * (sk + 2) / kBytesPerClk;
+                if (cost < best) {
+                    best = cost;
+                    bt = GemmTile{tile, bm, bn, tc, sk};
+                }
+            }
+        }
     }
+    // Tuning and test override: CVX_IGEMM_TILE="kind,tc,splitk" forces a tile
+    // configuration when it is valid for this shape (sweeps and coverage tests).
+    if (const char* env = getenv("CVX_IGEMM_TILE")) {
+        int kind = -1, tc = -1, sk = 0;
+        if (sscanf(env, "%d,%d,%d", &kind, &tc, &sk) == 3 && kind >= 0 &&
+            kind < igemm_num_tiles() && sk >= 1 && sk <= nchunks &&
+            (long)(sk - 1) * ((nchunks + sk - 1) / sk) < nchunks &&
+            igemm_tile_fits(g, kind, tc, nullptr)) {
+            int bm, bn;
+            igemm_tile_shape(kind, &bm, &bn);
+            bt = GemmTile{kind, bm, bn, tc, sk};
+        }
+    }
+    if (bt.kind < 0) return false;
     p->fam = FAM_IGEMM;
-    p->tile = t;
-    p->ws_bytes = t.splitk > 1 ? (size_t)t.splitk * g.n * g.cout * g.oh * g.ow * sizeof(float) : 0;
+    p->tile = bt;
+    p->ws_bytes = bt.splitk > 1 ? (size_t)bt.splitk * g.n * g.cout * g.oh * g.ow * sizeof(float) : 0;
     return true;
 }
 
@@ -209,14 +249,12 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
         snprintf(buf, buf_len, "direct k%d s%d cob=%d kernel=cvx::k_direct<%d>", g.k, g.stride,
                  p.direct_cob, p.direct_cob);
         break;
-    case FAM_IGEMM: {
-        const int wm = p.tile.bm == 32 ? 1 : 2, wn = 4 / wm;
+    case FAM_IGEMM:
         snprintf(buf, buf_len,
-                 "igemm_mfma k%d s%d bm=%d bn=%d ck=%d splitk=%d kernel=cvx::k_igemm<%d, %d, %d, %d, %d>",
-                 g.k, g.stride, p.tile.bm, p.tile.bn, p.tile.ck, p.tile.splitk, p.tile.bm, p.tile.bn,
-                 wm, wn, g.k);
+                 "igemm_mfma k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=cvx::k_igemm<%d, %d",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk,
+                 p.tile.bm, p.tile.bn);
         break;
-    }
     }
     return CVX_OK;
 }

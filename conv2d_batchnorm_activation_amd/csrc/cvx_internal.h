@@ -25,8 +25,9 @@ struct ConvGeom {
 
 // Tile configuration for the implicit-GEMM family.
 struct GemmTile {
+    int kind;         // index into the compiled tile table (k_igemm.hip)
     int bm, bn;       // output tile: bm output channels x bn output pixels
-    int ck;           // input channels staged per K chunk
+    int tc;           // 0: bn consecutive pixels; else 2-D tile of bn/tc rows x tc columns
     int splitk;       // number of K slices (1 = no split); >1 uses the workspace
 };
 
@@ -66,9 +67,12 @@ hipError_t launch_preprocess(const unsigned char* src, int n, int src_h, int src
                              const float mean[3], const float stdv[3], hipStream_t s);
 
 // igemm helpers used by the planner (defined next to the kernel).
-int igemm_rows_max(const ConvGeom& g, int bn);
-size_t igemm_lds_bytes(const ConvGeom& g, const GemmTile& t);
-bool igemm_tile_supported(const GemmTile& t);
+int igemm_num_tiles();
+void igemm_tile_shape(int tile, int* bm, int* bn);
+bool igemm_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes);
+long igemm_tiles_per_image(const ConvGeom& g, int tile, int tc);
+long igemm_stage_floats(const ConvGeom& g, int tile, int tc);  // per chunk
+int igemm_chunk_channels();
 
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 

@@ -23,6 +23,16 @@ __device__ __forceinline__ float apply_act(float v, int act)
     return v;
 }
 
+// Same activation with the hardware exponential and reciprocal (about 1 ulp each,
+// far inside the 1e-4 parity bound); exp(-v) overflowing to +inf gives -0 for
+// very negative v, as the exact form does.
+__device__ __forceinline__ float apply_act_fast(float v, int act)
+{
+    if (act == CVX_ACT_RELU) return fmaxf(v, 0.0f);
+    if (act == CVX_ACT_SILU) return v * __frcp_rn(1.0f + __expf(-v));
+    return v;
+}
+
 // `r` is read only when res_mode != CVX_RES_NONE.
 __device__ __forceinline__ float epilogue(float acc, float sc, float bi, int act, int res_mode,
                                           const float* __restrict__ r, long idx)

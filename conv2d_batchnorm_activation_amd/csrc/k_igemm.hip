@@ -6,28 +6,35 @@
 // c_in * kh * kw):
 //     M = c_out,  N = output pixels of one image,  K = c_in * kh * kw
 //     Y[co][q] = sum_k W[co][k] * X_im2col[k][q]
-// The page's reason for NHWC was that its tensor-core instructions needed the
+// The page moved to NHWC because its tensor-core instructions needed the
 // reduction dimension contiguous in global memory.  The MI355X matrix cores
-// read their operands from VGPRs, which we fill from LDS, so NCHW stays: the
-// output pixels (the N dimension) are contiguous, global loads and stores stay
-// coalesced, and the im2col matrix is never materialised.
+// take their operands from VGPRs, which we fill from LDS, so NCHW stays: output
+// pixels (N) are contiguous, global loads and stores stay coalesced, and the
+// im2col matrix is never materialised.
 //
-// Per workgroup (256 threads = 4 wave64s) one BM x BN output tile:
-//   * the weight block W[co0 .. co0+BM)[chunk] is staged in LDS as
-//     sW[(ci*KK + tap)][m] (m contiguous), zero-filled past c_out / c_in;
-//   * the input rows the tile's pixels need, for `ck` input channels, are staged
-//     as full zero-padded rows sX[ci][r][c] (c = input column + pad), read with
-//     one coalesced sweep per row; every staged element feeds up to KK taps;
-//   * each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks
-//     (v_mfma_f32_32x32x2_f32, true fp32, no reduced-precision emulation);
-//     the two K values of one MFMA are two adjacent input channels at one tap;
-//   * the epilogue (folded BN, residual, activation) runs on the accumulators
-//     and each output is stored once, masked to the real pixel count, so rows
-//     of any width are never overrun ("Bug fixed: TMA overflow").
-// When the tile count alone cannot fill the chip, the channel chunks are split
-// over blockIdx.z; each slice stores raw partial sums in the workspace and a
-// finishing kernel adds the slices in a fixed order (deterministic) and applies
+// Per workgroup (256 threads = 4 wave64s), one BM x BN output tile:
+//   * the reduction runs over chunks of CK input channels.  For each chunk the
+//     weight block W[co0 .. co0+BM)[ci0*KK .. (ci0+CK)*KK) goes to LDS as
+//     sW[t][m] (t = ci*KK + tap, odd row pitch BM+1: conflict-free transposed
+//     writes and contiguous MFMA reads), and the input region the tile's pixels
+//     read (PR rows x PC columns per channel, zero outside the image, so the
+//     padding costs nothing in the inner loop) goes to sX[ci][r][c];
+//   * every thread owns a fixed set of load slots (NW weight floats, NPX input
+//     floats per chunk), computed once; the loads of chunk i+1 are issued into
+//     registers before the MFMAs of chunk i, so global latency hides behind the
+//     matrix work, and only the LDS writes sit between the two barriers;
+//   * the four waves split the tile (WM x WN) and/or the chunk's channel pairs
+//     (WK); each wave computes 32x32 blocks with v_mfma_f32_32x32x2_f32 (true
+//     fp32), the two K values of one MFMA being two adjacent input channels at
+//     one tap; WK > 1 partial tiles are summed through LDS in wave order;
+//   * the epilogue (folded BN, residual, activation) runs on the accumulators and
+//     each output is stored once, masked to the real pixel count, so rows of any
+//     width are never overrun ("Bug fixed: TMA overflow").
+// When the tiles alone cannot fill the chip, chunks are also split over
+// blockIdx.z; each slice stores raw partial sums in the workspace and a
+// finishing kernel adds the slices in slice order (deterministic) and applies
 // the epilogue.
+#include "bufio.h"
 #include "cvx_internal.h"
 #include "epilogue.h"
 
@@ -35,53 +42,175 @@ namespace cvx {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int WM, int WN, int K>
-__global__ void __launch_bounds__(256) k_igemm(
-    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ scale,
-    const float* __restrict__ bias, const float* __restrict__ res, float* __restrict__ y,
-    float* __restrict__ partial, int cin, int H, int W, int cout, int stride, int pad, int OH,
-    int OW, int ck, int rows_max, int tiles_per_img, int chunks_per_split, int act, int res_mode)
+// n / d for 0 <= n < 2^31 with a precomputed multiplier (round-up method):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, q = (umulhi(n, m) + n) >> l.
+__device__ __forceinline__ int fdiv(int n, unsigned m, unsigned l)
 {
-    static_assert(WM * WN == 4, "four waves per workgroup");
+    unsigned hi = __umulhi((unsigned)n, m);
+    return (int)((hi + (unsigned)n) >> l);
+}
+
+void fastdiv_params(int d, unsigned* m, unsigned* l)
+{
+    unsigned s = 0;
+    while ((1ull << s) < (unsigned long long)d) ++s;
+    *l = s;
+    *m = (unsigned)(((1ull << 32) * ((1ull << s) - (unsigned long long)d)) / (unsigned long long)d + 1);
+}
+
+struct IgemmArgs {
+    const float* x;
+    const float* w;
+    const float* scale;
+    const float* bias;
+    const float* res;
+    float* y;
+    float* partial;
+    int cin, H, W, cout, stride, pad, OH, OW;
+    int tiles_per_img, chunks_per_split;
+    int tc;                 // 0: tiles are runs of BN consecutive pixels; else TR x tc blocks
+    int tiles_w;            // 2-D tiles: tiles across one band of rows
+    unsigned m_tc, l_tc;    // fast division by tc
+    int PR, PC;             // staged region per channel (launch constants)
+    unsigned m_rc, l_rc;    // fast division by PR*PC
+    unsigned m_c, l_c;      // fast division by PC
+    unsigned m_ow, l_ow;    // fast division by OW
+    int act, res_mode;
+};
+
+template <int BM, int BN, int WM, int WN, int WK, int K, int CK, int NPX>
+__global__ void __launch_bounds__(256) k_igemm(IgemmArgs a)
+{
+    static_assert(WM * WN * WK == 4, "four waves per workgroup");
     constexpr int TM = BM / WM, TN = BN / WN;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is made of 32x32 blocks");
     constexpr int MT = TM / 32, NT = TN / 32;
     constexpr int KK = K * K;
-    constexpr int BMP = BM + 1;  // odd row pitch: transposed LDS writes hit distinct banks
+    constexpr int BMP = BM + 1;
+    constexpr int CKK = CK * KK;
+    static_assert((BM * CKK) % 256 == 0, "weight block splits evenly over the threads");
+    constexpr int NW = BM * CKK / 256;
+    constexpr int PAIRS = CK / 2;
+    static_assert(CK % 2 == 0 && PAIRS % WK == 0, "channel pairs split evenly over WK waves");
 
     extern __shared__ float smem[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int hi = lane >> 5;   // which of the two K values of an MFMA this lane carries
-    const int l32 = lane & 31;
-    const int wm0 = (wave / WN) * TM;
-    const int wn0 = (wave % WN) * TN;
-
-    const int OHW = OH * OW;
-    const int b = blockIdx.x / tiles_per_img;
-    const int q0 = (blockIdx.x - b * tiles_per_img) * BN;
-    const int q_end = min(q0 + BN, OHW);
-    const int co0 = blockIdx.y * BM;
-    const int oh_a = q0 / OW;
-    const int oh_b = (q_end - 1) / OW;
-    const int PR = (oh_b - oh_a) * stride + K;      // staged rows for this tile
-    const int PW = W + 2 * pad;                     // staged row width
-    const int PRW = ((rows_max - 1) * stride + K) * PW;  // per-channel pitch in sX
-    const int iy0 = oh_a * stride - pad;
-
     float* sW = smem;
-    float* sX = smem + ck * KK * BMP;
+    float* sX = smem + CKK * BMP;
 
-    // LDS offset of each lane's output pixel inside a staged channel; lanes past
-    // the tile end point at the last real pixel (their results are not stored)
-    int loff[NT];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hi = lane >> 5;
+    const int l32 = lane & 31;
+    const int wk = wave % WK;
+    const int wmn = wave / WK;
+    const int wm0 = (wmn / WN) * TM;
+    const int wn0 = (wmn % WN) * TN;
+
+    const int OHW = a.OH * a.OW;
+    const int HW = a.H * a.W;
+    const int b = blockIdx.x / a.tiles_per_img;
+    const int tile = blockIdx.x - b * a.tiles_per_img;
+    const int co0 = blockIdx.y * BM;
+    // Tile origin.  Runs of pixels: q0 .. q0+BN-1 in row-major order; the staged
+    // region spans the rows they touch (from column ow_a*s - pad when they stay in
+    // one row, else whole rows).  2-D tiles: TR rows x tc columns from (oh0, ow0).
+    int q0 = 0, q_end = 0, oh_ref, ix0;
+    if (a.tc == 0) {
+        q0 = tile * BN;
+        q_end = min(q0 + BN, OHW);
+        oh_ref = fdiv(q0, a.m_ow, a.l_ow);
+        const int ow_a = q0 - oh_ref * a.OW;
+        const int oh_b = fdiv(q_end - 1, a.m_ow, a.l_ow);
+        ix0 = (oh_ref == oh_b ? ow_a * a.stride : 0) - a.pad;
+    } else {
+        const int band = tile / a.tiles_w;
+        const int tw = tile - band * a.tiles_w;
+        oh_ref = band * (BN / a.tc);
+        ix0 = tw * a.tc * a.stride - a.pad;
+        q0 = tw * a.tc;  // ow0
+    }
+    const int iy0 = oh_ref * a.stride - a.pad;
+    const int RC = a.PR * a.PC;
+    const int RE = CK * RC;  // staged input floats per chunk
+
+    // Each lane's output pixel per 32-column block: LDS offset within one staged
+    // channel (B operand), and output index (-1: outside the tile or the image,
+    // computed on a clamped in-region pixel and not stored).
+    int loff[NT], qout[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        int q = min(q0 + wn0 + nt * 32 + l32, q_end - 1);
-        int oh = q / OW;
-        int ow = q - oh * OW;
-        loff[nt] = (oh - oh_a) * stride * PW + ow * stride;
+        const int j = wn0 + nt * 32 + l32;
+        int oh, ow;
+        bool ok;
+        if (a.tc == 0) {
+            const int q = q0 + j;
+            ok = q < q_end;
+            const int qc = ok ? q : q_end - 1;
+            oh = fdiv(qc, a.m_ow, a.l_ow);
+            ow = qc - oh * a.OW;
+        } else {
+            const int jr = fdiv(j, a.m_tc, a.l_tc);
+            oh = oh_ref + jr;
+            ow = q0 + (j - jr * a.tc);
+            ok = oh < a.OH && ow < a.OW;
+            oh = min(oh, a.OH - 1);
+            ow = min(ow, a.OW - 1);
+        }
+        loff[nt] = (oh - oh_ref) * a.stride * a.PC + ow * a.stride - a.pad - ix0;
+        qout[nt] = ok ? oh * a.OW + ow : -1;
     }
+
+    // Input load slots: element e = tid + 256*i of the staged region, as a byte
+    // offset from the chunk's first channel plane within this image; kOOB (reads
+    // as 0) outside the image or past the region.  Channels past c_in fall
+    // outside the image's descriptor and read as 0 too.
+    unsigned goff[NPX];
+#pragma unroll
+    for (int i = 0; i < NPX; ++i) {
+        const int e = tid + 256 * i;
+        const int ci = fdiv(e, a.m_rc, a.l_rc);
+        const int rem = e - ci * RC;
+        const int r = fdiv(rem, a.m_c, a.l_c);
+        const int c = rem - r * a.PC;
+        const int iy = iy0 + r, ix = ix0 + c;
+        goff[i] = (e < RE && iy >= 0 && iy < a.H && ix >= 0 && ix < a.W)
+                      ? 4u * (unsigned)(ci * HW + iy * a.W + ix) : kOOB;
+    }
+    // Weight load slots: float f = tid + 256*j of the BM x CK*KK block.  Rows past
+    // c_out fall outside the descriptor (read 0); in a last, partial chunk the
+    // columns past c_in read the next row's weights, which multiply inputs that
+    // read as 0.
+    unsigned woff[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        const int f = tid + 256 * j;
+        const int m = f / CKK, t = f - m * CKK;
+        woff[j] = co0 + m < a.cout ? 4u * (unsigned)((co0 + m) * a.cin * KK + t) : kOOB;
+    }
+    const rsrc_t rx = make_rsrc(a.x + (long)b * a.cin * HW, 4u * (unsigned)(a.cin * HW));
+    const rsrc_t rw = make_rsrc(a.w, 4u * (unsigned)(a.cout * a.cin * KK));
+    float pw[NW], px[NPX];
+
+    auto load_chunk = [&](int chunk) {
+        const unsigned wb = 4u * (unsigned)(chunk * CK * KK);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) pw[j] = bload(rw, woff[j] + wb);
+        const unsigned xb = 4u * (unsigned)(chunk * CK * HW);
+#pragma unroll
+        for (int i = 0; i < NPX; ++i) px[i] = bload(rx, goff[i] + xb);
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int f = tid + 256 * j;
+            const int m = f / CKK, t = f - m * CKK;
+            sW[t * BMP + m] = pw[j];
+        }
+        // slots past the region store into LDS that is allocated but never read
+#pragma unroll
+        for (int i = 0; i < NPX; ++i) sX[tid + 256 * i] = px[i];
+    };
 
     f32x16 acc[MT][NT];
 #pragma unroll
@@ -91,47 +220,24 @@ __global__ void __launch_bounds__(256) k_igemm(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
 
-    const int nchunks = (cin + ck - 1) / ck;
-    const int c_begin = blockIdx.z * chunks_per_split;
-    const int c_end = min(nchunks, c_begin + chunks_per_split);
-    const float* xb = x + (long)b * cin * H * W;
+    const int nchunks = (a.cin + CK - 1) / CK;
+    const int c_begin = blockIdx.z * a.chunks_per_split;
+    const int c_end = min(nchunks, c_begin + a.chunks_per_split);
 
+    if (c_begin < c_end) load_chunk(c_begin);
     for (int chunk = c_begin; chunk < c_end; ++chunk) {
-        const int ci0 = chunk * ck;
-        __syncthreads();  // the previous chunk's reads are done
-        // weights: wave-strided rows m, lanes over the contiguous (ci, tap) run
-        for (int m = wave; m < BM; m += 4) {
-            const int co = co0 + m;
-            const float* wr = w + ((long)co * cin + ci0) * KK;
-            for (int t = lane; t < ck * KK; t += 64) {
-                const int ci = t / KK;
-                float v = 0.0f;
-                if (co < cout && ci0 + ci < cin) v = wr[t];
-                sW[t * BMP + m] = v;
-            }
-        }
-        // input rows: wave-strided (channel, row) pairs, lanes over columns
-        for (int row = wave; row < ck * PR; row += 4) {
-            const int ci = row / PR;
-            const int r = row - ci * PR;
-            const int cig = ci0 + ci;
-            const int iy = iy0 + r;
-            const bool ok = cig < cin && iy >= 0 && iy < H;
-            const float* src = xb + ((long)cig * H + iy) * W;
-            float* dst = sX + ci * PRW + r * PW;
-            for (int c = lane; c < PW; c += 64) {
-                const int ix = c - pad;
-                dst[c] = (ok && ix >= 0 && ix < W) ? src[ix] : 0.0f;
-            }
-        }
+        __syncthreads();  // every wave is done reading the previous chunk
+        store_chunk();
         __syncthreads();
-
-        for (int ci = 0; ci < ck; ci += 2) {
-            const float* wa = sW + ((ci + hi) * KK) * BMP + wm0 + l32;
-            const float* xa = sX + (ci + hi) * PRW;
+        if (chunk + 1 < c_end) load_chunk(chunk + 1);  // lands while the MFMAs run
+#pragma unroll
+        for (int jp = 0; jp < PAIRS / WK; ++jp) {
+            const int ci = 2 * (wk + WK * jp) + hi;
+            const float* wa = sW + ci * KK * BMP + wm0 + l32;
+            const float* xa = sX + ci * RC;
 #pragma unroll
             for (int tap = 0; tap < KK; ++tap) {
-                const int toff = (tap / K) * PW + (tap % K);
+                const int toff = (tap / K) * a.PC + (tap % K);
                 float av[MT], bv[NT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) av[mt] = wa[tap * BMP + mt * 32];
@@ -141,30 +247,107 @@ __global__ void __launch_bounds__(256) k_igemm(
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        acc[mt][nt] =
-                            __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt], bv[nt],
+                                                                           acc[mt][nt], 0, 0, 0);
             }
         }
     }
 
-    // D layout of the 32x32 block: lane l, register r holds row
-    // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
-    const long total = (long)gridDim.x / tiles_per_img * cout * OHW;  // n * cout * OHW
+    if constexpr (WK > 1) {
+        // sum the WK partial tiles of each (wm, wn) group through LDS, in wave order
+        __syncthreads();
+        float* red = smem;
+        constexpr int SLAB = MT * NT * 16 * 64;
+        if (wk > 0) {
+            float* dst = red + (wmn * (WK - 1) + wk - 1) * SLAB;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[((mt * NT + nt) * 16 + r) * 64 + lane] = acc[mt][nt][r];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int k = 1; k < WK; ++k) {
+            const float* src = red + (wmn * (WK - 1) + k - 1) * SLAB;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[mt][nt][r] += src[((mt * NT + nt) * 16 + r) * 64 + lane];
+        }
+    }
+
+    // D layout of a 32x32 block: lane l, register r holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32.  The epilogue issues every load it
+    // needs (scale, bias, residual) as one batch, then computes and stores; rows
+    // past c_out and pixels outside the tile get kOOB offsets (loads read 0,
+    // stores are dropped).
+    const unsigned plane_b = 4u * (unsigned)OHW;
+    unsigned rowoff[MT][16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = co0 + wm0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            rowoff[mt][r] = co < a.cout ? (unsigned)(b * a.cout + co) * plane_b : kOOB;
+        }
+    unsigned qb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qb[nt] = qout[nt] >= 0 ? 4u * (unsigned)qout[nt] : kOOB;
+    const unsigned out_bytes = 4u * (unsigned)((gridDim.x / a.tiles_per_img) * a.cout * OHW);
+    if (a.partial != nullptr) {
+        const rsrc_t rp = make_rsrc(a.partial + (long)blockIdx.z * (out_bytes / 4), out_bytes);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    bstore(rp, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB),
+                           acc[mt][nt][r]);
+        return;
+    }
+    const rsrc_t rsb = make_rsrc(a.scale, 4u * (unsigned)a.cout);
+    const rsrc_t rbb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
+    float sc[MT][16], bi[MT][16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = co0 + wm0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const unsigned o = co < a.cout ? 4u * (unsigned)co : kOOB;
+            sc[mt][r] = bload(rsb, o);
+            bi[mt][r] = bload(rbb, o);
+        }
+    const rsrc_t ry = make_rsrc(a.y, out_bytes);
+    float rv[MT][NT][16];
+    if (a.res_mode != CVX_RES_NONE) {
+        const rsrc_t rr = make_rsrc(a.res, out_bytes);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    rv[mt][nt][r] = bload(rr, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB));
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int q = q0 + wn0 + nt * 32 + l32;
-            if (q >= q_end) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = co0 + wm0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (co >= cout) continue;
-                const long idx = ((long)b * cout + co) * OHW + q;
-                if (partial != nullptr)
-                    partial[blockIdx.z * total + idx] = acc[mt][nt][r];
-                else
-                    y[idx] = epilogue(acc[mt][nt][r], scale[co], bias[co], act, res_mode, res, idx);
+                float z = fmaf(sc[mt][r], acc[mt][nt][r], bi[mt][r]);
+                if (a.res_mode == CVX_RES_BEFORE_ACT) z += rv[mt][nt][r];
+                z = apply_act_fast(z, a.act);
+                if (a.res_mode == CVX_RES_AFTER_ACT) z += rv[mt][nt][r];
+                bstore(ry, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB), z);
             }
         }
     }
@@ -187,74 +370,161 @@ __global__ void __launch_bounds__(256) k_splitk_finish(const float* __restrict__
     y[idx] = epilogue(s, scale[co], bias[co], act, res_mode, res, idx);
 }
 
-int igemm_rows_max(const ConvGeom& g, int bn)
+// ------------------------------------------------------------------ host side
+// The compiled tile configurations.  ck = 16 channels per chunk throughout.
+struct TileKind {
+    int bm, bn, wm, wn, wk, npx;
+};
+static constexpr TileKind kTiles[] = {
+    {32, 32, 1, 1, 4, 24},   // T0: small tiles, four waves split the reduction
+    {32, 64, 1, 2, 2, 24},   // T1
+    {64, 64, 2, 2, 1, 24},   // T2
+    {64, 128, 2, 2, 1, 24},  // T3: wide tiles for large maps / batches
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kCK = 16;
+
+int igemm_num_tiles() { return kNumTiles; }
+
+// Staged region per channel (rows x columns) for tile kind `tile` with layout tc
+// (0 = runs of pixels, else 2-D tiles of BN/tc rows x tc columns).
+static void region(const ConvGeom& g, int bn, int tc, int* pr, int* pc)
 {
-    int rows = (bn - 1) / g.ow + 2;
-    return rows < g.oh ? rows : g.oh;
+    if (tc > 0) {
+        *pr = (bn / tc - 1) * g.stride + g.k;
+        *pc = (tc - 1) * g.stride + g.k;
+        return;
+    }
+    if (g.ow % bn == 0) {  // runs never leave their output row
+        *pr = g.k;
+        *pc = (bn - 1) * g.stride + g.k;
+    } else if (bn % g.ow == 0 && bn / g.ow <= g.oh) {  // whole rows per tile
+        *pr = (bn / g.ow - 1) * g.stride + g.k;
+        *pc = g.w + 2 * g.pad;
+    } else {
+        int rows = (bn - 1) / g.ow + 2;
+        rows = rows < g.oh ? rows : g.oh;
+        *pr = (rows - 1) * g.stride + g.k;
+        *pc = g.w + 2 * g.pad;
+    }
 }
 
-size_t igemm_lds_bytes(const ConvGeom& g, const GemmTile& t)
+long igemm_tiles_per_image(const ConvGeom& g, int tile, int tc)
 {
+    const int bn = kTiles[tile].bn;
+    if (tc == 0) return (g.oh * g.ow + bn - 1) / bn;
+    const int tr = bn / tc;
+    return (long)((g.oh + tr - 1) / tr) * ((g.ow + tc - 1) / tc);
+}
+
+long igemm_stage_floats(const ConvGeom& g, int tile, int tc)
+{
+    int pr, pc;
+    region(g, kTiles[tile].bn, tc, &pr, &pc);
+    return (long)kCK * pr * pc + (long)kTiles[tile].bm * kCK * g.k * g.k;
+}
+
+bool igemm_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes)
+{
+    const TileKind& t = kTiles[tile];
+    // every buffer the kernel addresses must stay below 2^31 bytes (32-bit offsets)
+    const long lim = 0x7fffffffL;
+    if ((long)g.cin * g.h * g.w * 4 >= lim || (long)g.cout * g.cin * g.k * g.k * 4 >= lim ||
+        (long)g.n * g.cout * g.oh * g.ow * 4 >= lim)
+        return false;
+    if (tc < 0 || (tc > 0 && (t.bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
+    int pr, pc;
+    region(g, t.bn, tc, &pr, &pc);
+    const long re = (long)kCK * pr * pc;
+    if (re > 256L * t.npx) return false;
     const int kk = g.k * g.k;
-    const size_t sw = (size_t)t.ck * kk * (t.bm + 1);
-    const size_t prw = (size_t)((igemm_rows_max(g, t.bn) - 1) * g.stride + g.k) * (g.w + 2 * g.pad);
-    return (sw + (size_t)t.ck * prw) * sizeof(float);
+    const size_t stage = ((size_t)kCK * kk * (t.bm + 1) + 256 * (size_t)t.npx) * sizeof(float);
+    const size_t red = t.wk > 1 ? (size_t)(4 / t.wk) * (t.wk - 1) * (t.bm / t.wm / 32) *
+                                      (t.bn / t.wn / 32) * 16 * 64 * sizeof(float)
+                                : 0;
+    const size_t lds = stage > red ? stage : red;
+    if (lds > kMaxLdsBytes) return false;
+    if (lds_bytes) *lds_bytes = lds;
+    return true;
 }
 
-bool igemm_tile_supported(const GemmTile& t)
+void igemm_tile_shape(int tile, int* bm, int* bn)
 {
-    return (t.bm == 64 && t.bn == 64) || (t.bm == 32 && t.bn == 128) ||
-           (t.bm == 128 && t.bn == 64) || (t.bm == 64 && t.bn == 128);
+    *bm = kTiles[tile].bm;
+    *bn = kTiles[tile].bn;
+}
+
+int igemm_chunk_channels() { return kCK; }
+
+template <int K, int TILE>
+static void launch_tile(dim3 grid, size_t lds, hipStream_t s, const IgemmArgs& a)
+{
+    constexpr TileKind t = kTiles[TILE];
+    hipLaunchKernelGGL((k_igemm<t.bm, t.bn, t.wm, t.wn, t.wk, K, kCK, t.npx>), grid, dim3(256), lds,
+                       s, a);
 }
 
 template <int K>
-static hipError_t launch_igemm_k(const ConvGeom& g, const Plan& p, const float* x, const float* w,
-                                 const float* scale, const float* bias, const float* res, float* y,
-                                 float* partial, hipStream_t s)
+static void launch_k(int tile, dim3 grid, size_t lds, hipStream_t s, const IgemmArgs& a)
 {
-    const GemmTile& t = p.tile;
-    const int ohw = g.oh * g.ow;
-    const int tiles = (ohw + t.bn - 1) / t.bn;
-    const int nchunks = (g.cin + t.ck - 1) / t.ck;
-    const int per_split = (nchunks + t.splitk - 1) / t.splitk;
-    const int rows_max = igemm_rows_max(g, t.bn);
-    const size_t lds = igemm_lds_bytes(g, t);
-    dim3 grid((unsigned)(g.n * tiles), (unsigned)((g.cout + t.bm - 1) / t.bm), (unsigned)t.splitk);
-#define CVX_IGEMM(BM_, BN_, WM_, WN_)                                                            \
-    hipLaunchKernelGGL((k_igemm<BM_, BN_, WM_, WN_, K>), grid, dim3(256), lds, s, x, w, scale,   \
-                       bias, res, y, partial, g.cin, g.h, g.w, g.cout, g.stride, g.pad, g.oh,     \
-                       g.ow, t.ck, rows_max, tiles, per_split, g.act, g.res_mode)
-    if (t.bm == 64 && t.bn == 64)
-        CVX_IGEMM(64, 64, 2, 2);
-    else if (t.bm == 32 && t.bn == 128)
-        CVX_IGEMM(32, 128, 1, 4);
-    else if (t.bm == 128 && t.bn == 64)
-        CVX_IGEMM(128, 64, 2, 2);
-    else if (t.bm == 64 && t.bn == 128)
-        CVX_IGEMM(64, 128, 2, 2);
-    else
-        return hipErrorInvalidValue;
-#undef CVX_IGEMM
-    return hipGetLastError();
+    switch (tile) {
+    case 0: launch_tile<K, 0>(grid, lds, s, a); break;
+    case 1: launch_tile<K, 1>(grid, lds, s, a); break;
+    case 2: launch_tile<K, 2>(grid, lds, s, a); break;
+    case 3: launch_tile<K, 3>(grid, lds, s, a); break;
+    }
 }
 
 hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const float* w,
                         const float* scale, const float* bias, const float* res, float* y,
                         void* ws, hipStream_t s)
 {
-    float* partial = p.tile.splitk > 1 ? static_cast<float*>(ws) : nullptr;
-    hipError_t e;
+    const int tile = p.tile.kind;
+    if (tile < 0 || tile >= kNumTiles || (g.k != 1 && g.k != 3)) return hipErrorInvalidValue;
+    size_t lds = 0;
+    if (!igemm_tile_fits(g, tile, p.tile.tc, &lds)) return hipErrorInvalidValue;
+    const TileKind& t = kTiles[tile];
+    IgemmArgs a;
+    a.x = x;
+    a.w = w;
+    a.scale = scale;
+    a.bias = bias;
+    a.res = res;
+    a.y = y;
+    a.partial = p.tile.splitk > 1 ? static_cast<float*>(ws) : nullptr;
+    a.cin = g.cin;
+    a.H = g.h;
+    a.W = g.w;
+    a.cout = g.cout;
+    a.stride = g.stride;
+    a.pad = g.pad;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    const int ohw = g.oh * g.ow;
+    a.tc = p.tile.tc;
+    a.tiles_per_img = (int)igemm_tiles_per_image(g, tile, a.tc);
+    a.tiles_w = a.tc > 0 ? (g.ow + a.tc - 1) / a.tc : 0;
+    fastdiv_params(a.tc > 0 ? a.tc : 1, &a.m_tc, &a.l_tc);
+    const int nchunks = (g.cin + kCK - 1) / kCK;
+    a.chunks_per_split = (nchunks + p.tile.splitk - 1) / p.tile.splitk;
+    region(g, t.bn, a.tc, &a.PR, &a.PC);
+    fastdiv_params(a.PR * a.PC, &a.m_rc, &a.l_rc);
+    fastdiv_params(a.PC, &a.m_c, &a.l_c);
+    fastdiv_params(g.ow, &a.m_ow, &a.l_ow);
+    a.act = g.act;
+    a.res_mode = g.res_mode;
+    dim3 grid((unsigned)(g.n * a.tiles_per_img), (unsigned)((g.cout + t.bm - 1) / t.bm),
+              (unsigned)p.tile.splitk);
     if (g.k == 1)
-        e = launch_igemm_k<1>(g, p, x, w, scale, bias, res, y, partial, s);
-    else if (g.k == 3)
-        e = launch_igemm_k<3>(g, p, x, w, scale, bias, res, y, partial, s);
+        launch_k<1>(tile, grid, lds, s, a);
     else
-        return hipErrorInvalidValue;
-    if (e != hipSuccess || partial == nullptr) return e;
-    const long total = (long)g.n * g.cout * g.oh * g.ow;
-    dim3 grid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL(k_splitk_finish, grid, dim3(256), 0, s, partial, p.tile.splitk, total,
-                       g.cout, g.oh * g.ow, scale, bias, res, y, g.act, g.res_mode);
+        launch_k<3>(tile, grid, lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.partial == nullptr) return e;
+    const long total = (long)g.n * g.cout * ohw;
+    dim3 fgrid((unsigned)((total + 255) / 256));
+    hipLaunchKernelGGL(k_splitk_finish, fgrid, dim3(256), 0, s, a.partial, p.tile.splitk, total,
+                       g.cout, ohw, scale, bias, res, y, g.act, g.res_mode);
     return hipGetLastError();
 }
 

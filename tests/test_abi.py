@@ -114,13 +114,24 @@ def test_aliasing_rejected():
     assert _call(d, y=S - 4) == -5                  # y's tail covers scale
     r = _desc(res_mode=cvx.CVX_RES_AFTER_ACT)
     assert _call(r, r=Y + 4) == -5
-    # residual may equal x (read only), so that is not an aliasing error; a missing
-    # workspace is the next error this split-K shape reports
+    # residual may equal x (read only), so that is not an aliasing error; on a
+    # shape whose plan splits the reduction, the missing workspace is the next
+    # error reported (nothing is launched)
+    r = _split_desc(res_mode=cvx.CVX_RES_AFTER_ACT)
     assert _call(r, r=X) == -6
 
 
+def _split_desc(**kw):
+    """A layer whose plan splits the reduction over workgroups (needs a workspace)."""
+    for cin, hw in ((256, 20), (512, 20), (1024, 10), (2048, 7), (4096, 4)):
+        d = _desc(c_in=cin, h=hw, w=hw, c_out=256, **kw)
+        if cvx.cvx_conv_workspace_bytes(d) > 0:
+            return d
+    raise AssertionError("no split-reduction plan among the candidate shapes")
+
+
 def test_workspace_checks():
-    d = _desc(c_in=256, h=20, w=20, c_out=256)      # split-K plan
+    d = _split_desc()
     need = cvx.cvx_conv_workspace_bytes(d)
     assert need > 0
     assert _call(d) == -6

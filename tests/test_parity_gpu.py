@@ -284,3 +284,25 @@ def test_forward_repeat_is_stable():
     b = net(x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# every compiled tile configuration, both pixel layouts, with and without a split
+# reduction, on shapes with ragged edges in both dimensions
+FORCED = [(kind, tc, sk) for kind in range(4) for tc in (0, 4, 8, 16, 32) for sk in (1, 3)]
+
+
+@pytest.mark.parametrize("force", FORCED, ids=[f"t{k}tc{t}sk{s}" for k, t, s in FORCED])
+def test_igemm_forced_tiles(force, monkeypatch):
+    monkeypatch.setenv("CVX_IGEMM_TILE", "%d,%d,%d" % force)
+    for seed, n, cin, h, w, cout, k, s, p in [(200, 2, 48, 19, 27, 70, 3, 1, 1),
+                                              (201, 1, 40, 23, 21, 33, 3, 2, 1),
+                                              (202, 2, 64, 9, 13, 96, 1, 1, 0)]:
+        x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
+        d = cvx.make_desc(n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
+        plan = cvx.cvx_conv_plan(d)
+        oh, ow = cvx.cvx_conv_out_shape(d)
+        r = wl.residual_for(seed, (n, cout, oh, ow))
+        say(f"forced {force} seed {seed}: {plan}")
+        y, ok = gpu_conv(x, L, r)
+        assert ok, "write outside the output"
+        check(y, oracle_conv(x, L, r), f"forced {force} seed {seed}")
