@@ -40,6 +40,7 @@ cvx_status geom_from_desc(const cvx_conv_desc* d, ConvGeom* g)
     if (d == nullptr) return CVX_ERR_NULL;
     if (d->act < CVX_ACT_NONE || d->act > CVX_ACT_SILU) return CVX_ERR_ARG;
     if (d->res_mode < CVX_RES_NONE || d->res_mode > CVX_RES_AFTER_ACT) return CVX_ERR_ARG;
+    if (d->w_layout != CVX_W_OIHW && d->w_layout != CVX_W_PACKED) return CVX_ERR_ARG;
     if (d->n < 1 || d->c_in < 1 || d->h < 1 || d->w < 1 || d->c_out < 1) return CVX_ERR_SHAPE;
     if (d->kh < 1 || d->kw < 1 || d->stride < 1 || d->pad < 0 || d->groups < 1)
         return CVX_ERR_SHAPE;
@@ -55,7 +56,7 @@ cvx_status geom_from_desc(const cvx_conv_desc* d, ConvGeom* g)
     if ((long)d->n * d->c_out * oh * ow > kMaxElems) return CVX_ERR_SHAPE;
     if ((long)d->c_out * (d->c_in / d->groups) * d->kh * d->kw > kMaxElems) return CVX_ERR_SHAPE;
     *g = {d->n, d->c_in, d->h, d->w, d->c_out, d->kh, d->stride, d->pad, d->groups,
-          d->act, d->res_mode, oh, ow};
+          d->act, d->res_mode, oh, ow, d->w_layout};
     return CVX_OK;
 }
 
@@ -104,7 +105,8 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
     const double kCUs = 256.0, kFlopPerClk = 256.0, kChunkClk = 400.0, kStartClk = 3000.0,
-                 kLaunchClk = 4000.0, kBytesPerClk = 2000.0;
+                 kLaunchClk = 4000.0, kBytesPerClk = 2000.0, kLatencyClk = 2200.0;
+    const bool packed = g.w_layout == CVX_W_PACKED;
     const int ck = igemm_chunk_channels();
     const int nchunks = (g.cin + ck - 1) / ck;
     const int kk = g.k * g.k;
@@ -114,7 +116,9 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
         int bm, bn;
         igemm_tile_shape(tile, &bm, &bn);
         for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
-            if (!igemm_tile_fits(g, tile, tc, nullptr)) continue;
+            if (!(packed ? packed_tile_fits(g, tile, tc, nullptr)
+                         : igemm_tile_fits(g, tile, tc, nullptr)))
+                continue;
             const double stage_clk = igemm_stage_floats(g, tile, tc) / 256.0 * 6.0;
             const long tiles = (long)g.n * igemm_tiles_per_image(g, tile, tc) *
                                ((g.cout + bm - 1) / bm);
@@ -124,9 +128,19 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
                 if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
                 const long wgs = tiles * sk;
                 const double rounds = std::ceil(wgs / kCUs);
-                const double wg_clk = 2.0 * bm * bn * per * ck * kk / kFlopPerClk +
-                                      per * (kChunkClk + stage_clk) + kStartClk;
-                double cost = rounds * wg_clk;
+                const double chunk_mfma = 2.0 * bm * bn * ck * kk / kFlopPerClk;
+                double wg_clk;
+                if (packed) {
+                    // one memory round trip per stage of cps chunks, overlapped with
+                    // the previous stage's matrix work
+                    const int cps = packed_chunks_per_stage(tile, g.k);
+                    const int stages = (per + cps - 1) / cps;
+                    wg_clk = stages * std::max(kLatencyClk, cps * chunk_mfma + kChunkClk) +
+                             kLatencyClk + kStartClk;
+                } else {
+                    wg_clk = per * (chunk_mfma + kChunkClk + stage_clk) + kStartClk;
+                }
+                double cost = rounds * wg_clk + 1e-3 * wgs;  // ties: fewer workgroups
                 if (sk > 1)
                     cost += kLaunchClk +
                             (double)g.n * g.cout * g.oh * g.ow * 4.0 * (sk + 2) / kBytesPerClk;
@@ -144,14 +158,15 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
         if (sscanf(env, "%d,%d,%d", &kind, &tc, &sk) == 3 && kind >= 0 &&
             kind < igemm_num_tiles() && sk >= 1 && sk <= nchunks &&
             (long)(sk - 1) * ((nchunks + sk - 1) / sk) < nchunks &&
-            igemm_tile_fits(g, kind, tc, nullptr)) {
+            (packed ? packed_tile_fits(g, kind, tc, nullptr)
+                    : igemm_tile_fits(g, kind, tc, nullptr))) {
             int bm, bn;
             igemm_tile_shape(kind, &bm, &bn);
             bt = GemmTile{kind, bm, bn, tc, sk};
         }
     }
     if (bt.kind < 0) return false;
-    p->fam = FAM_IGEMM;
+    p->fam = packed ? FAM_IGEMM_PACKED : FAM_IGEMM;
     p->tile = bt;
     p->ws_bytes = bt.splitk > 1 ? (size_t)bt.splitk * g.n * g.cout * g.oh * g.ow * sizeof(float) : 0;
     return true;
@@ -186,13 +201,31 @@ cvx_status launch_conv(const ConvGeom& g, const Plan& p, const float* x, const f
     case FAM_DEPTHWISE: e = launch_depthwise(g, p, x, w, scale, bias, res, y, s); break;
     case FAM_DIRECT: e = launch_direct(g, p, x, w, scale, bias, res, y, s); break;
     case FAM_IGEMM: e = launch_igemm(g, p, x, w, scale, bias, res, y, ws, s); break;
+    case FAM_IGEMM_PACKED: e = launch_igemm_packed(g, p, x, w, scale, bias, res, y, ws, s); break;
     }
     return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
 }
 
 size_t elems_in(const ConvGeom& g) { return (size_t)g.n * g.cin * g.h * g.w; }
 size_t elems_out(const ConvGeom& g) { return (size_t)g.n * g.cout * g.oh * g.ow; }
-size_t elems_w(const ConvGeom& g) { return (size_t)g.cout * (g.cin / g.groups) * g.k * g.k; }
+size_t elems_oihw(const ConvGeom& g) { return (size_t)g.cout * (g.cin / g.groups) * g.k * g.k; }
+
+// floats of the packed form of a layer's weights (a copy of OIHW unless the plan
+// for the packed layout is the packed implicit-GEMM kernel)
+size_t elems_packed(const ConvGeom& g)
+{
+    ConvGeom gp = g;
+    gp.w_layout = CVX_W_PACKED;
+    Plan p;
+    if (make_plan(gp, &p) == CVX_OK && p.fam == FAM_IGEMM_PACKED)
+        return (size_t)packed_weight_floats(gp);
+    return elems_oihw(g);
+}
+
+size_t elems_w(const ConvGeom& g)
+{
+    return g.w_layout == CVX_W_PACKED ? elems_packed(g) : elems_oihw(g);
+}
 
 }  // namespace
 
@@ -241,6 +274,12 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
     st = make_plan(g, &p);
     if (st != CVX_OK) return st;
     switch (p.fam) {
+    case FAM_IGEMM_PACKED:
+        snprintf(buf, buf_len,
+                 "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=cvx::k_igemm_packed<%d, %d",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk,
+                 p.tile.bm, p.tile.bn);
+        break;
     case FAM_DEPTHWISE:
         snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d kernel=cvx::k_depthwise3x3<%d>",
                  g.stride, p.dw_ppb, p.dw_toh, g.stride);
@@ -266,6 +305,39 @@ size_t cvx_conv_workspace_bytes(const cvx_conv_desc* d)
     Plan p;
     if (make_plan(g, &p) != CVX_OK) return 0;
     return p.ws_bytes;
+}
+
+size_t cvx_packed_weights_bytes(const cvx_conv_desc* d)
+{
+    ConvGeom g;
+    if (geom_from_desc(d, &g) != CVX_OK) return 0;
+    Plan p;
+    if (make_plan(g, &p) != CVX_OK) return 0;
+    return elems_packed(g) * sizeof(float);
+}
+
+cvx_status cvx_pack_weights(const cvx_conv_desc* d, const float* w_oihw, float* w_packed,
+                            void* stream)
+{
+    ConvGeom g;
+    cvx_status st = geom_from_desc(d, &g);
+    if (st != CVX_OK) return st;
+    if (!w_oihw || !w_packed) return CVX_ERR_NULL;
+    if (!aligned4(w_oihw) || !aligned4(w_packed)) return CVX_ERR_ALIGN;
+    Plan p;
+    st = make_plan(g, &p);
+    if (st != CVX_OK) return st;
+    const size_t np = elems_packed(g), no = elems_oihw(g);
+    if (overlap(span(w_packed, np * sizeof(float)), span(w_oihw, no * sizeof(float))))
+        return CVX_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ConvGeom gp = g;
+    gp.w_layout = CVX_W_PACKED;
+    Plan pp;
+    make_plan(gp, &pp);
+    hipError_t e = pp.fam == FAM_IGEMM_PACKED ? launch_pack_weights(g, w_oihw, w_packed, s)
+                                              : launch_copy(w_oihw, w_packed, (long)no, s);
+    return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
 }
 
 cvx_status cvx_fold_bn(const float* gamma, const float* beta, const float* mean, const float* var,

@@ -14,13 +14,15 @@ namespace cvx {
 enum Family : int {
     FAM_DEPTHWISE = 0,  // depthwise 3x3 direct kernel, LDS halo tile per plane
     FAM_DIRECT = 1,     // direct VALU kernel (tiny c_in stems, grouped, large k)
-    FAM_IGEMM = 2,      // implicit GEMM on fp32 MFMA (dense 1x1 and 3x3)
+    FAM_IGEMM = 2,      // implicit GEMM on fp32 MFMA (dense 1x1 and 3x3), OIHW weights
+    FAM_IGEMM_PACKED = 3,  // the same, weights pre-packed in MFMA operand order
 };
 
 // Geometry of one convolution, derived from a validated cvx_conv_desc.
 struct ConvGeom {
     int n, cin, h, w, cout, k, stride, pad, groups, act, res_mode;
     int oh, ow;
+    int w_layout;  // CVX_W_OIHW or CVX_W_PACKED
 };
 
 // Tile configuration for the implicit-GEMM family.
@@ -66,7 +68,25 @@ hipError_t launch_preprocess(const unsigned char* src, int n, int src_h, int src
                              long src_row_bytes, float* dst, int dst_h, int dst_w,
                              const float mean[3], const float stdv[3], hipStream_t s);
 
+hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
+                               const float* scale, const float* bias, const float* res, float* y,
+                               void* ws, hipStream_t s);
+
+hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s);
+
+hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* partial,
+                                const float* scale, const float* bias, const float* res, float* y,
+                                hipStream_t s);
+
+hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s);
+
+// floats of the packed weight layout of the implicit-GEMM family
+long packed_weight_floats(const ConvGeom& g);
+bool packed_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes);
+int packed_chunks_per_stage(int tile, int k);
+
 // igemm helpers used by the planner (defined next to the kernel).
+void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc);
 int igemm_num_tiles();
 void igemm_tile_shape(int tile, int* bm, int* bn);
 bool igemm_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes);

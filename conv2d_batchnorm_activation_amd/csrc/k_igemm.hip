@@ -388,7 +388,7 @@ int igemm_num_tiles() { return kNumTiles; }
 
 // Staged region per channel (rows x columns) for tile kind `tile` with layout tc
 // (0 = runs of pixels, else 2-D tiles of BN/tc rows x tc columns).
-static void region(const ConvGeom& g, int bn, int tc, int* pr, int* pc)
+void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc)
 {
     if (tc > 0) {
         *pr = (bn / tc - 1) * g.stride + g.k;
@@ -420,7 +420,7 @@ long igemm_tiles_per_image(const ConvGeom& g, int tile, int tc)
 long igemm_stage_floats(const ConvGeom& g, int tile, int tc)
 {
     int pr, pc;
-    region(g, kTiles[tile].bn, tc, &pr, &pc);
+    igemm_region(g, kTiles[tile].bn, tc, &pr, &pc);
     return (long)kCK * pr * pc + (long)kTiles[tile].bm * kCK * g.k * g.k;
 }
 
@@ -434,7 +434,7 @@ bool igemm_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes)
         return false;
     if (tc < 0 || (tc > 0 && (t.bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
     int pr, pc;
-    region(g, t.bn, tc, &pr, &pc);
+    igemm_region(g, t.bn, tc, &pr, &pc);
     const long re = (long)kCK * pr * pc;
     if (re > 256L * t.npx) return false;
     const int kk = g.k * g.k;
@@ -500,14 +500,13 @@ hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const 
     a.pad = g.pad;
     a.OH = g.oh;
     a.OW = g.ow;
-    const int ohw = g.oh * g.ow;
     a.tc = p.tile.tc;
     a.tiles_per_img = (int)igemm_tiles_per_image(g, tile, a.tc);
     a.tiles_w = a.tc > 0 ? (g.ow + a.tc - 1) / a.tc : 0;
     fastdiv_params(a.tc > 0 ? a.tc : 1, &a.m_tc, &a.l_tc);
     const int nchunks = (g.cin + kCK - 1) / kCK;
     a.chunks_per_split = (nchunks + p.tile.splitk - 1) / p.tile.splitk;
-    region(g, t.bn, a.tc, &a.PR, &a.PC);
+    igemm_region(g, t.bn, a.tc, &a.PR, &a.PC);
     fastdiv_params(a.PR * a.PC, &a.m_rc, &a.l_rc);
     fastdiv_params(a.PC, &a.m_c, &a.l_c);
     fastdiv_params(g.ow, &a.m_ow, &a.l_ow);
@@ -521,10 +520,17 @@ hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const 
         launch_k<3>(tile, grid, lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.partial == nullptr) return e;
-    const long total = (long)g.n * g.cout * ohw;
+    return launch_splitk_finish(g, p.tile.splitk, a.partial, scale, bias, res, y, s);
+}
+
+hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* partial,
+                                const float* scale, const float* bias, const float* res, float* y,
+                                hipStream_t s)
+{
+    const long total = (long)g.n * g.cout * g.oh * g.ow;
     dim3 fgrid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL(k_splitk_finish, fgrid, dim3(256), 0, s, a.partial, p.tile.splitk, total,
-                       g.cout, ohw, scale, bias, res, y, g.act, g.res_mode);
+    hipLaunchKernelGGL(k_splitk_finish, fgrid, dim3(256), 0, s, partial, splitk, total, g.cout,
+                       g.oh * g.ow, scale, bias, res, y, g.act, g.res_mode);
     return hipGetLastError();
 }
 

@@ -77,4 +77,19 @@ hipError_t launch_gap_fc(const float* x, int n, int c, int hw, const float* fc_w
     return hipGetLastError();
 }
 
+// Plain copy (the packed form of weights that the direct kernels read as OIHW).
+__global__ void __launch_bounds__(256) k_copy(const float* __restrict__ src, float* __restrict__ dst,
+                                              long n)
+{
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s)
+{
+    dim3 grid((unsigned)((n + 255) / 256));
+    hipLaunchKernelGGL(k_copy, grid, dim3(256), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
 }  // namespace cvx

@@ -28,6 +28,7 @@ CVX_ACT_NONE, CVX_ACT_RELU, CVX_ACT_SILU = 0, 1, 2
 CVX_RES_NONE, CVX_RES_BEFORE_ACT, CVX_RES_AFTER_ACT = 0, 1, 2
 CVX_L_CONV, CVX_L_GAP, CVX_L_FC, CVX_L_PREPROC = 0, 1, 2, 3
 CVX_INPUT, CVX_NO_RES = -1, -2
+CVX_W_OIHW, CVX_W_PACKED = 0, 1
 STATUS_NAMES = {0: "CVX_OK", -1: "CVX_ERR_NULL", -2: "CVX_ERR_SHAPE", -3: "CVX_ERR_UNSUPPORTED",
                 -4: "CVX_ERR_ALIGN", -5: "CVX_ERR_ALIAS", -6: "CVX_ERR_WORKSPACE",
                 -7: "CVX_ERR_HIP", -8: "CVX_ERR_ARG"}
@@ -36,7 +37,7 @@ STATUS_NAMES = {0: "CVX_OK", -1: "CVX_ERR_NULL", -2: "CVX_ERR_SHAPE", -3: "CVX_E
 class cvx_conv_desc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in
                 ("n", "c_in", "h", "w", "c_out", "kh", "kw", "stride", "pad", "groups", "act",
-                 "res_mode")]
+                 "res_mode", "w_layout")]
 
 
 class cvx_layer(ctypes.Structure):
@@ -63,6 +64,10 @@ lib.cvx_conv_plan.argtypes = [_DP, ctypes.c_char_p, _I]
 lib.cvx_conv_plan.restype = _I
 lib.cvx_conv_workspace_bytes.argtypes = [_DP]
 lib.cvx_conv_workspace_bytes.restype = _Z
+lib.cvx_packed_weights_bytes.argtypes = [_DP]
+lib.cvx_packed_weights_bytes.restype = _Z
+lib.cvx_pack_weights.argtypes = [_DP, _P, _P, _P]
+lib.cvx_pack_weights.restype = _I
 lib.cvx_fold_bn.argtypes = [_P, _P, _P, _P, ctypes.c_float, _I, _P, _P, _P]
 lib.cvx_fold_bn.restype = _I
 lib.cvx_conv_bn_act.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
@@ -81,7 +86,7 @@ lib.cvx_forward.restype = _I
 
 #: every entry point include/cvx.h declares
 EXPORTS = ("cvx_status_str", "cvx_version", "cvx_conv_out_shape", "cvx_conv_plan",
-           "cvx_conv_workspace_bytes", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
+           "cvx_conv_workspace_bytes", "cvx_packed_weights_bytes", "cvx_pack_weights", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
            "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward")
 
 
@@ -117,8 +122,8 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(n, c_in, h, w, c_out, k, stride, pad, groups=1, act=CVX_ACT_NONE,
-              res_mode=CVX_RES_NONE) -> cvx_conv_desc:
-    return cvx_conv_desc(n, c_in, h, w, c_out, k, k, stride, pad, groups, act, res_mode)
+              res_mode=CVX_RES_NONE, w_layout=CVX_W_OIHW) -> cvx_conv_desc:
+    return cvx_conv_desc(n, c_in, h, w, c_out, k, k, stride, pad, groups, act, res_mode, w_layout)
 
 
 def cvx_status_str(status: int) -> str:
@@ -144,6 +149,15 @@ def cvx_conv_plan(desc: cvx_conv_desc) -> str:
 
 def cvx_conv_workspace_bytes(desc: cvx_conv_desc) -> int:
     return lib.cvx_conv_workspace_bytes(ctypes.byref(desc))
+
+
+def cvx_packed_weights_bytes(desc: cvx_conv_desc) -> int:
+    return lib.cvx_packed_weights_bytes(ctypes.byref(desc))
+
+
+def cvx_pack_weights(desc: cvx_conv_desc, w_oihw, w_packed, stream=None) -> None:
+    _check(lib.cvx_pack_weights(ctypes.byref(desc), _ptr(w_oihw), _ptr(w_packed), _stream(stream)),
+           "cvx_pack_weights")
 
 
 def cvx_fold_bn(gamma, beta, mean, var, eps: float, scale, bias, stream=None) -> None:

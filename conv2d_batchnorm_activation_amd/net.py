@@ -29,7 +29,8 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 
 class Net:
-    def __init__(self, layers: Sequence, input_shape: Sequence[int], device="cuda", eps: float = EPS):
+    def __init__(self, layers: Sequence, input_shape: Sequence[int], device="cuda", eps: float = EPS,
+                 w_layout: int = 1):
         self.device = torch.device(device)
         self.keep: List[torch.Tensor] = []
         self.input_shape = tuple(input_shape)
@@ -58,10 +59,16 @@ class Net:
             elif L.kind == cvx.CVX_L_CONV:
                 n, c, h, w = s_in
                 d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act,
-                                  L.res_mode)
+                                  L.res_mode, w_layout)
                 oh, ow = cvx.cvx_conv_out_shape(d)
                 p = L.params
                 wt = _dev(p["w"], self.device)
+                if w_layout == cvx.CVX_W_PACKED:
+                    wpk = torch.empty(cvx.cvx_packed_weights_bytes(d) // 4, dtype=torch.float32,
+                                      device=self.device)
+                    cvx.cvx_pack_weights(d, wt, wpk)
+                    self.keep.append(wt)
+                    wt = wpk
                 g, b, m, v = (_dev(p[k], self.device) for k in ("gamma", "beta", "mean", "var"))
                 scale = torch.empty(L.cout, dtype=torch.float32, device=self.device)
                 bias = torch.empty_like(scale)

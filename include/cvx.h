@@ -61,6 +61,13 @@ enum { CVX_ACT_NONE = 0, CVX_ACT_RELU = 1, CVX_ACT_SILU = 2 };
  *                       Optimisation", "Improvements", #7, now in the epilogue). */
 enum { CVX_RES_NONE = 0, CVX_RES_BEFORE_ACT = 1, CVX_RES_AFTER_ACT = 2 };
 
+/* Layout of the weight buffer a layer is given.  OIHW: [c_out][c_in/groups][kh][kw]
+ * as is.  PACKED: the buffer cvx_pack_weights produced from the OIHW weights for the
+ * same descriptor (a one-time transform at model load into the order the matrix
+ * cores read; "YOLO26N Inference Optimisation", "NHWC migration", "Weight
+ * layout").  Both give the same results; PACKED is the fast path. */
+enum { CVX_W_OIHW = 0, CVX_W_PACKED = 1 };
+
 /* One convolution layer.  Output extent: oh = (h + 2*pad - kh)/stride + 1 (floor),
  * likewise ow.  Supported: 1 <= kh, kw <= 7, 1 <= stride <= 4, 0 <= pad < k,
  * groups dividing c_in and c_out; dilation 1.  n*c*h*w of every tensor must stay
@@ -72,6 +79,7 @@ typedef struct cvx_conv_desc {
     int groups;          /* 1 = dense; c_in = c_out = groups: depthwise */
     int act;             /* CVX_ACT_*                              */
     int res_mode;        /* CVX_RES_*                              */
+    int w_layout;        /* CVX_W_OIHW or CVX_W_PACKED             */
 } cvx_conv_desc;
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -93,6 +101,23 @@ CVX_API cvx_status cvx_conv_plan(const cvx_conv_desc *d, char *buf, int buf_len)
 /* Workspace bytes cvx_conv_bn_act needs for `d` (0 when the selected kernel
  * needs none).  Host-only. */
 CVX_API size_t cvx_conv_workspace_bytes(const cvx_conv_desc *d);
+
+/* Bytes of the weight buffer cvx_pack_weights writes for `d` (whatever
+ * d->w_layout says).  Host only; 0 on an invalid descriptor. */
+CVX_API size_t cvx_packed_weights_bytes(const cvx_conv_desc *d);
+
+/*
+ * cvx_pack_weights -- one-time weight transform for layers run with
+ * w_layout = CVX_W_PACKED.  For the dense 1x1/3x3 kernels the OIHW weights are
+ * reordered into the matrix cores' operand order (zero-padded to whole 32-row,
+ * 16-channel and 4-tap groups); for the other kernels the packed form is a copy
+ * of the OIHW weights.  The packed form does not depend on anything but the
+ * descriptor's shape fields.
+ *   w_oihw : device [c_out][c_in/groups][kh][kw], read only.
+ *   w_packed: device, cvx_packed_weights_bytes(d) bytes, written; must not overlap w_oihw.
+ */
+CVX_API cvx_status cvx_pack_weights(const cvx_conv_desc *d, const float *w_oihw, float *w_packed,
+                                    void *stream);
 
 /*
  * cvx_fold_bn -- fold inference BatchNorm into a per-channel affine map:
@@ -122,7 +147,8 @@ CVX_API cvx_status cvx_fold_bn(const float *gamma, const float *beta, const floa
  * selected plan splits the reduction; then the workspace holds the partial sums).
  *   d        : host, layer description.
  *   x        : device [n][c_in][h][w].
- *   w        : device [c_out][c_in/groups][kh][kw].
+ *   w        : device; [c_out][c_in/groups][kh][kw] when d->w_layout is CVX_W_OIHW,
+ *              the cvx_pack_weights output for d when it is CVX_W_PACKED.
  *   scale,bias: device [c_out] (from cvx_fold_bn).
  *   residual : device [n][c_out][oh][ow]; required iff d->res_mode != CVX_RES_NONE,
  *              may equal x (read only) but must not overlap y.
@@ -181,7 +207,7 @@ typedef struct cvx_layer {
     cvx_conv_desc conv;    /* CONV: full description; GAP: n, c_in, h, w;
                               FC: n, c_in (in features), c_out; PREPROC: n, and
                               h, w = source frame height and width                */
-    const float *w;        /* CONV: OIHW weights; FC: [c_out][c_in] (device)       */
+    const float *w;        /* CONV: weights in conv.w_layout; FC: [c_out][c_in]    */
     const float *scale;    /* CONV: folded scale [c_out] (device)                  */
     const float *bias;     /* CONV: folded bias [c_out]; FC: bias [c_out] (device) */
     int dst_h, dst_w;      /* PREPROC: output extent                               */

@@ -73,7 +73,7 @@ def test_out_shape(h, k, s, p, expect):
     (dict(groups=3), -2),                         # 64 % 3 != 0
     (dict(k=9), -3), (dict(stride=5), -3), (dict(pad=3), -3),
     (dict(h=1, w=1, pad=0), -2),                  # window larger than the image
-    (dict(act=3), -8), (dict(res_mode=7), -8), (dict(act=-1), -8),
+    (dict(act=3), -8), (dict(res_mode=7), -8), (dict(act=-1), -8), (dict(w_layout=2), -8),
     (dict(n=70000), -2),
     (dict(n=4096, c_in=1024, h=1024, w=1024), -2),  # > 2^31 elements
 ])

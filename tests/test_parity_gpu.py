@@ -32,13 +32,22 @@ def setup_module(module):
         pytest.skip("no GPU")
 
 
-def gpu_conv(x, L, residual=None, guard=True):
-    """One layer through cvx_fold_bn + cvx_conv_bn_act.  Returns (y, guards_ok)."""
+PACKED, OIHW = 1, 0
+
+
+def gpu_conv(x, L, residual=None, layout=PACKED):
+    """One layer through cvx_fold_bn (+ cvx_pack_weights) + cvx_conv_bn_act.
+    Returns (y, guards_ok)."""
     n, c, h, w = x.shape
-    d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode)
+    d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
+                      layout)
     oh, ow = cvx.cvx_conv_out_shape(d)
     p = L.params
     xt, wt = dev(x), dev(p["w"])
+    if layout == PACKED:
+        wp = torch.full((cvx.cvx_packed_weights_bytes(d) // 4,), float("nan"), device=DEV)
+        cvx.cvx_pack_weights(d, wt, wp)
+        wt = wp
     g, b, m, v = (dev(p[k]) for k in ("gamma", "beta", "mean", "var"))
     scale = torch.empty(L.cout, device=DEV)
     bias = torch.empty(L.cout, device=DEV)
@@ -81,13 +90,14 @@ def test_single_depthwise_layer():
     check(y, oracle_conv(wk.x, wk.layers[0]), wk.name)
 
 
+@pytest.mark.parametrize("layout", [PACKED, OIHW], ids=["packed", "oihw"])
 @pytest.mark.parametrize("name", [s[0] for s in wl.SWEEP])
-def test_sweep_layer(name):
+def test_sweep_layer(name, layout):
     wk = wl.sweep_layer(name)
     L = wk.layers[0]
     r = wk.x if L.res_mode else None
-    say(f"sweep layer {name}")
-    y, ok = gpu_conv(wk.x, L, r)
+    say(f"sweep layer {name} layout {layout}")
+    y, ok = gpu_conv(wk.x, L, r, layout)
     assert ok, "write outside the output"
     check(y, oracle_conv(wk.x, L, r), name)
 
@@ -189,15 +199,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [PACKED, OIHW], ids=["packed", "oihw"])
 @pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
-def test_layer_sweep(case):
+def test_layer_sweep(case, layout):
     seed, n, cin, h, w, cout, k, s, p, g, act, rm = case
     x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, g, act, rm)
-    d = cvx.make_desc(n, cin, h, w, cout, k, s, p, g, act, rm)
+    d = cvx.make_desc(n, cin, h, w, cout, k, s, p, g, act, rm, layout)
     oh, ow = cvx.cvx_conv_out_shape(d)
     r = wl.residual_for(seed, (n, cout, oh, ow)) if rm else None
     say(f"case {case}: plan {cvx.cvx_conv_plan(d)}")
-    y, ok = gpu_conv(x, L, r)
+    y, ok = gpu_conv(x, L, r, layout)
     assert ok, "write outside the output"
     check(y, oracle_conv(x, L, r), f"case {seed}")
 
@@ -260,6 +271,22 @@ def test_gap_fc():
         check(out.cpu().numpy(), oracle.fc(oracle.gap(x), fw, fb), "gap_fc")
 
 
+def test_packed_weights_layout():
+    """The packed form holds every OIHW weight exactly once (the rest is zero
+    padding), for 3x3 and 1x1 shapes with ragged row, channel and tap groups."""
+    for (cout, cin, k) in [(70, 40, 3), (33, 19, 1), (256, 256, 3), (10, 192, 1)]:
+        d = cvx.make_desc(1, cin, 12, 12, cout, k, 1, k // 2, 1, 0, 0, PACKED)
+        w = np.random.default_rng(cout).normal(size=(cout, cin, k, k)).astype(np.float32)
+        wp = torch.full((cvx.cvx_packed_weights_bytes(d) // 4,), float("nan"), device=DEV)
+        say(f"pack weights {cout}x{cin}x{k}x{k}")
+        cvx.cvx_pack_weights(d, dev(w), wp)
+        torch.cuda.synchronize()
+        got = wp.cpu().numpy()
+        assert not np.isnan(got).any()
+        nz = np.sort(got[got != 0.0])
+        assert np.array_equal(nz, np.sort(w[w != 0.0].ravel()))
+
+
 def test_deterministic_across_runs():
     """Split reductions are summed in a fixed order: two runs are bit-identical."""
     for name in ("g_256x20_3x3", "f_256x20_1x1", "a_64x80_3x3"):
@@ -291,18 +318,19 @@ def test_forward_repeat_is_stable():
 FORCED = [(kind, tc, sk) for kind in range(4) for tc in (0, 4, 8, 16, 32) for sk in (1, 3)]
 
 
+@pytest.mark.parametrize("layout", [PACKED, OIHW], ids=["packed", "oihw"])
 @pytest.mark.parametrize("force", FORCED, ids=[f"t{k}tc{t}sk{s}" for k, t, s in FORCED])
-def test_igemm_forced_tiles(force, monkeypatch):
+def test_igemm_forced_tiles(force, layout, monkeypatch):
     monkeypatch.setenv("CVX_IGEMM_TILE", "%d,%d,%d" % force)
     for seed, n, cin, h, w, cout, k, s, p in [(200, 2, 48, 19, 27, 70, 3, 1, 1),
                                               (201, 1, 40, 23, 21, 33, 3, 2, 1),
                                               (202, 2, 64, 9, 13, 96, 1, 1, 0)]:
         x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
-        d = cvx.make_desc(n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
+        d = cvx.make_desc(n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT, layout)
         plan = cvx.cvx_conv_plan(d)
         oh, ow = cvx.cvx_conv_out_shape(d)
         r = wl.residual_for(seed, (n, cout, oh, ow))
         say(f"forced {force} seed {seed}: {plan}")
-        y, ok = gpu_conv(x, L, r)
+        y, ok = gpu_conv(x, L, r, layout)
         assert ok, "write outside the output"
         check(y, oracle_conv(x, L, r), f"forced {force} seed {seed}")
