@@ -69,6 +69,7 @@ def per_layer(wk, net, counts, reps: int):
             fn = lambda src=src, dst=dst, L=L: cvx.cvx_preprocess_u8(src, dst, L.pre_mean, L.pre_std)
             kernel = "cvx::k_preprocess"
             plan = "preprocess"
+            splitk = 1
         elif L.kind == cvx.CVX_L_CONV:
             lay = net.layers[i]
             d = lay.conv
@@ -81,6 +82,7 @@ def per_layer(wk, net, counts, reps: int):
                   cvx.cvx_conv_bn_act(d, xin, lay.w, lay.scale, lay.bias, res, y, ws, nws))
             plan = cvx.cvx_conv_plan(d)
             kernel = plan.split("kernel=")[1] if "kernel=" in plan else plan
+            splitk = int(plan.split("splitk=")[1].split()[0]) if "splitk=" in plan else 1
         else:
             continue
         ms = time_launches(fn, reps)
@@ -90,7 +92,8 @@ def per_layer(wk, net, counts, reps: int):
         bound = "mfma" if c["ai"] >= RIDGE else "hbm"
         frac = (gflops / (MFMA_F32_PEAK_TFLOPS * 1e3)) if bound == "mfma" else gbs / HBM_PEAK_GBS
         attainable = min(MFMA_F32_PEAK_TFLOPS * 1e3, c["ai"] * HBM_PEAK_GBS) if c["flop"] else None
-        rows.append({"layer": L.name, "plan": plan, "kernel": kernel, "us": round(us, 3),
+        rows.append({"layer": L.name, "plan": plan, "kernel": kernel, "splitk": splitk,
+                     "us": round(us, 3),
                      "gflop": c["flop"] / 1e9, "mbytes": c["bytes"] / 1e6, "ai": round(c["ai"], 2),
                      "gflops": round(gflops, 1), "gbs": round(gbs, 1), "bound": bound,
                      "frac_of_peak": round(frac, 4),
@@ -102,31 +105,259 @@ def per_layer(wk, net, counts, reps: int):
 
 
 def dominant(rows):
-    """Kernel with the largest total time over the forward's layers: its
-    algorithmic FLOPs (or bytes) per launch over its average launch time."""
+    """The kernel (exact template instantiation, as profilers name it) with the
+    largest total time over the forward's layers, and its roofline position:
+    algorithmic FLOPs (or bytes) per launch over its average launch time.
+
+    A split-K layer enqueues a second, finishing kernel, so its event time is not
+    one launch of the main kernel: the average is taken over the kernel's
+    single-launch layers (all of its layers when it has none of those)."""
     by = {}
     for r in rows:
-        k = by.setdefault(r["kernel"], {"us": 0.0, "flop": 0.0, "bytes": 0.0, "n": 0, "layers": []})
-        k["us"] += r["us"]
-        k["flop"] += r["gflop"] * 1e9
-        k["bytes"] += r["mbytes"] * 1e6
-        k["n"] += 1
-        k["layers"].append(r["layer"])
-    name, k = max(by.items(), key=lambda kv: kv[1]["us"])
-    avg_s = k["us"] / k["n"] * 1e-6
-    ai = k["flop"] / k["bytes"] if k["bytes"] else 0.0
-    if k["flop"] > 0 and ai >= RIDGE:
-        achieved = k["flop"] / k["n"] / avg_s / 1e12
+        k = by.setdefault(r["kernel"], [])
+        k.append(r)
+    name, group = max(by.items(), key=lambda kv: sum(r["us"] for r in kv[1]))
+    single = [r for r in group if r["splitk"] == 1]
+    use = single or group
+    n = len(use)
+    avg_us = sum(r["us"] for r in use) / n
+    flop = sum(r["gflop"] * 1e9 for r in use) / n
+    byts = sum(r["mbytes"] * 1e6 for r in use) / n
+    ai = flop / byts if byts else 0.0
+    if flop > 0 and ai >= RIDGE:
+        achieved = flop / (avg_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4)}
     else:
-        achieved = k["bytes"] / k["n"] / avg_s / 1e9
+        achieved = byts / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": None, "kernel": name, "launches_per_forward": k["n"],
-                 "avg_launch_us": round(k["us"] / k["n"], 3), "layers": k["layers"],
-                 "flop_per_launch": k["flop"] / k["n"], "bytes_per_launch": k["bytes"] / k["n"]})
+    roof.update({"traffic": traffic_for(name, [r["layer"] for r in use]),
+                 "kernel": name, "avg_launch_us": round(avg_us, 3),
+                 "measured_layers": [r["layer"] for r in use],
+                 "all_layers": [r["layer"] for r in group],
+                 "flop_per_launch": flop, "bytes_per_launch": byts})
     return roof
+
+
+# ---------------------------------------------------------------- HBM traffic
+# Measured HBM bytes per launch come from two rocprofv3 counter passes
+# (FETCH_SIZE, WRITE_SIZE) over `bench.py --pmc-probe`, scaled by what the same
+# counters read for a plain device copy of known size, and are kept as a small
+# text record under profiles/ together with a hash of the kernel's sources.  A
+# record whose hash no longer matches the sources is stale and gives null.
+CSRC = os.path.join(ROOT, "conv2d_batchnorm_activation_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    import hashlib
+    base = kernel.split("<")[0].split("::")[-1]
+    srcfile = {"k_igemm_packed": "k_igemm_packed.hip", "k_igemm": "k_igemm.hip",
+               "k_direct": "k_direct.hip", "k_depthwise3x3": "k_depthwise.hip",
+               "k_preprocess": "k_preprocess.hip"}.get(base)
+    h = hashlib.sha256()
+    for f in ([srcfile] if srcfile else []) + ["bufio.h", "epilogue.h", "cvx_internal.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_record(path: str) -> dict:
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", "|", " ")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    return rec
+
+
+TRAFFIC_FILE = os.path.join(PROFILES, "detector640_b1_traffic.txt")
+
+
+def traffic_for(kernel: str, layers) -> "float | None":
+    """Mean measured HBM bytes per launch of `kernel` over `layers`, from the
+    committed counter record, or None (no record, or the sources changed)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = kernel_sources_hash(kernel)
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if not line.startswith("record: "):
+                continue
+            rec = json.loads(line[len("record: "):])
+            if rec["kernel"] != kernel or rec["source_hash"] != want:
+                continue
+            per = rec["traffic_bytes_per_layer"]
+            if layers and all(l in per for l in layers):
+                return round(sum(per[l] for l in layers) / len(layers), 1)
+    return None
+
+
+COPY_BYTES = 64 << 20  # the calibration copy: 64 MiB read, 64 MiB written
+
+
+def pmc_probe(args) -> int:
+    """Short run for counter passes: one 64 MiB device copy (the calibration),
+    then each layer of the forward alone, `reps` times, in order.  Prints a
+    manifest line (JSON) that --pmc-summary uses to map dispatches to layers."""
+    import torch
+    import workloads as wl
+    from conv2d_batchnorm_activation_amd import accounting, cvx
+    from conv2d_batchnorm_activation_amd.net import Net
+    wk = wl.detector_pipeline(1)
+    net = Net(wk.layers, wk.x.shape)
+    counts = accounting.layer_counts(wk.layers, wk.x.shape)
+    calls = []
+    for i, L in enumerate(wk.layers):
+        s_in, s_out = net.layer_io[i]
+        if L.kind == cvx.CVX_L_PREPROC:
+            src = torch.from_numpy(wk.x).cuda()
+            dst = torch.empty(s_out, device="cuda")
+            calls.append((L.name, "cvx::k_preprocess", 1, counts[i]["bytes"],
+                          lambda src=src, dst=dst, L=L: cvx.cvx_preprocess_u8(src, dst, L.pre_mean, L.pre_std)))
+        elif L.kind == cvx.CVX_L_CONV:
+            lay = net.layers[i]
+            d = lay.conv
+            xin = torch.rand(s_in, device="cuda")
+            y = torch.empty(s_out, device="cuda")
+            res = xin if L.res_mode else None
+            nws = cvx.cvx_conv_workspace_bytes(d)
+            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+            plan = cvx.cvx_conv_plan(d)
+            splitk = int(plan.split("splitk=")[1].split()[0])
+            calls.append((L.name, plan.split("kernel=")[1], splitk, counts[i]["bytes"],
+                          lambda d=d, xin=xin, lay=lay, res=res, y=y, ws=ws, nws=nws:
+                          cvx.cvx_conv_bn_act(d, xin, lay.w, lay.scale, lay.bias, res, y, ws, nws)))
+    a = torch.empty(COPY_BYTES // 4, device="cuda").uniform_()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)  # calibration: marks the start of the probed dispatches
+    for name, kernel, splitk, byts, fn in calls:
+        for _ in range(args.reps):
+            fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"manifest": [{"layer": n, "kernel": k, "splitk": s, "reps": args.reps,
+                                    "algorithmic_bytes": by} for n, k, s, by, _ in calls]}))
+    return 0
+
+
+def _dispatches(d: str, counter: str):
+    """[(dispatch id, kernel name, counter value)] from a rocprofv3 counter CSV."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = int(r["Dispatch_Id"])
+                name, v = out.get(k, (r["Kernel_Name"], 0.0))
+                out[k] = (name, v + float(r["Counter_Value"]))
+    return [(k, n, v) for k, (n, v) in sorted(out.items())]
+
+
+def _probe_map(disp, manifest):
+    """Counter value per probed layer: the calibration copy is the last copy
+    dispatch moving about COPY_BYTES before the layers; the cvx dispatches after
+    it follow the manifest (a split-K layer adds one finishing dispatch per call,
+    not counted as the layer's main kernel)."""
+    cal = [i for i, (_, n, v) in enumerate(disp) if "copy" in n.lower() and "cvx::" not in n]
+    i0 = cal[-1]
+    cal_kib = disp[i0][2]
+    rest = [(n, v) for _, n, v in disp[i0 + 1:] if "cvx::" in n]
+    per, j = {}, 0
+    for m in manifest:
+        vals = []
+        for _ in range(m["reps"]):
+            n, v = rest[j]
+            assert m["kernel"] in n, (m, n)
+            vals.append(v)
+            j += 2 if m["splitk"] > 1 else 1
+        per[m["layer"]] = sum(vals) / len(vals)
+    return cal_kib, per
+
+
+def pmc_summary(args) -> int:
+    fetch_dir, write_dir = args.pmc_summary
+    with open(args.manifest) as fh:
+        manifest = json.loads(fh.read().strip().splitlines()[-1])["manifest"]
+    cf, fetch = _probe_map(_dispatches(fetch_dir, "FETCH_SIZE"), manifest)
+    cw, write = _probe_map(_dispatches(write_dir, "WRITE_SIZE"), manifest)
+    ff = COPY_BYTES / (cf * 1024.0)
+    fw = COPY_BYTES / (cw * 1024.0)
+    lines = ["# HBM traffic per launch, detector pipeline 640x640 b=1, each layer alone",
+             "",
+             f"Counter passes (rocprofv3 --pmc, one counter block per run): {args.cmd}",
+             "",
+             f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {cf:.0f} KiB "
+             f"(scale {ff:.4f}) and WRITE_SIZE {cw:.0f} KiB (scale {fw:.4f}).",
+             "traffic = FETCH_SIZE*1024*scale_f + WRITE_SIZE*1024*scale_w, averaged over the calls.",
+             "",
+             "| layer | kernel | FETCH KiB | WRITE KiB | traffic bytes | algorithmic bytes | traffic/alg |",
+             "|---|---|---|---|---|---|---|"]
+    recs = {}
+    for m in manifest:
+        L = m["layer"]
+        t = fetch[L] * 1024 * ff + write[L] * 1024 * fw
+        lines.append(f"| {L} | `{m['kernel']}` | {fetch[L]:.0f} | {write[L]:.0f} | {t:.0f} | "
+                     f"{m['algorithmic_bytes']:.0f} | {t / m['algorithmic_bytes']:.2f} |")
+        r = recs.setdefault(m["kernel"], {"kernel": m["kernel"],
+                                          "source_hash": kernel_sources_hash(m["kernel"]),
+                                          "traffic_bytes_per_layer": {}})
+        r["traffic_bytes_per_layer"][L] = round(t, 1)
+    lines.append("")
+    for r in recs.values():
+        lines.append("record: " + json.dumps(r))
+    print("\n".join(lines))
+    return 0
+
+
+def rocprof_summary(args) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(args.rocprof_summary, "**", "*kernel_stats.csv"), recursive=True)[0]
+    with open(f) as fh:
+        rows = list(csv.DictReader(fh))
+    print("# Kernel durations, detector pipeline 640x640 b=1 (bench.py)")
+    print()
+    print(f"Command: {args.cmd}")
+    print()
+    print("| kernel | calls | avg us | min us | max us | total % |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.1f} |")
+    traces = glob.glob(os.path.join(args.rocprof_summary, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        with open(traces[0]) as fh:
+            tr = list(csv.DictReader(fh))
+        groups = {}
+        for r in tr:
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if not name.startswith("cvx::"):
+                continue
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])) // max(wg, 1)
+            key = (name, r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"], grid,
+                   r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"], r["Scratch_Size"])
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        print()
+        print("Per launch shape (one row per layer shape):")
+        print()
+        print("| kernel | grid x,y,z (threads) | workgroups | vgpr | agpr | lds B | scratch | calls | avg us | median us |")
+        print("|---|---|---|---|---|---|---|---|---|---|")
+        for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            print(f"| `{key[0]}` | {key[1]},{key[2]},{key[3]} | {key[4]} | {key[5]} | {key[6]} | "
+                  f"{key[7]} | {key[8]} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | "
+                  f"{v[len(v) // 2] / 1e3:.2f} |")
+    return 0
 
 
 def cpu_baseline(wk, flop_per_forward: float, budget_s: float):
@@ -156,7 +387,20 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layers", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="short run for rocprofv3 counter passes (prints a manifest line)")
+    ap.add_argument("--reps", type=int, default=3, help="calls per layer in --pmc-probe")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two counter passes into the traffic record (stdout)")
+    ap.add_argument("--manifest", help="stdout of the --pmc-probe run (for --pmc-summary)")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="markdown table of a rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--cmd", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        return rocprof_summary(args)
+    if args.pmc_summary:
+        return pmc_summary(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
               f"multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -170,6 +414,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.pmc_probe:
+        return pmc_probe(args)
     wk = wl.detector_pipeline(args.batch)
     counts = accounting.layer_counts(wk.layers, wk.x.shape)
     flop = sum(c["flop"] for c in counts)

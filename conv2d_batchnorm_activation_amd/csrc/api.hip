@@ -273,26 +273,25 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
     Plan p;
     st = make_plan(g, &p);
     if (st != CVX_OK) return st;
+    char kn[96];
     switch (p.fam) {
     case FAM_IGEMM_PACKED:
-        snprintf(buf, buf_len,
-                 "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=cvx::k_igemm_packed<%d, %d",
-                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk,
-                 p.tile.bm, p.tile.bn);
+        packed_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+        snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
         break;
     case FAM_DEPTHWISE:
-        snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d kernel=cvx::k_depthwise3x3<%d>",
+        snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d splitk=1 kernel=cvx::k_depthwise3x3<%d>",
                  g.stride, p.dw_ppb, p.dw_toh, g.stride);
         break;
     case FAM_DIRECT:
-        snprintf(buf, buf_len, "direct k%d s%d cob=%d kernel=cvx::k_direct<%d>", g.k, g.stride,
-                 p.direct_cob, p.direct_cob);
+        snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
+                 g.stride, p.direct_cob, p.direct_cob);
         break;
     case FAM_IGEMM:
-        snprintf(buf, buf_len,
-                 "igemm_mfma k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=cvx::k_igemm<%d, %d",
-                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk,
-                 p.tile.bm, p.tile.bn);
+        igemm_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+        snprintf(buf, buf_len, "igemm_mfma k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
         break;
     }
     return CVX_OK;

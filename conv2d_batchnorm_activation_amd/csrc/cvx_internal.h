@@ -68,6 +68,11 @@ hipError_t launch_preprocess(const unsigned char* src, int n, int src_h, int src
                              long src_row_bytes, float* dst, int dst_h, int dst_w,
                              const float mean[3], const float stdv[3], hipStream_t s);
 
+// Exact symbol of the kernel a plan launches, as profilers print it
+// ("cvx::k_igemm_packed<32, 32, 1, 1, 4, 3, 24, 2>").
+void igemm_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
+void packed_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
+
 hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
                                const float* scale, const float* bias, const float* res, float* y,
                                void* ws, hipStream_t s);

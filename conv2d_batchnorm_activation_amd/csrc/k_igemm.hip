@@ -34,6 +34,8 @@
 // blockIdx.z; each slice stores raw partial sums in the workspace and a
 // finishing kernel adds the slices in slice order (deterministic) and applies
 // the epilogue.
+#include <stdio.h>
+
 #include "bufio.h"
 #include "cvx_internal.h"
 #include "epilogue.h"
@@ -521,6 +523,13 @@ hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.partial == nullptr) return e;
     return launch_splitk_finish(g, p.tile.splitk, a.partial, scale, bias, res, y, s);
+}
+
+void igemm_kernel_name(const ConvGeom& g, int tile, char* buf, int len)
+{
+    const TileKind& t = kTiles[tile];
+    snprintf(buf, len, "cvx::k_igemm<%d, %d, %d, %d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wn, t.wk,
+             g.k, kCK, t.npx);
 }
 
 hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* partial,

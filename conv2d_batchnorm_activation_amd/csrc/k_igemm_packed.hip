@@ -18,6 +18,8 @@
 //     instructions); out-of-range offsets deliver zeros, so padding is free.
 //   * two LDS buffers and two register sets: the loads for chunk i+1 are issued
 //     before the MFMAs of chunk i, and one barrier per chunk orders the buffers.
+#include <stdio.h>
+
 #include "bufio.h"
 #include "cvx_internal.h"
 #include "epilogue.h"
@@ -462,6 +464,13 @@ static constexpr PackedKind kPacked[] = {
 
 int packed_chunks_per_stage(int tile, int k) { return k == 3 ? kPacked[tile].cps3 : kPacked[tile].cps1; }
 constexpr int kNumPacked = sizeof(kPacked) / sizeof(kPacked[0]);
+
+void packed_kernel_name(const ConvGeom& g, int tile, char* buf, int len)
+{
+    const PackedKind& t = kPacked[tile];
+    snprintf(buf, len, "cvx::k_igemm_packed<%d, %d, %d, %d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wn,
+             t.wk, g.k, t.npx, packed_chunks_per_stage(tile, g.k));
+}
 
 long packed_weight_floats(const ConvGeom& g)
 {

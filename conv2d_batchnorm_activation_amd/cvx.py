@@ -142,8 +142,8 @@ def cvx_conv_out_shape(desc: cvx_conv_desc):
 
 
 def cvx_conv_plan(desc: cvx_conv_desc) -> str:
-    buf = ctypes.create_string_buffer(128)
-    _check(lib.cvx_conv_plan(ctypes.byref(desc), buf, 128), "cvx_conv_plan")
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.cvx_conv_plan(ctypes.byref(desc), buf, 256), "cvx_conv_plan")
     return buf.value.decode()
 
 

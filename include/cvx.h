@@ -95,7 +95,10 @@ CVX_API cvx_status cvx_conv_out_shape(const cvx_conv_desc *d, int *oh, int *ow);
 /* Host-only query: which kernel family and tile configuration the dispatcher
  * selects for `d` ("YOLO26N Inference Optimisation", "Improvements", #1 and #3:
  * one code path whose tile parameters are chosen per layer shape).  Writes a
- * short NUL-terminated description into buf (at most buf_len bytes). */
+ * short NUL-terminated description into buf (at most buf_len bytes, truncated
+ * to fit): family, tile, split-K factor ("splitk=S"; S > 1 adds a second,
+ * finishing launch) and, after "kernel=", the main kernel's symbol as profilers
+ * print it.  256 bytes always suffice. */
 CVX_API cvx_status cvx_conv_plan(const cvx_conv_desc *d, char *buf, int buf_len);
 
 /* Workspace bytes cvx_conv_bn_act needs for `d` (0 when the selected kernel
