@@ -7,6 +7,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "cvx_internal.h"
@@ -95,18 +98,97 @@ bool plan_depthwise(const ConvGeom& g, Plan* p)
     return true;
 }
 
-// Implicit-GEMM tile choice by a small cost model of one MI355X: 256 compute
-// units, one workgroup per unit per round, each unit retiring 256 fp32 MFMA
-// FLOP per clock; every chunk of input channels costs a fixed staging overhead,
-// every workgroup a fixed start-up latency, and a split reduction costs a
-// finishing pass over the partial sums.
+// Tuning and test override: CVX_IGEMM_TILE="kind,tc,splitk" forces a tile
+// configuration when it is valid for this shape (sweeps and coverage tests).
+bool forced_tile(int* kind, int* tc, int* sk)
+{
+    const char* env = getenv("CVX_IGEMM_TILE");
+    int k, t, s;
+    if (env == nullptr || sscanf(env, "%d,%d,%d", &k, &t, &s) != 3) return false;
+    *kind = k;
+    *tc = t;
+    *sk = s;
+    return true;
+}
+
+bool slices_ok(int nchunks, int sk)
+{
+    return sk >= 1 && sk <= nchunks && (long)(sk - 1) * ((nchunks + sk - 1) / sk) < nchunks;
+}
+
+// Packed-weight implicit GEMM: tile, tc and split count by a cost model of one
+// MI355X in clocks, fitted to in-kernel timelines (s_memtime per workgroup) of
+// the detector layers and to a sweep of every configuration of them.  A
+// workgroup pays a fixed ~6000 clocks (first loads from cold caches, the
+// cross-wave exchange, the epilogue); each stage of chunks costs its matrix time
+// (2 pairs x taps x NT x 64 clocks per SIMD and chunk) plus ~28 clocks per
+// vector-memory instruction the unit issues for it (the loads of a stage are
+// issued as a block); a split into s slices adds ~4000 + 800*NT*s clocks (the
+// partial sums' round trip through memory and the arrival count).  Up to
+// packed_occupancy(kind) workgroups share a compute unit, each slowing the
+// others by ~30%.
+bool plan_packed(const ConvGeom& g, Plan* p)
+{
+    if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
+    if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
+    const double kCUs = 256.0, kFixedClk = 6000.0, kLoadClk = 28.0, kSplitClk = 4000.0,
+                 kSplitEachClk = 800.0, kShare = 0.3;
+    const int nchunks = (g.cin + 15) / 16;
+    const int kk = g.k * g.k;
+    const long mblocks = (g.cout + 31) / 32;
+    double best = 1e300;
+    GemmTile bt{-1, 0, 0, 0, 1};
+    for (int kind = 0; kind < packed_num_kinds(); ++kind) {
+        const int bn = packed_tile_n(kind);
+        const int nt = bn / 32;
+        const int cps = packed_chunks_per_stage(kind, g.k);
+        const int occ = packed_occupancy(kind, g.k);
+        for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
+            if (!packed_tile_fits(g, kind, tc, nullptr)) continue;
+            const double stage = cps * (2.0 * kk * nt * 64.0 +
+                                        kLoadClk * packed_loads_per_chunk(g, kind, tc));
+            const long tiles = (long)g.n * packed_tiles_per_image(g, kind, tc) * mblocks;
+            for (int sk = 1; sk <= 8; ++sk) {
+                if (!slices_ok(nchunks, sk)) continue;
+                if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
+                const int per = (nchunks + sk - 1) / sk;
+                const int stages = (per + cps - 1) / cps;
+                const double wg = kFixedClk + stages * stage +
+                                  (sk > 1 ? kSplitClk + kSplitEachClk * nt * sk : 0.0);
+                const long wgs = tiles * sk;
+                const double per_cu = std::ceil(wgs / kCUs);  // workgroups one unit runs
+                const double together = std::min<double>(per_cu, occ);
+                const double cost = std::ceil(per_cu / together) * wg * (1.0 + kShare * (together - 1.0)) +
+                                    1e-3 * wgs;  // ties: fewer workgroups
+                if (cost < best) {
+                    best = cost;
+                    bt = GemmTile{kind, 32, bn, tc, sk};
+                }
+            }
+        }
+    }
+    int kind, tc, sk;
+    if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < packed_num_kinds() &&
+        slices_ok(nchunks, sk) && packed_tile_fits(g, kind, tc, nullptr))
+        bt = GemmTile{kind, 32, packed_tile_n(kind), tc, sk};
+    if (bt.kind < 0) return false;
+    p->fam = FAM_IGEMM_PACKED;
+    p->tile = bt;
+    p->ws_bytes = packed_workspace_bytes(g, bt.kind, bt.tc, bt.splitk);
+    return true;
+}
+
+// OIHW implicit GEMM (k_igemm.hip): tile choice by a small cost model of one
+// MI355X: 256 compute units, one workgroup per unit per round, each unit
+// retiring 256 fp32 MFMA FLOP per clock; every chunk of input channels costs a
+// fixed staging overhead, every workgroup a fixed start-up latency, and a split
+// reduction costs a finishing pass over the partial sums.
 bool plan_igemm(const ConvGeom& g, Plan* p)
 {
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
     const double kCUs = 256.0, kFlopPerClk = 256.0, kChunkClk = 400.0, kStartClk = 3000.0,
-                 kLaunchClk = 4000.0, kBytesPerClk = 2000.0, kLatencyClk = 2200.0;
-    const bool packed = g.w_layout == CVX_W_PACKED;
+                 kLaunchClk = 4000.0, kBytesPerClk = 2000.0;
     const int ck = igemm_chunk_channels();
     const int nchunks = (g.cin + ck - 1) / ck;
     const int kk = g.k * g.k;
@@ -116,30 +198,18 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
         int bm, bn;
         igemm_tile_shape(tile, &bm, &bn);
         for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
-            if (!(packed ? packed_tile_fits(g, tile, tc, nullptr)
-                         : igemm_tile_fits(g, tile, tc, nullptr)))
-                continue;
+            if (!igemm_tile_fits(g, tile, tc, nullptr)) continue;
             const double stage_clk = igemm_stage_floats(g, tile, tc) / 256.0 * 6.0;
             const long tiles = (long)g.n * igemm_tiles_per_image(g, tile, tc) *
                                ((g.cout + bm - 1) / bm);
-            for (int sk = 1; sk <= 8 && sk <= nchunks; ++sk) {
-                const int per = (nchunks + sk - 1) / sk;
-                if ((long)(sk - 1) * per >= nchunks) continue;  // an empty slice
+            for (int sk = 1; sk <= 8; ++sk) {
+                if (!slices_ok(nchunks, sk)) continue;
                 if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
+                const int per = (nchunks + sk - 1) / sk;
                 const long wgs = tiles * sk;
                 const double rounds = std::ceil(wgs / kCUs);
                 const double chunk_mfma = 2.0 * bm * bn * ck * kk / kFlopPerClk;
-                double wg_clk;
-                if (packed) {
-                    // one memory round trip per stage of cps chunks, overlapped with
-                    // the previous stage's matrix work
-                    const int cps = packed_chunks_per_stage(tile, g.k);
-                    const int stages = (per + cps - 1) / cps;
-                    wg_clk = stages * std::max(kLatencyClk, cps * chunk_mfma + kChunkClk) +
-                             kLatencyClk + kStartClk;
-                } else {
-                    wg_clk = per * (chunk_mfma + kChunkClk + stage_clk) + kStartClk;
-                }
+                const double wg_clk = per * (chunk_mfma + kChunkClk + stage_clk) + kStartClk;
                 double cost = rounds * wg_clk + 1e-3 * wgs;  // ties: fewer workgroups
                 if (sk > 1)
                     cost += kLaunchClk +
@@ -151,22 +221,15 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
             }
         }
     }
-    // Tuning and test override: CVX_IGEMM_TILE="kind,tc,splitk" forces a tile
-    // configuration when it is valid for this shape (sweeps and coverage tests).
-    if (const char* env = getenv("CVX_IGEMM_TILE")) {
-        int kind = -1, tc = -1, sk = 0;
-        if (sscanf(env, "%d,%d,%d", &kind, &tc, &sk) == 3 && kind >= 0 &&
-            kind < igemm_num_tiles() && sk >= 1 && sk <= nchunks &&
-            (long)(sk - 1) * ((nchunks + sk - 1) / sk) < nchunks &&
-            (packed ? packed_tile_fits(g, kind, tc, nullptr)
-                    : igemm_tile_fits(g, kind, tc, nullptr))) {
-            int bm, bn;
-            igemm_tile_shape(kind, &bm, &bn);
-            bt = GemmTile{kind, bm, bn, tc, sk};
-        }
+    int kind, tc, sk;
+    if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < igemm_num_tiles() &&
+        slices_ok(nchunks, sk) && igemm_tile_fits(g, kind, tc, nullptr)) {
+        int bm, bn;
+        igemm_tile_shape(kind, &bm, &bn);
+        bt = GemmTile{kind, bm, bn, tc, sk};
     }
     if (bt.kind < 0) return false;
-    p->fam = packed ? FAM_IGEMM_PACKED : FAM_IGEMM;
+    p->fam = FAM_IGEMM;
     p->tile = bt;
     p->ws_bytes = bt.splitk > 1 ? (size_t)bt.splitk * g.n * g.cout * g.oh * g.ow * sizeof(float) : 0;
     return true;
@@ -180,16 +243,58 @@ void plan_direct(const ConvGeom& g, Plan* p)
     p->ws_bytes = 0;
 }
 
-cvx_status make_plan(const ConvGeom& g, Plan* p)
+cvx_status plan_uncached(const ConvGeom& g, Plan* p)
 {
     *p = Plan{};
     if (plan_depthwise(g, p)) return CVX_OK;
-    if (plan_igemm(g, p)) return CVX_OK;
+    if (g.w_layout == CVX_W_PACKED ? plan_packed(g, p) : plan_igemm(g, p)) return CVX_OK;
     plan_direct(g, p);
     const int cout_g = g.cout / g.groups;
     if ((long)g.groups * ((cout_g + p->direct_cob - 1) / p->direct_cob) > 65535)
         return CVX_ERR_UNSUPPORTED;
     return CVX_OK;
+}
+
+// Plans are a pure function of the geometry (and of a forced tile, when one is
+// set), so they are remembered: a forward then plans each layer shape once, not
+// on every call.  Bounded, and safe to use from several host threads.
+struct PlanKey {
+    ConvGeom g;
+    int forced[3];
+    bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey& k) const
+    {
+        const unsigned char* b = reinterpret_cast<const unsigned char*>(&k);
+        size_t h = 1469598103934665603ull;  // FNV-1a
+        for (size_t i = 0; i < sizeof(PlanKey); ++i) h = (h ^ b[i]) * 1099511628211ull;
+        return h;
+    }
+};
+
+cvx_status make_plan(const ConvGeom& g, Plan* p)
+{
+    static std::mutex mu;
+    static std::unordered_map<PlanKey, std::pair<cvx_status, Plan>, PlanKeyHash> cache;
+    PlanKey key;
+    memset(&key, 0, sizeof(key));  // padding takes part in the hash and comparison
+    key.g = g;
+    key.forced[0] = key.forced[1] = key.forced[2] = -1;
+    forced_tile(&key.forced[0], &key.forced[1], &key.forced[2]);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            *p = it->second.second;
+            return it->second.first;
+        }
+    }
+    const cvx_status st = plan_uncached(g, p);
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() >= 4096) cache.clear();
+    cache.emplace(key, std::make_pair(st, *p));
+    return st;
 }
 
 cvx_status launch_conv(const ConvGeom& g, const Plan& p, const float* x, const float* w,
@@ -385,7 +490,7 @@ cvx_status cvx_conv_bn_act(const cvx_conv_desc* d, const float* x, const float* 
         return CVX_ERR_ALIAS;
     if (p.ws_bytes > 0) {
         if (workspace == nullptr || ws_bytes < p.ws_bytes) return CVX_ERR_WORKSPACE;
-        if (!aligned4(workspace)) return CVX_ERR_ALIGN;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return CVX_ERR_ALIGN;
         const Range wr = span(workspace, p.ws_bytes);
         if (overlap(wr, yr) || overlap(wr, span(x, elems_in(g) * sizeof(float))) ||
             overlap(wr, span(w, elems_w(g) * sizeof(float))) ||

@@ -85,10 +85,19 @@ hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* part
 
 hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s);
 
-// floats of the packed weight layout of the implicit-GEMM family
+// Packed-weight implicit-GEMM family (k_igemm_packed.hip).  A configuration is
+// a kind (tile of 32 x packed_tile_n(kind) outputs), tc and a split count.
 long packed_weight_floats(const ConvGeom& g);
-bool packed_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes);
-int packed_chunks_per_stage(int tile, int k);
+int packed_num_kinds();
+int packed_tile_n(int kind);
+int packed_chunks_per_stage(int kind, int k);
+long packed_tiles_per_image(const ConvGeom& g, int kind, int tc);
+bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes);
+size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits);
+// vector-memory instructions a workgroup issues per 16-channel chunk
+int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc);
+// workgroups of a configuration that fit one compute unit together
+int packed_occupancy(int kind, int k);
 
 // igemm helpers used by the planner (defined next to the kernel).
 void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc);

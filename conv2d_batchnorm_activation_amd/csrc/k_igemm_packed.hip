@@ -1,24 +1,42 @@
-// k_igemm_packed.hip -- the dense 1x1 / 3x3 implicit-GEMM kernel reading weights
-// that were packed once, at model load, into the matrix cores' operand order.
+// k_igemm_packed.hip -- the dense 1x1 / 3x3 convolution on fp32 matrix cores,
+// reading weights that were packed once, at model load, into the matrix
+// instruction's operand order.
 //
-// Same computation as k_igemm.hip (M = c_out, N = output pixels, K = c_in*kh*kw on
-// fp32 MFMA 32x32x2, folded BN / residual / activation in the epilogue); what
-// differs is how operands reach the matrix cores:
-//   * weights: a one-time transform (cvx_pack_weights) lays them out as
-//       [32-row block][16-channel chunk][channel pair][tap quad][lane][4]
-//     where lane l holds output channel 32*block + l%32 and input channel
-//     16*chunk + 2*pair + l/32 -- exactly the A-operand lane layout of
-//     v_mfma_f32_32x32x2_f32.  Each wave loads its A operands straight into
-//     registers with coalesced 16-byte loads (1 KB per wave instruction); no LDS
-//     traffic and no address arithmetic per element.  ("YOLO26N Inference
-//     Optimisation", "NHWC migration", "Weight layout": weights are reordered
-//     once at load time for the layout the kernels read.)
-//   * inputs: the staged region (as in k_igemm.hip) goes global -> LDS with
-//     LDS-direct buffer loads (no register round trip, no LDS write
-//     instructions); out-of-range offsets deliver zeros, so padding is free.
-//   * two LDS buffers and two register sets: the loads for chunk i+1 are issued
-//     before the MFMAs of chunk i, and one barrier per chunk orders the buffers.
+// Implicit GEMM: M = c_out, N = output pixels, K = c_in*kh*kw, computed with
+// v_mfma_f32_32x32x2_f32; the folded BatchNorm, the residual and the activation
+// are applied to the sums before the single store of each output
+// ("YOLO26N Inference Optimisation", "Improvements" #7; "Как я свертки
+// ускорял", "А теперь — хардкор на Metal", steps 4-5).
+//
+// Work decomposition.  A workgroup is four waves computing one tile of 32 output
+// channels x 32*NT output pixels; the waves split every 16-channel chunk of the
+// reduction (wave w takes channel pairs 2w and 2w+1), so each weight value a wave
+// loads feeds NT matrix instructions, and the four partial tiles are summed
+// through LDS at the end.  The pixels of a tile are either a run of consecutive
+// output pixels or a block of rows x `tc` columns.  Optionally the reduction is
+// split over `splits` workgroups; the last one to finish a tile adds the others'
+// partial sums (in split order) and applies the epilogue, so the layer is one
+// launch.
+//
+// Memory paths (one workgroup per compute unit, so what bounds a stage is how
+// many vector-memory instructions the unit must process):
+//   * weights: [32-row block][16-channel chunk][pair of channel pairs h (4)]
+//     [slot (5)][lane][4] for 3x3 -- lane l holds output channel 32*block + l%32
+//     and input channels of pairs 2h and 2h+1, its 18 taps (9 per pair) packed
+//     into five 16-byte slots, so a wave reads a chunk's weights with five
+//     coalesced loads; [block][chunk][h][lane][2] for 1x1 (one 8-byte load).
+//     ("YOLO26N Inference Optimisation", "NHWC migration", "Weight layout":
+//     weights are reordered once for the layout the kernels read.)
+//   * inputs: the chunk's input region goes global -> LDS with LDS-direct buffer
+//     loads, 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
+//     positions outside the image use out-of-range offsets and read as zero, so
+//     padding needs no code.
+//   * two LDS buffers and two register sets: the loads of stage s+1 are issued
+//     before the matrix work of stage s.
 #include <stdio.h>
+
+#include <atomic>
+#include <chrono>
 
 #include "bufio.h"
 #include "cvx_internal.h"
@@ -28,6 +46,14 @@ namespace cvx {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCh = 16;                        // input channels per chunk
+constexpr int kSC1 = 16;                       // cache policy: device-coherent (sc1)
+constexpr int kSlots3 = 5;                     // 16-byte weight slots per lane per h (3x3)
+constexpr int kBCFloats3 = 4 * kSlots3 * 256;  // floats per (block, chunk), 3x3: 5120
+constexpr int kBCFloats1 = 4 * 128;            // floats per (block, chunk), 1x1: 512
 
 __device__ __forceinline__ int pdiv(int n, unsigned m, unsigned l)
 {
@@ -35,75 +61,91 @@ __device__ __forceinline__ int pdiv(int n, unsigned m, unsigned l)
     return (int)((hi + (unsigned)n) >> l);
 }
 
+// LDS-direct loads of 16 and 4 bytes per lane (lane i writes dst + i*size).  The
+// 16-byte form is gfx950's; kept out of the kernel template so that the host
+// pass, which cannot check that form, still emits the kernels' launch stubs.
+__device__ __forceinline__ void lds_load16(rsrc_t r, __attribute__((address_space(3))) void* d, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(rsrc_t r, __attribute__((address_space(3))) void* d, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, off, 0, 0, 0);
+}
+
 struct PackedArgs {
     const float* x;
-    const float* wp;      // packed weights
+    const float* wp;
     const float* scale;
     const float* bias;
     const float* res;
     float* y;
-    float* partial;
-    int cin, H, W, cout, stride, pad, OH, OW;
-    int tiles_per_img, chunks_per_split, nchunks;
+    float* partial;             // [splits][n][c_out][oh*ow] when splits > 1
+    unsigned long long* ctr;    // one arrival counter per output tile when splits > 1
+    unsigned long long epoch;   // tag of this launch's arrivals (never 0)
+    int n, cin, H, W, cout, stride, pad, OH, OW;
+    int tiles_per_img, splits, chunks_per_split, nchunks;
     int tc, tiles_w;
-    unsigned m_tc, l_tc;
-    unsigned m_tpi, l_tpi;   // fast division by tiles_per_img
-    unsigned m_tw, l_tw;     // fast division by tiles_w (2-D tiles)
-    int step_ci, step_r, step_c;  // 256 in the mixed radix (channel, row, column)
-    int PR, PC;
-    unsigned m_rc, l_rc, m_c, l_c, m_ow, l_ow;
+    int run_in_row;             // flat tiles: output width is a multiple of the tile
+    unsigned m_tc, l_tc, m_tw, l_tw, m_ow, l_ow;
+    int PR, PCW;                // staged rows, LDS floats per staged row
+    int EPR, RE, rounds, REP;   // elements per row, elements per chunk, load rounds, LDS floats per chunk
+    unsigned m_rc, l_rc, m_c, l_c;
+    int step_ci, step_r, step_c;  // 256 elements in mixed radix (channel, row, element)
     unsigned wp_bytes;
+    int vout;                   // 16-byte epilogue accesses
     int act, res_mode;
 };
 
-// Floats of one (block, chunk, pair) group of packed weights.
-template <int K>
-constexpr int pair_floats()
-{
-    return K == 3 ? 3 * 64 * 4 : 64;
-}
+constexpr int kRoundsVec = 8, kRoundsScalar = 24;  // most staging rounds per chunk
 
-template <int BM, int BN, int WM, int WN, int WK, int K, int NPX, int CPS>
+template <int K, int NT, int CPS, int VEC>
 __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
 {
-    static_assert(WM * WN * WK == 4, "four waves per workgroup");
-    constexpr int TM = BM / WM, TN = BN / WN;
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is made of 32x32 blocks");
-    constexpr int MT = TM / 32, NT = TN / 32;
+    constexpr int NR = VEC ? kRoundsVec : kRoundsScalar;
     constexpr int KK = K * K;
-    constexpr int CK = 16;
-    constexpr int PAIRS = CK / 2;
-    static_assert(PAIRS % WK == 0, "channel pairs split evenly over WK waves");
-    constexpr int PPW = PAIRS / WK;           // pairs per wave per chunk
-    constexpr int TQ = K == 3 ? 3 : 1;        // 16-byte groups per pair (K=3)
-    constexpr int PF = pair_floats<K>();
+    constexpr int G = VEC ? 4 : 1;     // floats per staged element
+    constexpr int BN = 32 * NT;
+    constexpr int PITCH = BN + (NT < 4 ? 4 : 0);  // LDS row pitch of the partial-sum exchange
 
     extern __shared__ float smem[];
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: addresses stay scalar
     const int hi = lane >> 5;
     const int l32 = lane & 31;
-    const int wk = wave % WK;
-    const int wmn = wave / WK;
-    const int wm0 = (wmn / WN) * TM;
-    const int wn0 = (wmn % WN) * TN;
 
+    // Workgroup -> (row block, split, image, tile).  Consecutive workgroups are
+    // dealt to the eight XCDs in turn; numbering the tiles XCD by XCD keeps the
+    // tiles of one row block (same weights) and neighbouring pixels (shared
+    // input rows) in one XCD's L2.
+    int mb, sp, b, tile;
+    {
+        const unsigned h = blockIdx.x, G8 = gridDim.x;
+        const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
+        const int L = (int)(xcd * base + min(xcd, rem) + i8);
+        const int NB = a.n * a.tiles_per_img;
+        const int bt = L % NB;
+        const int ms = L / NB;
+        sp = ms % a.splits;
+        mb = ms / a.splits;
+        b = bt / a.tiles_per_img;
+        tile = bt - b * a.tiles_per_img;
+    }
+    const int co0 = mb * 32;
     const int OHW = a.OH * a.OW;
     const int HW = a.H * a.W;
-    const int b = pdiv(blockIdx.x, a.m_tpi, a.l_tpi);
-    const int tile = blockIdx.x - b * a.tiles_per_img;
-    const int co0 = blockIdx.y * BM;
 
     int q0 = 0, q_end = 0, oh_ref, ix0;
     if (a.tc == 0) {
         q0 = tile * BN;
         q_end = min(q0 + BN, OHW);
         oh_ref = pdiv(q0, a.m_ow, a.l_ow);
-        const int ow_a = q0 - oh_ref * a.OW;
-        const int oh_b = pdiv(q_end - 1, a.m_ow, a.l_ow);
-        ix0 = (oh_ref == oh_b ? ow_a * a.stride : 0) - a.pad;
+        // the staged columns follow the host's region: the run's own columns when
+        // runs never leave their row, else whole rows
+        ix0 = (a.run_in_row ? (q0 - oh_ref * a.OW) * a.stride : 0) - a.pad;
     } else {
         const int band = pdiv(tile, a.m_tw, a.l_tw);
         const int tw = tile - band * a.tiles_w;
@@ -112,34 +154,31 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
         q0 = tw * a.tc;  // first output column of the tile
     }
     const int iy0 = oh_ref * a.stride - a.pad;
-    const int RC = a.PR * a.PC;
-    const int RE = CK * RC;
-    const int REP = (RE + 255) & ~255;  // LDS pitch of one staged chunk
-    const int BUF = CPS * REP;          // floats of one stage buffer
+    const int gx0 = VEC ? (ix0 & ~3) : ix0;  // staged columns start on a 16-byte boundary
+    const int RS = a.PR * a.PCW;             // LDS floats per staged channel
+    const int BUF = CPS * a.REP;
 
-    // Input slots: element e = tid + 256*i of the staged region, as a byte offset
-    // from the chunk's first channel plane within this image; kOOB (reads as 0)
-    // outside the image or past the region.  Channels past c_in fall outside the
-    // image's descriptor and read as 0 too.  (channel, row, column) of e is found
-    // once and then stepped by 256 in mixed radix; rounds wholly past the region
-    // are skipped (uniform).
-    unsigned goff[NPX];
+    // Staged elements e = tid + 256*i: (channel, row, element-in-row) found once,
+    // then stepped by 256 in mixed radix; byte offset from the chunk's first
+    // channel, or kOOB outside the image.
+    unsigned goff[NR];
     {
+        const int per_ch = a.PR * a.EPR;
         int ci = pdiv(tid, a.m_rc, a.l_rc);
-        const int rem = tid - ci * RC;
+        const int rem = tid - ci * per_ch;
         int r = pdiv(rem, a.m_c, a.l_c);
-        int c = rem - r * a.PC;
+        int c = rem - r * a.EPR;
 #pragma unroll
-        for (int i = 0; i < NPX; ++i) {
+        for (int i = 0; i < NR; ++i) {
             goff[i] = kOOB;
-            if (256 * i < RE) {
+            if (i < a.rounds) {
                 const int e = tid + 256 * i;
-                const int iy = iy0 + r, ix = ix0 + c;
-                if (e < RE && iy >= 0 && iy < a.H && ix >= 0 && ix < a.W)
-                    goff[i] = 4u * (unsigned)(ci * HW + iy * a.W + ix);
+                const int iy = iy0 + r, gx = gx0 + G * c;
+                if (e < a.RE && iy >= 0 && iy < a.H && gx >= 0 && gx + G <= a.W)
+                    goff[i] = 4u * (unsigned)(ci * HW + iy * a.W + gx);
                 c += a.step_c;
-                const bool cc = c >= a.PC;
-                c -= cc ? a.PC : 0;
+                const bool cc = c >= a.EPR;
+                c -= cc ? a.EPR : 0;
                 r += a.step_r + (cc ? 1 : 0);
                 const bool rc = r >= a.PR;
                 r -= rc ? a.PR : 0;
@@ -147,120 +186,115 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
             }
         }
     }
-    const rsrc_t rx = make_rsrc(a.x + (long)b * a.cin * HW, 4u * (unsigned)(a.cin * HW));
+    const float* xim = a.x + (long)b * a.cin * HW;
     const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
-    // packed-weight byte offset of (row block mt, chunk 0, pair jp) for this lane
-    unsigned aoff[MT][PPW];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int jp = 0; jp < PPW; ++jp) {
-            const int blk = (co0 + wm0) / 32 + mt;
-            const int pair = wk + WK * jp;
-            aoff[mt][jp] = 4u * (unsigned)(((blk * a.nchunks) * PAIRS + pair) * PF +
-                                           (K == 3 ? lane * 4 : lane));
-        }
-    const unsigned chunk_stride_b = 4u * (unsigned)(PAIRS * PF);
+    constexpr int BCF = K == 3 ? kBCFloats3 : kBCFloats1;
+    const unsigned aoff = 4u * (unsigned)(mb * a.nchunks * BCF +
+                                          (K == 3 ? wave * kSlots3 * 256 + lane * 4
+                                                  : wave * 128 + lane * 2));
+    const unsigned chunk_b = 4u * BCF;
 
-    // A operands: two register sets of one stage (CPS chunks) each
-    f32x4 A0[CPS][MT][PPW][TQ], A1[CPS][MT][PPW][TQ];
-    float S0[CPS][MT][PPW], S1[CPS][MT][PPW];  // K == 1
-
-    const int c_begin = blockIdx.z * a.chunks_per_split;
+    const int c_begin = sp * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
     const int nstages = (c_end - c_begin + CPS - 1) / CPS;
 
-    // Load operations of one stage, addressed by a compile-time index `op`: the
-    // A loads (NA_ST of them) first, then the input rounds (CPS * NPX, rounds
-    // wholly past the region skipped by a uniform branch).  A chunk past the
-    // split's end loads through out-of-range offsets: zero weights and zero
-    // inputs, so the MFMAs need no branches.
-    constexpr int NA_C = K == 3 ? MT * PPW * TQ : MT * PPW;  // A loads per chunk
-    constexpr int NA_ST = CPS * NA_C;
-    constexpr int NOPS = NA_ST + CPS * NPX;
-    auto load_op = [&](int op, int stage, int buf, auto& A, auto& S) {
-        if (op < NA_ST) {
-            const int j = op / NA_C;
-            const int r0 = op % NA_C;
+    f32x4 A0[CPS][K == 3 ? kSlots3 : 1], A1[CPS][K == 3 ? kSlots3 : 1];
+    f32x2 S0[CPS], S1[CPS];
+
+    // One stage's loads.  A chunk past the split's end reads through out-of-range
+    // offsets (zero weights, zero inputs), so the matrix loop needs no branches.
+    auto issue = [&](int stage, int buf, auto& A, auto& S) {
+        rsrc_t rc[CPS];
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) {
             const int chunk = c_begin + stage * CPS + j;
-            const unsigned cb = chunk < c_end ? (unsigned)chunk * chunk_stride_b : kOOB;
+            const bool valid = chunk < c_end;
+            const unsigned cb = valid ? (unsigned)chunk * chunk_b : kOOB;
+            const unsigned ao = (aoff | (cb & kOOB)) + (cb & ~kOOB);
             if constexpr (K == 3) {
-                const int tq = r0 % TQ, jp = (r0 / TQ) % PPW, mt = r0 / (TQ * PPW);
-                A[j][mt][jp][tq] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rw, (int)(((aoff[mt][jp] + 4u * 256u * tq) | (cb & kOOB)) + (cb & ~kOOB)),
-                               0, 0));
+#pragma unroll
+                for (int s = 0; s < kSlots3; ++s)
+                    A[j][s] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ao + 1024u * s), 0, 0));
             } else {
-                const int jp = r0 % PPW, mt = r0 / PPW;
-                S[j][mt][jp] = bload(rw, (aoff[mt][jp] | (cb & kOOB)) + (cb & ~kOOB));
+                S[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)ao, 0, 0));
             }
-        } else {
-            const int j = (op - NA_ST) / NPX;
-            const int i = (op - NA_ST) % NPX;
-            if (256 * i < RE) {
-                const int chunk = c_begin + stage * CPS + j;
-                const unsigned xb = chunk < c_end ? 4u * (unsigned)(chunk * CK * HW) : kOOB;
-                float* dst = smem + buf * BUF + j * REP + wave * 64 + 256 * i;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx, (__attribute__((address_space(3))) void*)dst, 4,
-                    (goff[i] | (xb & kOOB)) + (xb & ~kOOB), 0, 0, 0);
+            // the chunk's own descriptor: based at its first channel, covering the
+            // channels that exist (none for a chunk past the split)
+            const int left = valid ? min(kCh, a.cin - chunk * kCh) : 0;
+            rc[j] = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+        }
+        // LDS destinations are formed here, from one scalar base per call (held
+        // for the whole kernel they would need a register per round, chunk and
+        // buffer)
+        int dbase = buf * BUF + wave * 64 * G;
+        asm volatile("" : "+s"(dbase));
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            if (i >= a.rounds) break;
+#pragma unroll
+            for (int j = 0; j < CPS; ++j) {
+                auto* d = (__attribute__((address_space(3))) void*)(smem + dbase + j * a.REP + 256 * G * i);
+                if constexpr (VEC)
+                    lds_load16(rc[j], d, goff[i]);
+                else
+                    lds_load4(rc[j], d, goff[i]);
             }
         }
     };
-    auto issue = [&](int stage, int buf, auto& A, auto& S) {
-#pragma unroll
-        for (int op = 0; op < NOPS; ++op) load_op(op, stage, buf, A, S);
-    };
-
-    // the first stage's loads go out before the rest of the set-up
     if (nstages > 0) issue(0, 0, A0, S0);
 
-    int loff[NT], qout[NT];
+    // Epilogue rows: after the exchange, wave w owns output rows 8w..8w+7 of the
+    // tile; lane -> row 8w + lane/8 and pixel quads 4*(lane%8) + 32*k.
+    const int erow = 8 * wave + (lane >> 3);
+    const int eco = co0 + erow;
+    const bool row_ok = eco < a.cout;
+    const bool single = a.partial == nullptr;
+    float sc = 0.0f, bi = 0.0f;
+    if (single) {
+        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
+        sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
+        bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
+    }
+
+    // LDS offset of each of this lane's pixels (tap 0) in a staged channel
+    int loff[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int j = wn0 + nt * 32 + l32;
+        const int j = nt * 32 + l32;
         int oh, ow;
-        bool ok;
         if (a.tc == 0) {
-            const int q = q0 + j;
-            ok = q < q_end;
-            const int qc = ok ? q : q_end - 1;
+            const int qc = min(q0 + j, q_end - 1);
             oh = pdiv(qc, a.m_ow, a.l_ow);
             ow = qc - oh * a.OW;
         } else {
             const int jr = pdiv(j, a.m_tc, a.l_tc);
-            oh = oh_ref + jr;
-            ow = q0 + (j - jr * a.tc);
-            ok = oh < a.OH && ow < a.OW;
-            oh = min(oh, a.OH - 1);
-            ow = min(ow, a.OW - 1);
+            oh = min(oh_ref + jr, a.OH - 1);
+            ow = min(q0 + (j - jr * a.tc), a.OW - 1);
         }
-        loff[nt] = (oh - oh_ref) * a.stride * a.PC + ow * a.stride - a.pad - ix0;
-        qout[nt] = ok ? oh * a.OW + ow : -1;
+        loff[nt] = (oh - oh_ref) * a.stride * a.PCW + ow * a.stride - a.pad - gx0;
     }
 
-    f32x16 acc[2][MT][NT];
+    f32x16 acc[NT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[h][mt][nt][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
-    // One stage's MFMAs.  The B operands of the next channel pair are read from
-    // LDS before the current pair's MFMAs are issued (the scheduling barrier keeps
-    // them there), so LDS latency hides behind matrix work; taps alternate between
-    // two accumulator chains.
-    constexpr int NPAIR = CPS * PPW;
+    // One stage's matrix work: for each chunk and each of the wave's two channel
+    // pairs, KK taps x NT pixel blocks.  The B operands of the next pair are read
+    // from LDS before the current pair's MFMAs are issued.
+    constexpr int NQ = CPS * 2;
     auto read_b = [&](int buf, int q, float (&bv)[KK][NT]) {
-        const int j = q / PPW, jp = q % PPW;
-        const int ci = 2 * (wk + WK * jp) + hi;
-        const float* xa = smem + buf * BUF + j * REP + ci * RC;
+        const int j = q >> 1, pp = q & 1;
+        // formed here, each stage: hoisting these addresses out of the stage loop
+        // would hold one register per (chunk, pair, tap row, block, buffer)
+        int base = buf * BUF + j * a.REP + (2 * (2 * wave + pp) + hi) * RS;
+        asm volatile("" : "+v"(base));
+        const float* xa = smem + base;
 #pragma unroll
         for (int tap = 0; tap < KK; ++tap) {
-            const int toff = (tap / K) * a.PC + (tap % K);
+            const int toff = (tap / K) * a.PCW + (tap % K);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
         }
@@ -269,214 +303,256 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
         float b0[KK][NT], b1[KK][NT];
         read_b(buf, 0, b0);
 #pragma unroll
-        for (int q = 0; q < NPAIR; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             float (&cur)[KK][NT] = (q & 1) ? b1 : b0;
             float (&nxt)[KK][NT] = (q & 1) ? b0 : b1;
-            if (q + 1 < NPAIR) read_b(buf, q + 1, nxt);
+            if (q + 1 < NQ) read_b(buf, q + 1, nxt);
             __builtin_amdgcn_sched_barrier(0);
-            const int j = q / PPW, jp = q % PPW;
+            const int j = q >> 1, pp = q & 1;
 #pragma unroll
-            for (int tap = 0; tap < KK; ++tap)
+            for (int tap = 0; tap < KK; ++tap) {
+                float av;
+                if constexpr (K == 3)
+                    av = A[j][(9 * pp + tap) / 4][(9 * pp + tap) % 4];
+                else
+                    av = S[j][pp];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    float av;
-                    if constexpr (K == 3)
-                        av = A[j][mt][jp][tap / 4][tap % 4];
-                    else
-                        av = S[j][mt][jp];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        f32x16& c = acc[(tap + q) & 1][mt][nt];
-                        c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, cur[tap][nt], c, 0, 0, 0);
-                    }
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, cur[tap][nt], acc[nt], 0, 0, 0);
+            }
         }
     };
 
-    // Epilogue operands are independent of the reduction: issue their loads with
-    // the first stage so they share its memory round trip.
+    // Epilogue geometry of this lane's quads: byte offset of a pixel within the
+    // output tensor, or kOOB outside the tile or past c_out.  With `vout` the
+    // quad's four pixels are contiguous and 16-byte aligned and move with one
+    // access.  Computed where used, so nothing of it is live during the stages.
     const unsigned plane_b = 4u * (unsigned)OHW;
-    unsigned rowoff[MT][16];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int co = co0 + wm0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            rowoff[mt][r] = co < a.cout ? (unsigned)(b * a.cout + co) * plane_b : kOOB;
+    const unsigned out_bytes = 4u * (unsigned)(a.n * a.cout * OHW);
+    auto at = [&](int k, int e) {
+        const int p = 32 * k + 4 * (lane & 7) + e;
+        bool ok;
+        int q;
+        if (a.tc == 0) {
+            q = q0 + p;
+            ok = q < q_end;
+        } else {
+            const int jr = pdiv(p, a.m_tc, a.l_tc);
+            const int oh = oh_ref + jr, ow = q0 + (p - jr * a.tc);
+            ok = oh < a.OH && ow < a.OW;
+            q = oh * a.OW + ow;
         }
-    unsigned qb[NT];
+        return ok && row_ok ? (unsigned)(b * a.cout + eco) * plane_b + 4u * (unsigned)q : kOOB;
+    };
+    // `dev` marks accesses coherent across the whole device (the sc1 cache
+    // policy): they bypass an XCD's own L2, so a partial sum written on one XCD is
+    // read correctly on another.
+    auto load_quad = [&](const rsrc_t& r, int k, bool dev = false) {
+        f32x4 v;
+        if (a.vout) {
+            v = __builtin_bit_cast(f32x4, dev ? __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(k, 0), 0, kSC1)
+                                              : __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(k, 0), 0, 0));
+        } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) qb[nt] = qout[nt] >= 0 ? 4u * (unsigned)qout[nt] : kOOB;
-    const unsigned out_bytes = 4u * (unsigned)((gridDim.x / a.tiles_per_img) * a.cout * OHW);
-    float sc[MT][16], bi[MT][16], rv[MT][NT][16];
-    const bool final_pass = a.partial == nullptr;
-    if (final_pass) {
-        const rsrc_t rsb = make_rsrc(a.scale, 4u * (unsigned)a.cout);
-        const rsrc_t rbb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
+            for (int e = 0; e < 4; ++e)
+                v[e] = __builtin_bit_cast(float, dev ? __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(k, e), 0, kSC1)
+                                                     : __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(k, e), 0, 0));
+        }
+        return v;
+    };
+    auto store_quad = [&](const rsrc_t& r, int k, f32x4 v, bool dev = false) {
+        if (a.vout) {
+            if (dev)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)at(k, 0), 0, kSC1);
+            else
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)at(k, 0), 0, 0);
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int co = co0 + wm0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const unsigned o = co < a.cout ? 4u * (unsigned)co : kOOB;
-                sc[mt][r] = bload(rsb, o);
-                bi[mt][r] = bload(rbb, o);
+            for (int e = 0; e < 4; ++e) {
+                const float f = v[e];  // a scalar copy: bit_cast of a vector element takes element 0
+                if (dev)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, (int)at(k, e), 0, kSC1);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, (int)at(k, e), 0, 0);
             }
-        if (a.res_mode != CVX_RES_NONE) {
-            const rsrc_t rr = make_rsrc(a.res, out_bytes);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        rv[mt][nt][r] =
-                            bload(rr, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB));
         }
-    }
+    };
+    f32x4 rv[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) rv[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const bool want_res = a.res_mode != CVX_RES_NONE;
+    auto load_res = [&]() {
+        const rsrc_t rr = make_rsrc(a.res, out_bytes);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) rv[k] = load_quad(rr, k);
+    };
 
-    // Stages alternate between (LDS buffer 0, register set 0) and (1, 1).  Each
-    // step: wait for this stage's loads, barrier (its LDS data visible to all
-    // waves; every wave done with the other buffer), issue the next stage's loads
-    // into the other buffer/set, then run this stage's MFMAs.
+    // Stages alternate between (LDS buffer 0, register set 0) and (1, 1): wait
+    // for this stage's loads, barrier (its data visible to every wave; every wave
+    // done with the other buffer), issue the next stage's loads, compute.  With
+    // no next stage, the residual loads go out instead.
     for (int st = 0; st < nstages; st += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (st + 1 < nstages) issue(st + 1, 1, A1, S1);
+        else if (single && want_res) load_res();
         compute(0, A0, S0);
         if (st + 1 >= nstages) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (st + 2 < nstages) issue(st + 2, 0, A0, S0);
+        else if (single && want_res) load_res();
         compute(1, A1, S1);
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[0][mt][nt] += acc[1][mt][nt];
+    if (nstages == 0 && single && want_res) load_res();
 
-    if constexpr (WK > 1) {
-        __syncthreads();
-        float* red = smem;
-        constexpr int SLAB = MT * NT * 16 * 64;
-        if (wk > 0) {
-            float* d = red + (wmn * (WK - 1) + wk - 1) * SLAB;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) d[((mt * NT + nt) * 16 + r) * 64 + lane] = acc[0][mt][nt][r];
-        }
-        __syncthreads();
-        if (wk > 0) return;
-#pragma unroll
-        for (int k = 1; k < WK; ++k) {
-            const float* src = red + (wmn * (WK - 1) + k - 1) * SLAB;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[0][mt][nt][r] += src[((mt * NT + nt) * 16 + r) * 64 + lane];
-        }
-    }
-
-    // epilogue: rows past c_out and pixels outside the tile use kOOB offsets
-    if (!final_pass) {
-        const rsrc_t rp = make_rsrc(a.partial + (long)blockIdx.z * (out_bytes / 4), out_bytes);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    bstore(rp, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB), acc[0][mt][nt][r]);
-        return;
-    }
-    const rsrc_t ry = make_rsrc(a.y, out_bytes);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    // Partial-sum exchange: every wave writes its 32 x BN tile, then wave w sums
+    // rows 8w..8w+7 of the four tiles in wave order.
+    __syncthreads();
+    {
+        float* red = smem + wave * 32 * PITCH;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float z = fmaf(sc[mt][r], acc[0][mt][nt][r], bi[mt][r]);
-                if (a.res_mode == CVX_RES_BEFORE_ACT) z += rv[mt][nt][r];
-                z = apply_act_fast(z, a.act);
-                if (a.res_mode == CVX_RES_AFTER_ACT) z += rv[mt][nt][r];
-                bstore(ry, (rowoff[mt][r] | (qb[nt] & kOOB)) + (qb[nt] & ~kOOB), z);
+            for (int r = 0; r < 16; ++r)
+                red[(8 * (r >> 2) + 4 * hi + (r & 3)) * PITCH + 32 * nt + l32] = acc[nt][r];
+    }
+    __syncthreads();
+    f32x4 v[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int off = erow * PITCH + 32 * k + 4 * (lane & 7);
+        v[k] = *reinterpret_cast<const f32x4*>(smem + off);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) v[k] += *reinterpret_cast<const f32x4*>(smem + s * 32 * PITCH + off);
+    }
+
+    if (!single) {
+        // Split reduction: publish this slice's sums, count arrivals at the tile's
+        // counter, and let the last arrival finish the tile.  The sums are stored
+        // and read with device-coherent accesses, and every wave waits for its
+        // stores to complete before the workgroup's arrival is counted, so the
+        // last arrival reads every slice.  Counters carry the launch's epoch in
+        // their upper bits, so whatever a counter held before (another launch's
+        // value, or anything at all in a fresh workspace) reads as zero arrivals;
+        // the last arrival resets it to 0.
+        const unsigned part_b = out_bytes;
+        {
+            const rsrc_t rps = make_rsrc(a.partial + (long)sp * (part_b / 4), part_b);
+#pragma unroll
+            for (int k = 0; k < NT; ++k) store_quad(rps, k, v[k], true);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            unsigned long long* c = a.ctr + ((long)(mb * a.n + b) * a.tiles_per_img + tile);
+            unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned long long before;
+            for (;;) {
+                before = (cur >> 8) == a.epoch ? (cur & 0xffull) : 0ull;
+                const unsigned long long nv = (a.epoch << 8) | (before + 1);
+                if (__hip_atomic_compare_exchange_strong(c, &cur, nv, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    break;
             }
+            const int last = before + 1 == (unsigned long long)a.splits;
+            if (last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        f32x4 tot[NT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) tot[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < a.splits; ++s) {
+            const rsrc_t rps = make_rsrc(a.partial + (long)s * (part_b / 4), part_b);
+#pragma unroll
+            for (int k = 0; k < NT; ++k) tot[k] += s == sp ? v[k] : load_quad(rps, k, true);
+        }
+#pragma unroll
+        for (int k = 0; k < NT; ++k) v[k] = tot[k];
+        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
+        sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
+        bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
+        if (want_res) load_res();
+    }
+
+    const rsrc_t ry = make_rsrc(a.y, out_bytes);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        f32x4 z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = fmaf(sc, v[k][e], bi);
+            if (a.res_mode == CVX_RES_BEFORE_ACT) t += rv[k][e];
+            t = apply_act_fast(t, a.act);
+            if (a.res_mode == CVX_RES_AFTER_ACT) t += rv[k][e];
+            z[e] = t;
+        }
+        store_quad(ry, k, z);
+    }
 }
 
-// One-time weight transform: OIHW -> [32-row block][16-channel chunk][pair]
-// [tap quad][lane][4] (3x3) or [block][chunk][pair][lane] (1x1); zero where the
-// row, channel or tap does not exist.
+// One-time weight transform, OIHW -> the packed order above; zero where the row,
+// channel or tap does not exist.
 __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ w, int cout, int cin,
                                                       int k, int nchunks, long total,
                                                       float* __restrict__ wp)
 {
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
-    const int kk = k * k;
-    int co, ci, tap;
+    int co, ci, tap = 0;
+    bool live = true;
     if (k == 3) {
         const int j = (int)(idx & 3);
         const int lane = (int)((idx >> 2) & 63);
-        const long g = idx >> 8;  // (block, chunk, pair, tq)
-        const int tq = (int)(g % 3);
-        const long g2 = g / 3;
-        const int pair = (int)(g2 % 8);
-        const long g3 = g2 / 8;
+        const long g = idx >> 8;  // (block, chunk, h, slot)
+        const int slot = (int)(g % kSlots3);
+        const long g2 = g / kSlots3;
+        const int h = (int)(g2 & 3);
+        const long g3 = g2 >> 2;
         const int chunk = (int)(g3 % nchunks);
         const int blk = (int)(g3 / nchunks);
+        const int f = 4 * slot + j;  // 0..19: 9*(pair within h) + tap; 18 and 19 unused
+        live = f < 18;
+        const int pp = f / 9;
+        tap = f - 9 * pp;
         co = blk * 32 + (lane & 31);
-        ci = chunk * 16 + 2 * pair + (lane >> 5);
-        tap = tq * 4 + j;
+        ci = chunk * kCh + 2 * (2 * h + pp) + (lane >> 5);
     } else {
-        const int lane = (int)(idx & 63);
-        const long g = idx >> 6;
-        const int pair = (int)(g % 8);
-        const long g3 = g / 8;
+        const int j = (int)(idx & 1);
+        const int lane = (int)((idx >> 1) & 63);
+        const long g = idx >> 7;  // (block, chunk, h)
+        const int h = (int)(g & 3);
+        const long g3 = g >> 2;
         const int chunk = (int)(g3 % nchunks);
         const int blk = (int)(g3 / nchunks);
         co = blk * 32 + (lane & 31);
-        ci = chunk * 16 + 2 * pair + (lane >> 5);
-        tap = 0;
+        ci = chunk * kCh + 2 * (2 * h + j) + (lane >> 5);
     }
     float v = 0.0f;
-    if (co < cout && ci < cin && tap < kk) v = w[((long)co * cin + ci) * kk + tap];
+    if (live && co < cout && ci < cin) v = w[((long)co * cin + ci) * (k * k) + tap];
     wp[idx] = v;
 }
 
 // ------------------------------------------------------------------ host side
+// Compiled configurations: NT pixel blocks per wave, and chunks per pipeline
+// stage for 3x3 and 1x1.  The tile is 32 x 32*NT.
 struct PackedKind {
-    int bm, bn, wm, wn, wk, npx;
-    int cps3, cps1;  // chunks per pipeline stage for 3x3 and 1x1
+    int nt, cps3, cps1;
 };
-static constexpr PackedKind kPacked[] = {
-    {32, 32, 1, 1, 4, 24, 2, 8},
-    {32, 64, 1, 2, 2, 24, 2, 8},
-    {64, 64, 2, 2, 1, 24, 1, 4},
-    {64, 128, 2, 2, 1, 24, 0, 4},  // 1x1 only (a 3x3 stage would not fit the registers)
-};
-
-int packed_chunks_per_stage(int tile, int k) { return k == 3 ? kPacked[tile].cps3 : kPacked[tile].cps1; }
+static constexpr PackedKind kPacked[] = {{1, 2, 8}, {2, 2, 8}, {4, 1, 4}};
 constexpr int kNumPacked = sizeof(kPacked) / sizeof(kPacked[0]);
 
-void packed_kernel_name(const ConvGeom& g, int tile, char* buf, int len)
-{
-    const PackedKind& t = kPacked[tile];
-    snprintf(buf, len, "cvx::k_igemm_packed<%d, %d, %d, %d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wn,
-             t.wk, g.k, t.npx, packed_chunks_per_stage(tile, g.k));
-}
+int packed_num_kinds() { return kNumPacked; }
+int packed_chunks_per_stage(int kind, int k) { return k == 3 ? kPacked[kind].cps3 : kPacked[kind].cps1; }
+int packed_tile_n(int kind) { return 32 * kPacked[kind].nt; }
 
 long packed_weight_floats(const ConvGeom& g)
 {
     const long blocks = (g.cout + 31) / 32;
-    const long nchunks = (g.cin + 15) / 16;
-    return blocks * nchunks * 8 * (g.k == 3 ? 3 * 64 * 4 : 64);
+    const long nchunks = (g.cin + kCh - 1) / kCh;
+    return blocks * nchunks * (g.k == 3 ? kBCFloats3 : kBCFloats1);
 }
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s)
@@ -484,66 +560,192 @@ hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hip
     const long total = packed_weight_floats(g);
     dim3 grid((unsigned)((total + 255) / 256));
     hipLaunchKernelGGL(k_pack_weights, grid, dim3(256), 0, s, w, g.cout, g.cin, g.k,
-                       (g.cin + 15) / 16, total, wp);
+                       (g.cin + kCh - 1) / kCh, total, wp);
     return hipGetLastError();
 }
 
-// the region geometry and tile counts are shared with the OIHW kernel
-void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc);
 void fastdiv_params(int d, unsigned* m, unsigned* l);
 
-bool packed_tile_fits(const ConvGeom& g, int tile, int tc, size_t* lds_bytes)
+long packed_tiles_per_image(const ConvGeom& g, int kind, int tc)
 {
-    if (packed_chunks_per_stage(tile, g.k) == 0) return false;
-    if (!igemm_tile_fits(g, tile, tc, nullptr)) return false;
-    const PackedKind& t = kPacked[tile];
-    int pr, pc;
-    igemm_region(g, t.bn, tc, &pr, &pc);
-    const long re = (long)16 * pr * pc;
-    if (re > 256L * t.npx) return false;
-    if (packed_weight_floats(g) * 4 >= 0x7fffffffL) return false;
-    const long rep = (re + 255) / 256 * 256;
-    const size_t stage = 2 * (size_t)packed_chunks_per_stage(tile, g.k) * rep * sizeof(float);
-    const size_t red = t.wk > 1 ? (size_t)(4 / t.wk) * (t.wk - 1) * (t.bm / t.wm / 32) *
-                                      (t.bn / t.wn / 32) * 16 * 64 * sizeof(float)
-                                : 0;
-    const size_t lds = stage > red ? stage : red;
-    if (lds > kMaxLdsBytes) return false;
+    const int bn = packed_tile_n(kind);
+    if (tc == 0) return (g.oh * g.ow + bn - 1) / bn;
+    const int tr = bn / tc;
+    return (long)((g.oh + tr - 1) / tr) * ((g.ow + tc - 1) / tc);
+}
+
+// Staged region of a tile: rows, and columns from the first column a tile can
+// touch; `vec` widens each row to whole 16-byte elements aligned to the image.
+struct Region {
+    int pr, pc, pcw, epr, re, rounds, rep;
+};
+
+static Region packed_region(const ConvGeom& g, int kind, int tc, bool vec)
+{
+    Region r;
+    const int bn = packed_tile_n(kind);
+    if (tc > 0) {
+        r.pr = (bn / tc - 1) * g.stride + g.k;
+        r.pc = (tc - 1) * g.stride + g.k;
+    } else if (g.ow % bn == 0) {  // runs never leave their output row
+        r.pr = g.k;
+        r.pc = (bn - 1) * g.stride + g.k;
+    } else if (bn % g.ow == 0 && bn / g.ow <= g.oh) {  // whole rows per tile
+        r.pr = (bn / g.ow - 1) * g.stride + g.k;
+        r.pc = g.w + 2 * g.pad;
+    } else {
+        int rows = (bn - 1) / g.ow + 2;
+        rows = rows < g.oh ? rows : g.oh;
+        r.pr = (rows - 1) * g.stride + g.k;
+        r.pc = g.w + 2 * g.pad;
+    }
+    if (vec) {
+        // The first staged column ix0 = (first output column)*stride - pad starts
+        // (ix0 mod 4) floats into its 16-byte element.  For flat runs (which start
+        // at a multiple of 32 pixels of a row, or at column 0) and for 2-D tiles
+        // whose column step tc*stride is a multiple of 4, that residue is the
+        // same for every tile: (-pad) mod 4; otherwise allow for 3.
+        const bool fixed = tc == 0 || (tc * g.stride) % 4 == 0;
+        const int shift = fixed ? ((-g.pad) & 3) : 3;
+        r.pcw = (r.pc + shift + 3) & ~3;
+        r.epr = r.pcw / 4;
+    } else {
+        r.pcw = r.pc;
+        r.epr = r.pc;
+    }
+    r.re = kCh * r.pr * r.epr;
+    r.rounds = (r.re + 255) / 256;
+    r.rep = r.rounds * 256 * (vec ? 4 : 1);
+    return r;
+}
+
+static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
+{
+    const int nt = kPacked[kind].nt;
+    const size_t stage = 2 * (size_t)packed_chunks_per_stage(kind, g.k) * r.rep * sizeof(float);
+    const size_t red = (size_t)4 * 32 * (32 * nt + (nt < 4 ? 4 : 0)) * sizeof(float);
+    return stage > red ? stage : red;
+}
+
+bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
+{
+    if (kind < 0 || kind >= kNumPacked) return false;
+    if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
+    const int bn = packed_tile_n(kind);
+    if (tc < 0 || (tc > 0 && (tc > bn || bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
+    const long lim = 0x7fffffffL;
+    if ((long)g.cin * g.h * g.w * 4 >= lim || packed_weight_floats(g) * 4 >= lim ||
+        (long)g.n * g.cout * g.oh * g.ow * 4 >= lim)
+        return false;
+    // both staging forms must fit: which one runs depends on pointer alignment
+    size_t lds = 0;
+    for (int vec = 0; vec < 2; ++vec) {
+        const Region r = packed_region(g, kind, tc, vec != 0);
+        if (r.rounds > (vec ? kRoundsVec : kRoundsScalar)) return false;
+        const size_t l = packed_lds(g, kind, r);
+        if (l > kMaxLdsBytes) return false;
+        lds = l > lds ? l : lds;
+    }
     if (lds_bytes) *lds_bytes = lds;
     return true;
 }
 
-template <int K, int TILE>
-static void launch_packed_tile(dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
+// Split-K partial sums, then one 8-byte arrival counter per output tile.
+static size_t packed_partial_bytes(const ConvGeom& g, int splits)
 {
-    constexpr PackedKind t = kPacked[TILE];
+    return ((size_t)splits * g.n * g.cout * g.oh * g.ow * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
+{
+    if (splits <= 1) return 0;
+    const size_t tiles = (size_t)g.n * packed_tiles_per_image(g, kind, tc) * ((g.cout + 31) / 32);
+    return packed_partial_bytes(g, splits) + tiles * sizeof(unsigned long long);
+}
+
+// Waves per SIMD the compiled kernels allow (512 registers per lane, VGPRs plus
+// accumulation registers, as the compiler reports them for gfx950), capped by
+// LDS at two workgroups.
+int packed_occupancy(int kind, int k)
+{
+    static constexpr int kRegs[2][kNumPacked] = {{144, 205, 295},   // 1x1: NT = 1, 2, 4
+                                                 {175, 250, 360}};  // 3x3
+    const int regs = kRegs[k == 3 ? 1 : 0][kind];
+    const int occ = 512 / regs;
+    return occ < 1 ? 1 : occ > 2 ? 2 : occ;
+}
+
+int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc)
+{
+    const bool vec = g.w % 4 == 0;
+    const Region r = packed_region(g, kind, tc, vec);
+    return 4 * (g.k == 3 ? kSlots3 : 1) + 4 * r.rounds;
+}
+
+void packed_kernel_name(const ConvGeom& g, int kind, char* buf, int len)
+{
+    const PackedKind& t = kPacked[kind];
+    const bool vec = g.w % 4 == 0;  // as launched on 16-byte aligned tensors
+    snprintf(buf, len, "cvx::k_igemm_packed<%d, %d, %d, %d>", g.k, t.nt,
+             packed_chunks_per_stage(kind, g.k), vec ? 1 : 0);
+}
+
+// A fresh tag per split launch.  The first value mixes the clock and an address,
+// so a workspace's earlier contents practically never hold the same tag.
+static unsigned long long next_epoch()
+{
+    static std::atomic<unsigned long long> ctr{
+        (((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() *
+          0x9E3779B97F4A7C15ull) ^
+         (unsigned long long)reinterpret_cast<uintptr_t>(&ctr)) >> 9};
+    for (;;) {
+        const unsigned long long e = ctr.fetch_add(1) & ((1ull << 56) - 1);
+        if (e != 0) return e;
+    }
+}
+
+template <int K, int NT, int CPS, int VEC>
+static void launch_packed_cfg(dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
+{
+    hipLaunchKernelGGL((k_igemm_packed<K, NT, CPS, VEC>), grid, dim3(256), lds, s, a);
+}
+
+template <int K, int KIND>
+static void launch_packed_kind(bool vec, dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
+{
+    constexpr PackedKind t = kPacked[KIND];
     constexpr int cps = K == 3 ? t.cps3 : t.cps1;
-    if constexpr (cps == 0) return;
+    if (vec)
+        launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
     else
-    hipLaunchKernelGGL((k_igemm_packed<t.bm, t.bn, t.wm, t.wn, t.wk, K, t.npx, cps>), grid,
-                       dim3(256), lds, s, a);
+        launch_packed_cfg<K, t.nt, cps, 0>(grid, lds, s, a);
 }
 
 template <int K>
-static void launch_packed_k(int tile, dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
+static void launch_packed_k(int kind, bool vec, dim3 grid, size_t lds, hipStream_t s,
+                            const PackedArgs& a)
 {
-    switch (tile) {
-    case 0: launch_packed_tile<K, 0>(grid, lds, s, a); break;
-    case 1: launch_packed_tile<K, 1>(grid, lds, s, a); break;
-    case 2: launch_packed_tile<K, 2>(grid, lds, s, a); break;
-    case 3: launch_packed_tile<K, 3>(grid, lds, s, a); break;
+    switch (kind) {
+    case 0: launch_packed_kind<K, 0>(vec, grid, lds, s, a); break;
+    case 1: launch_packed_kind<K, 1>(vec, grid, lds, s, a); break;
+    case 2: launch_packed_kind<K, 2>(vec, grid, lds, s, a); break;
     }
 }
+
+static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
                                const float* scale, const float* bias, const float* res, float* y,
                                void* ws, hipStream_t s)
 {
-    const int tile = p.tile.kind;
-    if (tile < 0 || tile >= kNumPacked || (g.k != 1 && g.k != 3)) return hipErrorInvalidValue;
-    size_t lds = 0;
-    if (!packed_tile_fits(g, tile, p.tile.tc, &lds)) return hipErrorInvalidValue;
-    const PackedKind& t = kPacked[tile];
+    const int kind = p.tile.kind;
+    const int tc = p.tile.tc;
+    const int splits = p.tile.splitk;
+    if (!packed_tile_fits(g, kind, tc, nullptr)) return hipErrorInvalidValue;
+    if (splits < 1 || (splits > 1 && ws == nullptr)) return hipErrorInvalidValue;
+    const bool vec = g.w % 4 == 0 && al16(x);
+    const Region r = packed_region(g, kind, tc, vec);
+    const size_t lds = packed_lds(g, kind, r);
     PackedArgs a;
     a.x = x;
     a.wp = wp;
@@ -551,7 +753,7 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     a.bias = bias;
     a.res = res;
     a.y = y;
-    a.partial = p.tile.splitk > 1 ? static_cast<float*>(ws) : nullptr;
+    a.n = g.n;
     a.cin = g.cin;
     a.H = g.h;
     a.W = g.w;
@@ -560,37 +762,53 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     a.pad = g.pad;
     a.OH = g.oh;
     a.OW = g.ow;
-    a.tc = p.tile.tc;
-    a.tiles_per_img = (int)igemm_tiles_per_image(g, tile, a.tc);
-    a.tiles_w = a.tc > 0 ? (g.ow + a.tc - 1) / a.tc : 0;
-    fastdiv_params(a.tc > 0 ? a.tc : 1, &a.m_tc, &a.l_tc);
-    fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
+    a.tc = tc;
+    a.tiles_per_img = (int)packed_tiles_per_image(g, kind, tc);
+    a.splits = splits;
+    a.nchunks = (g.cin + kCh - 1) / kCh;
+    a.chunks_per_split = (a.nchunks + splits - 1) / splits;
+    a.tiles_w = tc > 0 ? (g.ow + tc - 1) / tc : 0;
+    a.run_in_row = tc == 0 && g.ow % packed_tile_n(kind) == 0;
+    fastdiv_params(tc > 0 ? tc : 1, &a.m_tc, &a.l_tc);
     fastdiv_params(a.tiles_w > 0 ? a.tiles_w : 1, &a.m_tw, &a.l_tw);
-    a.nchunks = (g.cin + 15) / 16;
-    a.chunks_per_split = (a.nchunks + p.tile.splitk - 1) / p.tile.splitk;
-    igemm_region(g, t.bn, a.tc, &a.PR, &a.PC);
-    fastdiv_params(a.PR * a.PC, &a.m_rc, &a.l_rc);
-    fastdiv_params(a.PC, &a.m_c, &a.l_c);
     fastdiv_params(g.ow, &a.m_ow, &a.l_ow);
+    a.PR = r.pr;
+    a.PCW = r.pcw;
+    a.EPR = r.epr;
+    a.RE = r.re;
+    a.rounds = r.rounds;
+    a.REP = r.rep;
+    fastdiv_params(r.pr * r.epr, &a.m_rc, &a.l_rc);
+    fastdiv_params(r.epr, &a.m_c, &a.l_c);
     {
-        const int rc = a.PR * a.PC;
+        const int rc = r.pr * r.epr;
         a.step_ci = 256 / rc;
         const int rem = 256 % rc;
-        a.step_r = rem / a.PC;
-        a.step_c = rem % a.PC;
+        a.step_r = rem / r.epr;
+        a.step_c = rem % r.epr;
     }
     a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
     a.act = g.act;
     a.res_mode = g.res_mode;
-    dim3 grid((unsigned)(g.n * a.tiles_per_img), (unsigned)((g.cout + t.bm - 1) / t.bm),
-              (unsigned)p.tile.splitk);
+    if (splits > 1) {
+        a.partial = static_cast<float*>(ws);
+        a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
+                                                      packed_partial_bytes(g, splits));
+        a.epoch = next_epoch();
+    } else {
+        a.partial = nullptr;
+        a.ctr = nullptr;
+        a.epoch = 0;
+    }
+    // 16-byte epilogue accesses when a lane's quad of pixels is contiguous and aligned
+    const bool quads = tc > 0 ? (tc % 4 == 0 && g.ow % 4 == 0) : (g.oh * g.ow) % 4 == 0;
+    a.vout = quads && al16(y) && (res == nullptr || al16(res)) && (ws == nullptr || al16(ws)) ? 1 : 0;
+    dim3 grid((unsigned)((long)g.n * a.tiles_per_img * ((g.cout + 31) / 32) * splits));
     if (g.k == 1)
-        launch_packed_k<1>(tile, grid, lds, s, a);
+        launch_packed_k<1>(kind, vec, grid, lds, s, a);
     else
-        launch_packed_k<3>(tile, grid, lds, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.partial == nullptr) return e;
-    return launch_splitk_finish(g, p.tile.splitk, a.partial, scale, bias, res, y, s);
+        launch_packed_k<3>(kind, vec, grid, lds, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace cvx

@@ -146,8 +146,11 @@ CVX_API cvx_status cvx_fold_bn(const float *gamma, const float *beta, const floa
  * a zero-padded cross-correlation ("Как я свертки ускорял", "А теперь — хардкор на
  * Metal", steps 2-5: window origin = output position * stride - pad, out-of-image
  * taps read as zero, BN and the activation applied while the sum is still in
- * registers, one store per output), in one launch per layer (or two when the
- * selected plan splits the reduction; then the workspace holds the partial sums).
+ * registers, one store per output), in one launch per layer.  When the selected
+ * plan splits the reduction over several workgroups, the workspace holds their
+ * partial sums and one arrival counter per output tile; with packed weights the
+ * last workgroup of a tile adds the partial sums in split order (results do not
+ * depend on timing), with OIHW weights a second launch does.
  *   d        : host, layer description.
  *   x        : device [n][c_in][h][w].
  *   w        : device; [c_out][c_in/groups][kh][kw] when d->w_layout is CVX_W_OIHW,
@@ -157,8 +160,10 @@ CVX_API cvx_status cvx_fold_bn(const float *gamma, const float *beta, const floa
  *              may equal x (read only) but must not overlap y.
  *   y        : device [n][c_out][oh][ow]; must not overlap x, w, scale, bias, residual.
  *              Only the n*c_out*oh*ow elements are written (no row padding).
- *   workspace: device scratch of cvx_conv_workspace_bytes(d) bytes (may be NULL when
- *              that is 0); contents on entry are ignored.
+ *   workspace: device scratch of cvx_conv_workspace_bytes(d) bytes, 16-byte
+ *              aligned (may be NULL when that is 0); contents on entry are ignored.
+ *              Two calls in flight at once (e.g. on two streams) must not share a
+ *              workspace.
  */
 CVX_API cvx_status cvx_conv_bn_act(const cvx_conv_desc *d, const float *x, const float *w,
                            const float *scale, const float *bias, const float *residual,

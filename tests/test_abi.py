@@ -137,6 +137,7 @@ def test_workspace_checks():
     assert _call(d) == -6
     assert _call(d, ws=WS, ws_bytes=need - 4) == -6
     assert _call(d, ws=Y, ws_bytes=need) == -5      # workspace overlapping the output
+    assert _call(d, ws=WS + 8, ws_bytes=need) == -4  # split workspaces are 16-byte aligned
     assert cvx.cvx_conv_workspace_bytes(_desc(groups=64, c_in=64, c_out=64)) == 0
 
 

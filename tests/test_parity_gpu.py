@@ -334,3 +334,147 @@ def test_igemm_forced_tiles(force, layout, monkeypatch):
         y, ok = gpu_conv(x, L, r, layout)
         assert ok, "write outside the output"
         check(y, oracle_conv(x, L, r), f"forced {force} seed {seed}")
+
+
+def _packed_setup(x, L, layout=PACKED):
+    n, c, h, w = x.shape
+    d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
+                      layout)
+    p = L.params
+    wt = dev(p["w"])
+    wp = torch.empty(cvx.cvx_packed_weights_bytes(d) // 4, device=DEV)
+    cvx.cvx_pack_weights(d, wt, wp)
+    g, b, m, v = (dev(p[k]) for k in ("gamma", "beta", "mean", "var"))
+    scale = torch.empty(L.cout, device=DEV)
+    bias = torch.empty(L.cout, device=DEV)
+    cvx.cvx_fold_bn(g, b, m, v, wl.EPS, scale, bias)
+    return d, wp, scale, bias
+
+
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_split_reduction_workspace_contents_ignored(fill, monkeypatch):
+    """The split reduction's arrival counters live in the workspace: whatever it
+    holds on entry (all-ones bytes, random bytes), and after a previous call,
+    the result is the same and correct."""
+    for force, (seed, n, cin, h, w, cout, k, s, p) in [
+            ("0,8,3", (210, 1, 128, 40, 40, 128, 3, 1, 1)),
+            ("1,0,4", (211, 2, 256, 20, 20, 96, 3, 1, 1)),
+            ("2,16,2", (212, 1, 96, 17, 23, 64, 1, 1, 0))]:
+        monkeypatch.setenv("CVX_IGEMM_TILE", force)
+        x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU,
+                                   wl.RES_AFTER_ACT)
+        d, wp, scale, bias = _packed_setup(x, L)
+        plan = cvx.cvx_conv_plan(d)
+        assert "splitk=1 " not in plan, plan
+        oh, ow = cvx.cvx_conv_out_shape(d)
+        r = wl.residual_for(seed, (n, cout, oh, ow))
+        ref = oracle_conv(x, L, r)
+        nws = cvx.cvx_conv_workspace_bytes(d)
+        if fill == "ones":
+            ws = torch.full((nws,), 255, dtype=torch.uint8, device=DEV)
+        else:
+            ws = torch.randint(0, 256, (nws,), dtype=torch.uint8, device=DEV,
+                               generator=torch.Generator(device=DEV).manual_seed(seed))
+        xt, rt = dev(x), dev(r)
+        say(f"split workspace {fill} {force}: {plan}")
+        first = None
+        for call in range(3):
+            out = Guarded((n, cout, oh, ow))
+            cvx.cvx_conv_bn_act(d, xt, wp, scale, bias, rt, out.t, ws, nws)
+            torch.cuda.synchronize()
+            y = out.t.cpu().numpy()
+            assert out.guards_intact(), "write outside the output"
+            check(y, ref, f"{force} call {call}")
+            if first is None:
+                first = y
+            else:
+                assert np.array_equal(first, y), "split reduction is not deterministic"
+
+
+@pytest.mark.parametrize("force", ["0,8,1", "1,16,1", "0,8,2", "2,0,3"])
+def test_misaligned_tensors(force, monkeypatch):
+    """x, y and the residual 4 bytes off a 16-byte boundary: the kernels fall back
+    to 4-byte staging and 4-byte epilogue accesses and give the same result."""
+    monkeypatch.setenv("CVX_IGEMM_TILE", force)
+    seed, n, cin, h, w, cout, k, s, p = 220, 1, 64, 24, 40, 80, 3, 1, 1
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU,
+                               wl.RES_BEFORE_ACT)
+    d, wp, scale, bias = _packed_setup(x, L)
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    r = wl.residual_for(seed, (n, cout, oh, ow))
+    ref = oracle_conv(x, L, r)
+    nx, ny = x.size, n * cout * oh * ow
+    xbuf = torch.zeros(nx + 4, device=DEV)
+    xbuf[1:1 + nx] = dev(x).reshape(-1)
+    rbuf = torch.zeros(ny + 4, device=DEV)
+    rbuf[1:1 + ny] = dev(r).reshape(-1)
+    out = Guarded((ny + 4,))
+    nws = cvx.cvx_conv_workspace_bytes(d)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    say(f"misaligned {force}: {cvx.cvx_conv_plan(d)}")
+    cvx.cvx_conv_bn_act(d, xbuf[1:].data_ptr(), wp, scale, bias, rbuf[1:].data_ptr(),
+                        out.t[1:].data_ptr(), ws, nws)
+    torch.cuda.synchronize()
+    y = out.t.cpu().numpy()
+    assert out.guards_intact(), "write outside the output"
+    assert np.isnan(y[0]) and np.all(np.isnan(y[1 + ny:])), "write outside the output"
+    check(y[1:1 + ny].reshape(n, cout, oh, ow), ref, f"misaligned {force}")
+
+
+def test_forward_graph_replays_match_eager():
+    """The detector forward captured once as a HIP graph and replayed several
+    times, with eager work and synchronisation between replays: every replay
+    equals the eager forward exactly.  (The library records no memsets; the
+    split reduction's counters reset themselves, so a replayed launch, whose
+    arguments are frozen, finds them as a fresh launch would.)"""
+    wk = wl.detector_pipeline(1)
+    net = Net(wk.layers, wk.x.shape, device=DEV)
+    x = dev(wk.x)
+    say("detector forward: eager reference")
+    eager = net(x).clone()
+    torch.cuda.synchronize()
+    check(eager.cpu().numpy(), oracle.forward(wk.layers, wk.x), "eager forward")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        net(x)
+    torch.cuda.synchronize()
+    for i in range(4):
+        say(f"graph replay {i}")
+        net.output.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(net.output, eager), f"replay {i} differs from the eager forward"
+        other = net(x)  # eager work between replays, on the same buffers
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+
+
+def test_split_layer_graph_replays(monkeypatch):
+    """One split-reduction layer (4 slices) captured as 3 back-to-back launches
+    and replayed: each replay gives the eager result."""
+    monkeypatch.setenv("CVX_IGEMM_TILE", "0,0,4")
+    seed, n, cin, h, w, cout, k, s, p = 230, 1, 256, 20, 20, 256, 3, 1, 1
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
+    d, wp, scale, bias = _packed_setup(x, L)
+    assert "splitk=4 " in cvx.cvx_conv_plan(d)
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    xt = dev(x)
+    y = torch.empty((n, cout, oh, ow), device=DEV)
+    nws = cvx.cvx_conv_workspace_bytes(d)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    say("split layer: eager")
+    cvx.cvx_conv_bn_act(d, xt, wp, scale, bias, xt, y, ws, nws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    check(eager.cpu().numpy(), oracle_conv(x, L, x), "split layer eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            cvx.cvx_conv_bn_act(d, xt, wp, scale, bias, xt, y, ws, nws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        say(f"split layer replay {i}")
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {i}"
