@@ -142,9 +142,11 @@ bool plan_packed(const ConvGeom& g, Plan* p)
         const int bn = packed_tile_n(kind);
         const int nt = bn / 32;
         const int cps = packed_chunks_per_stage(kind, g.k);
-        const int occ = packed_occupancy(kind, g.k);
         for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
-            if (!packed_tile_fits(g, kind, tc, nullptr)) continue;
+            size_t lds = 0;
+            if (!packed_tile_fits(g, kind, tc, &lds)) continue;
+            const int occ = std::max(1, std::min<int>(packed_occupancy(kind, g.k),
+                                                      (int)(kMaxLdsBytes / std::max<size_t>(lds, 1))));
             const double stage = cps * (2.0 * kk * nt * 64.0 +
                                         kLoadClk * packed_loads_per_chunk(g, kind, tc));
             const long tiles = (long)g.n * packed_tiles_per_image(g, kind, tc) * mblocks;
@@ -240,6 +242,7 @@ void plan_direct(const ConvGeom& g, Plan* p)
     const int cout_g = g.cout / g.groups;
     p->fam = FAM_DIRECT;
     p->direct_cob = cout_g >= 16 ? 16 : cout_g >= 8 ? 8 : cout_g >= 4 ? 4 : 1;
+    p->direct_stem = stem_shape(g) ? 1 : 0;
     p->ws_bytes = 0;
 }
 
@@ -390,8 +393,12 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
                  g.stride, p.dw_ppb, p.dw_toh, g.stride);
         break;
     case FAM_DIRECT:
-        snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
-                 g.stride, p.direct_cob, p.direct_cob);
+        if (p.direct_stem)
+            snprintf(buf, buf_len, "stem k3 s%d splitk=1 kernel=cvx::k_stem<%d, 8, %d>", g.stride,
+                     g.cin, g.stride);
+        else
+            snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
+                     g.stride, p.direct_cob, p.direct_cob);
         break;
     case FAM_IGEMM:
         igemm_kernel_name(g, p.tile.kind, kn, sizeof(kn));

@@ -39,6 +39,7 @@ struct Plan {
     int dw_ppb;        // FAM_DEPTHWISE: planes per workgroup
     int dw_toh;        // FAM_DEPTHWISE: output rows per workgroup
     int direct_cob;    // FAM_DIRECT: output channels per thread
+    int direct_stem;   // FAM_DIRECT: the stem kernel (k_stem) when tensors are 16-byte aligned
     size_t ws_bytes;   // workspace the plan needs
 };
 
@@ -60,6 +61,10 @@ hipError_t launch_direct(const ConvGeom& g, const Plan& p, const float* x, const
 hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const float* w,
                         const float* scale, const float* bias, const float* res, float* y,
                         void* ws, hipStream_t s);
+
+// 3x3 pad-1 stride-1/2 layers with 1 or 3 input channels and widths a multiple of
+// 4 (the detector and MNIST stems) run on k_stem.
+bool stem_shape(const ConvGeom& g);
 
 hipError_t launch_gap_fc(const float* x, int n, int c, int hw, const float* fc_w,
                          const float* fc_b, int out_f, float* out, hipStream_t s);
@@ -108,6 +113,7 @@ long igemm_tiles_per_image(const ConvGeom& g, int tile, int tc);
 long igemm_stage_floats(const ConvGeom& g, int tile, int tc);  // per chunk
 int igemm_chunk_channels();
 
-constexpr size_t kMaxLdsBytes = 64 * 1024;
+// LDS one workgroup may use on gfx950 (160 KB per compute unit)
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 }  // namespace cvx

@@ -203,30 +203,58 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
 
     // One stage's loads.  A chunk past the split's end reads through out-of-range
     // offsets (zero weights, zero inputs), so the matrix loop needs no branches.
+    // One stage's loads as numbered operations: for each chunk j, its weight
+    // loads (kSlots3 for 3x3, 1 for 1x1), then its input rounds (a uniform guard
+    // skips rounds past the region).  A chunk past the split's end reads through
+    // out-of-range offsets and an empty descriptor (zeros), so the matrix loop
+    // needs no branches.
+    constexpr int NAJ = K == 3 ? kSlots3 : 1;
+    constexpr int NOPJ = NAJ + NR;
+    constexpr int NOPS = CPS * NOPJ;
+    auto load_op = [&](int op, int stage, int buf, auto& A, auto& S) {
+        const int j = op / NOPJ, r = op % NOPJ;
+        const int chunk = c_begin + stage * CPS + j;
+        const bool valid = chunk < c_end;
+        if (r < NAJ) {
+            const unsigned cb = valid ? (unsigned)chunk * chunk_b : kOOB;
+            const unsigned ao = (aoff | (cb & kOOB)) + (cb & ~kOOB);
+            if constexpr (K == 3)
+                A[j][r] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ao + 1024u * r), 0, 0));
+            else
+                S[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)ao, 0, 0));
+        } else {
+            const int i = r - NAJ;
+            if (i < a.rounds) {
+                // the chunk's own descriptor: based at its first channel, covering
+                // the channels that exist (none for a chunk past the split)
+                const int left = valid ? min(kCh, a.cin - chunk * kCh) : 0;
+                const rsrc_t rc = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+                // LDS destinations are formed here, from one scalar base (held for
+                // the whole kernel they would need a register per round, chunk
+                // and buffer)
+                int dbase = buf * BUF + wave * 64 * G;
+                asm volatile("" : "+s"(dbase));
+                auto* d = (__attribute__((address_space(3))) void*)(smem + dbase + j * a.REP + 256 * G * i);
+                if constexpr (VEC)
+                    lds_load16(rc, d, goff[i]);
+                else
+                    lds_load4(rc, d, goff[i]);
+            }
+        }
+    };
+    // The same loads as one block: all weight loads, then input rounds in
+    // round-major order under one guard per round.
     auto issue = [&](int stage, int buf, auto& A, auto& S) {
         rsrc_t rc[CPS];
 #pragma unroll
         for (int j = 0; j < CPS; ++j) {
-            const int chunk = c_begin + stage * CPS + j;
-            const bool valid = chunk < c_end;
-            const unsigned cb = valid ? (unsigned)chunk * chunk_b : kOOB;
-            const unsigned ao = (aoff | (cb & kOOB)) + (cb & ~kOOB);
-            if constexpr (K == 3) {
 #pragma unroll
-                for (int s = 0; s < kSlots3; ++s)
-                    A[j][s] = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ao + 1024u * s), 0, 0));
-            } else {
-                S[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)ao, 0, 0));
-            }
-            // the chunk's own descriptor: based at its first channel, covering the
-            // channels that exist (none for a chunk past the split)
-            const int left = valid ? min(kCh, a.cin - chunk * kCh) : 0;
+            for (int r = 0; r < NAJ; ++r) load_op(j * NOPJ + r, stage, buf, A, S);
+            const int chunk = c_begin + stage * CPS + j;
+            const int left = chunk < c_end ? min(kCh, a.cin - chunk * kCh) : 0;
             rc[j] = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
         }
-        // LDS destinations are formed here, from one scalar base per call (held
-        // for the whole kernel they would need a register per round, chunk and
-        // buffer)
         int dbase = buf * BUF + wave * 64 * G;
         asm volatile("" : "+s"(dbase));
 #pragma unroll
@@ -299,7 +327,16 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
             for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
         }
     };
-    auto compute = [&](int buf, auto& A, auto& S) {
+    // For 3x3 the next stage's loads are interleaved with this stage's matrix
+    // work, one after every second matrix instruction from the start: a wave that
+    // issued them as a block would stall while the unit's address path works
+    // through every wave's loads.  (1x1 stages have too few matrix instructions
+    // to hide them; they keep the block.)
+    constexpr int ILV = 2;
+    constexpr bool INTERLEAVE = K == 3;
+    auto compute = [&](int buf, auto& A, auto& S, bool nxt_on, int nstage, int nbuf, auto& An,
+                       auto& Sn) {
+        if (!INTERLEAVE && nxt_on) issue(nstage, nbuf, An, Sn);
         float b0[KK][NT], b1[KK][NT];
         read_b(buf, 0, b0);
 #pragma unroll
@@ -319,6 +356,19 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, cur[tap][nt], acc[nt], 0, 0, 0);
+                if constexpr (INTERLEAVE) {
+                    const int sl = q * KK + tap;
+                    if (nxt_on && sl % ILV == 0 && sl / ILV < NOPS) {
+                        load_op(sl / ILV, nstage, nbuf, An, Sn);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+        if constexpr (INTERLEAVE) {
+            if (nxt_on) {
+#pragma unroll
+                for (int op = (NQ * KK + ILV - 1) / ILV; op < NOPS; ++op) load_op(op, nstage, nbuf, An, Sn);
             }
         }
     };
@@ -389,20 +439,18 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
 
     // Stages alternate between (LDS buffer 0, register set 0) and (1, 1): wait
     // for this stage's loads, barrier (its data visible to every wave; every wave
-    // done with the other buffer), issue the next stage's loads, compute.  With
-    // no next stage, the residual loads go out instead.
+    // done with the other buffer), then compute while the next stage's loads go
+    // out.  Before the last stage, the residual loads go out.
     for (int st = 0; st < nstages; st += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (st + 1 < nstages) issue(st + 1, 1, A1, S1);
-        else if (single && want_res) load_res();
-        compute(0, A0, S0);
+        if (st + 1 >= nstages && single && want_res) load_res();
+        compute(0, A0, S0, st + 1 < nstages, st + 1, 1, A1, S1);
         if (st + 1 >= nstages) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (st + 2 < nstages) issue(st + 2, 0, A0, S0);
-        else if (single && want_res) load_res();
-        compute(1, A1, S1);
+        if (st + 2 >= nstages && single && want_res) load_res();
+        compute(1, A1, S1, st + 2 < nstages, st + 2, 0, A0, S0);
     }
     if (nstages == 0 && single && want_res) load_res();
 
@@ -668,8 +716,8 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
 // LDS at two workgroups.
 int packed_occupancy(int kind, int k)
 {
-    static constexpr int kRegs[2][kNumPacked] = {{144, 205, 295},   // 1x1: NT = 1, 2, 4
-                                                 {175, 250, 360}};  // 3x3
+    static constexpr int kRegs[2][kNumPacked] = {{143, 204, 294},   // 1x1: NT = 1, 2, 4
+                                                 {186, 261, 367}};  // 3x3
     const int regs = kRegs[k == 3 ? 1 : 0][kind];
     const int occ = 512 / regs;
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;

@@ -478,3 +478,44 @@ def test_split_layer_graph_replays(monkeypatch):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, eager), f"replay {i}"
+
+
+STEM_CASES = [(cin, s, res) for cin in (1, 3) for s in (1, 2)
+              for res in (wl.RES_NONE, wl.RES_BEFORE_ACT, wl.RES_AFTER_ACT)]
+
+
+@pytest.mark.parametrize("cin,stride,res_mode", STEM_CASES,
+                         ids=[f"c{c}s{s}r{r}" for c, s, r in STEM_CASES])
+def test_stem_kernel(cin, stride, res_mode):
+    """The stem kernel (3x3 pad 1, 1 or 3 input channels, widths a multiple of 4):
+    20 output channels (a partial group of 8), a frame whose borders are all
+    padding, batch 2; then the same layer on an input 4 bytes off alignment, which
+    the generic direct kernel takes."""
+    seed = 240 + 10 * cin + stride + 3 * res_mode
+    n, h, w, cout = 2, 20, 48, 20
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, 3, stride, 1, 1, wl.ACT_SILU, res_mode)
+    d = cvx.make_desc(n, cin, h, w, cout, 3, stride, 1, 1, wl.ACT_SILU, res_mode, OIHW)
+    plan = cvx.cvx_conv_plan(d)
+    assert "k_stem" in plan, plan
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    r = wl.residual_for(seed, (n, cout, oh, ow)) if res_mode else None
+    ref = oracle_conv(x, L, r)
+    say(f"stem cin {cin} s{stride} res {res_mode}: {plan}")
+    y, ok = gpu_conv(x, L, r, OIHW)
+    assert ok, "write outside the output"
+    check(y, ref, f"stem cin {cin} s{stride}")
+    # misaligned input: generic kernel
+    p = L.params
+    xbuf = torch.zeros(x.size + 4, device=DEV)
+    xbuf[1:1 + x.size] = dev(x).reshape(-1)
+    g_, b_, m_, v_ = (dev(p[k]) for k in ("gamma", "beta", "mean", "var"))
+    scale = torch.empty(cout, device=DEV)
+    bias = torch.empty(cout, device=DEV)
+    cvx.cvx_fold_bn(g_, b_, m_, v_, wl.EPS, scale, bias)
+    out = Guarded((n, cout, oh, ow))
+    say(f"stem cin {cin} s{stride} res {res_mode}: misaligned input")
+    cvx.cvx_conv_bn_act(d, xbuf[1:].data_ptr(), dev(p["w"]), scale, bias,
+                        dev(r) if r is not None else None, out.t, None, 0)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    check(out.t.cpu().numpy(), ref, f"stem cin {cin} s{stride} misaligned")
