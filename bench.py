@@ -188,7 +188,7 @@ def kernel_sources_hash(kernel: str) -> str:
     import hashlib
     base = kernel.split("<")[0].split("::")[-1]
     srcfile = {"k_igemm_packed": "k_igemm_packed.hip", "k_igemm": "k_igemm.hip",
-               "k_direct": "k_direct.hip", "k_depthwise3x3": "k_depthwise.hip",
+               "k_direct": "k_direct.hip", "k_stem": "k_direct.hip", "k_depthwise3x3": "k_depthwise.hip",
                "k_preprocess": "k_preprocess.hip"}.get(base)
     h = hashlib.sha256()
     for f in ([srcfile] if srcfile else []) + ["bufio.h", "epilogue.h", "cvx_internal.h"]:
@@ -296,8 +296,8 @@ def _dispatches(d: str, counter: str):
 def _probe_map(disp, manifest):
     """Counter value per probed layer: the calibration copy is the last copy
     dispatch moving about COPY_BYTES before the layers; the cvx dispatches after
-    it follow the manifest (a split-K layer adds one finishing dispatch per call,
-    not counted as the layer's main kernel)."""
+    it follow the manifest, one dispatch per call (a split-K layer finishes its
+    tiles inside the same launch)."""
     cal = [i for i, (_, n, v) in enumerate(disp) if "copy" in n.lower() and "cvx::" not in n]
     i0 = cal[-1]
     cal_kib = disp[i0][2]
@@ -309,7 +309,7 @@ def _probe_map(disp, manifest):
             n, v = rest[j]
             assert m["kernel"] in n, (m, n)
             vals.append(v)
-            j += 2 if m["splitk"] > 1 else 1
+            j += 1
         per[m["layer"]] = sum(vals) / len(vals)
     return cal_kib, per
 
