@@ -117,22 +117,21 @@ bool slices_ok(int nchunks, int sk)
 }
 
 // Packed-weight implicit GEMM: tile, tc and split count by a cost model of one
-// MI355X in clocks, fitted to in-kernel timelines (s_memtime per workgroup) of
-// the detector layers and to a sweep of every configuration of them.  A
-// workgroup pays a fixed ~6000 clocks (first loads from cold caches, the
-// cross-wave exchange, the epilogue); each stage of chunks costs its matrix time
-// (2 pairs x taps x NT x 64 clocks per SIMD and chunk) plus ~28 clocks per
-// vector-memory instruction the unit issues for it (the loads of a stage are
-// issued as a block); a split into s slices adds ~4000 + 800*NT*s clocks (the
-// partial sums' round trip through memory and the arrival count).  Up to
-// packed_occupancy(kind) workgroups share a compute unit, each slowing the
-// others by ~30%.
+// MI355X in clocks.  A workgroup pays a fixed start (kernel arguments, address
+// set-up, the cross-wave exchange and the epilogue) plus its first stage's loads,
+// which nothing overlaps; after that the producers load stage s+1 while the
+// consumers compute stage s, so a stage costs the larger of its matrix time
+// (2 pairs x taps x NT x 64 clocks per SIMD and chunk) and its load time
+// (~30 clocks per vector-memory instruction the unit issues), plus a barrier.
+// A split into s slices adds ~4000 + 800*NT*s clocks (the partial sums' round
+// trip through memory and the arrival count).  Up to packed_occupancy(kind)
+// workgroups share a compute unit, each slowing the others by ~30%.
 bool plan_packed(const ConvGeom& g, Plan* p)
 {
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
-    const double kCUs = 256.0, kFixedClk = 6000.0, kLoadClk = 28.0, kSplitClk = 4000.0,
-                 kSplitEachClk = 800.0, kShare = 0.3;
+    const double kCUs = 256.0, kFixedClk = 4000.0, kLoadClk = 30.0, kBarrierClk = 150.0,
+                 kSplitClk = 4000.0, kSplitEachClk = 800.0, kShare = 0.3;
     const int nchunks = (g.cin + 15) / 16;
     const int kk = g.k * g.k;
     const long mblocks = (g.cout + 31) / 32;
@@ -147,15 +146,15 @@ bool plan_packed(const ConvGeom& g, Plan* p)
             if (!packed_tile_fits(g, kind, tc, &lds)) continue;
             const int occ = std::max(1, std::min<int>(packed_occupancy(kind, g.k),
                                                       (int)(kMaxLdsBytes / std::max<size_t>(lds, 1))));
-            const double stage = cps * (2.0 * kk * nt * 64.0 +
-                                        kLoadClk * packed_loads_per_chunk(g, kind, tc));
+            const double loads = cps * kLoadClk * packed_loads_per_chunk(g, kind, tc);
+            const double stage = std::max(cps * 2.0 * kk * nt * 64.0, loads) + kBarrierClk;
             const long tiles = (long)g.n * packed_tiles_per_image(g, kind, tc) * mblocks;
             for (int sk = 1; sk <= 8; ++sk) {
                 if (!slices_ok(nchunks, sk)) continue;
                 if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
                 const int per = (nchunks + sk - 1) / sk;
                 const int stages = (per + cps - 1) / cps;
-                const double wg = kFixedClk + stages * stage +
+                const double wg = kFixedClk + loads + stages * stage +
                                   (sk > 1 ? kSplitClk + kSplitEachClk * nt * sk : 0.0);
                 const long wgs = tiles * sk;
                 const double per_cu = std::ceil(wgs / kCUs);  // workgroups one unit runs

@@ -37,4 +37,20 @@ __device__ __forceinline__ void bstore(rsrc_t r, unsigned off_bytes, float v)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off_bytes, 0, 0);
 }
 
+// Touches every 64-byte line of the kernel's argument block with scalar loads
+// issued together and waits once.  Left alone, the compiler loads the fields
+// in several batches, each waited on before the next is issued, so a large
+// argument block costs several memory round trips per workgroup; afterwards
+// every field is a scalar-cache hit.
+template <int BYTES>
+__device__ __forceinline__ void warm_kernargs()
+{
+    typedef const __attribute__((address_space(4))) unsigned* kptr;
+    const kptr k = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+    unsigned v = k[(BYTES - 4) / 4];
+#pragma unroll
+    for (int o = 0; o < BYTES - 4; o += 64) v |= k[o / 4];
+    asm volatile("" ::"s"(v));
+}
+
 }  // namespace cvx

@@ -2,41 +2,58 @@
 // reading weights that were packed once, at model load, into the matrix
 // instruction's operand order.
 //
-// Implicit GEMM: M = c_out, N = output pixels, K = c_in*kh*kw, computed with
+// Implicit GEMM: M = output pixels, N = c_out, K = c_in*kh*kw, computed with
 // v_mfma_f32_32x32x2_f32; the folded BatchNorm, the residual and the activation
 // are applied to the sums before the single store of each output
 // ("YOLO26N Inference Optimisation", "Improvements" #7; "Как я свертки
 // ускорял", "А теперь — хардкор на Metal", steps 4-5).
 //
-// Work decomposition.  A workgroup is four waves computing one tile of 32 output
-// channels x 32*NT output pixels; the waves split every 16-channel chunk of the
-// reduction (wave w takes channel pairs 2w and 2w+1), so each weight value a wave
-// loads feeds NT matrix instructions, and the four partial tiles are summed
-// through LDS at the end.  The pixels of a tile are either a run of consecutive
-// output pixels or a block of rows x `tc` columns.  Optionally the reduction is
-// split over `splits` workgroups; the last one to finish a tile adds the others'
-// partial sums (in split order) and applies the epilogue, so the layer is one
-// launch.
+// Work decomposition.  A workgroup computes one tile of 32 output channels x
+// 32*NT output pixels with eight waves in two roles:
+//   * four producer waves (one per SIMD) only move data: every stage of CPS
+//     16-channel chunks goes global -> LDS with LDS-direct buffer loads, the
+//     weights as contiguous 1 KB blocks and the input region row by row;
+//   * four consumer waves (one per SIMD) only compute: each takes two of a
+//     chunk's eight channel pairs (wave w: pairs 2w, 2w+1), reads its operands
+//     from LDS and issues the matrix instructions; the four partial tiles are
+//     summed through LDS at the end.
+// A unit's vector-memory path takes ~30 clocks per 64-lane load, so a wave that
+// issues loads stalls while the queue drains; with the roles split, only the
+// producers wait there and the consumers' matrix pipes stay busy.  Three LDS
+// buffers and one barrier per stage: at barrier s the producers have landed
+// stage s+1 and the consumers have finished stage s-1, so stage s+2 loads while
+// stage s computes, and the consumers read the next stage's first operands
+// before the barrier that separates the two.
 //
-// Memory paths (one workgroup per compute unit, so what bounds a stage is how
-// many vector-memory instructions the unit must process):
-//   * weights: [32-row block][16-channel chunk][pair of channel pairs h (4)]
-//     [slot (5)][lane][4] for 3x3 -- lane l holds output channel 32*block + l%32
-//     and input channels of pairs 2h and 2h+1, its 18 taps (9 per pair) packed
-//     into five 16-byte slots, so a wave reads a chunk's weights with five
-//     coalesced loads; [block][chunk][h][lane][2] for 1x1 (one 8-byte load).
-//     ("YOLO26N Inference Optimisation", "NHWC migration", "Weight layout":
-//     weights are reordered once for the layout the kernels read.)
-//   * inputs: the chunk's input region goes global -> LDS with LDS-direct buffer
-//     loads, 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
+// The pixels of a tile are either a run of consecutive output pixels or a block
+// of rows x `tc` columns.  Optionally the reduction is split over `splits`
+// workgroups; the last one to finish a tile adds the others' partial sums (in
+// split order) and applies the epilogue, so the layer is one launch.
+//
+// Operand order.  The input is the A operand (lane l: pixel l%32 of a block,
+// channel 2*pair + l/32) and the weights the B operand (lane l: output channel
+// l%32, same channel), so a lane's accumulators hold four runs of four
+// consecutive pixels of one output channel: the exchange and the epilogue move
+// them 16 bytes at a time.
+//
+// Layouts:
+//   * packed weights: [32-row block][16-channel chunk][pair of channel pairs h
+//     (4)][slot (5)][lane][4] for 3x3 -- lane l holds output channel
+//     32*block + l%32 and input channels of pairs 2h and 2h+1, its 18 taps (9
+//     per pair) in five 16-byte slots; [block][chunk][h][lane][2] for 1x1.
+//     A (block, chunk) is one contiguous run of 20 KB (3x3) or 2 KB (1x1),
+//     copied to LDS unchanged.  ("YOLO26N Inference Optimisation", "NHWC
+//     migration", "Weight layout": weights are reordered once for the layout
+//     the kernels read.)
+//   * inputs: 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
 //     positions outside the image use out-of-range offsets and read as zero, so
 //     padding needs no code.
-//   * two LDS buffers and two register sets: the loads of stage s+1 are issued
-//     before the matrix work of stage s.
+//   * LDS stage buffer: [chunk j][weights | staged input region].
 #include <stdio.h>
 
 #include <atomic>
 #include <chrono>
+#include <type_traits>
 
 #include "bufio.h"
 #include "cvx_internal.h"
@@ -54,6 +71,7 @@ constexpr int kSC1 = 16;                       // cache policy: device-coherent 
 constexpr int kSlots3 = 5;                     // 16-byte weight slots per lane per h (3x3)
 constexpr int kBCFloats3 = 4 * kSlots3 * 256;  // floats per (block, chunk), 3x3: 5120
 constexpr int kBCFloats1 = 4 * 128;            // floats per (block, chunk), 1x1: 512
+constexpr int kThreads = 512;                  // four consumer and four producer waves
 
 __device__ __forceinline__ int pdiv(int n, unsigned m, unsigned l)
 {
@@ -90,8 +108,9 @@ struct PackedArgs {
     unsigned m_tc, l_tc, m_tw, l_tw, m_ow, l_ow;
     int PR, PCW;                // staged rows, LDS floats per staged row
     int EPR, RE, rounds, REP;   // elements per row, elements per chunk, load rounds, LDS floats per chunk
-    unsigned m_rc, l_rc, m_c, l_c;
-    int step_ci, step_r, step_c;  // 256 elements in mixed radix (channel, row, element)
+    unsigned m_rc, l_rc, m_c, l_c;  // divide by staged elements per channel, per row
+    unsigned m_nb, l_nb, m_sp, l_sp, m_tpi, l_tpi;  // divide by n*tiles, splits, tiles per image
+    int tr;                     // output rows of a 2-D tile (BN / tc)
     unsigned wp_bytes;
     int vout;                   // 16-byte epilogue accesses
     int act, res_mode;
@@ -100,16 +119,19 @@ struct PackedArgs {
 constexpr int kRoundsVec = 8, kRoundsScalar = 24;  // most staging rounds per chunk
 
 template <int K, int NT, int CPS, int VEC>
-__global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
+__global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 {
     constexpr int NR = VEC ? kRoundsVec : kRoundsScalar;
     constexpr int KK = K * K;
     constexpr int G = VEC ? 4 : 1;     // floats per staged element
     constexpr int BN = 32 * NT;
     constexpr int PITCH = BN + (NT < 4 ? 4 : 0);  // LDS row pitch of the partial-sum exchange
+    constexpr int WF = K == 3 ? kBCFloats3 : kBCFloats1;  // weight floats per chunk
+    constexpr int NWL = WF / 256;      // 1 KB weight blocks per chunk: 20 (3x3), 2 (1x1)
 
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     __shared__ int s_last;
+    warm_kernargs<sizeof(PackedArgs)>();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,12 +148,11 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
         const unsigned h = blockIdx.x, G8 = gridDim.x;
         const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
         const int L = (int)(xcd * base + min(xcd, rem) + i8);
-        const int NB = a.n * a.tiles_per_img;
-        const int bt = L % NB;
-        const int ms = L / NB;
-        sp = ms % a.splits;
-        mb = ms / a.splits;
-        b = bt / a.tiles_per_img;
+        const int ms = pdiv(L, a.m_nb, a.l_nb);
+        const int bt = L - ms * (a.n * a.tiles_per_img);
+        mb = pdiv(ms, a.m_sp, a.l_sp);
+        sp = ms - mb * a.splits;
+        b = pdiv(bt, a.m_tpi, a.l_tpi);
         tile = bt - b * a.tiles_per_img;
     }
     const int co0 = mb * 32;
@@ -149,131 +170,114 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
     } else {
         const int band = pdiv(tile, a.m_tw, a.l_tw);
         const int tw = tile - band * a.tiles_w;
-        oh_ref = band * (BN / a.tc);
+        oh_ref = band * a.tr;
         ix0 = tw * a.tc * a.stride - a.pad;
         q0 = tw * a.tc;  // first output column of the tile
     }
-    const int iy0 = oh_ref * a.stride - a.pad;
     const int gx0 = VEC ? (ix0 & ~3) : ix0;  // staged columns start on a 16-byte boundary
-    const int RS = a.PR * a.PCW;             // LDS floats per staged channel
-    const int BUF = CPS * a.REP;
-
-    // Staged elements e = tid + 256*i: (channel, row, element-in-row) found once,
-    // then stepped by 256 in mixed radix; byte offset from the chunk's first
-    // channel, or kOOB outside the image.
-    unsigned goff[NR];
-    {
-        const int per_ch = a.PR * a.EPR;
-        int ci = pdiv(tid, a.m_rc, a.l_rc);
-        const int rem = tid - ci * per_ch;
-        int r = pdiv(rem, a.m_c, a.l_c);
-        int c = rem - r * a.EPR;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            goff[i] = kOOB;
-            if (i < a.rounds) {
-                const int e = tid + 256 * i;
-                const int iy = iy0 + r, gx = gx0 + G * c;
-                if (e < a.RE && iy >= 0 && iy < a.H && gx >= 0 && gx + G <= a.W)
-                    goff[i] = 4u * (unsigned)(ci * HW + iy * a.W + gx);
-                c += a.step_c;
-                const bool cc = c >= a.EPR;
-                c -= cc ? a.EPR : 0;
-                r += a.step_r + (cc ? 1 : 0);
-                const bool rc = r >= a.PR;
-                r -= rc ? a.PR : 0;
-                ci += a.step_ci + (rc ? 1 : 0);
-            }
-        }
-    }
-    const float* xim = a.x + (long)b * a.cin * HW;
-    const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
-    constexpr int BCF = K == 3 ? kBCFloats3 : kBCFloats1;
-    const unsigned aoff = 4u * (unsigned)(mb * a.nchunks * BCF +
-                                          (K == 3 ? wave * kSlots3 * 256 + lane * 4
-                                                  : wave * 128 + lane * 2));
-    const unsigned chunk_b = 4u * BCF;
+    const int CHF = WF + a.REP;              // LDS floats per chunk: weights, then the input region
+    const int BUF = CPS * CHF;               // one of three stage buffers
 
     const int c_begin = sp * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
     const int nstages = (c_end - c_begin + CPS - 1) / CPS;
 
-    f32x4 A0[CPS][K == 3 ? kSlots3 : 1], A1[CPS][K == 3 ? kSlots3 : 1];
-    f32x2 S0[CPS], S1[CPS];
-
-    // One stage's loads.  A chunk past the split's end reads through out-of-range
-    // offsets (zero weights, zero inputs), so the matrix loop needs no branches.
-    // One stage's loads as numbered operations: for each chunk j, its weight
-    // loads (kSlots3 for 3x3, 1 for 1x1), then its input rounds (a uniform guard
-    // skips rounds past the region).  A chunk past the split's end reads through
-    // out-of-range offsets and an empty descriptor (zeros), so the matrix loop
-    // needs no branches.
-    constexpr int NAJ = K == 3 ? kSlots3 : 1;
-    constexpr int NOPJ = NAJ + NR;
-    constexpr int NOPS = CPS * NOPJ;
-    auto load_op = [&](int op, int stage, int buf, auto& A, auto& S) {
-        const int j = op / NOPJ, r = op % NOPJ;
-        const int chunk = c_begin + stage * CPS + j;
-        const bool valid = chunk < c_end;
-        if (r < NAJ) {
-            const unsigned cb = valid ? (unsigned)chunk * chunk_b : kOOB;
-            const unsigned ao = (aoff | (cb & kOOB)) + (cb & ~kOOB);
-            if constexpr (K == 3)
-                A[j][r] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ao + 1024u * r), 0, 0));
-            else
-                S[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)ao, 0, 0));
-        } else {
-            const int i = r - NAJ;
-            if (i < a.rounds) {
-                // the chunk's own descriptor: based at its first channel, covering
-                // the channels that exist (none for a chunk past the split)
-                const int left = valid ? min(kCh, a.cin - chunk * kCh) : 0;
-                const rsrc_t rc = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
-                // LDS destinations are formed here, from one scalar base (held for
-                // the whole kernel they would need a register per round, chunk
-                // and buffer)
-                int dbase = buf * BUF + wave * 64 * G;
-                asm volatile("" : "+s"(dbase));
-                auto* d = (__attribute__((address_space(3))) void*)(smem + dbase + j * a.REP + 256 * G * i);
-                if constexpr (VEC)
-                    lds_load16(rc, d, goff[i]);
-                else
-                    lds_load4(rc, d, goff[i]);
-            }
-        }
-    };
-    // The same loads as one block: all weight loads, then input rounds in
-    // round-major order under one guard per round.
-    auto issue = [&](int stage, int buf, auto& A, auto& S) {
-        rsrc_t rc[CPS];
-#pragma unroll
-        for (int j = 0; j < CPS; ++j) {
-#pragma unroll
-            for (int r = 0; r < NAJ; ++r) load_op(j * NOPJ + r, stage, buf, A, S);
-            const int chunk = c_begin + stage * CPS + j;
-            const int left = chunk < c_end ? min(kCh, a.cin - chunk * kCh) : 0;
-            rc[j] = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
-        }
-        int dbase = buf * BUF + wave * 64 * G;
-        asm volatile("" : "+s"(dbase));
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            if (i >= a.rounds) break;
+    if (wave >= 4) {
+        // ---------------------------------------------------------- producers
+        const int ptid = tid - 256;
+        const int pw = wave - 4;
+        const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
+        const unsigned wrow = 4u * (unsigned)(mb * a.nchunks * WF) + 16u * (unsigned)lane;
+        // A stage's weights: the chunk's 1 KB blocks, dealt to the four producer
+        // waves in turn.  A chunk past the split's end reads through
+        // out-of-range offsets (and its input through an empty descriptor):
+        // zeros land in LDS, so the consumers need no branches.
+        auto issue_w = [&](int st, int sb) {
 #pragma unroll
             for (int j = 0; j < CPS; ++j) {
-                auto* d = (__attribute__((address_space(3))) void*)(smem + dbase + j * a.REP + 256 * G * i);
-                if constexpr (VEC)
-                    lds_load16(rc[j], d, goff[i]);
-                else
-                    lds_load4(rc[j], d, goff[i]);
+                const int chunk = c_begin + st * CPS + j;
+                int cbase = sb + j * CHF;
+                asm volatile("" : "+s"(cbase));
+                const unsigned wo = chunk < c_end ? wrow + 4u * (unsigned)(chunk * WF) : kOOB;
+#pragma unroll
+                for (int l = 0; l < (NWL + 3) / 4; ++l) {
+                    const int blk = pw + 4 * l;
+                    if (blk < NWL)
+                        lds_load16(rw, (__attribute__((address_space(3))) void*)(smem + cbase + 256 * blk),
+                                   wo + 1024u * blk);
+                }
+            }
+        };
+        // The first two stages' weights go out before anything else is worked out.
+        if (nstages > 0) issue_w(0, 0);
+        if (nstages > 1) issue_w(1, BUF);
+
+        // Staged input elements e = ptid + 256*i -> (channel, row, element of the
+        // row) -> byte offset from the chunk's first channel, or kOOB outside the
+        // image (or past the region).
+        const int iy0 = oh_ref * a.stride - a.pad;
+        const int per_ch = a.PR * a.EPR;
+        unsigned goff[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            goff[i] = kOOB;
+            if (i < a.rounds) {
+                const int e = ptid + 256 * i;
+                const int ci = pdiv(e, a.m_rc, a.l_rc);
+                const int rem = e - ci * per_ch;
+                const int r = pdiv(rem, a.m_c, a.l_c);
+                const int iy = iy0 + r, gx = gx0 + G * (rem - r * a.EPR);
+                const bool ok = e < a.RE && (unsigned)iy < (unsigned)a.H && gx >= 0 && gx + G <= a.W;
+                goff[i] = ok ? 4u * (unsigned)(ci * HW + iy * a.W + gx) : kOOB;
             }
         }
-    };
-    if (nstages > 0) issue(0, 0, A0, S0);
+        const float* xim = a.x + (long)b * a.cin * HW;
+        auto issue_x = [&](int st, int sb) {
+#pragma unroll
+            for (int j = 0; j < CPS; ++j) {
+                const int chunk = c_begin + st * CPS + j;
+                int cbase = sb + j * CHF;
+                asm volatile("" : "+s"(cbase));
+                const int left = chunk < c_end ? min(kCh, a.cin - chunk * kCh) : 0;
+                const rsrc_t rc = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if (i >= a.rounds) break;
+                    auto* d = (__attribute__((address_space(3))) void*)(smem + cbase + WF + 256 * G * i +
+                                                                         pw * 64 * G);
+                    if constexpr (VEC)
+                        lds_load16(rc, d, goff[i]);
+                    else
+                        lds_load4(rc, d, goff[i]);
+                }
+            }
+        };
+        // Barrier s (s = 0 .. nstages-1) follows the landing of stage s+1; stage
+        // s+2 then goes into the buffer of stage s-1, which the consumers have
+        // left by barrier s.
+        if (nstages > 0) issue_x(0, 0);
+        if (nstages > 1) issue_x(1, BUF);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int sb = 2 * BUF;
+        for (int st = 1; st < nstages; ++st) {
+            if (st + 1 < nstages) {
+                issue_w(st + 1, sb);
+                issue_x(st + 1, sb);
+            }
+            sb = sb == 2 * BUF ? 0 : sb + BUF;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        // then the consumers' exchange barriers (and the split's two)
+        const int tail = a.partial == nullptr ? 2 : 4;
+        for (int i = 0; i < tail; ++i) __syncthreads();
+        return;
+    }
 
-    // Epilogue rows: after the exchange, wave w owns output rows 8w..8w+7 of the
-    // tile; lane -> row 8w + lane/8 and pixel quads 4*(lane%8) + 32*k.
+    // -------------------------------------------------------------- consumers
+    // Epilogue rows: after the exchange, wave w owns output channels 8w..8w+7 of
+    // the tile; lane -> channel 8w + lane/8 and pixel quads 4*(lane%8) + 32*k.
     const int erow = 8 * wave + (lane >> 3);
     const int eco = co0 + erow;
     const bool row_ok = eco < a.cout;
@@ -286,6 +290,7 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
     }
 
     // LDS offset of each of this lane's pixels (tap 0) in a staged channel
+    const int RS = a.PR * a.PCW;  // LDS floats per staged channel
     int loff[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -309,15 +314,31 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
-    // One stage's matrix work: for each chunk and each of the wave's two channel
-    // pairs, KK taps x NT pixel blocks.  The B operands of the next pair are read
-    // from LDS before the current pair's MFMAs are issued.
-    constexpr int NQ = CPS * 2;
-    auto read_b = [&](int buf, int q, float (&bv)[KK][NT]) {
+    // Matrix work, pair by pair: for each chunk, this wave's weights (its
+    // h = wave block of the chunk) and, for each of its two channel pairs, KK
+    // taps x NT pixel blocks.  The input operands of the next pair and the
+    // weights of the next chunk are read from LDS before the current pair's
+    // instructions, also across a stage boundary: the next stage has landed by
+    // the current stage's barrier.
+    constexpr int NAS = K == 3 ? kSlots3 : 1;
+    auto read_a = [&](int sb, int j, f32x4 (&av)[NAS]) {
+        int base = sb + j * CHF + wave * (WF / 4);
+        asm volatile("" : "+s"(base));
+        base &= ~3;  // a multiple of 4 floats already: 16-byte reads, not split ones
+        if constexpr (K == 3) {
+#pragma unroll
+            for (int s = 0; s < kSlots3; ++s)
+                av[s] = *reinterpret_cast<const f32x4*>(smem + base + 256 * s + 4 * lane);
+        } else {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(smem + base + 2 * lane);
+            av[0] = f32x4{v[0], v[1], 0.0f, 0.0f};
+        }
+    };
+    auto read_b = [&](int sb, int q, float (&bv)[KK][NT]) {
         const int j = q >> 1, pp = q & 1;
-        // formed here, each stage: hoisting these addresses out of the stage loop
-        // would hold one register per (chunk, pair, tap row, block, buffer)
-        int base = buf * BUF + j * a.REP + (2 * (2 * wave + pp) + hi) * RS;
+        // formed here: hoisting these addresses would hold one register per
+        // (chunk, pair, buffer)
+        int base = sb + j * CHF + WF + (2 * (2 * wave + pp) + hi) * RS;
         asm volatile("" : "+v"(base));
         const float* xa = smem + base;
 #pragma unroll
@@ -327,48 +348,42 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
             for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
         }
     };
-    // For 3x3 the next stage's loads are interleaved with this stage's matrix
-    // work, one after every second matrix instruction from the start: a wave that
-    // issued them as a block would stall while the unit's address path works
-    // through every wave's loads.  (1x1 stages have too few matrix instructions
-    // to hide them; they keep the block.)
-    constexpr int ILV = 2;
-    constexpr bool INTERLEAVE = K == 3;
-    auto compute = [&](int buf, auto& A, auto& S, bool nxt_on, int nstage, int nbuf, auto& An,
-                       auto& Sn) {
-        if (!INTERLEAVE && nxt_on) issue(nstage, nbuf, An, Sn);
-        float b0[KK][NT], b1[KK][NT];
-        read_b(buf, 0, b0);
+    constexpr int NQ = CPS * 2;
+    float b0[KK][NT], b1[KK][NT];
+    f32x4 a0[NAS], a1[NAS];
+    // One stage at buffer `sb`, the next stage's at `nsb` (when `more`).  Pair q
+    // uses input registers q&1 (NQ is even); chunk c of the layer uses weight
+    // registers c&1, i.e. (SP*CPS + j)&1 for stage parity SP.
+    auto stage = [&](auto spc, int sb, int nsb, bool more) {
+        constexpr int SP = decltype(spc)::value;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             float (&cur)[KK][NT] = (q & 1) ? b1 : b0;
             float (&nxt)[KK][NT] = (q & 1) ? b0 : b1;
-            if (q + 1 < NQ) read_b(buf, q + 1, nxt);
-            __builtin_amdgcn_sched_barrier(0);
             const int j = q >> 1, pp = q & 1;
+            f32x4 (&ac)[NAS] = ((SP * CPS + j) & 1) ? a1 : a0;
+            f32x4 (&an)[NAS] = ((SP * CPS + j) & 1) ? a0 : a1;
+            if (q + 1 < NQ)
+                read_b(sb, q + 1, nxt);
+            else if (more)
+                read_b(nsb, 0, nxt);
+            if (pp == 0) {
+                if (j + 1 < CPS)
+                    read_a(sb, j + 1, an);
+                else if (more)
+                    read_a(nsb, 0, an);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int tap = 0; tap < KK; ++tap) {
-                float av;
+                float wv;
                 if constexpr (K == 3)
-                    av = A[j][(9 * pp + tap) / 4][(9 * pp + tap) % 4];
+                    wv = ac[(9 * pp + tap) / 4][(9 * pp + tap) % 4];
                 else
-                    av = S[j][pp];
+                    wv = ac[0][pp];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, cur[tap][nt], acc[nt], 0, 0, 0);
-                if constexpr (INTERLEAVE) {
-                    const int sl = q * KK + tap;
-                    if (nxt_on && sl % ILV == 0 && sl / ILV < NOPS) {
-                        load_op(sl / ILV, nstage, nbuf, An, Sn);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            }
-        }
-        if constexpr (INTERLEAVE) {
-            if (nxt_on) {
-#pragma unroll
-                for (int op = (NQ * KK + ILV - 1) / ILV; op < NOPS; ++op) load_op(op, nstage, nbuf, An, Sn);
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[tap][nt], wv, acc[nt], 0, 0, 0);
             }
         }
     };
@@ -437,33 +452,44 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
         for (int k = 0; k < NT; ++k) rv[k] = load_quad(rr, k);
     };
 
-    // Stages alternate between (LDS buffer 0, register set 0) and (1, 1): wait
-    // for this stage's loads, barrier (its data visible to every wave; every wave
-    // done with the other buffer), then compute while the next stage's loads go
-    // out.  Before the last stage, the residual loads go out.
-    for (int st = 0; st < nstages; st += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (st + 1 >= nstages && single && want_res) load_res();
-        compute(0, A0, S0, st + 1 < nstages, st + 1, 1, A1, S1);
-        if (st + 1 >= nstages) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (st + 2 >= nstages && single && want_res) load_res();
-        compute(1, A1, S1, st + 2 < nstages, st + 2, 0, A0, S0);
+    // Barrier s: the producers have landed stage s+1, this wave has finished
+    // stage s-1 (whose buffer now takes stage s+2).  The residual loads go out
+    // with the last stage.
+    __syncthreads();
+    if (nstages > 0) {
+        read_a(0, 0, a0);
+        read_b(0, 0, b0);
+    }
+    {
+        int sb = 0;
+        for (int st = 0; st < nstages; st += 2) {
+            if (st > 0) __syncthreads();
+            if (st + 1 == nstages && single && want_res) load_res();
+            const int sb1 = sb == 2 * BUF ? 0 : sb + BUF;
+            stage(std::integral_constant<int, 0>{}, sb, sb1, st + 1 < nstages);
+            if (st + 1 >= nstages) break;
+            __syncthreads();
+            if (st + 2 == nstages && single && want_res) load_res();
+            const int sb2 = sb1 == 2 * BUF ? 0 : sb1 + BUF;
+            stage(std::integral_constant<int, 1>{}, sb1, sb2, st + 2 < nstages);
+            sb = sb2;
+        }
     }
     if (nstages == 0 && single && want_res) load_res();
 
-    // Partial-sum exchange: every wave writes its 32 x BN tile, then wave w sums
-    // rows 8w..8w+7 of the four tiles in wave order.
+    // Partial-sum exchange (the producers have left): every wave writes its
+    // BN x 32 tile as [channel][pixel], then wave w sums channels 8w..8w+7 of the
+    // four tiles in wave order.  Lane (hi, l32) holds channel l32 and the pixel
+    // runs 32*nt + 8*g + 4*hi + 0..3, g = 0..3.
     __syncthreads();
     {
-        float* red = smem + wave * 32 * PITCH;
+        float* red = smem + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                red[(8 * (r >> 2) + 4 * hi + (r & 3)) * PITCH + 32 * nt + l32] = acc[nt][r];
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4*>(red + 32 * nt + 8 * g) =
+                    f32x4{acc[nt][4 * g], acc[nt][4 * g + 1], acc[nt][4 * g + 2], acc[nt][4 * g + 3]};
     }
     __syncthreads();
     f32x4 v[NT];
@@ -489,6 +515,14 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
             const rsrc_t rps = make_rsrc(a.partial + (long)sp * (part_b / 4), part_b);
 #pragma unroll
             for (int k = 0; k < NT; ++k) store_quad(rps, k, v[k], true);
+        }
+        // whichever workgroup finishes the tile needs these: fetched by all,
+        // while the stores drain
+        {
+            const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
+            sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
+            bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
+            if (want_res) load_res();
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -519,10 +553,6 @@ __global__ void __launch_bounds__(256) k_igemm_packed(PackedArgs a)
         }
 #pragma unroll
         for (int k = 0; k < NT; ++k) v[k] = tot[k];
-        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
-        sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
-        bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
-        if (want_res) load_res();
     }
 
     const rsrc_t ry = make_rsrc(a.y, out_bytes);
@@ -589,7 +619,7 @@ __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ 
 struct PackedKind {
     int nt, cps3, cps1;
 };
-static constexpr PackedKind kPacked[] = {{1, 2, 8}, {2, 2, 8}, {4, 1, 4}};
+static constexpr PackedKind kPacked[] = {{1, 1, 4}, {2, 1, 4}, {4, 1, 2}};
 constexpr int kNumPacked = sizeof(kPacked) / sizeof(kPacked[0]);
 
 int packed_num_kinds() { return kNumPacked; }
@@ -670,7 +700,8 @@ static Region packed_region(const ConvGeom& g, int kind, int tc, bool vec)
 static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
 {
     const int nt = kPacked[kind].nt;
-    const size_t stage = 2 * (size_t)packed_chunks_per_stage(kind, g.k) * r.rep * sizeof(float);
+    const size_t wf = g.k == 3 ? kBCFloats3 : kBCFloats1;
+    const size_t stage = 3 * (size_t)packed_chunks_per_stage(kind, g.k) * (wf + r.rep) * sizeof(float);
     const size_t red = (size_t)4 * 32 * (32 * nt + (nt < 4 ? 4 : 0)) * sizeof(float);
     return stage > red ? stage : red;
 }
@@ -691,7 +722,7 @@ bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
         const Region r = packed_region(g, kind, tc, vec != 0);
         if (r.rounds > (vec ? kRoundsVec : kRoundsScalar)) return false;
         const size_t l = packed_lds(g, kind, r);
-        if (l > kMaxLdsBytes) return false;
+        if (l + 256 > kMaxLdsBytes) return false;  // leaves room for the static flag
         lds = l > lds ? l : lds;
     }
     if (lds_bytes) *lds_bytes = lds;
@@ -711,23 +742,26 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
     return packed_partial_bytes(g, splits) + tiles * sizeof(unsigned long long);
 }
 
-// Waves per SIMD the compiled kernels allow (512 registers per lane, VGPRs plus
-// accumulation registers, as the compiler reports them for gfx950), capped by
-// LDS at two workgroups.
+// Workgroups per compute unit the compiled kernels allow: each puts two waves
+// on every SIMD, and a SIMD holds 512 registers per lane (VGPRs plus
+// accumulation registers, as the compiler reports them for gfx950); capped at
+// two (LDS).
 int packed_occupancy(int kind, int k)
 {
-    static constexpr int kRegs[2][kNumPacked] = {{143, 204, 294},   // 1x1: NT = 1, 2, 4
-                                                 {186, 261, 367}};  // 3x3
+    static constexpr int kRegs[2][kNumPacked] = {{78, 120, 197},    // 1x1: NT = 1, 2, 4
+                                                 {115, 174, 256}};  // 3x3
     const int regs = kRegs[k == 3 ? 1 : 0][kind];
-    const int occ = 512 / regs;
+    const int occ = 512 / regs / 2;
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;
 }
 
+// Vector-memory instructions the producers issue per chunk: the weights' 1 KB
+// blocks and four per input round.
 int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc)
 {
     const bool vec = g.w % 4 == 0;
     const Region r = packed_region(g, kind, tc, vec);
-    return 4 * (g.k == 3 ? kSlots3 : 1) + 4 * r.rounds;
+    return (g.k == 3 ? kBCFloats3 : kBCFloats1) / 256 + 4 * r.rounds;
 }
 
 void packed_kernel_name(const ConvGeom& g, int kind, char* buf, int len)
@@ -755,7 +789,7 @@ static unsigned long long next_epoch()
 template <int K, int NT, int CPS, int VEC>
 static void launch_packed_cfg(dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
 {
-    hipLaunchKernelGGL((k_igemm_packed<K, NT, CPS, VEC>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_igemm_packed<K, NT, CPS, VEC>), grid, dim3(kThreads), lds, s, a);
 }
 
 template <int K, int KIND>
@@ -828,13 +862,10 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     a.REP = r.rep;
     fastdiv_params(r.pr * r.epr, &a.m_rc, &a.l_rc);
     fastdiv_params(r.epr, &a.m_c, &a.l_c);
-    {
-        const int rc = r.pr * r.epr;
-        a.step_ci = 256 / rc;
-        const int rem = 256 % rc;
-        a.step_r = rem / r.epr;
-        a.step_c = rem % r.epr;
-    }
+    fastdiv_params(g.n * a.tiles_per_img, &a.m_nb, &a.l_nb);
+    fastdiv_params(splits, &a.m_sp, &a.l_sp);
+    fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
+    a.tr = tc > 0 ? packed_tile_n(kind) / tc : 0;
     a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
     a.act = g.act;
     a.res_mode = g.res_mode;
