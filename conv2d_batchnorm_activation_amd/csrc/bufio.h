@@ -53,4 +53,13 @@ __device__ __forceinline__ void warm_kernargs()
     asm volatile("" ::"s"(v));
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight stay
+// in flight across it (a plain __syncthreads() also waits for those).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace cvx

@@ -127,7 +127,6 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     constexpr int BN = 32 * NT;
     constexpr int PITCH = BN + (NT < 4 ? 4 : 0);  // LDS row pitch of the partial-sum exchange
     constexpr int WF = K == 3 ? kBCFloats3 : kBCFloats1;  // weight floats per chunk
-    constexpr int NWL = WF / 256;      // 1 KB weight blocks per chunk: 20 (3x3), 2 (1x1)
 
     extern __shared__ __attribute__((aligned(16))) float smem[];
     __shared__ int s_last;
@@ -175,7 +174,7 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         q0 = tw * a.tc;  // first output column of the tile
     }
     const int gx0 = VEC ? (ix0 & ~3) : ix0;  // staged columns start on a 16-byte boundary
-    const int CHF = WF + a.REP;              // LDS floats per chunk: weights, then the input region
+    const int CHF = a.REP;                   // LDS floats per chunk: its staged input region
     const int BUF = CPS * CHF;               // one of three stage buffers
 
     const int c_begin = sp * a.chunks_per_split;
@@ -186,32 +185,6 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         // ---------------------------------------------------------- producers
         const int ptid = tid - 256;
         const int pw = wave - 4;
-        const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
-        const unsigned wrow = 4u * (unsigned)(mb * a.nchunks * WF) + 16u * (unsigned)lane;
-        // A stage's weights: the chunk's 1 KB blocks, dealt to the four producer
-        // waves in turn.  A chunk past the split's end reads through
-        // out-of-range offsets (and its input through an empty descriptor):
-        // zeros land in LDS, so the consumers need no branches.
-        auto issue_w = [&](int st, int sb) {
-#pragma unroll
-            for (int j = 0; j < CPS; ++j) {
-                const int chunk = c_begin + st * CPS + j;
-                int cbase = sb + j * CHF;
-                asm volatile("" : "+s"(cbase));
-                const unsigned wo = chunk < c_end ? wrow + 4u * (unsigned)(chunk * WF) : kOOB;
-#pragma unroll
-                for (int l = 0; l < (NWL + 3) / 4; ++l) {
-                    const int blk = pw + 4 * l;
-                    if (blk < NWL)
-                        lds_load16(rw, (__attribute__((address_space(3))) void*)(smem + cbase + 256 * blk),
-                                   wo + 1024u * blk);
-                }
-            }
-        };
-        // The first two stages' weights go out before anything else is worked out.
-        if (nstages > 0) issue_w(0, 0);
-        if (nstages > 1) issue_w(1, BUF);
-
         // Staged input elements e = ptid + 256*i -> (channel, row, element of the
         // row) -> byte offset from the chunk's first channel, or kOOB outside the
         // image (or past the region).
@@ -243,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
                     if (i >= a.rounds) break;
-                    auto* d = (__attribute__((address_space(3))) void*)(smem + cbase + WF + 256 * G * i +
+                    auto* d = (__attribute__((address_space(3))) void*)(smem + cbase + 256 * G * i +
                                                                          pw * 64 * G);
                     if constexpr (VEC)
                         lds_load16(rc, d, goff[i]);
@@ -258,16 +231,13 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         if (nstages > 0) issue_x(0, 0);
         if (nstages > 1) issue_x(1, BUF);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        lds_barrier();
         int sb = 2 * BUF;
         for (int st = 1; st < nstages; ++st) {
-            if (st + 1 < nstages) {
-                issue_w(st + 1, sb);
-                issue_x(st + 1, sb);
-            }
+            if (st + 1 < nstages) issue_x(st + 1, sb);
             sb = sb == 2 * BUF ? 0 : sb + BUF;
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            lds_barrier();
         }
         // then the consumers' exchange barriers (and the split's two)
         const int tail = a.partial == nullptr ? 2 : 4;
@@ -320,25 +290,39 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     // weights of the next chunk are read from LDS before the current pair's
     // instructions, also across a stage boundary: the next stage has landed by
     // the current stage's barrier.
-    constexpr int NAS = K == 3 ? kSlots3 : 1;
-    auto read_a = [&](int sb, int j, f32x4 (&av)[NAS]) {
-        int base = sb + j * CHF + wave * (WF / 4);
-        asm volatile("" : "+s"(base));
-        base &= ~3;  // a multiple of 4 floats already: 16-byte reads, not split ones
-        if constexpr (K == 3) {
+    // This wave's weights of a chunk (its h = wave block) go global -> registers
+    // in the operand's lane order: for 3x3 four 16-byte loads and an 8-byte one
+    // (the last slot's two live taps; loading its padding too would leave two
+    // registers the compiler reuses while the load is in flight), for 1x1 one
+    // 8-byte load.  A chunk past the split's end reads zeros.
+    struct AT {
+        f32x4 q[K == 3 ? 4 : 0 + 1];
+        f32x2 t;
+        __device__ float operator[](int f) const { return K == 3 ? (f < 16 ? q[f / 4][f % 4] : t[f - 16]) : t[f]; }
+    };
+    const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
+    const unsigned wrow = 4u * (unsigned)(mb * a.nchunks * WF + wave * (WF / 4)) +
+                          (K == 3 ? 16u : 8u) * (unsigned)lane;
+    auto load_a = [&](int st, AT (&av)[CPS]) {
 #pragma unroll
-            for (int s = 0; s < kSlots3; ++s)
-                av[s] = *reinterpret_cast<const f32x4*>(smem + base + 256 * s + 4 * lane);
-        } else {
-            const f32x2 v = *reinterpret_cast<const f32x2*>(smem + base + 2 * lane);
-            av[0] = f32x4{v[0], v[1], 0.0f, 0.0f};
+        for (int j = 0; j < CPS; ++j) {
+            const int chunk = c_begin + st * CPS + j;
+            const unsigned wo = chunk < c_end ? wrow + 4u * (unsigned)(chunk * WF) : kOOB;
+            if constexpr (K == 3) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    av[j].q[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wo + 1024u * s), 0, 0));
+                av[j].t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(wo + 4096u), 0, 0));
+            } else {
+                av[j].t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)wo, 0, 0));
+            }
         }
     };
     auto read_b = [&](int sb, int q, float (&bv)[KK][NT]) {
         const int j = q >> 1, pp = q & 1;
         // formed here: hoisting these addresses would hold one register per
         // (chunk, pair, buffer)
-        int base = sb + j * CHF + WF + (2 * (2 * wave + pp) + hi) * RS;
+        int base = sb + j * CHF + (2 * (2 * wave + pp) + hi) * RS;
         asm volatile("" : "+v"(base));
         const float* xa = smem + base;
 #pragma unroll
@@ -350,42 +334,31 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     };
     constexpr int NQ = CPS * 2;
     float b0[KK][NT], b1[KK][NT];
-    f32x4 a0[NAS], a1[NAS];
-    // One stage at buffer `sb`, the next stage's at `nsb` (when `more`).  Pair q
-    // uses input registers q&1 (NQ is even); chunk c of the layer uses weight
-    // registers c&1, i.e. (SP*CPS + j)&1 for stage parity SP.
-    auto stage = [&](auto spc, int sb, int nsb, bool more) {
-        constexpr int SP = decltype(spc)::value;
+    AT a0[CPS], a1[CPS];
+    // One stage at buffer `sb`, the next stage's at `nsb` (when `more`), with
+    // weight registers `ac`; once its matrix instructions are issued those
+    // registers take the weights of stage st+2.  Pair q uses input registers q&1
+    // (NQ is even).
+    auto stage = [&](int st, AT (&ac)[CPS], int sb, int nsb, bool more) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             float (&cur)[KK][NT] = (q & 1) ? b1 : b0;
             float (&nxt)[KK][NT] = (q & 1) ? b0 : b1;
             const int j = q >> 1, pp = q & 1;
-            f32x4 (&ac)[NAS] = ((SP * CPS + j) & 1) ? a1 : a0;
-            f32x4 (&an)[NAS] = ((SP * CPS + j) & 1) ? a0 : a1;
             if (q + 1 < NQ)
                 read_b(sb, q + 1, nxt);
             else if (more)
                 read_b(nsb, 0, nxt);
-            if (pp == 0) {
-                if (j + 1 < CPS)
-                    read_a(sb, j + 1, an);
-                else if (more)
-                    read_a(nsb, 0, an);
-            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int tap = 0; tap < KK; ++tap) {
-                float wv;
-                if constexpr (K == 3)
-                    wv = ac[(9 * pp + tap) / 4][(9 * pp + tap) % 4];
-                else
-                    wv = ac[0][pp];
+                const float wv = ac[j][K == 3 ? 9 * pp + tap : pp];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[tap][nt], wv, acc[nt], 0, 0, 0);
             }
         }
+        load_a(st + 2, ac);  // past the end: zeros, issued anyway (keeps wait counts exact)
     };
 
     // Epilogue geometry of this lane's quads: byte offset of a pixel within the
@@ -446,36 +419,42 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 #pragma unroll
     for (int k = 0; k < NT; ++k) rv[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const bool want_res = a.res_mode != CVX_RES_NONE;
+    // without a residual the descriptor is empty and the loads return zeros
     auto load_res = [&]() {
-        const rsrc_t rr = make_rsrc(a.res, out_bytes);
+        const rsrc_t rr = make_rsrc(a.res, want_res ? out_bytes : 0u);
 #pragma unroll
         for (int k = 0; k < NT; ++k) rv[k] = load_quad(rr, k);
     };
 
     // Barrier s: the producers have landed stage s+1, this wave has finished
-    // stage s-1 (whose buffer now takes stage s+2).  The residual loads go out
-    // with the last stage.
-    __syncthreads();
-    if (nstages > 0) {
-        read_a(0, 0, a0);
-        read_b(0, 0, b0);
-    }
+    // stage s-1 (whose buffer now takes stage s+2).  The barrier orders LDS only,
+    // so the weight loads in flight stay in flight.
+    // Every global load of the loop is issued unconditionally, in a fixed order
+    // (weights of stages 0 and 1, the residual, then stage st+2's weights at the
+    // end of stage st), so each wait for a stage's weights leaves the later loads
+    // in flight.
+    load_a(0, a0);
+    load_a(1, a1);
+    load_res();
+    lds_barrier();
+    if (nstages > 0) read_b(0, 0, b0);
     {
-        int sb = 0;
-        for (int st = 0; st < nstages; st += 2) {
-            if (st > 0) __syncthreads();
-            if (st + 1 == nstages && single && want_res) load_res();
+        // stages in pairs (weight registers a0, a1), then an odd last one
+        int sb = 0, st = 0;
+        for (; st + 1 < nstages; st += 2) {
+            if (st > 0) lds_barrier();
             const int sb1 = sb == 2 * BUF ? 0 : sb + BUF;
-            stage(std::integral_constant<int, 0>{}, sb, sb1, st + 1 < nstages);
-            if (st + 1 >= nstages) break;
-            __syncthreads();
-            if (st + 2 == nstages && single && want_res) load_res();
+            stage(st, a0, sb, sb1, true);
+            lds_barrier();
             const int sb2 = sb1 == 2 * BUF ? 0 : sb1 + BUF;
-            stage(std::integral_constant<int, 1>{}, sb1, sb2, st + 2 < nstages);
+            stage(st + 1, a1, sb1, sb2, st + 2 < nstages);
             sb = sb2;
         }
+        if (st < nstages) {
+            if (st > 0) lds_barrier();
+            stage(st, a0, sb, sb, false);
+        }
     }
-    if (nstages == 0 && single && want_res) load_res();
 
     // Partial-sum exchange (the producers have left): every wave writes its
     // BN x 32 tile as [channel][pixel], then wave w sums channels 8w..8w+7 of the
@@ -516,13 +495,12 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 #pragma unroll
             for (int k = 0; k < NT; ++k) store_quad(rps, k, v[k], true);
         }
-        // whichever workgroup finishes the tile needs these: fetched by all,
-        // while the stores drain
+        // whichever workgroup finishes the tile needs these (and the residual,
+        // already here): fetched by all, while the stores drain
         {
             const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
             sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
             bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
-            if (want_res) load_res();
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -700,8 +678,7 @@ static Region packed_region(const ConvGeom& g, int kind, int tc, bool vec)
 static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
 {
     const int nt = kPacked[kind].nt;
-    const size_t wf = g.k == 3 ? kBCFloats3 : kBCFloats1;
-    const size_t stage = 3 * (size_t)packed_chunks_per_stage(kind, g.k) * (wf + r.rep) * sizeof(float);
+    const size_t stage = 3 * (size_t)packed_chunks_per_stage(kind, g.k) * r.rep * sizeof(float);
     const size_t red = (size_t)4 * 32 * (32 * nt + (nt < 4 ? 4 : 0)) * sizeof(float);
     return stage > red ? stage : red;
 }
@@ -748,8 +725,8 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
 // two (LDS).
 int packed_occupancy(int kind, int k)
 {
-    static constexpr int kRegs[2][kNumPacked] = {{78, 120, 197},    // 1x1: NT = 1, 2, 4
-                                                 {115, 174, 256}};  // 3x3
+    static constexpr int kRegs[2][kNumPacked] = {{56, 81, 123},    // 1x1: NT = 1, 2, 4
+                                                 {87, 127, 207}};  // 3x3
     const int regs = kRegs[k == 3 ? 1 : 0][kind];
     const int occ = 512 / regs / 2;
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;
