@@ -109,6 +109,7 @@ struct PackedArgs {
     int PR, PCW;                // staged rows, LDS floats per staged row
     int EPR, RE, rounds, REP;   // elements per row, elements per chunk, load rounds, LDS floats per chunk
     unsigned m_rc, l_rc, m_c, l_c;  // divide by staged elements per channel, per row
+    int step_ci, step_r, step_c;    // 256 staged elements in mixed radix (channel, row, element)
     unsigned m_nb, l_nb, m_sp, l_sp, m_tpi, l_tpi;  // divide by n*tiles, splits, tiles per image
     int tr;                     // output rows of a 2-D tile (BN / tc)
     unsigned wp_bytes;
@@ -187,21 +188,34 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         const int pw = wave - 4;
         // Staged input elements e = ptid + 256*i -> (channel, row, element of the
         // row) -> byte offset from the chunk's first channel, or kOOB outside the
-        // image (or past the region).
+        // image (or past the region).  Found once by division, then stepped by 256
+        // elements in mixed radix with selects (full-rate operations, no branches).
         const int iy0 = oh_ref * a.stride - a.pad;
-        const int per_ch = a.PR * a.EPR;
         unsigned goff[NR];
+        {
+            int ci = pdiv(ptid, a.m_rc, a.l_rc);
+            const int rem = ptid - ci * (a.PR * a.EPR);
+            int r = pdiv(rem, a.m_c, a.l_c);
+            int c = rem - r * a.EPR;
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            goff[i] = kOOB;
-            if (i < a.rounds) {
-                const int e = ptid + 256 * i;
-                const int ci = pdiv(e, a.m_rc, a.l_rc);
-                const int rem = e - ci * per_ch;
-                const int r = pdiv(rem, a.m_c, a.l_c);
-                const int iy = iy0 + r, gx = gx0 + G * (rem - r * a.EPR);
-                const bool ok = e < a.RE && (unsigned)iy < (unsigned)a.H && gx >= 0 && gx + G <= a.W;
-                goff[i] = ok ? 4u * (unsigned)(ci * HW + iy * a.W + gx) : kOOB;
+            for (int i = 0; i < NR; ++i) {
+                goff[i] = kOOB;
+                if (i < a.rounds) {
+                    const int iy = iy0 + r, gx = gx0 + G * c;
+                    const bool ok = (ptid + 256 * i < a.RE) & ((unsigned)iy < (unsigned)a.H) & (gx >= 0) &
+                                    (gx + G <= a.W);
+                    // 24-bit products: the host keeps H*W below 2^24
+                    const unsigned lin = __umul24((unsigned)ci, (unsigned)HW) +
+                                         __umul24((unsigned)iy, (unsigned)a.W) + (unsigned)gx;
+                    goff[i] = ok ? 4u * lin : kOOB;
+                    c += a.step_c;
+                    const bool cc = c >= a.EPR;
+                    c -= cc ? a.EPR : 0;
+                    r += a.step_r + (cc ? 1 : 0);
+                    const bool rc = r >= a.PR;
+                    r -= rc ? a.PR : 0;
+                    ci += a.step_ci + (rc ? 1 : 0);
+                }
             }
         }
         const float* xim = a.x + (long)b * a.cin * HW;
@@ -690,6 +704,7 @@ bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
     const int bn = packed_tile_n(kind);
     if (tc < 0 || (tc > 0 && (tc > bn || bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
     const long lim = 0x7fffffffL;
+    if ((long)g.h * g.w >= (1L << 24)) return false;  // staging offsets use 24-bit products
     if ((long)g.cin * g.h * g.w * 4 >= lim || packed_weight_floats(g) * 4 >= lim ||
         (long)g.n * g.cout * g.oh * g.ow * 4 >= lim)
         return false;
@@ -839,6 +854,12 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     a.REP = r.rep;
     fastdiv_params(r.pr * r.epr, &a.m_rc, &a.l_rc);
     fastdiv_params(r.epr, &a.m_c, &a.l_c);
+    {
+        const int rc = r.pr * r.epr;
+        a.step_ci = 256 / rc;
+        a.step_r = (256 % rc) / r.epr;
+        a.step_c = (256 % rc) % r.epr;
+    }
     fastdiv_params(g.n * a.tiles_per_img, &a.m_nb, &a.l_nb);
     fastdiv_params(splits, &a.m_sp, &a.l_sp);
     fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
