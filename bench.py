@@ -143,9 +143,9 @@ def dominant(rows):
     largest total time over the forward's layers, and its roofline position:
     algorithmic FLOPs (or bytes) per launch over its average launch time.
 
-    A split-K layer enqueues a second, finishing kernel, so its event time is not
-    one launch of the main kernel: the average is taken over the kernel's
-    single-launch layers (all of its layers when it has none of those)."""
+    A split-K layer's launch also carries the partial sums' round trip through
+    memory, so the average is taken over the kernel's layers without a split
+    (all of its layers when it has none of those)."""
     by = {}
     for r in rows:
         k = by.setdefault(r["kernel"], [])

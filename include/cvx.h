@@ -96,9 +96,9 @@ CVX_API cvx_status cvx_conv_out_shape(const cvx_conv_desc *d, int *oh, int *ow);
  * selects for `d` ("YOLO26N Inference Optimisation", "Improvements", #1 and #3:
  * one code path whose tile parameters are chosen per layer shape).  Writes a
  * short NUL-terminated description into buf (at most buf_len bytes, truncated
- * to fit): family, tile, split-K factor ("splitk=S"; S > 1 adds a second,
- * finishing launch) and, after "kernel=", the main kernel's symbol as profilers
- * print it.  256 bytes always suffice. */
+ * to fit): family, tile, split-K factor ("splitk=S"; with OIHW weights S > 1
+ * adds a second, finishing launch) and, after "kernel=", the main kernel's
+ * symbol as profilers print it.  256 bytes always suffice. */
 CVX_API cvx_status cvx_conv_plan(const cvx_conv_desc *d, char *buf, int buf_len);
 
 /* Workspace bytes cvx_conv_bn_act needs for `d` (0 when the selected kernel
@@ -112,8 +112,9 @@ CVX_API size_t cvx_packed_weights_bytes(const cvx_conv_desc *d);
 /*
  * cvx_pack_weights -- one-time weight transform for layers run with
  * w_layout = CVX_W_PACKED.  For the dense 1x1/3x3 kernels the OIHW weights are
- * reordered into the matrix cores' operand order (zero-padded to whole 32-row,
- * 16-channel and 4-tap groups); for the other kernels the packed form is a copy
+ * reordered into the matrix cores' operand order (zero-padded to whole 32-row
+ * and 16-channel groups, a 3x3 chunk's 18 taps per lane in five 16-byte slots);
+ * for the other kernels the packed form is a copy
  * of the OIHW weights.  The packed form does not depend on anything but the
  * descriptor's shape fields.
  *   w_oihw : device [c_out][c_in/groups][kh][kw], read only.
