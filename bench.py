@@ -87,6 +87,25 @@ def time_graph(g, inner: int, replays: int, warm: int = 2) -> float:
     return s.elapsed_time(e) / (replays * inner)
 
 
+def residual_source(s_in, s_out, res_mode) -> str:
+    """Which tensor a layer timed alone gets as its residual: its own input when
+    that has the output's shape (the detector's stride-1 equal-width layers),
+    else a tensor of the output's shape ("own"), or none.  The kernels read the
+    residual with the output's shape, so a smaller buffer would be read past its
+    end."""
+    if not res_mode:
+        return "none"
+    return "input" if tuple(s_in) == tuple(s_out) else "own"
+
+
+def layer_residual(xin, s_out, res_mode):
+    import torch
+    src = residual_source(xin.shape, s_out, res_mode)
+    if src == "none":
+        return None
+    return xin if src == "input" else torch.rand(s_out, device=xin.device)
+
+
 def per_layer(wk, net, counts, reps: int):
     """Each layer alone, on inputs of its own shape, timed with events."""
     import torch
@@ -107,7 +126,7 @@ def per_layer(wk, net, counts, reps: int):
             d = lay.conv
             xin = torch.rand(s_in, device="cuda")
             y = torch.empty(s_out, device="cuda")
-            res = xin if L.res_mode else None
+            res = layer_residual(xin, s_out, L.res_mode)
             nws = cvx.cvx_conv_workspace_bytes(d)
             ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
             fn = (lambda d=d, xin=xin, lay=lay, res=res, y=y, ws=ws, nws=nws:
@@ -256,7 +275,7 @@ def pmc_probe(args) -> int:
             d = lay.conv
             xin = torch.rand(s_in, device="cuda")
             y = torch.empty(s_out, device="cuda")
-            res = xin if L.res_mode else None
+            res = layer_residual(xin, s_out, L.res_mode)
             nws = cvx.cvx_conv_workspace_bytes(d)
             ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
             plan = cvx.cvx_conv_plan(d)
@@ -394,6 +413,59 @@ def rocprof_summary(args) -> int:
     return 0
 
 
+def forward_time_ms(net, x, steps: int) -> float:
+    """Milliseconds per forward: the forward captured once as a graph, replayed
+    `steps` times between two events."""
+    import torch
+    g = capture(lambda: net(x), 1)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def other_workloads(layer_reps: int, steps: int):
+    """The other configurations, reported beside the headline (not part of
+    `value`): the MNIST depthwise-separable net at batch 256 (with per-layer
+    rows: its depthwise and pointwise layers are large enough to show bandwidth
+    rather than launch latency) and at batch 1, the single depthwise layer, and
+    the detector pipeline at batch 8.  Per-layer inputs are reused across the
+    timed launches, so they are cache-resident (hot) figures."""
+    import torch
+    import workloads as wl
+    from conv2d_batchnorm_activation_amd import accounting
+    from conv2d_batchnorm_activation_amd.net import Net
+    out = {}
+    for name, wk, layers in [("mnist_b256", wl.mnist_cnn(256), True),
+                             ("mnist_b1", wl.mnist_cnn(1), False),
+                             ("depthwise_48x28x28", wl.depthwise_single(), True),
+                             ("detector_b8", wl.detector_pipeline(8), False)]:
+        log(f"{name}: timing the forward")
+        counts = accounting.layer_counts(wk.layers, wk.x.shape)
+        flop = sum(c["flop"] for c in counts)
+        byts = sum(c["bytes"] for c in counts)
+        net = Net(wk.layers, wk.x.shape)
+        x = torch.from_numpy(wk.x).cuda()
+        ms = forward_time_ms(net, x, steps)
+        log(f"{name}: {ms * 1e3:.1f} us/forward ({flop / 1e9:.3f} GFLOP, {byts / 1e6:.1f} MB)")
+        entry = {"workload": wk.name, "batch": int(wk.x.shape[0]), "us_per_forward": round(ms * 1e3, 2),
+                 "gflops": round(flop / (ms * 1e-3) / 1e9, 1),
+                 "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
+        if layers:
+            entry["layers"] = per_layer(wk, net, counts, layer_reps)
+        out[name] = entry
+        del net
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wk, flop_per_forward: float, budget_s: float):
     import oracle
     reps = 0
@@ -421,6 +493,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layers", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for rocprofv3 counter passes (prints a manifest line)")
     ap.add_argument("--reps", type=int, default=3, help="calls per layer in --pmc-probe")
@@ -514,6 +587,8 @@ def main() -> int:
         "layers": rows,
         "cpu_baseline": None,
     }
+    if not args.no_others and not args.no_layers:
+        result["other_workloads"] = other_workloads(args.layer_reps, args.steps)
     if not args.no_cpu_baseline and args.batch == 1:
         result["cpu_baseline"] = cpu_baseline(wk, flop, args.cpu_budget)
     print(json.dumps(result))
