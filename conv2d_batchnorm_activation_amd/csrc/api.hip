@@ -75,6 +75,25 @@ bool plan_depthwise(const ConvGeom& g, Plan* p)
     const int pw = g.w + 2 * g.pad;
     const int ohw = g.oh * g.ow;
     const int planes = g.n * g.cout;
+    // Small planes: the plane kernel, `ppb` whole planes per workgroup -- small
+    // enough that about eight workgroups share a compute unit when there are
+    // planes enough (the per-plane arithmetic needs waves to hide its LDS
+    // latency behind), at most about 8K floats of staging -- for tensors within
+    // a buffer's 2^31-byte range.
+    if ((long)g.h * g.w <= 4096 && (long)planes * g.h * g.w * 4 < 0x7fffffffL &&
+        (long)planes * ohw * 4 < 0x7fffffffL) {
+        const int cap = std::max(4, std::min(64, (int)(8192 / ((long)g.h * g.w))) & ~3);
+        const int want = ((planes + 2047) / 2048 + 3) & ~3;  // ~8 workgroups per compute unit
+        int ppb = std::max(4, std::min(cap, want));
+        // large planes with few of them: a plane per workgroup (all waves on it)
+        if (g.oh * g.ow >= 192 && (long)planes < 4L * 256) ppb = 1;
+        if (dw_planes_lds_bytes(g, ppb) > kMaxLdsBytes) return false;
+        p->dw_ppb = ppb;
+        p->dw_toh = 0;
+        p->fam = FAM_DEPTHWISE;
+        p->ws_bytes = 0;
+        return true;
+    }
     const size_t budget = 32 * 1024 / sizeof(float);  // floats of halo tile per workgroup
     if (ohw <= 1024 && (size_t)((g.oh - 1) * g.stride + 3) * pw <= budget) {
         // whole planes; several per workgroup when they are small
@@ -388,8 +407,12 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
                  g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
         break;
     case FAM_DEPTHWISE:
-        snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d splitk=1 kernel=cvx::k_depthwise3x3<%d>",
-                 g.stride, p.dw_ppb, p.dw_toh, g.stride);
+        if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
+            snprintf(buf, buf_len, "depthwise3x3 s%d planes ppb=%d splitk=1 kernel=cvx::k_dw_planes<%d, 1, 1, %d>",
+                     g.stride, p.dw_ppb, g.stride, g.oh * g.ow <= 256 ? 4 : 0);
+        else
+            snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d splitk=1 kernel=cvx::k_depthwise3x3<%d>",
+                     g.stride, p.dw_ppb, p.dw_toh, g.stride);
         break;
     case FAM_DIRECT:
         if (p.direct_stem)

@@ -186,7 +186,9 @@ CASES = [
     (31, 1, 64, 13, 13, 64, 3, 1, 1, 64, A, AF),
     (32, 3, 7, 9, 31, 7, 3, 1, 1, 7, A, B4),
     (33, 1, 4, 64, 300, 4, 3, 1, 1, 4, R, 0),      # band path (large plane)
-    (34, 1, 3, 97, 41, 3, 3, 2, 1, 3, A, AF),      # band path, stride 2, odd sizes
+    (34, 1, 3, 97, 41, 3, 3, 2, 1, 3, A, AF),      # plane path, 4 planes of 3977 floats
+    (37, 1, 3, 97, 83, 3, 3, 2, 1, 3, A, AF),      # band path, stride 2, odd sizes
+    (38, 3, 5, 7, 7, 5, 3, 1, 1, 5, R, B4),        # plane path, odd plane size (49)
     (35, 2, 5, 1, 1, 5, 3, 1, 1, 5, R, 0),
     (36, 1, 6, 8, 8, 6, 3, 2, 0, 6, A, 0),         # no padding
     # direct (tiny c_in, grouped, large kernels)
@@ -389,6 +391,33 @@ def test_split_reduction_workspace_contents_ignored(fill, monkeypatch):
                 first = y
             else:
                 assert np.array_equal(first, y), "split reduction is not deterministic"
+
+
+@pytest.mark.parametrize("hw", [(7, 7), (14, 14)], ids=["7x7", "14x14"])
+def test_depthwise_misaligned_input(hw):
+    """The depthwise plane kernel on an input 4 bytes off a 16-byte boundary
+    stages with 4-byte loads and gives the same result."""
+    h, w = hw
+    seed, n, c = 230 + h, 3, 12
+    x, L = wl.random_conv_case(seed, n, c, h, w, c, 3, 1, 1, c, wl.ACT_RELU, wl.RES_BEFORE_ACT)
+    d = cvx.make_desc(n, c, h, w, c, 3, 1, 1, c, wl.ACT_RELU, wl.RES_BEFORE_ACT, OIHW)
+    plan = cvx.cvx_conv_plan(d)
+    assert "k_dw_planes" in plan, plan
+    r = wl.residual_for(seed, (n, c, h, w))
+    ref = oracle_conv(x, L, r)
+    p = L.params
+    xbuf = torch.zeros(x.size + 4, device=DEV)
+    xbuf[1:1 + x.size] = dev(x).reshape(-1)
+    g_, b_, m_, v_ = (dev(p[k]) for k in ("gamma", "beta", "mean", "var"))
+    scale = torch.empty(c, device=DEV)
+    bias = torch.empty(c, device=DEV)
+    cvx.cvx_fold_bn(g_, b_, m_, v_, wl.EPS, scale, bias)
+    out = Guarded((n, c, h, w))
+    say(f"depthwise misaligned {h}x{w}: {plan}")
+    cvx.cvx_conv_bn_act(d, xbuf[1:].data_ptr(), dev(p["w"]), scale, bias, dev(r), out.t, None, 0)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    check(out.t.cpu().numpy(), ref, f"dw misaligned {h}x{w}")
 
 
 @pytest.mark.parametrize("force", ["0,8,1", "1,16,1", "0,8,2", "2,0,3"])
