@@ -145,7 +145,8 @@ bool slices_ok(int nchunks, int sk)
 // A split into s slices adds ~4000 + 800*NT*s clocks (the partial sums' round
 // trip through memory and the arrival count).  Up to packed_occupancy(kind)
 // workgroups share a compute unit, each slowing the others by ~30%.
-bool plan_packed(const ConvGeom& g, Plan* p)
+// `max_split` bounds the split (1 when no workspace is at hand).
+bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8)
 {
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
@@ -168,7 +169,7 @@ bool plan_packed(const ConvGeom& g, Plan* p)
             const double loads = cps * kLoadClk * packed_loads_per_chunk(g, kind, tc);
             const double stage = std::max(cps * 2.0 * kk * nt * 64.0, loads) + kBarrierClk;
             const long tiles = (long)g.n * packed_tiles_per_image(g, kind, tc) * mblocks;
-            for (int sk = 1; sk <= 8; ++sk) {
+            for (int sk = 1; sk <= max_split; ++sk) {
                 if (!slices_ok(nchunks, sk)) continue;
                 if ((long)sk * g.n * g.cout * g.oh * g.ow * 4 >= 0x7fffffffL) continue;
                 const int per = (nchunks + sk - 1) / sk;
@@ -189,7 +190,7 @@ bool plan_packed(const ConvGeom& g, Plan* p)
     }
     int kind, tc, sk;
     if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < packed_num_kinds() &&
-        slices_ok(nchunks, sk) && packed_tile_fits(g, kind, tc, nullptr))
+        sk <= max_split && slices_ok(nchunks, sk) && packed_tile_fits(g, kind, tc, nullptr))
         bt = GemmTile{kind, 32, packed_tile_n(kind), tc, sk};
     if (bt.kind < 0) return false;
     p->fam = FAM_IGEMM_PACKED;
@@ -268,6 +269,14 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
 {
     *p = Plan{};
     if (plan_depthwise(g, p)) return CVX_OK;
+    // 1x1 layers over batches of small planes: whole images per workgroup (a
+    // forced packed tile keeps the packed kernel, for sweeps and tests)
+    int fk, ft, fs;
+    if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs) && pointwise_fits(g)) {
+        p->fam = FAM_POINTWISE;
+        p->ws_bytes = 0;
+        return CVX_OK;
+    }
     if (g.w_layout == CVX_W_PACKED ? plan_packed(g, p) : plan_igemm(g, p)) return CVX_OK;
     plan_direct(g, p);
     const int cout_g = g.cout / g.groups;
@@ -328,6 +337,17 @@ cvx_status launch_conv(const ConvGeom& g, const Plan& p, const float* x, const f
     case FAM_DIRECT: e = launch_direct(g, p, x, w, scale, bias, res, y, s); break;
     case FAM_IGEMM: e = launch_igemm(g, p, x, w, scale, bias, res, y, ws, s); break;
     case FAM_IGEMM_PACKED: e = launch_igemm_packed(g, p, x, w, scale, bias, res, y, ws, s); break;
+    case FAM_POINTWISE:
+        if (pointwise_aligned(x, res, y)) {
+            e = launch_pointwise(g, x, w, scale, bias, res, y, s);
+        } else {
+            // 16-byte staging and stores need aligned tensors; otherwise the
+            // packed kernel (same weights), unsplit: the plan has no workspace
+            Plan q = Plan{};
+            if (!plan_packed(g, &q, 1)) return CVX_ERR_UNSUPPORTED;
+            e = launch_igemm_packed(g, q, x, w, scale, bias, res, y, nullptr, s);
+        }
+        break;
     }
     return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
 }
@@ -343,7 +363,7 @@ size_t elems_packed(const ConvGeom& g)
     ConvGeom gp = g;
     gp.w_layout = CVX_W_PACKED;
     Plan p;
-    if (make_plan(gp, &p) == CVX_OK && p.fam == FAM_IGEMM_PACKED)
+    if (make_plan(gp, &p) == CVX_OK && (p.fam == FAM_IGEMM_PACKED || p.fam == FAM_POINTWISE))
         return (size_t)packed_weight_floats(gp);
     return elems_oihw(g);
 }
@@ -406,6 +426,7 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
         snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
                  g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
         break;
+    case FAM_POINTWISE: pointwise_describe(g, buf, buf_len); break;
     case FAM_DEPTHWISE:
         if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
             snprintf(buf, buf_len, "depthwise3x3 s%d planes ppb=%d splitk=1 kernel=cvx::k_dw_planes<%d, 1, 1, %d>",
@@ -468,7 +489,8 @@ cvx_status cvx_pack_weights(const cvx_conv_desc* d, const float* w_oihw, float* 
     gp.w_layout = CVX_W_PACKED;
     Plan pp;
     make_plan(gp, &pp);
-    hipError_t e = pp.fam == FAM_IGEMM_PACKED ? launch_pack_weights(g, w_oihw, w_packed, s)
+    const bool packed = pp.fam == FAM_IGEMM_PACKED || pp.fam == FAM_POINTWISE;
+    hipError_t e = packed ? launch_pack_weights(g, w_oihw, w_packed, s)
                                               : launch_copy(w_oihw, w_packed, (long)no, s);
     return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
 }

@@ -16,6 +16,7 @@ enum Family : int {
     FAM_DIRECT = 1,     // direct VALU kernel (tiny c_in stems, grouped, large k)
     FAM_IGEMM = 2,      // implicit GEMM on fp32 MFMA (dense 1x1 and 3x3), OIHW weights
     FAM_IGEMM_PACKED = 3,  // the same, weights pre-packed in MFMA operand order
+    FAM_POINTWISE = 4,  // 1x1 over batches of small planes, whole images per workgroup (packed weights)
 };
 
 // Geometry of one convolution, derived from a validated cvx_conv_desc.
@@ -83,6 +84,15 @@ void packed_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
 hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
                                const float* scale, const float* bias, const float* res, float* y,
                                void* ws, hipStream_t s);
+
+// Pointwise family (k_pointwise.hip): 1x1, no padding, packed weights, c_in a
+// multiple of 16 and c_out of 32, planes small enough for a whole image per
+// workgroup; x, y and the residual 16-byte aligned at launch.
+bool pointwise_fits(const ConvGeom& g);
+bool pointwise_aligned(const float* x, const float* res, const float* y);
+void pointwise_describe(const ConvGeom& g, char* buf, int len);
+hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                            const float* bias, const float* res, float* y, hipStream_t s);
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s);
 

@@ -1,0 +1,484 @@
+// k_pointwise.hip -- 1x1 convolution (stride 1 or 2, no padding) + folded
+// BatchNorm + residual + activation on fp32 matrix cores, for batches of small
+// planes.
+//
+// A 1x1 layer is one matrix product per image, Y[c_out][OH*OW] =
+// W[c_out][c_in] X[c_in][OH*OW] (the pointwise and shortcut layers of the
+// depthwise-separable MNIST net, "Как я свертки ускорял"; the 1x1 layers of
+// "YOLO26N Inference Optimisation").  When a plane holds at most a few hundred
+// pixels, one workgroup takes one whole image and a group of CO output
+// channels (all of them, or an equal share), so that
+//   * a chunk of 16 input channels of the image is one contiguous run (stride
+//     1) or 16 x OH input rows (stride s: rows s*oh), copied to LDS with
+//     16-byte LDS-direct loads whatever the plane's width;
+//   * the input is read once, however many output channels there are;
+//   * the image's CO output planes are one contiguous run of CO*OH*OW floats:
+//     the tile is written to LDS in exactly that order, then every residual
+//     load and output store moves 16 contiguous bytes per lane.
+// Roles as in the packed implicit GEMM: four producer waves stage chunk st+2
+// while four consumer waves compute chunk st (three LDS buffers, one barrier
+// per chunk).  The tile's 32x32 blocks (pixel block x channel block) are split
+// over the consumer waves in a wpx x (4 / wpx) grid; each block is a chain of
+// v_mfma_f32_32x32x2_f32 with the input as the A operand (lane l: pixel l%32,
+// channel 2k + l/32) and the weights, in the packed 1x1 order, as B (lane l:
+// output channel l%32, same channel), so a lane's sums cover runs of four
+// consecutive pixels of one output channel.
+#include <stdio.h>
+
+#include "bufio.h"
+#include "cvx_internal.h"
+#include "epilogue.h"
+
+namespace cvx {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPwThreads = 512;    // four producer and four consumer waves
+constexpr int kPwMaxRounds = 8;    // input staging rounds (256 16-byte elements) per chunk
+constexpr int kPwWRounds = 3;      // weight staging rounds per chunk: up to six channel blocks
+constexpr int kPwMaxCB = 6;
+constexpr int kPwBatch = 8;        // residual quads a thread has in flight before it stores
+constexpr int kPwChunkW = 512;     // packed 1x1 weight floats per (32-channel block, chunk)
+
+__device__ __forceinline__ int pw_div(int n, unsigned m, unsigned l)
+{
+    return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> l);
+}
+
+// 16-byte LDS-direct load (lane i writes d + 16 i); outside the kernel template
+// so the host pass, which cannot check this gfx950 form, still emits the stubs.
+__device__ __forceinline__ void pw_lds_load16(rsrc_t r, __attribute__((address_space(3))) void* d, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
+}
+
+struct PwArgs {
+    const float* x;
+    const float* wp;
+    const float* scale;
+    const float* bias;
+    const float* res;
+    float* y;
+    int cin, cout, HW, OHW;
+    int groups_co;              // channel groups per image: c_out / CO
+    int CO, CB, PB;             // channels of a tile, its 32-channel blocks, its 32-pixel blocks
+    int nchunks;                // c_in / 16
+    unsigned m_g, l_g;          // divide by groups_co
+    // Staging of one chunk: element e (16 bytes) -> row r = e / RQ and quad e % RQ;
+    // row r -> channel r / RPC, first float (r % RPC) * RSTR of that channel.
+    int rounds, RE, RQ, RPC, RSTR;
+    unsigned m_rq, l_rq, m_rpc, l_rpc;
+    int wrounds;
+    // A staged chunk in LDS: pixel q -> (oh, ow) = divmod(q, OWD) at float
+    // oh*WS + S*ow + channel*CS.
+    int OWD, WS, S, CS;
+    unsigned m_owd, l_owd;
+    int wpx, pb_per, cb_per;    // consumer grid: waves along pixels, blocks per wave
+    int BUF, WOFF;              // floats per stage buffer, weights' offset within it
+    unsigned wp_bytes;
+    int act, res_mode;
+};
+
+template <int MP, int MC>
+__global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    warm_kernargs<sizeof(PwArgs)>();
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: addresses stay scalar
+    const int hi = lane >> 5;
+    const int l32 = lane & 31;
+
+    // Workgroup -> (image, channel group), numbered XCD by XCD so the groups of
+    // one image share an L2.
+    int img, grp;
+    {
+        const unsigned h = blockIdx.x, G8 = gridDim.x;
+        const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
+        const int L = (int)(xcd * base + min(xcd, rem) + i8);
+        img = pw_div(L, a.m_g, a.l_g);
+        grp = L - img * a.groups_co;
+    }
+    const int nst = a.nchunks;
+    const int BUF = a.BUF;
+    const float* xim = a.x + (long)img * a.cin * a.HW;
+
+    if (wave >= 4) {
+        // ---------------------------------------------------------- producers
+        const int ptid = tid - 256;
+        const int pw = wave - 4;
+        // byte offsets of this lane's staged elements within a chunk, the same
+        // for every chunk; past the chunk's elements an out-of-range offset
+        unsigned goff[kPwMaxRounds];
+#pragma unroll
+        for (int i = 0; i < kPwMaxRounds; ++i) {
+            goff[i] = kOOB;
+            if (i < a.rounds) {
+                const int e = ptid + 256 * i;
+                const int r = pw_div(e, a.m_rq, a.l_rq);
+                const int c = pw_div(r, a.m_rpc, a.l_rpc);
+                const int f = c * a.HW + (r - c * a.RPC) * a.RSTR + 4 * (e - r * a.RQ);
+                goff[i] = e < a.RE ? 4u * (unsigned)f : kOOB;
+            }
+        }
+        // the group's weights of a chunk: CB blocks of 2 KB, kPwChunkW floats apart
+        // per chunk and nchunks * kPwChunkW apart per block
+        unsigned woff[kPwWRounds];
+#pragma unroll
+        for (int j = 0; j < kPwWRounds; ++j) {
+            const int e = ptid + 256 * j;
+            const int blk = e >> 7;
+            woff[j] = blk < a.CB ? 4u * ((unsigned)((grp * a.CB + blk) * a.nchunks) * kPwChunkW +
+                                         4u * (unsigned)(e & 127))
+                                 : kOOB;
+        }
+        auto issue = [&](int st, int sb) {
+            const rsrc_t rx = make_rsrc(xim + (long)st * 16 * a.HW, 64u * (unsigned)a.HW);
+            const rsrc_t rw = make_rsrc(a.wp + (long)st * kPwChunkW, a.wp_bytes - 4u * kPwChunkW * (unsigned)st);
+#pragma unroll
+            for (int i = 0; i < kPwMaxRounds; ++i) {
+                if (i >= a.rounds) break;
+                pw_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + sb + 1024 * i + 256 * pw), goff[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < kPwWRounds; ++j) {
+                if (j >= a.wrounds) break;
+                pw_lds_load16(rw, (__attribute__((address_space(3))) void*)(smem + sb + a.WOFF + 1024 * j + 256 * pw),
+                              woff[j]);
+            }
+        };
+        // Barrier s (s = 0 .. nst-1) follows the landing of chunk s+1; chunk s+2
+        // then goes into the buffer of chunk s-1, which the consumers have left
+        // by barrier s.
+        issue(0, 0);
+        if (nst > 1) issue(1, BUF);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        int sb = 2 * BUF;
+        for (int st = 1; st < nst; ++st) {
+            if (st + 1 < nst) issue(st + 1, sb);
+            sb = sb == 2 * BUF ? 0 : sb + BUF;
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        __syncthreads();  // the consumers' exchange
+    } else {
+        // -------------------------------------------------------------- consumers
+        const int wx = wave % a.wpx;
+        const int wc = wave / a.wpx;
+        const int pb0 = wx * a.pb_per;
+        const int cb0 = wc * a.cb_per;
+        // A wave owns pixel blocks pb0 .. pb0+MP-1 and channel blocks cb0 ..
+        // cb0+MC-1 of the tile.  Blocks past the tile (the template covers the
+        // largest share) compute on clamped, in-range operands and are dropped.
+        int abase[MP];
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) {
+            const int q = min(32 * (pb0 + mp) + l32, a.OHW - 1);
+            const int oh = pw_div(q, a.m_owd, a.l_owd);
+            abase[mp] = hi * a.CS + oh * a.WS + a.S * (q - oh * a.OWD);
+        }
+        int boff[MC];
+        float sc[MC], bi[MC];
+        {
+            const rsrc_t rs = make_rsrc(a.scale, 4u * (unsigned)a.cout);
+            const rsrc_t rb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                const int cb = min(cb0 + mc, a.CB - 1);
+                boff[mc] = a.WOFF + cb * kPwChunkW + 2 * lane;
+                const unsigned co = (unsigned)(grp * a.CO + 32 * cb + l32);
+                sc[mc] = bload(rs, 4u * co);
+                bi[mc] = bload(rb, 4u * co);
+            }
+        }
+        f32x16 acc[MP][MC];
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mp][mc][r] = 0.0f;
+
+        const int cs2 = 2 * a.CS;
+        int sb = 0;
+        for (int st = 0; st < nst; ++st) {
+            lds_barrier();
+            // weights of the chunk: pairs 2h, 2h+1 of each channel block
+            f32x2 bw[MC][4];
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    bw[mc][h] = *reinterpret_cast<const f32x2*>(smem + sb + boff[mc] + 128 * h);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float av[MP];
+#pragma unroll
+                for (int mp = 0; mp < MP; ++mp) av[mp] = smem[sb + abase[mp] + k * cs2];
+#pragma unroll
+                for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+                    for (int mc = 0; mc < MC; ++mc)
+                        acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mp], bw[mc][k >> 1][k & 1],
+                                                                          acc[mp][mc], 0, 0, 0);
+            }
+            sb = sb == 2 * BUF ? 0 : sb + BUF;
+        }
+
+        // Exchange: scale and bias applied, each sum goes to its place in the
+        // image's [channel][pixel] output run (the staging buffers are free once
+        // every wave is past this barrier).
+        __syncthreads();
+        const bool quads = (a.OHW & 3) == 0;
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) {
+            const int pb = pb0 + mp;
+            if (pb >= a.PB) break;
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                const int cb = cb0 + mc;
+                if (cb >= a.CB) break;
+                float* row = smem + (32 * cb + l32) * a.OHW;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int q = 32 * pb + 8 * g + 4 * hi;
+                    f32x4 z;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[r] = fmaf(sc[mc], acc[mp][mc][4 * g + r], bi[mc]);
+                    if (quads) {
+                        if (q < a.OHW) *reinterpret_cast<f32x4*>(row + q) = z;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (q + r < a.OHW) row[q + r] = z[r];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // Copy-out by all waves: the tile's run of CO*OHW floats, 16 bytes a lane.
+    const long obase = ((long)img * a.cout + (long)grp * a.CO) * a.OHW;
+    const int tq = a.CO * a.OHW / 4;
+    const unsigned run_b = 16u * (unsigned)tq;
+    const bool want_res = a.res_mode != CVX_RES_NONE;
+    const rsrc_t ry = make_rsrc(a.y + obase, run_b);
+    const rsrc_t rr = want_res ? make_rsrc(a.res + obase, run_b) : make_rsrc(a.y, 0u);
+    for (int b0 = 0; b0 < tq; b0 += kPwBatch * kPwThreads) {
+        f32x4 rv[kPwBatch];
+#pragma unroll
+        for (int j = 0; j < kPwBatch; ++j) {
+            const int e = b0 + tid + kPwThreads * j;
+            rv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (want_res)
+                rv[j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(e < tq ? 16u * (unsigned)e : kOOB), 0, 0));
+        }
+#pragma unroll
+        for (int j = 0; j < kPwBatch; ++j) {
+            const int e = b0 + tid + kPwThreads * j;
+            if (e >= tq) break;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(smem + 4 * e);
+            f32x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float t = v[r];
+                if (a.res_mode == CVX_RES_BEFORE_ACT) t += rv[j][r];
+                t = apply_act_fast(t, a.act);
+                if (a.res_mode == CVX_RES_AFTER_ACT) t += rv[j][r];
+                o[r] = t;
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ry, (int)(16u * (unsigned)e), 0, 0);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+// Compiled shares of a consumer wave: MP pixel blocks x MC channel blocks.
+struct PwKind {
+    int mp, mc;
+};
+static constexpr PwKind kPwKinds[] = {{2, 3}, {1, 3}, {2, 2}, {1, 2}};
+constexpr int kNumPwKinds = sizeof(kPwKinds) / sizeof(kPwKinds[0]);
+
+void fastdiv_params(int d, unsigned* m, unsigned* l);
+
+// Staging geometry of one chunk: rows of RQ 16-byte elements.
+struct PwStage {
+    int rq, rpc, rstr, re, rounds;
+    int cs, ws, owd;
+};
+
+static bool pw_stage(const ConvGeom& g, PwStage* s)
+{
+    const int hw = g.h * g.w, ohw = g.oh * g.ow;
+    if (g.stride == 1) {
+        // the chunk is one run of 16*HW floats, 16-byte aligned when c_in*HW and
+        // 16*HW are multiples of 4 (c_in is a multiple of 16)
+        s->rq = 4 * hw;
+        s->rpc = 1;
+        s->rstr = 0;
+        s->re = 4 * hw;
+        s->cs = hw;
+        s->ws = 0;
+        s->owd = ohw;  // one staged row per channel: (oh, ow) = (0, q)
+    } else {
+        // rows s*oh of every channel, each widened to whole 16-byte elements
+        // (the widening reads at most 12 bytes of the next row, never used)
+        if (hw % 4 != 0 || (g.stride * g.w) % 4 != 0) return false;
+        const int wq = (g.w + 3) / 4;
+        s->rq = wq;
+        s->rpc = g.oh;
+        s->rstr = g.stride * g.w;
+        s->re = 16 * g.oh * wq;
+        s->cs = g.oh * 4 * wq;
+        s->ws = 4 * wq;
+        s->owd = g.ow;
+    }
+    s->rounds = (s->re + 255) / 256;
+    return s->rounds <= kPwMaxRounds;
+}
+
+// Channel groups per image, consumer grid and compiled share for a layer;
+// false when the pointwise kernel does not take it.
+struct PwConfig {
+    int groups, kind, wpx, pb_per, cb_per;
+    size_t lds;
+};
+
+static bool pw_config(const ConvGeom& g, PwConfig* c)
+{
+    if (g.groups != 1 || g.k != 1 || g.pad != 0 || g.cin % 16 != 0 || g.cout % 32 != 0) return false;
+    const long lim = 0x7fffffffL;
+    if ((long)g.n * g.cin * g.h * g.w * 4 >= lim || (long)g.n * g.cout * g.oh * g.ow * 4 >= lim ||
+        packed_weight_floats(g) * 4 >= lim)
+        return false;
+    PwStage s;
+    if (!pw_stage(g, &s)) return false;
+    const int ohw = g.oh * g.ow;
+    const int pb = (ohw + 31) / 32;
+    const int cbt = g.cout / 32;
+    double best = 1e300;
+    bool found = false;
+    for (int groups = 1; groups <= cbt; ++groups) {
+        if (cbt % groups != 0) continue;
+        const int cb = cbt / groups;
+        if (cb > kPwMaxCB) continue;
+        const int wrounds = (cb * 128 + 255) / 256;
+        const size_t buf = (size_t)s.rounds * 1024 + (size_t)wrounds * 1024;
+        const size_t xch = (size_t)32 * cb * ohw;
+        const size_t lds = 4 * (3 * buf > xch ? 3 * buf : xch);
+        if (lds > kMaxLdsBytes) continue;
+        for (int wpx = 4; wpx >= 1; wpx /= 2) {
+            const int pb_per = (pb + wpx - 1) / wpx;
+            const int cb_per = (cb + 4 / wpx - 1) / (4 / wpx);
+            for (int kind = 0; kind < kNumPwKinds; ++kind) {
+                if (kPwKinds[kind].mp < pb_per || kPwKinds[kind].mc < cb_per) continue;
+                // every wave runs MP x MC block chains (clamped ones too): the
+                // matrix work per workgroup, times the rounds of workgroups (one
+                // per compute unit), plus a start-up per round
+                const long wgs = (long)g.n * groups;
+                const double rounds = std::ceil(wgs / 256.0);
+                const double units = (double)kPwKinds[kind].mp * kPwKinds[kind].mc;
+                const double cost = rounds * (units * (g.cin / 2) * 64.0 + 5000.0) + 1e-3 * units;
+                if (cost < best) {
+                    best = cost;
+                    *c = PwConfig{groups, kind, wpx, pb_per, cb_per, lds};
+                    found = true;
+                }
+            }
+        }
+    }
+    // enough workgroups to spread over the chip
+    return found && (long)g.n * c->groups >= 64;
+}
+
+bool pointwise_fits(const ConvGeom& g)
+{
+    PwConfig c;
+    return pw_config(g, &c);
+}
+
+void pointwise_describe(const ConvGeom& g, char* buf, int len)
+{
+    PwConfig c{};
+    pw_config(g, &c);
+    snprintf(buf, len, "pointwise k1 s%d groups=%d wpx=%d splitk=1 kernel=cvx::k_pointwise<%d, %d>",
+             g.stride, c.groups, c.wpx, kPwKinds[c.kind].mp, kPwKinds[c.kind].mc);
+}
+
+bool pointwise_aligned(const float* x, const float* res, const float* y)
+{
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    return al(x) && al(y) && (res == nullptr || al(res));
+}
+
+template <int MP, int MC>
+static void launch_pw(dim3 grid, size_t lds, hipStream_t s, const PwArgs& a)
+{
+    hipLaunchKernelGGL((k_pointwise<MP, MC>), grid, dim3(kPwThreads), lds, s, a);
+}
+
+hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                            const float* bias, const float* res, float* y, hipStream_t s)
+{
+    PwConfig c;
+    PwStage st;
+    if (!pw_config(g, &c) || !pw_stage(g, &st)) return hipErrorInvalidValue;
+    if (!pointwise_aligned(x, res, y)) return hipErrorInvalidValue;
+    PwArgs a;
+    a.x = x;
+    a.wp = wp;
+    a.scale = scale;
+    a.bias = bias;
+    a.res = res;
+    a.y = y;
+    a.cin = g.cin;
+    a.cout = g.cout;
+    a.HW = g.h * g.w;
+    a.OHW = g.oh * g.ow;
+    a.groups_co = c.groups;
+    a.CO = g.cout / c.groups;
+    a.CB = a.CO / 32;
+    a.PB = (a.OHW + 31) / 32;
+    a.nchunks = g.cin / 16;
+    fastdiv_params(c.groups, &a.m_g, &a.l_g);
+    a.rounds = st.rounds;
+    a.RE = st.re;
+    a.RQ = st.rq;
+    a.RPC = st.rpc;
+    a.RSTR = st.rstr;
+    fastdiv_params(st.rq, &a.m_rq, &a.l_rq);
+    fastdiv_params(st.rpc, &a.m_rpc, &a.l_rpc);
+    a.wrounds = (a.CB * 128 + 255) / 256;
+    a.OWD = st.owd;
+    a.WS = st.ws;
+    a.S = g.stride;
+    a.CS = st.cs;
+    fastdiv_params(st.owd, &a.m_owd, &a.l_owd);
+    a.wpx = c.wpx;
+    a.pb_per = c.pb_per;
+    a.cb_per = c.cb_per;
+    a.BUF = st.rounds * 1024 + a.wrounds * 1024;
+    a.WOFF = st.rounds * 1024;
+    a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+    a.act = g.act;
+    a.res_mode = g.res_mode;
+    dim3 grid((unsigned)((long)g.n * c.groups));
+    switch (c.kind) {
+    case 0: launch_pw<2, 3>(grid, c.lds, s, a); break;
+    case 1: launch_pw<1, 3>(grid, c.lds, s, a); break;
+    case 2: launch_pw<2, 2>(grid, c.lds, s, a); break;
+    case 3: launch_pw<1, 2>(grid, c.lds, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cvx

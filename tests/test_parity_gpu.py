@@ -181,6 +181,14 @@ CASES = [
     (22, 1, 20, 13, 13, 37, 1, 1, 0, 1, A, AF),
     (23, 1, 300, 5, 7, 70, 1, 1, 0, 1, A, 0),
     (24, 1, 192, 1, 1, 10, 1, 1, 0, 1, N_, 0),
+    # 1x1 over batches of small planes (whole images per workgroup with packed weights)
+    (25, 64, 48, 14, 14, 96, 1, 1, 0, 1, R, B4),   # MNIST block-0 pointwise shape
+    (26, 64, 96, 7, 7, 192, 1, 1, 0, 1, R, B4),    # 49-pixel planes, channel blocks over waves
+    (27, 64, 48, 28, 28, 96, 1, 2, 0, 1, N_, 0),   # strided shortcut, rows staging
+    (28, 64, 96, 14, 14, 192, 1, 2, 0, 1, N_, 0),  # strided, 14-wide rows widened to 16
+    (29, 70, 32, 5, 5, 64, 1, 1, 0, 1, A, AF),     # 25-pixel planes, SiLU, residual after
+    (19, 64, 64, 7, 7, 256, 1, 1, 0, 1, A, 0),     # 256 channels: two channel groups
+    (18, 66, 16, 10, 10, 32, 1, 2, 0, 1, R, B4),   # stride 2, 10x10 -> 5x5
     # depthwise 3x3
     (30, 2, 48, 28, 28, 48, 3, 2, 1, 48, R, 0),
     (31, 1, 64, 13, 13, 64, 3, 1, 1, 64, A, AF),
@@ -418,6 +426,40 @@ def test_depthwise_misaligned_input(hw):
     torch.cuda.synchronize()
     assert out.guards_intact(), "write outside the output"
     check(out.t.cpu().numpy(), ref, f"dw misaligned {h}x{w}")
+
+
+POINTWISE_CASES = [c for c in CASES if 18 <= c[0] <= 19 or 25 <= c[0] <= 29]
+
+
+@pytest.mark.parametrize("case", POINTWISE_CASES, ids=[f"case{c[0]}" for c in POINTWISE_CASES])
+def test_pointwise_plan_and_misaligned(case):
+    """The batched small-plane 1x1 layers plan onto the pointwise kernel; with
+    x, y and the residual 4 bytes off a 16-byte boundary the same layer falls
+    back to the packed kernel (same packed weights) and gives the same result."""
+    seed, n, cin, h, w, cout, k, s, p, g, act, rm = case
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, g, act, rm)
+    d, wp, scale, bias = _packed_setup(x, L)
+    plan = cvx.cvx_conv_plan(d)
+    assert "k_pointwise" in plan, plan
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    r = wl.residual_for(seed, (n, cout, oh, ow)) if rm else None
+    ref = oracle_conv(x, L, r)
+    nx, ny = x.size, n * cout * oh * ow
+    xbuf = torch.zeros(nx + 4, device=DEV)
+    xbuf[1:1 + nx] = dev(x).reshape(-1)
+    rptr = None
+    if rm:
+        rbuf = torch.zeros(ny + 4, device=DEV)
+        rbuf[1:1 + ny] = dev(r).reshape(-1)
+        rptr = rbuf[1:].data_ptr()
+    out = Guarded((ny + 4,))
+    say(f"pointwise misaligned case {seed}: {plan}")
+    cvx.cvx_conv_bn_act(d, xbuf[1:].data_ptr(), wp, scale, bias, rptr, out.t[1:].data_ptr(), None, 0)
+    torch.cuda.synchronize()
+    y = out.t.cpu().numpy()
+    assert out.guards_intact(), "write outside the output"
+    assert np.isnan(y[0]) and np.all(np.isnan(y[1 + ny:])), "write outside the output"
+    check(y[1:1 + ny].reshape(n, cout, oh, ow), ref, f"pointwise misaligned {seed}")
 
 
 @pytest.mark.parametrize("force", ["0,8,1", "1,16,1", "0,8,2", "2,0,3"])
