@@ -25,6 +25,9 @@
 // consecutive pixels of one output channel.
 #include <stdio.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "bufio.h"
 #include "cvx_internal.h"
 #include "epilogue.h"
@@ -40,12 +43,37 @@ constexpr int kPwThreads = 512;    // four producer and four consumer waves
 constexpr int kPwMaxRounds = 8;    // input staging rounds (256 16-byte elements) per chunk
 constexpr int kPwWRounds = 3;      // weight staging rounds per chunk: up to six channel blocks
 constexpr int kPwMaxCB = 6;
-constexpr int kPwBatch = 8;        // residual quads a thread has in flight before it stores
+constexpr int kPwResQ = 20;        // output quads per producer thread: tiles of up to 20480 floats
 constexpr int kPwChunkW = 512;     // packed 1x1 weight floats per (32-channel block, chunk)
 
 __device__ __forceinline__ int pw_div(int n, unsigned m, unsigned l)
 {
     return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> l);
+}
+
+// Waits until at most n of this wave's vector-memory loads are outstanding (loads
+// complete in order), leaving the other counters alone.  The count is an
+// immediate, so one instruction per value.
+__device__ __forceinline__ void pw_wait_vm(int n)
+{
+#define PW_VM(k) \
+    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+    switch (n) {
+        PW_VM(0) PW_VM(1) PW_VM(2) PW_VM(3) PW_VM(4) PW_VM(5) PW_VM(6) PW_VM(7) PW_VM(8) PW_VM(9)
+        PW_VM(10) PW_VM(11) PW_VM(12) PW_VM(13) PW_VM(14) PW_VM(15) PW_VM(16) PW_VM(17) PW_VM(18)
+        PW_VM(19) PW_VM(20) PW_VM(21) PW_VM(22) PW_VM(23) PW_VM(24) PW_VM(25) PW_VM(26) PW_VM(27)
+        PW_VM(28) PW_VM(29) PW_VM(30) PW_VM(31) PW_VM(32) PW_VM(33) PW_VM(34) PW_VM(35)
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+#undef PW_VM
+}
+
+// Keeps the compiler from moving memory operations across this point (the
+// waits above count loads in issue order).
+__device__ __forceinline__ void pw_order()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // 16-byte LDS-direct load (lane i writes d + 16 i); outside the kernel template
@@ -78,6 +106,8 @@ struct PwArgs {
     unsigned m_owd, l_owd;
     int wpx, pb_per, cb_per;    // consumer grid: waves along pixels, blocks per wave
     int BUF, WOFF;              // floats per stage buffer, weights' offset within it
+    int SPARE;                  // LDS float offset of a 16-byte slot that takes dropped sums
+    int rq, rq_per;             // output quads per producer thread, residual quads loaded per chunk
     unsigned wp_bytes;
     int act, res_mode;
 };
@@ -106,25 +136,26 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
     }
     const int nst = a.nchunks;
     const int BUF = a.BUF;
-    const float* xim = a.x + (long)img * a.cin * a.HW;
 
     if (wave >= 4) {
         // ---------------------------------------------------------- producers
         const int ptid = tid - 256;
         const int pw = wave - 4;
+        const float* xim = a.x + (long)img * a.cin * a.HW;
         // byte offsets of this lane's staged elements within a chunk, the same
-        // for every chunk; past the chunk's elements an out-of-range offset
+        // for every chunk (a stride-1 chunk is one run); past the chunk's
+        // elements an out-of-range offset
         unsigned goff[kPwMaxRounds];
 #pragma unroll
         for (int i = 0; i < kPwMaxRounds; ++i) {
-            goff[i] = kOOB;
-            if (i < a.rounds) {
-                const int e = ptid + 256 * i;
+            const int e = ptid + 256 * i;
+            int f = 4 * e;
+            if (a.RPC > 1) {
                 const int r = pw_div(e, a.m_rq, a.l_rq);
                 const int c = pw_div(r, a.m_rpc, a.l_rpc);
-                const int f = c * a.HW + (r - c * a.RPC) * a.RSTR + 4 * (e - r * a.RQ);
-                goff[i] = e < a.RE ? 4u * (unsigned)f : kOOB;
+                f = c * a.HW + (r - c * a.RPC) * a.RSTR + 4 * (e - r * a.RQ);
             }
+            goff[i] = e < a.RE ? 4u * (unsigned)f : kOOB;
         }
         // the group's weights of a chunk: CB blocks of 2 KB, kPwChunkW floats apart
         // per chunk and nchunks * kPwChunkW apart per block
@@ -137,6 +168,7 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
                                          4u * (unsigned)(e & 127))
                                  : kOOB;
         }
+        // one chunk: a.rounds + a.wrounds loads per wave
         auto issue = [&](int st, int sb) {
             const rsrc_t rx = make_rsrc(xim + (long)st * 16 * a.HW, 64u * (unsigned)a.HW);
             const rsrc_t rw = make_rsrc(a.wp + (long)st * kPwChunkW, a.wp_bytes - 4u * kPwChunkW * (unsigned)st);
@@ -152,152 +184,218 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
                               woff[j]);
             }
         };
-        // Barrier s (s = 0 .. nst-1) follows the landing of chunk s+1; chunk s+2
-        // then goes into the buffer of chunk s-1, which the consumers have left
-        // by barrier s.
+        const int nld = a.rounds + a.wrounds;
+        // This thread's output quads e = ptid + 256 j of the tile's run; their
+        // residual comes to registers, a share per chunk while the consumers
+        // compute.
+        const long obase = ((long)img * a.cout + (long)grp * a.CO) * a.OHW;
+        const int tq = a.CO * a.OHW / 4;
+        const unsigned run_b = 16u * (unsigned)tq;
+        const bool want_res = a.res_mode != CVX_RES_NONE;
+        const rsrc_t rres = make_rsrc(want_res ? a.res + obase : a.y, want_res ? run_b : 0u);
+        f32x4 rv[kPwResQ];  // only the first a.rq are loaded, and only those are read
+        auto load_res = [&](int lo, int hi_) {
+#pragma unroll
+            for (int j = 0; j < kPwResQ; ++j) {
+                if (j >= lo && j < hi_) {
+                    const int e = ptid + 256 * j;
+                    rv[j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(e < tq ? 16u * (unsigned)e : kOOB), 0, 0));
+                }
+            }
+        };
+
+        // Stage buffers: chunk s is in buffer s % 3.  The consumers read chunk s
+        // between barriers s-1 and s, so its buffer takes chunk s+3 right after
+        // barrier s; barrier s needs chunk s+1 landed.  Chunks are thus issued
+        // two barriers before they are needed.
+        auto bufof = [&](int s3) { return (s3 % 3) * BUF; };
+        pw_order();
         issue(0, 0);
         if (nst > 1) issue(1, BUF);
-        __builtin_amdgcn_s_waitcnt(0);
+        if (nst > 2) issue(2, 2 * BUF);
+        pw_order();
+        pw_wait_vm(nst > 2 ? nld : 0);  // chunks 0 and 1
         lds_barrier();
-        int sb = 2 * BUF;
+        int rdone = 0;
         for (int st = 1; st < nst; ++st) {
-            if (st + 1 < nst) issue(st + 1, sb);
-            sb = sb == 2 * BUF ? 0 : sb + BUF;
-            __builtin_amdgcn_s_waitcnt(0);
+            // after barrier st-1: the buffer of chunk st-1 is free
+            int piece = 0;
+            if (want_res) {
+                const int upto = min(a.rq, st * a.rq_per);
+                piece = upto - rdone;
+                load_res(rdone, upto);
+                rdone = upto;
+            }
+            pw_order();
+            const bool more = st + 2 < nst;
+            if (more) issue(st + 2, bufof(st + 2));
+            pw_order();
+            pw_wait_vm(piece + (more ? nld : 0));  // chunk st+1 (and every earlier load)
             lds_barrier();
         }
+        if (want_res) load_res(rdone, a.rq);
         __syncthreads();  // the consumers' exchange
-    } else {
-        // -------------------------------------------------------------- consumers
-        const int wx = wave % a.wpx;
-        const int wc = wave / a.wpx;
-        const int pb0 = wx * a.pb_per;
-        const int cb0 = wc * a.cb_per;
-        // A wave owns pixel blocks pb0 .. pb0+MP-1 and channel blocks cb0 ..
-        // cb0+MC-1 of the tile.  Blocks past the tile (the template covers the
-        // largest share) compute on clamped, in-range operands and are dropped.
-        int abase[MP];
-#pragma unroll
-        for (int mp = 0; mp < MP; ++mp) {
-            const int q = min(32 * (pb0 + mp) + l32, a.OHW - 1);
-            const int oh = pw_div(q, a.m_owd, a.l_owd);
-            abase[mp] = hi * a.CS + oh * a.WS + a.S * (q - oh * a.OWD);
-        }
-        int boff[MC];
-        float sc[MC], bi[MC];
-        {
-            const rsrc_t rs = make_rsrc(a.scale, 4u * (unsigned)a.cout);
-            const rsrc_t rb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
-#pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                const int cb = min(cb0 + mc, a.CB - 1);
-                boff[mc] = a.WOFF + cb * kPwChunkW + 2 * lane;
-                const unsigned co = (unsigned)(grp * a.CO + 32 * cb + l32);
-                sc[mc] = bload(rs, 4u * co);
-                bi[mc] = bload(rb, 4u * co);
-            }
-        }
-        f32x16 acc[MP][MC];
-#pragma unroll
-        for (int mp = 0; mp < MP; ++mp)
-#pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mp][mc][r] = 0.0f;
 
-        const int cs2 = 2 * a.CS;
-        int sb = 0;
-        for (int st = 0; st < nst; ++st) {
-            lds_barrier();
-            // weights of the chunk: pairs 2h, 2h+1 of each channel block
-            f32x2 bw[MC][4];
-#pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    bw[mc][h] = *reinterpret_cast<const f32x2*>(smem + sb + boff[mc] + 128 * h);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float av[MP];
-#pragma unroll
-                for (int mp = 0; mp < MP; ++mp) av[mp] = smem[sb + abase[mp] + k * cs2];
-#pragma unroll
-                for (int mp = 0; mp < MP; ++mp)
-#pragma unroll
-                    for (int mc = 0; mc < MC; ++mc)
-                        acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mp], bw[mc][k >> 1][k & 1],
-                                                                          acc[mp][mc], 0, 0, 0);
-            }
-            sb = sb == 2 * BUF ? 0 : sb + BUF;
-        }
-
-        // Exchange: scale and bias applied, each sum goes to its place in the
-        // image's [channel][pixel] output run (the staging buffers are free once
-        // every wave is past this barrier).
+        // ------------------------------------------------------------ copy-out
+        // The tile's finished run, 16 bytes a lane: residual and activation
+        // applied on the way.
         __syncthreads();
-        const bool quads = (a.OHW & 3) == 0;
+        const rsrc_t ry = make_rsrc(a.y + obase, run_b);
+        auto copy_out = [&](auto act_fn) {
 #pragma unroll
-        for (int mp = 0; mp < MP; ++mp) {
-            const int pb = pb0 + mp;
-            if (pb >= a.PB) break;
+            for (int j = 0; j < kPwResQ; ++j) {
+                if (j >= a.rq) break;
+                const int e = ptid + 256 * j;
+                const f32x4 v = reinterpret_cast<const f32x4*>(smem)[min(e, tq - 1)];
+                f32x4 o;
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                const int cb = cb0 + mc;
-                if (cb >= a.CB) break;
-                float* row = smem + (32 * cb + l32) * a.OHW;
+                for (int k = 0; k < 4; ++k) {
+                    float t = v[k];
+                    t = a.res_mode == CVX_RES_BEFORE_ACT ? t + rv[j][k] : t;
+                    t = act_fn(t);
+                    o[k] = a.res_mode == CVX_RES_AFTER_ACT ? t + rv[j][k] : t;
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ry,
+                                                       (int)(e < tq ? 16u * (unsigned)e : kOOB), 0, 0);
+            }
+        };
+        if (a.act == CVX_ACT_RELU)
+            copy_out([](float t) { return fmaxf(t, 0.0f); });
+        else if (a.act == CVX_ACT_SILU)
+            copy_out([](float t) { return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)); });
+        else
+            copy_out([](float t) { return t; });
+        return;
+    }
+
+    // -------------------------------------------------------------- consumers
+    const int wx = wave % a.wpx;
+    const int wc = wave / a.wpx;
+    const int pb0 = wx * a.pb_per;
+    const int cb0 = wc * a.cb_per;
+    // A wave owns pixel blocks pb0 .. pb0+MP-1 and channel blocks cb0 ..
+    // cb0+MC-1 of the tile.  Blocks past the tile (the template covers the
+    // largest share) compute on clamped, in-range operands and are dropped.
+    int abase[MP];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int q = 32 * pb + 8 * g + 4 * hi;
-                    f32x4 z;
+    for (int mp = 0; mp < MP; ++mp) {
+        const int q = min(32 * (pb0 + mp) + l32, a.OHW - 1);
+        const int oh = pw_div(q, a.m_owd, a.l_owd);
+        abase[mp] = hi * a.CS + oh * a.WS + a.S * (q - oh * a.OWD);
+    }
+    int boff[MC];
+    float sc[MC], bi[MC];
+    {
+        const rsrc_t rs = make_rsrc(a.scale, 4u * (unsigned)a.cout);
+        const rsrc_t rb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) z[r] = fmaf(sc[mc], acc[mp][mc][4 * g + r], bi[mc]);
-                    if (quads) {
-                        if (q < a.OHW) *reinterpret_cast<f32x4*>(row + q) = z;
-                    } else {
+        for (int mc = 0; mc < MC; ++mc) {
+            const int cb = min(cb0 + mc, a.CB - 1);
+            boff[mc] = a.WOFF + cb * kPwChunkW + 2 * lane;
+            const unsigned co = (unsigned)(grp * a.CO + 32 * cb + l32);
+            sc[mc] = bload(rs, 4u * co);
+            bi[mc] = bload(rb, 4u * co);
+        }
+    }
+    f32x16 acc[MP][MC];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (q + r < a.OHW) row[q + r] = z[r];
-                    }
+    for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mp][mc][r] = 0.0f;
+
+    // A chunk's operands: input of eight channel pairs for MP pixel blocks,
+    // weights of the pairs for MC channel blocks.  Those of chunk st+1 are read
+    // (between barriers st and st+1) while chunk st's matrix instructions run,
+    // pair by pair: a wave may have only 15 LDS reads in flight, so issuing a
+    // whole chunk's reads at once would stall in front of the matrix work.
+    struct Ops {
+        float x[8][MP];
+        f32x2 w[MC][4];
+    };
+    const int cs2 = 2 * a.CS;
+    // reads of pair k: its input, and at even k the weights of pairs k, k+1
+    auto read_pair = [&](int sbuf, Ops& o, int k) {
+        if ((k & 1) == 0) {
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+                o.w[mc][k >> 1] = *reinterpret_cast<const f32x2*>(smem + sbuf + boff[mc] + 64 * k);
+        }
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) o.x[k][mp] = smem[sbuf + abase[mp] + k * cs2];
+    };
+    // chunk in `o`, and the next chunk's operands from buffer `nbuf` into `n`,
+    // one pair's reads ahead of each pair's matrix instructions (so the last
+    // reads have landed by the barrier's LDS wait).  After the last chunk these
+    // reads take whatever a buffer holds, unused: no branch between the matrix
+    // instructions.
+    auto compute = [&](const Ops& o, Ops& n, int nbuf) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            read_pair(nbuf, n, k);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc)
+                    acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.x[k][mp], o.w[mc][k >> 1][k & 1],
+                                                                      acc[mp][mc], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto nextb = [&](int b) { return b == 2 * BUF ? 0 : b + BUF; };
+    Ops o0, o1;
+    lds_barrier();  // barrier 0: chunks 0 and 1 have landed
+#pragma unroll
+    for (int k = 0; k < 8; ++k) read_pair(0, o0, k);
+    int sb = 0;     // buffer of chunk st
+    for (int st = 0;;) {
+        // chunk st in o0
+        if (st > 0) lds_barrier();
+        compute(o0, o1, nextb(sb));
+        sb = nextb(sb);
+        if (++st >= nst) break;
+        // chunk st in o1
+        lds_barrier();
+        compute(o1, o0, nextb(sb));
+        sb = nextb(sb);
+        if (++st >= nst) break;
+    }
+
+    // Exchange: every sum, scaled and biased, goes to its place in the tile's
+    // [channel][pixel] output run (over the stage buffers, free once every wave
+    // is past this barrier); pixels past the plane go to a spare slot.
+    __syncthreads();
+    const bool quads = (a.OHW & 3) == 0;
+#pragma unroll
+    for (int mp = 0; mp < MP; ++mp) {
+        const int pb = pb0 + mp;
+        if (pb >= a.PB) break;
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            const int cb = cb0 + mc;
+            if (cb >= a.CB) break;
+            const int row = (32 * cb + l32) * a.OHW;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int q = 32 * pb + 8 * g + 4 * hi;
+                f32x4 z;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[e] = fmaf(sc[mc], acc[mp][mc][4 * g + e], bi[mc]);
+                if (quads) {
+                    // in 16-byte units, so the store is one 16-byte LDS write
+                    const int r4 = (32 * cb + l32) * (a.OHW >> 2) + 8 * pb + 2 * g + hi;
+                    reinterpret_cast<f32x4*>(smem)[q < a.OHW ? r4 : (a.SPARE >> 2)] = z;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) smem[q + e < a.OHW ? row + q + e : a.SPARE] = z[e];
                 }
             }
         }
     }
-    __syncthreads();
-
-    // Copy-out by all waves: the tile's run of CO*OHW floats, 16 bytes a lane.
-    const long obase = ((long)img * a.cout + (long)grp * a.CO) * a.OHW;
-    const int tq = a.CO * a.OHW / 4;
-    const unsigned run_b = 16u * (unsigned)tq;
-    const bool want_res = a.res_mode != CVX_RES_NONE;
-    const rsrc_t ry = make_rsrc(a.y + obase, run_b);
-    const rsrc_t rr = want_res ? make_rsrc(a.res + obase, run_b) : make_rsrc(a.y, 0u);
-    for (int b0 = 0; b0 < tq; b0 += kPwBatch * kPwThreads) {
-        f32x4 rv[kPwBatch];
-#pragma unroll
-        for (int j = 0; j < kPwBatch; ++j) {
-            const int e = b0 + tid + kPwThreads * j;
-            rv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (want_res)
-                rv[j] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(e < tq ? 16u * (unsigned)e : kOOB), 0, 0));
-        }
-#pragma unroll
-        for (int j = 0; j < kPwBatch; ++j) {
-            const int e = b0 + tid + kPwThreads * j;
-            if (e >= tq) break;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(smem + 4 * e);
-            f32x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float t = v[r];
-                if (a.res_mode == CVX_RES_BEFORE_ACT) t += rv[j][r];
-                t = apply_act_fast(t, a.act);
-                if (a.res_mode == CVX_RES_AFTER_ACT) t += rv[j][r];
-                o[r] = t;
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ry, (int)(16u * (unsigned)e), 0, 0);
-        }
-    }
+    __syncthreads();  // the producers copy the run out
 }
 
 // ------------------------------------------------------------------ host side
@@ -374,8 +472,10 @@ static bool pw_config(const ConvGeom& g, PwConfig* c)
         const int wrounds = (cb * 128 + 255) / 256;
         const size_t buf = (size_t)s.rounds * 1024 + (size_t)wrounds * 1024;
         const size_t xch = (size_t)32 * cb * ohw;
-        const size_t lds = 4 * (3 * buf > xch ? 3 * buf : xch);
-        if (lds > kMaxLdsBytes) continue;
+        // the exchange (plus a spare slot) over the stage buffers; the producers
+        // hold the residual of up to kPwResQ output quads each
+        const size_t lds = 4 * std::max(3 * buf, xch + 4);
+        if (lds > kMaxLdsBytes || xch > (size_t)kPwResQ * 256 * 4) continue;
         for (int wpx = 4; wpx >= 1; wpx /= 2) {
             const int pb_per = (pb + wpx - 1) / wpx;
             const int cb_per = (cb + 4 / wpx - 1) / (4 / wpx);
@@ -468,6 +568,11 @@ hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, 
     a.cb_per = c.cb_per;
     a.BUF = st.rounds * 1024 + a.wrounds * 1024;
     a.WOFF = st.rounds * 1024;
+    const int tq = a.CO * a.OHW / 4;
+    a.SPARE = a.CO * a.OHW;
+    a.rq = (tq + 255) / 256;
+    // residual loads spread over the chunks' iterations (all but the first)
+    a.rq_per = (a.rq + std::max(1, a.nchunks - 1) - 1) / std::max(1, a.nchunks - 1);
     a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
     a.act = g.act;
     a.res_mode = g.res_mode;
