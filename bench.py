@@ -322,7 +322,7 @@ def _probe_map(disp, manifest):
     i0 = cal[-1]
     cal_kib = disp[i0][2]
     rest = [(n, v) for _, n, v in disp[i0 + 1:] if "cvx::" in n]
-    per, j = {}, 0
+    per, names, j = {}, {}, 0
     for m in manifest:
         vals = []
         for _ in range(m["reps"]):
@@ -331,15 +331,16 @@ def _probe_map(disp, manifest):
             vals.append(v)
             j += 1
         per[m["layer"]] = sum(vals) / len(vals)
-    return cal_kib, per
+        names[m["layer"]] = n.split("(")[0].replace("void ", "").strip()  # the variant that ran
+    return cal_kib, per, names
 
 
 def pmc_summary(args) -> int:
     fetch_dir, write_dir = args.pmc_summary
     with open(args.manifest) as fh:
         manifest = json.loads(fh.read().strip().splitlines()[-1])["manifest"]
-    cf, fetch = _probe_map(_dispatches(fetch_dir, "FETCH_SIZE"), manifest)
-    cw, write = _probe_map(_dispatches(write_dir, "WRITE_SIZE"), manifest)
+    cf, fetch, names = _probe_map(_dispatches(fetch_dir, "FETCH_SIZE"), manifest)
+    cw, write, _ = _probe_map(_dispatches(write_dir, "WRITE_SIZE"), manifest)
     ff = COPY_BYTES / (cf * 1024.0)
     fw = COPY_BYTES / (cw * 1024.0)
     lines = ["# HBM traffic per launch, detector pipeline 640x640 b=1, each layer alone",
@@ -356,11 +357,11 @@ def pmc_summary(args) -> int:
     for m in manifest:
         L = m["layer"]
         t = fetch[L] * 1024 * ff + write[L] * 1024 * fw
-        lines.append(f"| {L} | `{m['kernel']}` | {fetch[L]:.0f} | {write[L]:.0f} | {t:.0f} | "
+        k = names[L]
+        lines.append(f"| {L} | `{k}` | {fetch[L]:.0f} | {write[L]:.0f} | {t:.0f} | "
                      f"{m['algorithmic_bytes']:.0f} | {t / m['algorithmic_bytes']:.2f} |")
-        r = recs.setdefault(m["kernel"], {"kernel": m["kernel"],
-                                          "source_hash": kernel_sources_hash(m["kernel"]),
-                                          "traffic_bytes_per_layer": {}})
+        r = recs.setdefault(k, {"kernel": k, "source_hash": kernel_sources_hash(k),
+                                "traffic_bytes_per_layer": {}})
         r["traffic_bytes_per_layer"][L] = round(t, 1)
     lines.append("")
     for r in recs.values():
@@ -376,7 +377,7 @@ def rocprof_summary(args) -> int:
     f = glob.glob(os.path.join(args.rocprof_summary, "**", "*kernel_stats.csv"), recursive=True)[0]
     with open(f) as fh:
         rows = list(csv.DictReader(fh))
-    print("# Kernel durations, detector pipeline 640x640 b=1 (bench.py)")
+    print(f"# Kernel durations, {args.title}")
     print()
     print(f"Command: {args.cmd}")
     print()
@@ -495,6 +496,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layers", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
+    ap.add_argument("--others-only", action="store_true",
+                    help="time only the other configurations and print them (for profiling)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for rocprofv3 counter passes (prints a manifest line)")
     ap.add_argument("--reps", type=int, default=3, help="calls per layer in --pmc-probe")
@@ -504,6 +507,8 @@ def main() -> int:
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="markdown table of a rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
+    ap.add_argument("--title", default="detector pipeline 640x640 b=1 (bench.py)",
+                    help="workload named in a --rocprof-summary heading")
     args = ap.parse_args()
     if args.rocprof_summary:
         return rocprof_summary(args)
@@ -524,6 +529,9 @@ def main() -> int:
         return 1
     if args.pmc_probe:
         return pmc_probe(args)
+    if args.others_only:
+        print(json.dumps({"other_workloads": other_workloads(args.layer_reps, args.steps)}))
+        return 0
     wk = wl.detector_pipeline(args.batch)
     counts = accounting.layer_counts(wk.layers, wk.x.shape)
     flop = sum(c["flop"] for c in counts)
