@@ -35,26 +35,48 @@ hipError_t launch_fold_bn(const float* gamma, const float* beta, const float* me
 // One workgroup per image.  With fc_w == nullptr the pooled vector is the
 // output ([n][c]); with hw == 1 the pool is the identity and this is a plain fc.
 // The pooled vector lives in LDS (c <= kTailMaxC, checked by the host).
+// When the image fits (c*hw <= kTailStage floats, 16-byte aligned and a
+// multiple of 4), it is first copied to LDS with independent 16-byte loads --
+// one memory round trip for the image rather than one per plane -- and each
+// thread then sums a plane from LDS.
 constexpr int kTailMaxC = 4096;
+constexpr int kTailStage = 12288;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) k_gap_fc(const float* __restrict__ x, int c, int hw,
                                                 const float* __restrict__ fc_w,
                                                 const float* __restrict__ fc_b, int out_f,
-                                                float* __restrict__ out)
+                                                float* __restrict__ out, int staged)
 {
     __shared__ float pooled[kTailMaxC];
+    __shared__ __attribute__((aligned(16))) float img[kTailStage];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const float* xb = x + (long)b * c * hw;
     const float inv = 1.0f / (float)hw;
-    // each wave pools whole planes: lanes stride over the plane, then reduce
-    for (int ch = wave; ch < c; ch += 4) {
-        const float* p = xb + (long)ch * hw;
-        float s = 0.0f;
-        for (int q = lane; q < hw; q += 64) s += p[q];
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) pooled[ch] = s * inv;
+    if (staged) {
+        const int n4 = c * hw / 4;
+        const f32x4* x4 = reinterpret_cast<const f32x4*>(xb);
+#pragma unroll 4
+        for (int e = threadIdx.x; e < n4; e += 256) reinterpret_cast<f32x4*>(img)[e] = x4[e];
+        __syncthreads();
+        for (int ch = threadIdx.x; ch < c; ch += 256) {
+            const float* p = img + ch * hw;
+            float s = 0.0f;
+            for (int q = 0; q < hw; ++q) s += p[q];
+            pooled[ch] = s * inv;
+        }
+    } else {
+        // each wave pools whole planes: lanes stride over the plane, then reduce
+        for (int ch = wave; ch < c; ch += 4) {
+            const float* p = xb + (long)ch * hw;
+            float s = 0.0f;
+            for (int q = lane; q < hw; q += 64) s += p[q];
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+            if (lane == 0) pooled[ch] = s * inv;
+        }
     }
     __syncthreads();
     if (fc_w == nullptr) {
@@ -73,7 +95,9 @@ __global__ void __launch_bounds__(256) k_gap_fc(const float* __restrict__ x, int
 hipError_t launch_gap_fc(const float* x, int n, int c, int hw, const float* fc_w,
                          const float* fc_b, int out_f, float* out, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_gap_fc, dim3(n), dim3(256), 0, s, x, c, hw, fc_w, fc_b, out_f, out);
+    const int staged = (long)c * hw <= kTailStage && (c * hw) % 4 == 0 &&
+                       (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+    hipLaunchKernelGGL(k_gap_fc, dim3(n), dim3(256), 0, s, x, c, hw, fc_w, fc_b, out_f, out, staged);
     return hipGetLastError();
 }
 
