@@ -437,8 +437,8 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
         break;
     case FAM_DIRECT:
         if (p.direct_stem)
-            snprintf(buf, buf_len, "stem k3 s%d splitk=1 kernel=cvx::k_stem<%d, 16, %d>", g.stride,
-                     g.cin, g.stride);
+            snprintf(buf, buf_len, "stem k3 s%d splitk=1 kernel=cvx::k_stem<%d, %d, %d>", g.stride,
+                     g.cin, stem_cob(g), g.stride);
         else
             snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
                      g.stride, p.direct_cob, p.direct_cob);

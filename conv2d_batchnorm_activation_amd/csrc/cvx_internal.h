@@ -66,6 +66,8 @@ hipError_t launch_igemm(const ConvGeom& g, const Plan& p, const float* x, const 
 // 3x3 pad-1 stride-1/2 layers with 1 or 3 input channels and widths a multiple of
 // 4 (the detector and MNIST stems) run on k_stem.
 bool stem_shape(const ConvGeom& g);
+// output channels per k_stem workgroup (8 or 16)
+int stem_cob(const ConvGeom& g);
 // LDS bytes of the depthwise plane kernel for `ppb` planes per workgroup.
 size_t dw_planes_lds_bytes(const ConvGeom& g, int ppb);
 

@@ -23,13 +23,15 @@ __device__ __forceinline__ float apply_act(float v, int act)
     return v;
 }
 
-// Same activation with the hardware exponential and reciprocal (about 1 ulp each,
-// far inside the 1e-4 parity bound); exp(-v) overflowing to +inf gives -0 for
-// very negative v, as the exact form does.
+// Same activation with the hardware exponential and reciprocal instructions
+// (v_exp_f32, v_rcp_f32: about 1 ulp each, far inside the 1e-4 parity bound; a
+// correctly rounded reciprocal would expand to a dozen instructions per
+// output); exp(-v) overflowing to +inf gives a zero reciprocal and -0 for very
+// negative v, as the exact form does.
 __device__ __forceinline__ float apply_act_fast(float v, int act)
 {
     if (act == CVX_ACT_RELU) return fmaxf(v, 0.0f);
-    if (act == CVX_ACT_SILU) return v * __frcp_rn(1.0f + __expf(-v));
+    if (act == CVX_ACT_SILU) return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
     return v;
 }
 

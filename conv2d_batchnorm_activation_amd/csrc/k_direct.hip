@@ -79,30 +79,24 @@ __global__ void __launch_bounds__(256) k_direct(const float* __restrict__ x,
 }
 
 // Stem layers (3x3, pad 1, stride 1 or 2, one or three input channels, widths a
-// multiple of 4).  A workgroup takes 256 consecutive output pixels of one image
-// (flattened over rows) and COB output channels.  It stages the input rows those
-// pixels touch (every input channel, whole rows; each wave takes whole rows,
-// at a pitch of 64 quads so a partial last load zero-fills its own row) in LDS
-// with 16-byte LDS-direct loads, all in flight at once.  The workgroup has two
-// threads per pixel (8 waves, so latency has other waves to hide behind, and
-// three workgroups still fit a compute unit's LDS); each holds its pixel's
-// CIN x 9 window in registers (the pad column reads as zero) and computes half
-// of the COB channels, two at a time, storing each pair as soon as it is done so
-// that the stores overlap the rest of the arithmetic.  The weights
-// are the same for every lane: scalar loads straight into the multiply-adds'
-// scalar operand (read per lane from LDS, every wave would pull a kilobyte per
-// read through LDS).  Stores are one float per channel, coalesced across the
-// wave.  ("YOLO26N Inference Optimisation", "Baseline benchmark": the
-// detector's stem convolutions; "Как я свертки ускорял", "Пациента на стол":
-// the MNIST net's first convolution.)
-constexpr int kStemCob = 16;      // output channels per workgroup
-constexpr int kStemSplit = 2;     // threads per output pixel
-constexpr int kStemThreads = 256 * kStemSplit;
-
-__device__ __forceinline__ void stem_lds_load16(rsrc_t r, __attribute__((address_space(3))) void* d, unsigned off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
-}
+// multiple of 4): the detector's stem convolutions ("YOLO26N Inference
+// Optimisation", "Baseline benchmark") and the MNIST net's first convolution
+// ("Как я свертки ускорял", "Пациента на стол").  Their reduction (9 or 27
+// taps) is too short for the matrix cores and they are bound by the output
+// stores, so:
+//   * a thread computes a quad of four consecutive output pixels (a quad never
+//     leaves its row) for COB output channels, and stores each channel's quad
+//     with one 16-byte store, coalesced across the wave;
+//   * its input window (3 rows x 6 columns at stride 1, 3 x 9 at stride 2, per
+//     input channel) comes straight to registers, one 16-byte load per aligned
+//     group of four columns and single loads for the edge columns; rows and
+//     columns outside the image read through out-of-range offsets as zeros (the
+//     padding), and neighbouring quads share their rows in the caches;
+//   * the workgroup's weights, scale and bias go to LDS once and are read with
+//     lane-uniform addresses (broadcast reads);
+//   * a workgroup is one wave, and quads are numbered over batch x rows x
+//     columns, so even a single image gives hundreds of workgroups.
+constexpr int kStemThreads = 64;
 
 template <int CIN, int COB, int S>
 __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__ x,
@@ -110,138 +104,159 @@ __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__
                                               const float* __restrict__ scale,
                                               const float* __restrict__ bias,
                                               const float* __restrict__ res,
-                                              float* __restrict__ y, int h, int wd, int cout,
-                                              int oh, int ow, int nrows, int act, int res_mode)
+                                              float* __restrict__ y, int nquads, int h, int wd,
+                                              int cout, int ohw, int qrow, int Q, unsigned m_q,
+                                              unsigned l_q, unsigned m_r, unsigned l_r,
+                                              unsigned x_bytes, unsigned y_bytes, int act,
+                                              int res_mode)
 {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int KT = CIN * 9;         // taps per output channel
+    constexpr int KP = (KT + 3) & ~3;   // padded to whole 16-byte groups
+    constexpr int WC = S == 1 ? 6 : 9;  // window columns of a quad
+    __shared__ __attribute__((aligned(16))) float sw[COB * KP];
+    __shared__ float ssc[COB], sbi[COB];
     const int t = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int b = blockIdx.z;
     const int co0 = blockIdx.y * COB;
-    const int ohw = oh * ow;
-    const int p0 = blockIdx.x * 256;
-    const int oy_first = p0 / ow;
-    const int iy_first = oy_first * S - 1;  // staged row 0
-    const int hw = h * wd;
-    const int qpr = wd >> 2;                // 16-byte quads per row
-    const int nq = (qpr + 63) >> 6;         // loads per row
-    const int pitch = 256 * nq;             // LDS floats per staged row
-    const int srows = CIN * nrows;          // staged rows: [channel][row]
-
-    // Staging: wave w takes staged rows w, w+8, ...; rows outside the image and
-    // quads past the row's end read through out-of-range offsets as zeros.
-    {
-        const int lane = t & 63;
-        const rsrc_t rx = make_rsrc(x + (long)b * CIN * hw, 4u * (unsigned)(CIN * hw));
-        for (int r = wave; r < srows; r += kStemThreads / 64) {
-            const int ci = r / nrows;  // uniform
-            const int iy = iy_first + (r - ci * nrows);
-            const bool rok = iy >= 0 && iy < h;
-            for (int j = 0; j < nq; ++j) {
-                const int qx = 64 * j + lane;
-                const unsigned off = rok && qx < qpr ? 4u * (unsigned)(ci * hw + iy * wd + 4 * qx) : kOOB;
-                int base = r * pitch + 256 * j;
-                asm volatile("" : "+s"(base));
-                stem_lds_load16(rx, (__attribute__((address_space(3))) void*)(lds + base), off);
-            }
-        }
+    for (int i = t; i < COB * KP; i += kStemThreads) {
+        const int c = i / KP, k = i - c * KP;
+        const int co = co0 + c;
+        sw[i] = (co < cout && k < KT) ? w[(long)co * KT + k] : 0.0f;
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    if (t < COB) {
+        const int co = min(co0 + t, cout - 1);
+        ssc[t] = scale[co];
+        sbi[t] = bias[co];
+    }
     __syncthreads();
 
-    const int p = p0 + (t & 255);
-    const int part = __builtin_amdgcn_readfirstlane(t >> 8);  // channels COB / kStemSplit * part ...
-    if (p >= ohw) return;
-    const int oy = p / ow;
-    const int ox = p - oy * ow;
-    const int rrow = (oy - oy_first) * S;  // staged row of window row 0
+    const int g = blockIdx.x * kStemThreads + t;
+    if (g >= nquads) return;
+    const int img = (int)((__umulhi((unsigned)g, m_q) + (unsigned)g) >> l_q);
+    const int qi = g - img * Q;
+    const int oy = (int)((__umulhi((unsigned)qi, m_r) + (unsigned)qi) >> l_r);
+    const int ox = 4 * (qi - oy * qrow);
+    const int c0 = ox * S;  // first column of the aligned group (16-byte aligned)
 
-    float win[CIN * 9];
+    const rsrc_t rx = make_rsrc(x, x_bytes);
+    float win[CIN][3][WC];
 #pragma unroll
     for (int ci = 0; ci < CIN; ++ci)
 #pragma unroll
-        for (int kh = 0; kh < 3; ++kh)
+        for (int kh = 0; kh < 3; ++kh) {
+            const int iy = oy * S - 1 + kh;
+            const bool rok = (unsigned)iy < (unsigned)h;
+            const unsigned row = rok ? (unsigned)(((img * CIN + ci) * h + iy) * wd) : 0u;
+            win[ci][kh][0] = bload(rx, rok && c0 > 0 ? 4u * (row + c0 - 1) : kOOB);
+            const f32x4 m0 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(rok ? 4u * (row + c0) : kOOB), 0, 0));
 #pragma unroll
-            for (int kw = 0; kw < 3; ++kw) {
-                const int col = ox * S - 1 + kw;
-                const bool ok = col >= 0 && col < wd;
-                const int idx = ok ? (ci * nrows + rrow + kh) * pitch + col : 0;
-                const float v = lds[idx];
-                win[ci * 9 + kh * 3 + kw] = ok ? v : 0.0f;
+            for (int e = 0; e < 4; ++e) win[ci][kh][1 + e] = m0[e];
+            if constexpr (S == 1) {
+                win[ci][kh][5] = bload(rx, rok && c0 + 4 < wd ? 4u * (row + c0 + 4) : kOOB);
+            } else {
+                // columns c0+4 .. c0+7 stay inside the row: wd = 2*ow
+                const f32x4 m1 = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(rok ? 4u * (row + c0 + 4) : kOOB), 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) win[ci][kh][5 + e] = m1[e];
             }
+        }
 
-    // Stores through a descriptor over the output: a channel past c_out gets an
-    // out-of-range offset and is dropped, so the epilogue has no branches and the
-    // pair's two accumulation chains interleave.
-    const unsigned out_bytes = 4u * (unsigned)(gridDim.z * cout * ohw);
-    const rsrc_t ry = make_rsrc(y, out_bytes);
-    const rsrc_t rr = make_rsrc(res, res_mode != CVX_RES_NONE ? out_bytes : 0u);
-    const unsigned obase = (unsigned)(b * cout * ohw + p);
-#pragma unroll 1
-    for (int g = part * (COB / kStemSplit / 2); g < (part + 1) * (COB / kStemSplit / 2); ++g) {
-        const int c0 = min(co0 + 2 * g, cout - 1), c1 = min(co0 + 2 * g + 1, cout - 1);  // uniform
-        const float* w0 = w + (long)c0 * CIN * 9;
-        const float* w1 = w + (long)c1 * CIN * 9;
-        float a0 = 0.0f, a1 = 0.0f;
+    // A channel past c_out gets an out-of-range offset: its store is dropped.
+    // Vector-memory stores and loads share one completion counter, so any load
+    // after the first store would wait for the stores before it: the residual
+    // quads of all COB channels are loaded first.
+    const rsrc_t ry = make_rsrc(y, y_bytes);
+    const unsigned obase = (unsigned)(img * cout * ohw + oy * (4 * qrow) + ox);
+    auto offset = [&](int c) { return co0 + c < cout ? 4u * (obase + (unsigned)((co0 + c) * ohw)) : kOOB; };
+    f32x4 r[COB];
+    if (res_mode != CVX_RES_NONE) {
+        const rsrc_t rr = make_rsrc(res, y_bytes);
 #pragma unroll
-        for (int tap = 0; tap < CIN * 9; ++tap) {
-            a0 = fmaf(w0[tap], win[tap], a0);
-            a1 = fmaf(w1[tap], win[tap], a1);
-        }
-        const float acc[2] = {a0, a1};
-        const float scs[2] = {scale[c0], scale[c1]}, bis[2] = {bias[c0], bias[c1]};
+        for (int c = 0; c < COB; ++c)
+            r[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)offset(c), 0, 0));
+    } else {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int co = co0 + 2 * g + e;
-            const unsigned o = co < cout ? 4u * (obase + (unsigned)(co * ohw)) : kOOB;
-            const float r = bload(rr, o);
-            float v = fmaf(scs[e], acc[e], bis[e]);
-            if (res_mode == CVX_RES_BEFORE_ACT) v += r;
-            v = apply_act_fast(v, act);
-            if (res_mode == CVX_RES_AFTER_ACT) v += r;
-            bstore(ry, o, v);
-        }
+        for (int c = 0; c < COB; ++c) r[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // one loop per activation, so the epilogue has no branches
+    auto channels = [&](auto act_fn) {
+#pragma unroll
+        for (int c = 0; c < COB; ++c) {
+            float wv[KP];
+#pragma unroll
+            for (int k = 0; k < KP; k += 4) {
+                const f32x4 q = *reinterpret_cast<const f32x4*>(sw + c * KP + k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wv[k + e] = q[e];
+            }
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ci = 0; ci < CIN; ++ci)
+#pragma unroll
+                for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw) {
+                        const float wt = wv[ci * 9 + kh * 3 + kw];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[j] = fmaf(wt, win[ci][kh][j * S + kw], acc[j]);
+                    }
+            const float sc = ssc[c], bi = sbi[c];
+            f32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = fmaf(sc, acc[j], bi);
+                v = res_mode == CVX_RES_BEFORE_ACT ? v + r[c][j] : v;
+                v = act_fn(v);
+                o[j] = res_mode == CVX_RES_AFTER_ACT ? v + r[c][j] : v;
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ry, (int)offset(c), 0, 0);
+        }
+    };
+    if (act == CVX_ACT_SILU)
+        channels([](float v) { return apply_act_fast(v, CVX_ACT_SILU); });
+    else if (act == CVX_ACT_RELU)
+        channels([](float v) { return fmaxf(v, 0.0f); });
+    else
+        channels([](float v) { return v; });
 }
 
-// Staged input rows of the stem kernel's largest workgroup: 256 consecutive
-// output pixels span at most ceil(255 / ow) + 1 output rows.
-static int stem_rows(const ConvGeom& g)
-{
-    int rows_out = (255 + g.ow - 1) / g.ow + 1;
-    rows_out = rows_out < g.oh ? rows_out : g.oh;
-    return (rows_out - 1) * g.stride + 3;
-}
-
-// Staged rows at a pitch of whole 64-quad loads.
-static size_t stem_lds(const ConvGeom& g)
-{
-    const long pitch = 256L * ((g.w / 4 + 63) / 64);
-    return (size_t)g.cin * stem_rows(g) * pitch * sizeof(float);
-}
+// Output channels per stem workgroup: 16 when there are enough channels to
+// share each window's loads, else 8 (more workgroups for a 16-channel stem).
+int stem_cob(const ConvGeom& g) { return g.cout >= 32 ? 16 : 8; }
 
 bool stem_shape(const ConvGeom& g)
 {
     return g.groups == 1 && g.k == 3 && g.pad == 1 && (g.stride == 1 || g.stride == 2) &&
            (g.cin == 1 || g.cin == 3) && g.w % 4 == 0 && g.ow % 4 == 0 && g.w == g.ow * g.stride &&
-           stem_lds(g) <= kMaxLdsBytes;
+           (long)g.n * g.cin * g.h * g.w * 4 < 0x7fffffffL && (long)g.n * g.cout * g.oh * g.ow * 4 < 0x7fffffffL;
 }
 
 static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <int CIN>
-static void launch_stem_cin(const ConvGeom& g, dim3 grid, hipStream_t s, const float* x,
-                            const float* w, const float* scale, const float* bias, const float* res,
-                            float* y)
+void fastdiv_params(int d, unsigned* m, unsigned* l);
+
+template <int CIN, int COB>
+static void launch_stem_cin(const ConvGeom& g, hipStream_t s, const float* x, const float* w,
+                            const float* scale, const float* bias, const float* res, float* y)
 {
-    const size_t lds = stem_lds(g);
-    const int nrows = stem_rows(g);
+    const int qrow = g.ow / 4;
+    const int Q = g.oh * qrow;
+    const int nquads = g.n * Q;
+    unsigned m_q, l_q, m_r, l_r;
+    fastdiv_params(Q, &m_q, &l_q);
+    fastdiv_params(qrow, &m_r, &l_r);
+    const unsigned xb = (unsigned)((long)g.n * g.cin * g.h * g.w * 4);
+    const unsigned yb = (unsigned)((long)g.n * g.cout * g.oh * g.ow * 4);
+    dim3 grid((unsigned)((nquads + kStemThreads - 1) / kStemThreads), (unsigned)((g.cout + COB - 1) / COB));
     if (g.stride == 2)
-        hipLaunchKernelGGL((k_stem<CIN, kStemCob, 2>), grid, dim3(kStemThreads), lds, s, x, w, scale, bias, res,
-                           y, g.h, g.w, g.cout, g.oh, g.ow, nrows, g.act, g.res_mode);
+        hipLaunchKernelGGL((k_stem<CIN, COB, 2>), grid, dim3(kStemThreads), 0, s, x, w, scale, bias, res, y,
+                           nquads, g.h, g.w, g.cout, g.oh * g.ow, qrow, Q, m_q, l_q, m_r, l_r, xb, yb, g.act,
+                           g.res_mode);
     else
-        hipLaunchKernelGGL((k_stem<CIN, kStemCob, 1>), grid, dim3(kStemThreads), lds, s, x, w, scale, bias, res,
-                           y, g.h, g.w, g.cout, g.oh, g.ow, nrows, g.act, g.res_mode);
+        hipLaunchKernelGGL((k_stem<CIN, COB, 1>), grid, dim3(kStemThreads), 0, s, x, w, scale, bias, res, y,
+                           nquads, g.h, g.w, g.cout, g.oh * g.ow, qrow, Q, m_q, l_q, m_r, l_r, xb, yb, g.act,
+                           g.res_mode);
 }
 
 hipError_t launch_direct(const ConvGeom& g, const Plan& p, const float* x, const float* w,
@@ -251,12 +266,14 @@ hipError_t launch_direct(const ConvGeom& g, const Plan& p, const float* x, const
     const int cout_g = g.cout / g.groups;
     const int ohw = g.oh * g.ow;
     if (p.direct_stem && al16(x) && al16(y) && (res == nullptr || al16(res))) {
-        dim3 grid((unsigned)((g.oh * g.ow + 255) / 256), (unsigned)((g.cout + kStemCob - 1) / kStemCob),
-                  (unsigned)g.n);
-        if (g.cin == 1)
-            launch_stem_cin<1>(g, grid, s, x, w, scale, bias, res, y);
-        else
-            launch_stem_cin<3>(g, grid, s, x, w, scale, bias, res, y);
+        const bool c16 = stem_cob(g) == 16;
+        if (g.cin == 1) {
+            if (c16) launch_stem_cin<1, 16>(g, s, x, w, scale, bias, res, y);
+            else launch_stem_cin<1, 8>(g, s, x, w, scale, bias, res, y);
+        } else {
+            if (c16) launch_stem_cin<3, 16>(g, s, x, w, scale, bias, res, y);
+            else launch_stem_cin<3, 8>(g, s, x, w, scale, bias, res, y);
+        }
         return hipGetLastError();
     }
     const int cob = p.direct_cob;

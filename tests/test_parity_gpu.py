@@ -551,19 +551,21 @@ def test_split_layer_graph_replays(monkeypatch):
         assert torch.equal(y, eager), f"replay {i}"
 
 
-STEM_CASES = [(cin, s, res) for cin in (1, 3) for s in (1, 2)
-              for res in (wl.RES_NONE, wl.RES_BEFORE_ACT, wl.RES_AFTER_ACT)]
+STEM_CASES = [(cin, s, res, 20) for cin in (1, 3) for s in (1, 2)
+              for res in (wl.RES_NONE, wl.RES_BEFORE_ACT, wl.RES_AFTER_ACT)] + \
+             [(cin, s, wl.RES_AFTER_ACT, 40) for cin in (1, 3) for s in (1, 2)]
 
 
-@pytest.mark.parametrize("cin,stride,res_mode", STEM_CASES,
-                         ids=[f"c{c}s{s}r{r}" for c, s, r in STEM_CASES])
-def test_stem_kernel(cin, stride, res_mode):
+@pytest.mark.parametrize("cin,stride,res_mode,cout", STEM_CASES,
+                         ids=[f"c{c}s{s}r{r}o{o}" for c, s, r, o in STEM_CASES])
+def test_stem_kernel(cin, stride, res_mode, cout):
     """The stem kernel (3x3 pad 1, 1 or 3 input channels, widths a multiple of 4):
-    20 output channels (a partial group of 8), a frame whose borders are all
-    padding, batch 2; then the same layer on an input 4 bytes off alignment, which
-    the generic direct kernel takes."""
-    seed = 240 + 10 * cin + stride + 3 * res_mode
-    n, h, w, cout = 2, 20, 48, 20
+    20 output channels (groups of 8, the last partial) or 40 (groups of 16, the
+    last partial), a frame whose borders are all padding, batch 2 (quads are
+    numbered across images); then the same layer on an input 4 bytes off
+    alignment, which the generic direct kernel takes."""
+    seed = 240 + 10 * cin + stride + 3 * res_mode + cout
+    n, h, w = 2, 20, 48
     x, L = wl.random_conv_case(seed, n, cin, h, w, cout, 3, stride, 1, 1, wl.ACT_SILU, res_mode)
     d = cvx.make_desc(n, cin, h, w, cout, 3, stride, 1, 1, wl.ACT_SILU, res_mode, OIHW)
     plan = cvx.cvx_conv_plan(d)
