@@ -53,6 +53,23 @@ __device__ __forceinline__ void warm_kernargs()
     asm volatile("" ::"s"(v));
 }
 
+// Waits until at most n of this wave's vector-memory operations are outstanding
+// (loads complete in issue order), leaving the other counters alone.  The count
+// is an immediate, so one instruction per value; above 35 it waits for all.
+__device__ __forceinline__ void wait_vm_at_most(int n)
+{
+#define CVX_VM(k) \
+    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+    switch (n) {
+        CVX_VM(0) CVX_VM(1) CVX_VM(2) CVX_VM(3) CVX_VM(4) CVX_VM(5) CVX_VM(6) CVX_VM(7) CVX_VM(8) CVX_VM(9)
+        CVX_VM(10) CVX_VM(11) CVX_VM(12) CVX_VM(13) CVX_VM(14) CVX_VM(15) CVX_VM(16) CVX_VM(17) CVX_VM(18)
+        CVX_VM(19) CVX_VM(20) CVX_VM(21) CVX_VM(22) CVX_VM(23) CVX_VM(24) CVX_VM(25) CVX_VM(26) CVX_VM(27)
+        CVX_VM(28) CVX_VM(29) CVX_VM(30) CVX_VM(31) CVX_VM(32) CVX_VM(33) CVX_VM(34) CVX_VM(35)
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+#undef CVX_VM
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads in flight stay
 // in flight across it (a plain __syncthreads() also waits for those).
 __device__ __forceinline__ void lds_barrier()

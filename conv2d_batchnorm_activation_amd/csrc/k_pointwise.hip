@@ -51,23 +51,6 @@ __device__ __forceinline__ int pw_div(int n, unsigned m, unsigned l)
     return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> l);
 }
 
-// Waits until at most n of this wave's vector-memory loads are outstanding (loads
-// complete in order), leaving the other counters alone.  The count is an
-// immediate, so one instruction per value.
-__device__ __forceinline__ void pw_wait_vm(int n)
-{
-#define PW_VM(k) \
-    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
-    switch (n) {
-        PW_VM(0) PW_VM(1) PW_VM(2) PW_VM(3) PW_VM(4) PW_VM(5) PW_VM(6) PW_VM(7) PW_VM(8) PW_VM(9)
-        PW_VM(10) PW_VM(11) PW_VM(12) PW_VM(13) PW_VM(14) PW_VM(15) PW_VM(16) PW_VM(17) PW_VM(18)
-        PW_VM(19) PW_VM(20) PW_VM(21) PW_VM(22) PW_VM(23) PW_VM(24) PW_VM(25) PW_VM(26) PW_VM(27)
-        PW_VM(28) PW_VM(29) PW_VM(30) PW_VM(31) PW_VM(32) PW_VM(33) PW_VM(34) PW_VM(35)
-        default: __builtin_amdgcn_s_waitcnt(0); break;
-    }
-#undef PW_VM
-}
-
 // Keeps the compiler from moving memory operations across this point (the
 // waits above count loads in issue order).
 __device__ __forceinline__ void pw_order()
@@ -206,17 +189,20 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
         };
 
         // Stage buffers: chunk s is in buffer s % 3.  The consumers read chunk s
-        // between barriers s-1 and s, so its buffer takes chunk s+3 right after
-        // barrier s; barrier s needs chunk s+1 landed.  Chunks are thus issued
-        // two barriers before they are needed.
+        // between barriers s-1 and s (chunk 0 between an opening barrier and
+        // barrier 0), so its buffer takes chunk s+3 right after barrier s;
+        // barrier s needs chunk s+1 landed.  Chunks are thus issued two barriers
+        // before they are needed.
         auto bufof = [&](int s3) { return (s3 % 3) * BUF; };
         pw_order();
         issue(0, 0);
         if (nst > 1) issue(1, BUF);
         if (nst > 2) issue(2, 2 * BUF);
         pw_order();
-        pw_wait_vm(nst > 2 ? nld : 0);  // chunks 0 and 1
-        lds_barrier();
+        wait_vm_at_most(nld * (min(nst, 3) - 1));  // chunk 0
+        lds_barrier();                              // opening barrier
+        wait_vm_at_most(nst > 2 ? nld : 0);         // chunk 1
+        lds_barrier();                              // barrier 0
         int rdone = 0;
         for (int st = 1; st < nst; ++st) {
             // after barrier st-1: the buffer of chunk st-1 is free
@@ -231,7 +217,7 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
             const bool more = st + 2 < nst;
             if (more) issue(st + 2, bufof(st + 2));
             pw_order();
-            pw_wait_vm(piece + (more ? nld : 0));  // chunk st+1 (and every earlier load)
+            wait_vm_at_most(piece + (more ? nld : 0));  // chunk st+1 (and every earlier load)
             lds_barrier();
         }
         if (want_res) load_res(rdone, a.rq);
@@ -347,9 +333,10 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
     };
     auto nextb = [&](int b) { return b == 2 * BUF ? 0 : b + BUF; };
     Ops o0, o1;
-    lds_barrier();  // barrier 0: chunks 0 and 1 have landed
+    lds_barrier();  // opening barrier: chunk 0 has landed
 #pragma unroll
     for (int k = 0; k < 8; ++k) read_pair(0, o0, k);
+    lds_barrier();  // barrier 0: chunk 1 has landed, chunk 0's buffer is read
     int sb = 0;     // buffer of chunk st
     for (int st = 0;;) {
         // chunk st in o0
