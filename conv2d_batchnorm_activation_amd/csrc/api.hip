@@ -84,6 +84,22 @@ bool plan_depthwise(const ConvGeom& g, Plan* p)
         (long)planes * ohw * 4 < 0x7fffffffL) {
         const int cap = std::max(4, std::min(64, (int)(8192 / ((long)g.h * g.w))) & ~3);
         const int want = ((planes + 2047) / 2048 + 3) & ~3;  // ~8 workgroups per compute unit
+        // Widths with a row-strip instance: the same size class, rounded down to
+        // a divisor of C so that a workgroup's channels (and their weights, scales
+        // and biases) are one run.
+        // (Few large planes go to the plane kernel below, which spreads one
+        // plane over the whole workgroup.)
+        if (dw_rows_shape(g) && !(g.oh * g.ow >= 192 && (long)planes < 4L * 256)) {
+            int ppb = std::max(1, std::min(cap, want));
+            while (g.cout % ppb != 0) --ppb;
+            if (dw_rows_lds_bytes(g, ppb) <= kMaxLdsBytes) {
+                p->dw_ppb = ppb;
+                p->dw_toh = -1;
+                p->fam = FAM_DEPTHWISE;
+                p->ws_bytes = 0;
+                return true;
+            }
+        }
         int ppb = std::max(4, std::min(cap, want));
         // large planes with few of them: a plane per workgroup (all waves on it)
         if (g.oh * g.ow >= 192 && (long)planes < 4L * 256) ppb = 1;
@@ -428,7 +444,12 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
         break;
     case FAM_POINTWISE: pointwise_describe(g, buf, buf_len); break;
     case FAM_DEPTHWISE:
-        if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
+        if (p.dw_toh == -1) {  // named as launched on 16-byte aligned tensors
+            const int hw = g.h * g.w;
+            const int vw = g.w % 4 == 0 && hw % 4 == 0 ? 4 : g.w % 2 == 0 && hw % 2 == 0 ? 2 : 1;
+            snprintf(buf, buf_len, "depthwise3x3 s%d rows ppb=%d splitk=1 kernel=cvx::k_dw_rows<%d, %d, %d>",
+                     g.stride, p.dw_ppb, g.w, g.stride, vw);
+        } else if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
             snprintf(buf, buf_len, "depthwise3x3 s%d planes ppb=%d splitk=1 kernel=cvx::k_dw_planes<%d, 1, 1, %d>",
                      g.stride, p.dw_ppb, g.stride, g.oh * g.ow <= 256 ? 4 : 0);
         else

@@ -38,7 +38,7 @@ struct Plan {
     Family fam;
     GemmTile tile;     // FAM_IGEMM only
     int dw_ppb;        // FAM_DEPTHWISE: planes per workgroup
-    int dw_toh;        // FAM_DEPTHWISE: output rows per workgroup
+    int dw_toh;        // FAM_DEPTHWISE: output rows per workgroup (0: plane kernel, -1: row-strip kernel)
     int direct_cob;    // FAM_DIRECT: output channels per thread
     int direct_stem;   // FAM_DIRECT: the stem kernel (k_stem) when tensors are 16-byte aligned
     size_t ws_bytes;   // workspace the plan needs
@@ -70,6 +70,9 @@ bool stem_shape(const ConvGeom& g);
 int stem_cob(const ConvGeom& g);
 // LDS bytes of the depthwise plane kernel for `ppb` planes per workgroup.
 size_t dw_planes_lds_bytes(const ConvGeom& g, int ppb);
+// The depthwise row-strip kernel (known widths, pad 1) and its LDS bytes.
+bool dw_rows_shape(const ConvGeom& g);
+size_t dw_rows_lds_bytes(const ConvGeom& g, int ppb);
 
 hipError_t launch_gap_fc(const float* x, int n, int c, int hw, const float* fc_w,
                          const float* fc_b, int out_f, float* out, hipStream_t s);

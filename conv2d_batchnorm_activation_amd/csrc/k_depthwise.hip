@@ -208,6 +208,7 @@ __global__ void __launch_bounds__(256) k_dw_planes(
             const float* tp = tile + pl * HW;
 #pragma unroll
             for (int k = 0; k < KM; ++k) {
+                if (64 * k >= OHW) break;  // uniform: blocks of 64 outputs the plane has
                 float acc = 0.0f;
 #pragma unroll
                 for (int kh = 0; kh < 3; ++kh)
@@ -282,6 +283,182 @@ __global__ void __launch_bounds__(256) k_dw_planes(
     }
 }
 
+// Row strips for the small planes of known widths (7, 13, 14, 28; pad 1, stride
+// 1 or 2): a lane takes one output row of one plane and, for each of its three
+// input rows, reads the row once (VW floats per LDS read) and feeds all OW
+// outputs of the row from registers -- about three LDS reads per output instead
+// of nine.  64 / OH planes share a wave.  The workgroup's planes are a run of
+// consecutive channels (`ppb` divides C), so their weights, scales and biases
+// are runs too and come to LDS with LDS-direct loads together with the input:
+// no register round trip before the arithmetic starts.  Rows outside the plane
+// contribute nothing (a select on the row's partial sums; the columns' zero
+// padding is known at compile time).  The output run and its store are those
+// of the plane kernel.
+template <int W, int S, int VW>
+__global__ void __launch_bounds__(256) k_dw_rows(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ scale,
+    const float* __restrict__ bias, const float* __restrict__ res, float* __restrict__ y,
+    int planes, int C, int H, int OH, int ppb, int obuf_off, int prm_off, unsigned m_oh,
+    unsigned l_oh, int vec, int vout, int act, int res_mode)
+{
+    constexpr int OW = (W - 1) / S + 1;  // pad 1
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int plane0 = blockIdx.x * ppb;
+    const int np = min(ppb, planes - plane0);
+    const int ch0 = plane0 - (plane0 / C) * C;  // the run's first channel; ppb divides C
+    const int HW = H * W;
+    const int n = np * HW;
+    {
+        // the planes' run
+        const rsrc_t rx = make_rsrc(x, 4u * (unsigned)(planes * HW));
+        const unsigned base = 4u * (unsigned)(plane0 * HW);
+        if (vec) {
+            const int rounds = (((n + 3) >> 2) + 255) >> 8;
+            for (int i = 0; i < rounds; ++i) {
+                const int q = t + 256 * i;
+                int d = 1024 * i + 256 * wave;
+                asm volatile("" : "+s"(d));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(lds + d), 16,
+                                                         4 * q < n ? base + 16u * (unsigned)q : kOOB, 0, 0, 0);
+            }
+        } else {
+            const int rounds = (n + 255) >> 8;
+            for (int i = 0; i < rounds; ++i) {
+                const int e = t + 256 * i;
+                int d = 256 * i + 64 * wave;
+                asm volatile("" : "+s"(d));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(lds + d), 4,
+                                                         e < n ? base + 4u * (unsigned)e : kOOB, 0, 0, 0);
+            }
+        }
+        // weights [pl][9], scales [pl], biases [pl], each region whole rounds of
+        // 256 floats (lanes past a run still write their slot, with zero)
+        const int wr = (9 * ppb + 255) >> 8, sr = (ppb + 255) >> 8;
+        const rsrc_t rw = make_rsrc(w + ch0 * 9, 36u * (unsigned)np);
+        for (int i = 0; i < wr; ++i) {
+            const int e = t + 256 * i;
+            int d = prm_off + 256 * i + 64 * wave;
+            asm volatile("" : "+s"(d));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(lds + d), 4,
+                                                     e < 9 * np ? 4u * (unsigned)e : kOOB, 0, 0, 0);
+        }
+        const rsrc_t rs = make_rsrc(scale + ch0, 4u * (unsigned)np);
+        const rsrc_t rb = make_rsrc(bias + ch0, 4u * (unsigned)np);
+        for (int i = 0; i < sr; ++i) {
+            const int e = t + 256 * i;
+            int d = prm_off + 256 * (wr + i) + 64 * wave;
+            asm volatile("" : "+s"(d));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + d), 4,
+                                                     e < np ? 4u * (unsigned)e : kOOB, 0, 0, 0);
+            int d2 = prm_off + 256 * (wr + sr + i) + 64 * wave;
+            asm volatile("" : "+s"(d2));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(lds + d2), 4,
+                                                     e < np ? 4u * (unsigned)e : kOOB, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int OHW = OH * OW;
+    float* const obuf = lds + obuf_off;
+    const float* const wts = lds + prm_off;
+    const float* const scs = wts + 256 * ((9 * ppb + 255) >> 8);
+    const float* const bis = scs + 256 * ((ppb + 255) >> 8);
+    const int ppw = 64 / OH;  // planes per wave pass (the host keeps OH <= 64)
+    const int lp = (int)((__umulhi((unsigned)lane, m_oh) + (unsigned)lane) >> l_oh);
+    const int oy = lane - lp * OH;
+    for (int pl0 = wave * ppw; pl0 < np; pl0 += 4 * ppw) {
+        const int pl = min(pl0 + lp, np - 1);
+        const bool live = lp < ppw && pl0 + lp < np;
+        float wk[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) wk[k] = wts[pl * 9 + k];
+        const float sc = scs[pl], bi = bis[pl];
+        float acc[OW];
+#pragma unroll
+        for (int o = 0; o < OW; ++o) acc[o] = 0.0f;
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int ih = oy * S - 1 + kh;
+            const bool rok = (unsigned)ih < (unsigned)H;
+            const float* rp = lds + pl * HW + (rok ? ih : 0) * W;
+            float r[W];
+#pragma unroll
+            for (int c = 0; c < W; c += VW) {
+                if constexpr (VW == 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(rp + c);
+                    r[c] = v[0]; r[c + 1] = v[1]; r[c + 2] = v[2]; r[c + 3] = v[3];
+                } else if constexpr (VW == 2) {
+                    typedef float f32x2 __attribute__((ext_vector_type(2)));
+                    const f32x2 v = *reinterpret_cast<const f32x2*>(rp + c);
+                    r[c] = v[0]; r[c + 1] = v[1];
+                } else {
+                    r[c] = rp[c];
+                }
+            }
+#pragma unroll
+            for (int o = 0; o < OW; ++o) {
+                float racc = 0.0f;
+#pragma unroll
+                for (int kw = 0; kw < 3; ++kw) {
+                    const int c = o * S - 1 + kw;
+                    if (c >= 0 && c < W) racc = fmaf(wk[kh * 3 + kw], r[c], racc);
+                }
+                acc[o] += rok ? racc : 0.0f;
+            }
+        }
+        if (live) {
+            float* op = obuf + pl * OHW + oy * OW;
+#pragma unroll
+            for (int o = 0; o < OW; ++o) op[o] = fmaf(sc, acc[o], bi);
+        }
+    }
+    __syncthreads();
+
+    // The output run: residual, activation, store (as the plane kernel).
+    const unsigned out_bytes = 4u * (unsigned)(planes * OHW);
+    const rsrc_t ry = make_rsrc(y, out_bytes);
+    const rsrc_t rr = make_rsrc(res, res_mode != CVX_RES_NONE ? out_bytes : 0u);
+    const unsigned obase = 4u * (unsigned)(plane0 * OHW);
+    const int m = np * OHW;
+    auto fin = [&](float z, float rv) {
+        if (res_mode == CVX_RES_BEFORE_ACT) z += rv;
+        z = apply_act_fast(z, act);
+        if (res_mode == CVX_RES_AFTER_ACT) z += rv;
+        return z;
+    };
+    if (vout) {
+        for (int q = t; 4 * q < m; q += 256) {
+            const unsigned off = obase + 16u * (unsigned)q;
+            f32x4 rv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (res_mode != CVX_RES_NONE)
+                rv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)off, 0, 0));
+            const f32x4 z = *reinterpret_cast<const f32x4*>(obuf + 4 * q);
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fin(z[e], rv[e]);
+            if (4 * q + 4 <= m) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry, (int)off, 0, 0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f = v[e];
+                    if (4 * q + e < m) bstore(ry, off + 4u * e, f);
+                }
+            }
+        }
+    } else {
+        for (int j = t; j < m; j += 256) {
+            const unsigned off = obase + 4u * (unsigned)j;
+            const float rv = res_mode != CVX_RES_NONE ? bload(rr, off) : 0.0f;
+            bstore(ry, off, fin(obuf[j], rv));
+        }
+    }
+}
+
 void fastdiv_params(int d, unsigned* m, unsigned* l);
 
 // Zeroed floats before and after the plane kernel's staged run: taps reach
@@ -310,11 +487,61 @@ size_t dw_planes_lds_bytes(const ConvGeom& g, int ppb)
 
 static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The row-strip kernel's shapes: pad 1, widths with a compiled instance, at most
+// 64 output rows (a plane's rows fit one wave).
+bool dw_rows_shape(const ConvGeom& g)
+{
+    if (g.pad != 1 || g.oh > 64) return false;
+    if (g.stride == 1) return g.w == 7 || g.w == 13 || g.w == 14 || g.w == 28;
+    if (g.stride == 2) return g.w == 14 || g.w == 28;
+    return false;
+}
+
+// LDS floats of the row kernel: the staged run (whole 1 KB loads), the output
+// run, then weights [ppb][9], scales and biases.
+static size_t dw_rows_run_floats(const ConvGeom& g, int ppb)
+{
+    const long n = (long)ppb * g.h * g.w;
+    return (size_t)((n + 1023) / 1024 * 1024);
+}
+
+size_t dw_rows_lds_bytes(const ConvGeom& g, int ppb)
+{
+    const size_t wr = (9 * (size_t)ppb + 255) / 256, sr = ((size_t)ppb + 255) / 256;
+    return (dw_rows_run_floats(g, ppb) + (((size_t)ppb * g.oh * g.ow + 3) & ~(size_t)3) +
+            256 * (wr + 2 * sr)) * sizeof(float);
+}
+
 hipError_t launch_depthwise(const ConvGeom& g, const Plan& p, const float* x, const float* w,
                             const float* scale, const float* bias, const float* res, float* y,
                             hipStream_t s)
 {
     const int planes = g.n * g.cout;
+    if (p.dw_toh == -1) {  // row-strip kernel
+        const int ppb = p.dw_ppb;
+        const int vec = al16(x) && ((long)ppb * g.h * g.w) % 4 == 0;
+        const int vout = al16(y) && (res == nullptr || al16(res)) && ((long)ppb * g.oh * g.ow) % 4 == 0;
+        const int obuf_off = (int)dw_rows_run_floats(g, ppb);
+        const int prm_off = obuf_off + (int)((((size_t)ppb * g.oh * g.ow + 3) & ~(size_t)3));
+        const size_t lds = dw_rows_lds_bytes(g, ppb);
+        unsigned m_oh, l_oh;
+        fastdiv_params(g.oh, &m_oh, &l_oh);
+        dim3 grid((unsigned)((planes + ppb - 1) / ppb));
+        const int hw = g.h * g.w;
+#define CVX_DWR(W_, S_, VW_)                                                                        \
+    hipLaunchKernelGGL((k_dw_rows<W_, S_, VW_>), grid, dim3(256), lds, s, x, w, scale, bias, res, y,  \
+                       planes, g.cout, g.h, g.oh, ppb, obuf_off, prm_off, m_oh, l_oh, vec, vout, g.act, \
+                       g.res_mode)
+        if (g.stride == 1 && g.w == 7) CVX_DWR(7, 1, 1);
+        else if (g.stride == 1 && g.w == 13) CVX_DWR(13, 1, 1);
+        else if (g.stride == 1 && g.w == 14) { if (hw % 2 == 0) CVX_DWR(14, 1, 2); else CVX_DWR(14, 1, 1); }
+        else if (g.stride == 1 && g.w == 28) { if (hw % 4 == 0) CVX_DWR(28, 1, 4); else CVX_DWR(28, 1, 1); }
+        else if (g.stride == 2 && g.w == 14) { if (hw % 2 == 0) CVX_DWR(14, 2, 2); else CVX_DWR(14, 2, 1); }
+        else if (g.stride == 2 && g.w == 28) { if (hw % 4 == 0) CVX_DWR(28, 2, 4); else CVX_DWR(28, 2, 1); }
+        else return hipErrorInvalidValue;
+#undef CVX_DWR
+        return hipGetLastError();
+    }
     if (p.dw_toh == 0) {  // plane kernel
         // 16-byte staging needs every run to start on a 16-byte boundary
         const bool vec = al16(x) && ((long)p.dw_ppb * g.h * g.w) % 4 == 0;

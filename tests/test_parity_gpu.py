@@ -196,7 +196,9 @@ CASES = [
     (33, 1, 4, 64, 300, 4, 3, 1, 1, 4, R, 0),      # band path (large plane)
     (34, 1, 3, 97, 41, 3, 3, 2, 1, 3, A, AF),      # plane path, 4 planes of 3977 floats
     (37, 1, 3, 97, 83, 3, 3, 2, 1, 3, A, AF),      # band path, stride 2, odd sizes
-    (38, 3, 5, 7, 7, 5, 3, 1, 1, 5, R, B4),        # plane path, odd plane size (49)
+    (38, 3, 5, 7, 7, 5, 3, 1, 1, 5, R, B4),        # row strips, 49-float planes, 5 channels
+    (39, 2, 8, 10, 14, 8, 3, 2, 1, 8, A, AF),      # row strips, 14-wide stride 2, H != W
+    (46, 3, 12, 5, 28, 12, 3, 1, 1, 12, N_, B4),   # row strips, 28-wide rows, 16-byte reads
     (35, 2, 5, 1, 1, 5, 3, 1, 1, 5, R, 0),
     (36, 1, 6, 8, 8, 6, 3, 2, 0, 6, A, 0),         # no padding
     # direct (tiny c_in, grouped, large kernels)
@@ -401,16 +403,17 @@ def test_split_reduction_workspace_contents_ignored(fill, monkeypatch):
                 assert np.array_equal(first, y), "split reduction is not deterministic"
 
 
-@pytest.mark.parametrize("hw", [(7, 7), (14, 14)], ids=["7x7", "14x14"])
+@pytest.mark.parametrize("hw", [(7, 7), (14, 14), (28, 28), (9, 11)], ids=["7x7", "14x14", "28x28", "9x11"])
 def test_depthwise_misaligned_input(hw):
-    """The depthwise plane kernel on an input 4 bytes off a 16-byte boundary
-    stages with 4-byte loads and gives the same result."""
+    """The depthwise small-plane kernels (row strips for the widths they are
+    compiled for, the plane kernel otherwise) on an input 4 bytes off a 16-byte
+    boundary stage with 4-byte loads and give the same result."""
     h, w = hw
     seed, n, c = 230 + h, 3, 12
     x, L = wl.random_conv_case(seed, n, c, h, w, c, 3, 1, 1, c, wl.ACT_RELU, wl.RES_BEFORE_ACT)
     d = cvx.make_desc(n, c, h, w, c, 3, 1, 1, c, wl.ACT_RELU, wl.RES_BEFORE_ACT, OIHW)
     plan = cvx.cvx_conv_plan(d)
-    assert "k_dw_planes" in plan, plan
+    assert "k_dw_planes" in plan or "k_dw_rows" in plan, plan
     r = wl.residual_for(seed, (n, c, h, w))
     ref = oracle_conv(x, L, r)
     p = L.params
