@@ -391,7 +391,46 @@ size_t elems_w(const ConvGeom& g)
 
 }  // namespace
 
-// ====================================================================== C ABI
+// The text cvx_conv_plan returns for a planned layer.
+static void describe_plan(const ConvGeom& g, const Plan& p, char* buf, int buf_len)
+{
+    char kn[96];
+    switch (p.fam) {
+    case FAM_IGEMM_PACKED:
+        packed_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+        snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
+        break;
+    case FAM_POINTWISE: pointwise_describe(g, nullptr, buf, buf_len); break;
+    case FAM_DEPTHWISE:
+        if (p.dw_toh == -1) {  // named as launched on 16-byte aligned tensors
+            const int hw = g.h * g.w;
+            const int vw = g.w % 4 == 0 && hw % 4 == 0 ? 4 : g.w % 2 == 0 && hw % 2 == 0 ? 2 : 1;
+            snprintf(buf, buf_len, "depthwise3x3 s%d rows ppb=%d splitk=1 kernel=cvx::k_dw_rows<%d, %d, %d>",
+                     g.stride, p.dw_ppb, g.w, g.stride, vw);
+        } else if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
+            snprintf(buf, buf_len, "depthwise3x3 s%d planes ppb=%d splitk=1 kernel=cvx::k_dw_planes<%d, 1, 1, %d>",
+                     g.stride, p.dw_ppb, g.stride, g.oh * g.ow <= 256 ? 4 : 0);
+        else
+            snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d splitk=1 kernel=cvx::k_depthwise3x3<%d>",
+                     g.stride, p.dw_ppb, p.dw_toh, g.stride);
+        break;
+    case FAM_DIRECT:
+        if (p.direct_stem)
+            snprintf(buf, buf_len, "stem k3 s%d splitk=1 kernel=cvx::k_stem<%d, %d, %d>", g.stride,
+                     g.cin, stem_cob(g), g.stride);
+        else
+            snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
+                     g.stride, p.direct_cob, p.direct_cob);
+        break;
+    case FAM_IGEMM:
+        igemm_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+        snprintf(buf, buf_len, "igemm_mfma k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
+                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
+        break;
+    }
+}
+
 extern "C" {
 
 const char* cvx_status_str(cvx_status s)
@@ -435,41 +474,7 @@ cvx_status cvx_conv_plan(const cvx_conv_desc* d, char* buf, int buf_len)
     Plan p;
     st = make_plan(g, &p);
     if (st != CVX_OK) return st;
-    char kn[96];
-    switch (p.fam) {
-    case FAM_IGEMM_PACKED:
-        packed_kernel_name(g, p.tile.kind, kn, sizeof(kn));
-        snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
-                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
-        break;
-    case FAM_POINTWISE: pointwise_describe(g, buf, buf_len); break;
-    case FAM_DEPTHWISE:
-        if (p.dw_toh == -1) {  // named as launched on 16-byte aligned tensors
-            const int hw = g.h * g.w;
-            const int vw = g.w % 4 == 0 && hw % 4 == 0 ? 4 : g.w % 2 == 0 && hw % 2 == 0 ? 2 : 1;
-            snprintf(buf, buf_len, "depthwise3x3 s%d rows ppb=%d splitk=1 kernel=cvx::k_dw_rows<%d, %d, %d>",
-                     g.stride, p.dw_ppb, g.w, g.stride, vw);
-        } else if (p.dw_toh == 0)  // named as launched on a 16-byte aligned input
-            snprintf(buf, buf_len, "depthwise3x3 s%d planes ppb=%d splitk=1 kernel=cvx::k_dw_planes<%d, 1, 1, %d>",
-                     g.stride, p.dw_ppb, g.stride, g.oh * g.ow <= 256 ? 4 : 0);
-        else
-            snprintf(buf, buf_len, "depthwise3x3 s%d ppb=%d toh=%d splitk=1 kernel=cvx::k_depthwise3x3<%d>",
-                     g.stride, p.dw_ppb, p.dw_toh, g.stride);
-        break;
-    case FAM_DIRECT:
-        if (p.direct_stem)
-            snprintf(buf, buf_len, "stem k3 s%d splitk=1 kernel=cvx::k_stem<%d, %d, %d>", g.stride,
-                     g.cin, stem_cob(g), g.stride);
-        else
-            snprintf(buf, buf_len, "direct k%d s%d cob=%d splitk=1 kernel=cvx::k_direct<%d>", g.k,
-                     g.stride, p.direct_cob, p.direct_cob);
-        break;
-    case FAM_IGEMM:
-        igemm_kernel_name(g, p.tile.kind, kn, sizeof(kn));
-        snprintf(buf, buf_len, "igemm_mfma k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
-                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
-        break;
-    }
+    describe_plan(g, p, buf, buf_len);
     return CVX_OK;
 }
 
@@ -628,6 +633,8 @@ struct NodePlan {
     Plan p;
     bool fuse_next;      // GAP whose only reader is the following FC: run as one kernel
     bool skipped;        // FC folded into the preceding GAP
+    bool merged;         // 1x1 shortcut computed inside its reader's kernel: no output
+    int pair;            // the merged shortcut this layer computes with its own product, or -1
     int last_use;        // last layer index reading this output
     size_t offset;       // workspace offset of the output (non-final layers)
 };
@@ -664,6 +671,7 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         const cvx_layer& l = L[i];
         NodePlan& np = lp->nodes[i];
         np.last_use = i;
+        np.pair = -1;
         if (l.kind < CVX_L_CONV || l.kind > CVX_L_PREPROC) return CVX_ERR_ARG;
         if (l.in < CVX_INPUT || l.in >= i) return CVX_ERR_ARG;
         if (l.kind == CVX_L_PREPROC) {
@@ -727,13 +735,41 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
             lp->nodes[i + 1].skipped = true;
         }
     }
+    // A 1x1 shortcut convolution (BN, no activation) whose one reader is a
+    // later pointwise layer adding it before its activation: both are one
+    // product over the two inputs' channels (k_pointwise with two sources), and
+    // the shortcut's output is never written.  Both inputs are intermediate
+    // outputs (256-byte aligned) and so is the result, as the kernel needs.
+    std::vector<int> readers(nl, 0);
+    for (int i = 0; i < nl; ++i) {
+        if (L[i].kind == CVX_L_PREPROC) continue;
+        if (L[i].in >= 0) ++readers[L[i].in];
+        if (L[i].kind == CVX_L_CONV && L[i].conv.res_mode != CVX_RES_NONE && L[i].res >= 0) ++readers[L[i].res];
+    }
+    for (int i = 0; i + 1 < nl; ++i) {
+        const cvx_layer& l = L[i];
+        NodePlan& np = lp->nodes[i];
+        if (l.kind != CVX_L_CONV || np.p.fam != FAM_POINTWISE || l.conv.res_mode != CVX_RES_BEFORE_ACT ||
+            l.res < 0 || l.in < 0)
+            continue;
+        const int j = l.res;
+        const cvx_layer& sl = L[j];
+        NodePlan& sp = lp->nodes[j];
+        if (sl.kind != CVX_L_CONV || sp.p.fam != FAM_POINTWISE || sl.conv.act != CVX_ACT_NONE ||
+            sl.conv.res_mode != CVX_RES_NONE || sl.in < 0 || readers[j] != 1 || sp.merged || sp.pair >= 0)
+            continue;
+        if (!pointwise_pair_fits(np.g, sp.g)) continue;
+        sp.merged = true;
+        np.pair = j;
+        lp->nodes[sl.in].last_use = std::max(lp->nodes[sl.in].last_use, i);
+    }
     // first-fit placement of intermediate outputs over their live ranges
     lp->act_bytes = 0;
     lp->layer_ws = 0;
     std::vector<int> placed;
     for (int i = 0; i < nl - 1; ++i) {
         NodePlan& np = lp->nodes[i];
-        if (np.fuse_next) {  // pooled vector never materialised
+        if (np.fuse_next || np.merged) {  // pooled vector / shortcut never materialised
             np.offset = 0;
             continue;
         }
@@ -786,6 +822,50 @@ size_t cvx_forward_workspace_bytes(const cvx_layer* layers, int n_layers, cvx_st
     return st == CVX_OK ? lp.total() : 0;
 }
 
+cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, int buf_len)
+{
+    if (buf == nullptr || buf_len < 1) return CVX_ERR_NULL;
+    ListPlan lp;
+    cvx_status st = plan_list(layers, n_layers, &lp);
+    if (st != CVX_OK) return st;
+    int pos = 0;
+    buf[0] = '\0';
+    for (int i = 0; i < n_layers && pos < buf_len - 1; ++i) {
+        const cvx_layer& l = layers[i];
+        const NodePlan& np = lp.nodes[i];
+        char line[320];
+        switch (l.kind) {
+        case CVX_L_PREPROC: snprintf(line, sizeof(line), "preprocess"); break;
+        case CVX_L_CONV:
+            if (np.merged) {
+                int into = -1;
+                for (int j = i + 1; j < n_layers; ++j)
+                    if (lp.nodes[j].pair == i) into = j;
+                snprintf(line, sizeof(line), "merged into %d", into);
+            } else if (np.pair >= 0) {
+                char d[256];
+                pointwise_describe(np.g, &lp.nodes[np.pair].g, d, sizeof(d));
+                snprintf(line, sizeof(line), "%s shortcut=%d", d, np.pair);
+            } else {
+                describe_plan(np.g, np.p, line, sizeof(line));
+            }
+            break;
+        case CVX_L_GAP:
+            snprintf(line, sizeof(line), np.fuse_next ? "gap+fc kernel=cvx::k_gap_fc" : "gap kernel=cvx::k_gap_fc");
+            break;
+        default:
+            if (np.skipped)
+                snprintf(line, sizeof(line), "merged into %d", i - 1);
+            else
+                snprintf(line, sizeof(line), "fc kernel=cvx::k_gap_fc");
+            break;
+        }
+        const int w = snprintf(buf + pos, buf_len - pos, "%s%d %s", i ? "\n" : "", i, line);
+        pos = std::min(buf_len - 1, pos + std::max(w, 0));
+    }
+    return CVX_OK;
+}
+
 cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input, float* output,
                        void* workspace, size_t ws_bytes, void* stream)
 {
@@ -833,7 +913,7 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
     for (int i = 0; i < n_layers; ++i) {
         const cvx_layer& l = layers[i];
         const NodePlan& np = lp.nodes[i];
-        if (np.skipped) continue;
+        if (np.skipped || np.merged) continue;
         hipError_t e = hipSuccess;
         cvx_status cs = CVX_OK;
         switch (l.kind) {
@@ -843,6 +923,12 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
                                   l.std, s);
             break;
         case CVX_L_CONV: {
+            if (np.pair >= 0) {
+                const cvx_layer& sl = layers[np.pair];
+                e = launch_pointwise_pair(np.g, in_ptr(l.in), l.w, l.scale, l.bias, lp.nodes[np.pair].g,
+                                          in_ptr(sl.in), sl.w, sl.scale, sl.bias, out_ptr(i), s);
+                break;
+            }
             const float* res = l.conv.res_mode != CVX_RES_NONE ? in_ptr(l.res) : nullptr;
             cs = launch_conv(np.g, np.p, in_ptr(l.in), l.w, l.scale, l.bias, res, out_ptr(i),
                              layer_ws, s);

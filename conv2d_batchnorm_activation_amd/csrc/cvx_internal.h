@@ -95,9 +95,15 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
 // workgroup; x, y and the residual 16-byte aligned at launch.
 bool pointwise_fits(const ConvGeom& g);
 bool pointwise_aligned(const float* x, const float* res, const float* y);
-void pointwise_describe(const ConvGeom& g, char* buf, int len);
+void pointwise_describe(const ConvGeom& g, const ConvGeom* g2, char* buf, int len);
 hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, const float* scale,
                             const float* bias, const float* res, float* y, hipStream_t s);
+// A 1x1 layer g and a second 1x1 convolution g2 (same batch, c_out and output
+// plane, its own input x2) in one kernel: y = act(BN(g's conv) + BN2(g2's conv)).
+bool pointwise_pair_fits(const ConvGeom& g, const ConvGeom& g2);
+hipError_t launch_pointwise_pair(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                                 const float* bias, const ConvGeom& g2, const float* x2, const float* wp2,
+                                 const float* scale2, const float* bias2, float* y, hipStream_t s);
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s);
 

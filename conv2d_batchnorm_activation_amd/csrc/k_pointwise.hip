@@ -1,6 +1,7 @@
 // k_pointwise.hip -- 1x1 convolution (stride 1 or 2, no padding) + folded
 // BatchNorm + residual + activation on fp32 matrix cores, for batches of small
-// planes.
+// planes; optionally with a second 1x1 convolution (a block's shortcut) summed
+// into the same output ahead of the activation.
 //
 // A 1x1 layer is one matrix product per image, Y[c_out][OH*OW] =
 // W[c_out][c_in] X[c_in][OH*OW] (the pointwise and shortcut layers of the
@@ -15,6 +16,12 @@
 //   * the image's CO output planes are one contiguous run of CO*OH*OW floats:
 //     the tile is written to LDS in exactly that order, then every residual
 //     load and output store moves 16 contiguous bytes per lane.
+// The reduction runs over the chunks of one or two sources, each with its own
+// input, packed weights and BatchNorm scale: a block's last 1x1 layer and its
+// shortcut convolution, whose sum the block's activation takes, are one
+// product over the channels of both.  Each source's scale multiplies its
+// weights as they are read (one multiply per weight and lane), so the sums are
+// already scaled and the epilogue only adds the biases.
 // Roles as in the packed implicit GEMM: four producer waves stage chunk st+2
 // while four consumer waves compute chunk st (three LDS buffers, one barrier
 // per chunk).  The tile's 32x32 blocks (pixel block x channel block) are split
@@ -27,6 +34,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "bufio.h"
 #include "cvx_internal.h"
@@ -52,7 +60,7 @@ __device__ __forceinline__ int pw_div(int n, unsigned m, unsigned l)
 }
 
 // Keeps the compiler from moving memory operations across this point (the
-// waits above count loads in issue order).
+// waits count loads in issue order).
 __device__ __forceinline__ void pw_order()
 {
     asm volatile("" ::: "memory");
@@ -66,36 +74,46 @@ __device__ __forceinline__ void pw_lds_load16(rsrc_t r, __attribute__((address_s
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
 }
 
-struct PwArgs {
+// One source of the reduction: its input, packed weights and BatchNorm scale,
+// and how a chunk of it is staged and read.
+struct PwSrc {
     const float* x;
     const float* wp;
     const float* scale;
-    const float* bias;
-    const float* res;
-    float* y;
-    int cin, cout, HW, OHW;
-    int groups_co;              // channel groups per image: c_out / CO
-    int CO, CB, PB;             // channels of a tile, its 32-channel blocks, its 32-pixel blocks
-    int nchunks;                // c_in / 16
-    unsigned m_g, l_g;          // divide by groups_co
+    int cin, HW, nchunks;
     // Staging of one chunk: element e (16 bytes) -> row r = e / RQ and quad e % RQ;
     // row r -> channel r / RPC, first float (r % RPC) * RSTR of that channel.
     int rounds, RE, RQ, RPC, RSTR;
     unsigned m_rq, l_rq, m_rpc, l_rpc;
-    int wrounds;
     // A staged chunk in LDS: pixel q -> (oh, ow) = divmod(q, OWD) at float
     // oh*WS + S*ow + channel*CS.
     int OWD, WS, S, CS;
     unsigned m_owd, l_owd;
+    unsigned wp_bytes;
+};
+
+struct PwArgs {
+    PwSrc src[2];               // chunks n1 .. nchunks-1 come from src[1]
+    const float* bias;
+    const float* bias2;         // the second source's bias, or null
+    const float* res;
+    float* y;
+    int cout, OHW;
+    int groups_co;              // channel groups per image: c_out / CO
+    int CO, CB, PB;             // channels of a tile, its 32-channel blocks, its 32-pixel blocks
+    int nchunks, n1;            // chunks of both sources; chunks of src[0]
+    unsigned m_g, l_g;          // divide by groups_co
+    int wrounds;
     int wpx, pb_per, cb_per;    // consumer grid: waves along pixels, blocks per wave
     int BUF, WOFF;              // floats per stage buffer, weights' offset within it
     int SPARE;                  // LDS float offset of a 16-byte slot that takes dropped sums
     int rq, rq_per;             // output quads per producer thread, residual quads loaded per chunk
-    unsigned wp_bytes;
     int act, res_mode;
 };
 
-template <int MP, int MC>
+// TWO: a second source follows the first (compiled apart, so a one-source
+// layer carries none of its arguments, registers or branches).
+template <int MP, int MC, bool TWO>
 __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -118,56 +136,81 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
         grp = L - img * a.groups_co;
     }
     const int nst = a.nchunks;
+    const int n1 = TWO ? a.n1 : a.nchunks;
     const int BUF = a.BUF;
 
     if (wave >= 4) {
         // ---------------------------------------------------------- producers
         const int ptid = tid - 256;
         const int pw = wave - 4;
-        const float* xim = a.x + (long)img * a.cin * a.HW;
-        // byte offsets of this lane's staged elements within a chunk, the same
-        // for every chunk (a stride-1 chunk is one run); past the chunk's
-        // elements an out-of-range offset
-        unsigned goff[kPwMaxRounds];
+        // byte offsets of this lane's staged elements within a chunk of each
+        // source, the same for every chunk of it (a stride-1 chunk is one run);
+        // past the chunk's elements an out-of-range offset
+        unsigned goff[2][kPwMaxRounds];
+        unsigned woff[2][kPwWRounds];
+        auto setup_src = [&](auto S) {
+            constexpr int s = decltype(S)::value;
+            const PwSrc& sr = a.src[s];
+            if (sr.RPC > 1) {
+                const int HW = sr.HW, RPC = sr.RPC, RSTR = sr.RSTR, RQ = sr.RQ, RE = sr.RE;
 #pragma unroll
-        for (int i = 0; i < kPwMaxRounds; ++i) {
-            const int e = ptid + 256 * i;
-            int f = 4 * e;
-            if (a.RPC > 1) {
-                const int r = pw_div(e, a.m_rq, a.l_rq);
-                const int c = pw_div(r, a.m_rpc, a.l_rpc);
-                f = c * a.HW + (r - c * a.RPC) * a.RSTR + 4 * (e - r * a.RQ);
+                for (int i = 0; i < kPwMaxRounds; ++i) {
+                    const int e = ptid + 256 * i;
+                    const int r = pw_div(e, sr.m_rq, sr.l_rq);
+                    const int c = pw_div(r, sr.m_rpc, sr.l_rpc);
+                    const int f = c * HW + (r - c * RPC) * RSTR + 4 * (e - r * RQ);
+                    goff[s][i] = e < RE ? 4u * (unsigned)f : kOOB;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPwMaxRounds; ++i) {
+                    const int e = ptid + 256 * i;
+                    goff[s][i] = e < sr.RE ? 16u * (unsigned)e : kOOB;
+                }
             }
-            goff[i] = e < a.RE ? 4u * (unsigned)f : kOOB;
-        }
-        // the group's weights of a chunk: CB blocks of 2 KB, kPwChunkW floats apart
-        // per chunk and nchunks * kPwChunkW apart per block
-        unsigned woff[kPwWRounds];
+            // the group's weights of a chunk: CB blocks of 2 KB, kPwChunkW floats
+            // apart per chunk and nchunks * kPwChunkW apart per block
 #pragma unroll
-        for (int j = 0; j < kPwWRounds; ++j) {
-            const int e = ptid + 256 * j;
-            const int blk = e >> 7;
-            woff[j] = blk < a.CB ? 4u * ((unsigned)((grp * a.CB + blk) * a.nchunks) * kPwChunkW +
-                                         4u * (unsigned)(e & 127))
-                                 : kOOB;
+            for (int j = 0; j < kPwWRounds; ++j) {
+                const int e = ptid + 256 * j;
+                const int blk = e >> 7;
+                woff[s][j] = blk < a.CB ? 4u * ((unsigned)((grp * a.CB + blk) * sr.nchunks) * kPwChunkW +
+                                                4u * (unsigned)(e & 127))
+                                        : kOOB;
+            }
+        };
+        // the second source's offsets are worked out while the first chunks
+        // load, unless those chunks already need them
+        setup_src(std::integral_constant<int, 0>{});
+        if constexpr (TWO) {
+            if (n1 < 3) setup_src(std::integral_constant<int, 1>{});
         }
-        // one chunk: a.rounds + a.wrounds loads per wave
-        auto issue = [&](int st, int sb) {
-            const rsrc_t rx = make_rsrc(xim + (long)st * 16 * a.HW, 64u * (unsigned)a.HW);
-            const rsrc_t rw = make_rsrc(a.wp + (long)st * kPwChunkW, a.wp_bytes - 4u * kPwChunkW * (unsigned)st);
+        // chunk c of source sr into stage buffer sb: sr.rounds + a.wrounds loads
+        // per wave
+        auto issue_src = [&](const PwSrc& sr, const unsigned* go, const unsigned* wo, int c, int sb) {
+            const float* xim = sr.x + (long)img * sr.cin * sr.HW;
+            const rsrc_t rx = make_rsrc(xim + (long)c * 16 * sr.HW, 64u * (unsigned)sr.HW);
+            const rsrc_t rw = make_rsrc(sr.wp + (long)c * kPwChunkW, sr.wp_bytes - 4u * kPwChunkW * (unsigned)c);
 #pragma unroll
             for (int i = 0; i < kPwMaxRounds; ++i) {
-                if (i >= a.rounds) break;
-                pw_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + sb + 1024 * i + 256 * pw), goff[i]);
+                if (i >= sr.rounds) break;
+                pw_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + sb + 1024 * i + 256 * pw), go[i]);
             }
 #pragma unroll
             for (int j = 0; j < kPwWRounds; ++j) {
                 if (j >= a.wrounds) break;
                 pw_lds_load16(rw, (__attribute__((address_space(3))) void*)(smem + sb + a.WOFF + 1024 * j + 256 * pw),
-                              woff[j]);
+                              wo[j]);
             }
         };
-        const int nld = a.rounds + a.wrounds;
+        auto issue = [&](int st, int sb) {
+            if (!TWO || st < n1)
+                issue_src(a.src[0], goff[0], woff[0], st, sb);
+            else
+                issue_src(a.src[1], goff[1], woff[1], st - n1, sb);
+        };
+        // loads per wave of chunk st
+        auto nld = [&](int st) { return (!TWO || st < n1 ? a.src[0].rounds : a.src[1].rounds) + a.wrounds; };
         // This thread's output quads e = ptid + 256 j of the tile's run; their
         // residual comes to registers, a share per chunk while the consumers
         // compute.
@@ -199,10 +242,13 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
         if (nst > 1) issue(1, BUF);
         if (nst > 2) issue(2, 2 * BUF);
         pw_order();
-        wait_vm_at_most(nld * (min(nst, 3) - 1));  // chunk 0
-        lds_barrier();                              // opening barrier
-        wait_vm_at_most(nst > 2 ? nld : 0);         // chunk 1
-        lds_barrier();                              // barrier 0
+        if constexpr (TWO) {
+            if (n1 >= 3) setup_src(std::integral_constant<int, 1>{});
+        }
+        wait_vm_at_most((nst > 1 ? nld(1) : 0) + (nst > 2 ? nld(2) : 0));  // chunk 0
+        lds_barrier();                                                     // opening barrier
+        wait_vm_at_most(nst > 2 ? nld(2) : 0);                             // chunk 1
+        lds_barrier();                                                     // barrier 0
         int rdone = 0;
         for (int st = 1; st < nst; ++st) {
             // after barrier st-1: the buffer of chunk st-1 is free
@@ -217,7 +263,7 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
             const bool more = st + 2 < nst;
             if (more) issue(st + 2, bufof(st + 2));
             pw_order();
-            wait_vm_at_most(piece + (more ? nld : 0));  // chunk st+1 (and every earlier load)
+            wait_vm_at_most(piece + (more ? nld(st + 2) : 0));  // chunk st+1 (and every earlier load)
             lds_barrier();
         }
         if (want_res) load_res(rdone, a.rq);
@@ -263,25 +309,40 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
     // A wave owns pixel blocks pb0 .. pb0+MP-1 and channel blocks cb0 ..
     // cb0+MC-1 of the tile.  Blocks past the tile (the template covers the
     // largest share) compute on clamped, in-range operands and are dropped.
-    int abase[MP];
-#pragma unroll
-    for (int mp = 0; mp < MP; ++mp) {
-        const int q = min(32 * (pb0 + mp) + l32, a.OHW - 1);
-        const int oh = pw_div(q, a.m_owd, a.l_owd);
-        abase[mp] = hi * a.CS + oh * a.WS + a.S * (q - oh * a.OWD);
-    }
+    // Per source: this lane's LDS offset of its pixel in a staged chunk, and the
+    // BatchNorm scale of its output channel, which multiplies the weights.
+    int abase[2][MP];
+    int cs2[2];
+    float bsc[2][MC];
     int boff[MC];
-    float sc[MC], bi[MC];
+    float bi[MC];
     {
-        const rsrc_t rs = make_rsrc(a.scale, 4u * (unsigned)a.cout);
+#pragma unroll
+        for (int s = 0; s < (TWO ? 2 : 1); ++s) {
+            const PwSrc& sr = a.src[s];
+            cs2[s] = 2 * sr.CS;
+#pragma unroll
+            for (int mp = 0; mp < MP; ++mp) {
+                const int q = min(32 * (pb0 + mp) + l32, a.OHW - 1);
+                const int oh = pw_div(q, sr.m_owd, sr.l_owd);
+                abase[s][mp] = hi * sr.CS + oh * sr.WS + sr.S * (q - oh * sr.OWD);
+            }
+            const rsrc_t rs = make_rsrc(sr.scale, 4u * (unsigned)a.cout);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                const int cb = min(cb0 + mc, a.CB - 1);
+                bsc[s][mc] = bload(rs, 4u * (unsigned)(grp * a.CO + 32 * cb + l32));
+            }
+        }
         const rsrc_t rb = make_rsrc(a.bias, 4u * (unsigned)a.cout);
+        // a null second bias reads as zeros (a range of 0 bytes)
+        const rsrc_t rb2 = make_rsrc(a.bias2 ? a.bias2 : a.bias, a.bias2 ? 4u * (unsigned)a.cout : 0u);
 #pragma unroll
         for (int mc = 0; mc < MC; ++mc) {
             const int cb = min(cb0 + mc, a.CB - 1);
             boff[mc] = a.WOFF + cb * kPwChunkW + 2 * lane;
             const unsigned co = (unsigned)(grp * a.CO + 32 * cb + l32);
-            sc[mc] = bload(rs, 4u * co);
-            bi[mc] = bload(rb, 4u * co);
+            bi[mc] = TWO ? bload(rb, 4u * co) + bload(rb2, 4u * co) : bload(rb, 4u * co);
         }
     }
     f32x16 acc[MP][MC];
@@ -301,57 +362,113 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
         float x[8][MP];
         f32x2 w[MC][4];
     };
-    const int cs2 = 2 * a.CS;
+    // where a chunk of one source is read: pixel offsets and channel-pair stride
+    struct View {
+        int ab[MP];
+        int c2;
+    };
+    auto view = [&](int ch, View& v) {
+        const bool s1 = TWO && ch >= n1;  // uniform
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) v.ab[mp] = s1 ? abase[1][mp] : abase[0][mp];
+        v.c2 = s1 ? cs2[1] : cs2[0];
+    };
     // reads of pair k: its input, and at even k the weights of pairs k, k+1
-    auto read_pair = [&](int sbuf, Ops& o, int k) {
+    auto read_pair = [&](int sbuf, const View& v, Ops& o, int k) {
         if ((k & 1) == 0) {
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc)
                 o.w[mc][k >> 1] = *reinterpret_cast<const f32x2*>(smem + sbuf + boff[mc] + 64 * k);
         }
 #pragma unroll
-        for (int mp = 0; mp < MP; ++mp) o.x[k][mp] = smem[sbuf + abase[mp] + k * cs2];
+        for (int mp = 0; mp < MP; ++mp) o.x[k][mp] = smem[sbuf + v.ab[mp] + k * v.c2];
     };
-    // chunk in `o`, and the next chunk's operands from buffer `nbuf` into `n`,
+    // chunk ch (in `o`), and chunk ch+1's operands from buffer `nbuf` into `n`,
     // one pair's reads ahead of each pair's matrix instructions (so the last
     // reads have landed by the barrier's LDS wait).  After the last chunk these
     // reads take whatever a buffer holds, unused: no branch between the matrix
-    // instructions.
-    auto compute = [&](const Ops& o, Ops& n, int nbuf) {
+    // instructions.  The first source's sums are scaled once, when the second
+    // source starts (or in the epilogue); the second source's weights are
+    // scaled as they are used, those of pairs k+2, k+3 among pair k's matrix
+    // instructions (a multiply right after the read would wait for it).
+    auto compute = [&](const Ops& o, Ops& n, int nbuf, int ch, auto SCALED) {
+        constexpr bool scaled = decltype(SCALED)::value;
+        View v;
+        view(ch + 1, v);
+        f32x2 w[MC][4];  // scaled weights (second source only)
+        if constexpr (scaled) {
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) w[mc][0] = o.w[mc][0] * bsc[1][mc];
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            read_pair(nbuf, n, k);
+            read_pair(nbuf, v, n, k);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mp = 0; mp < MP; ++mp)
 #pragma unroll
-                for (int mc = 0; mc < MC; ++mc)
-                    acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.x[k][mp], o.w[mc][k >> 1][k & 1],
-                                                                      acc[mp][mc], 0, 0, 0);
+                for (int mc = 0; mc < MC; ++mc) {
+                    if constexpr (scaled)
+                        acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.x[k][mp], w[mc][k >> 1][k & 1],
+                                                                          acc[mp][mc], 0, 0, 0);
+                    else
+                        acc[mp][mc] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.x[k][mp], o.w[mc][k >> 1][k & 1],
+                                                                          acc[mp][mc], 0, 0, 0);
+                }
+            if constexpr (scaled) {
+                if ((k & 1) == 0 && k + 2 < 8) {
+#pragma unroll
+                    for (int mc = 0; mc < MC; ++mc) w[mc][(k >> 1) + 1] = o.w[mc][(k >> 1) + 1] * bsc[1][mc];
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto nextb = [&](int b) { return b == 2 * BUF ? 0 : b + BUF; };
     Ops o0, o1;
     lds_barrier();  // opening barrier: chunk 0 has landed
+    {
+        View v;
+        view(0, v);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) read_pair(0, o0, k);
+        for (int k = 0; k < 8; ++k) read_pair(0, v, o0, k);
+    }
     lds_barrier();  // barrier 0: chunk 1 has landed, chunk 0's buffer is read
     int sb = 0;     // buffer of chunk st
-    for (int st = 0;;) {
-        // chunk st in o0
-        if (st > 0) lds_barrier();
-        compute(o0, o1, nextb(sb));
-        sb = nextb(sb);
-        if (++st >= nst) break;
-        // chunk st in o1
-        lds_barrier();
-        compute(o1, o0, nextb(sb));
-        sb = nextb(sb);
-        if (++st >= nst) break;
+    int st = 0;
+    // chunks st .. end-1, chunk st's operands in o0 (and so again on return)
+    auto run = [&](int end, auto SCALED) {
+        for (;;) {
+            if (st > 0) lds_barrier();
+            compute(o0, o1, nextb(sb), st, SCALED);
+            sb = nextb(sb);
+            if (++st >= end) {
+                o0 = o1;
+                break;
+            }
+            lds_barrier();
+            compute(o1, o0, nextb(sb), st, SCALED);
+            sb = nextb(sb);
+            if (++st >= end) break;
+        }
+    };
+    // the first source's chunks plain, then (with a second source) its sums
+    // scaled and the second source's chunks with scaled weights: two loops,
+    // not a branch per chunk, which would hold two register assignments
+    run(n1, std::false_type{});
+    if (TWO) {
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) acc[mp][mc] *= bsc[0][mc];
+        run(nst, std::true_type{});
     }
+    // a single source's sums take their scale here
+    float esc[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) esc[mc] = TWO ? 1.0f : bsc[0][mc];
 
-    // Exchange: every sum, scaled and biased, goes to its place in the tile's
+    // Exchange: every scaled sum plus its biases goes to its place in the tile's
     // [channel][pixel] output run (over the stage buffers, free once every wave
     // is past this barrier); pixels past the plane go to a spare slot.
     __syncthreads();
@@ -370,7 +487,7 @@ __global__ void __launch_bounds__(kPwThreads) k_pointwise(PwArgs a)
                 const int q = 32 * pb + 8 * g + 4 * hi;
                 f32x4 z;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[e] = fmaf(sc[mc], acc[mp][mc][4 * g + e], bi[mc]);
+                for (int e = 0; e < 4; ++e) z[e] = fmaf(esc[mc], acc[mp][mc][4 * g + e], bi[mc]);
                 if (quads) {
                     // in 16-byte units, so the store is one 16-byte LDS write
                     const int r4 = (32 * cb + l32) * (a.OHW >> 2) + 8 * pb + 2 * g + hi;
@@ -431,22 +548,33 @@ static bool pw_stage(const ConvGeom& g, PwStage* s)
     return s->rounds <= kPwMaxRounds;
 }
 
-// Channel groups per image, consumer grid and compiled share for a layer;
-// false when the pointwise kernel does not take it.
+static bool pw_layer_ok(const ConvGeom& g)
+{
+    if (g.groups != 1 || g.k != 1 || g.pad != 0 || g.cin % 16 != 0 || g.cout % 32 != 0) return false;
+    const long lim = 0x7fffffffL;
+    return (long)g.n * g.cin * g.h * g.w * 4 < lim && (long)g.n * g.cout * g.oh * g.ow * 4 < lim &&
+           packed_weight_floats(g) * 4 < lim;
+}
+
+// Channel groups per image, consumer grid and compiled share for a layer, or for
+// a layer g and a second source g2 over the same output; false when the
+// pointwise kernel does not take it.
 struct PwConfig {
     int groups, kind, wpx, pb_per, cb_per;
     size_t lds;
 };
 
-static bool pw_config(const ConvGeom& g, PwConfig* c)
+static bool pw_config(const ConvGeom& g, const ConvGeom* g2, PwConfig* c)
 {
-    if (g.groups != 1 || g.k != 1 || g.pad != 0 || g.cin % 16 != 0 || g.cout % 32 != 0) return false;
-    const long lim = 0x7fffffffL;
-    if ((long)g.n * g.cin * g.h * g.w * 4 >= lim || (long)g.n * g.cout * g.oh * g.ow * 4 >= lim ||
-        packed_weight_floats(g) * 4 >= lim)
-        return false;
-    PwStage s;
-    if (!pw_stage(g, &s)) return false;
+    PwStage s, s2;
+    if (!pw_layer_ok(g) || !pw_stage(g, &s)) return false;
+    int rounds = s.rounds, cin_all = g.cin;
+    if (g2 != nullptr) {
+        if (!pw_layer_ok(*g2) || !pw_stage(*g2, &s2)) return false;
+        if (g2->n != g.n || g2->cout != g.cout || g2->oh != g.oh || g2->ow != g.ow) return false;
+        rounds = std::max(rounds, s2.rounds);
+        cin_all += g2->cin;
+    }
     const int ohw = g.oh * g.ow;
     const int pb = (ohw + 31) / 32;
     const int cbt = g.cout / 32;
@@ -455,9 +583,11 @@ static bool pw_config(const ConvGeom& g, PwConfig* c)
     for (int groups = 1; groups <= cbt; ++groups) {
         if (cbt % groups != 0) continue;
         const int cb = cbt / groups;
-        if (cb > kPwMaxCB) continue;
+        // at most six channel blocks a tile, and enough workgroups to spread
+        // over the chip
+        if (cb > kPwMaxCB || (long)g.n * groups < 64) continue;
         const int wrounds = (cb * 128 + 255) / 256;
-        const size_t buf = (size_t)s.rounds * 1024 + (size_t)wrounds * 1024;
+        const size_t buf = (size_t)rounds * 1024 + (size_t)wrounds * 1024;
         const size_t xch = (size_t)32 * cb * ohw;
         // the exchange (plus a spare slot) over the stage buffers; the producers
         // hold the residual of up to kPwResQ output quads each
@@ -472,9 +602,9 @@ static bool pw_config(const ConvGeom& g, PwConfig* c)
                 // matrix work per workgroup, times the rounds of workgroups (one
                 // per compute unit), plus a start-up per round
                 const long wgs = (long)g.n * groups;
-                const double rounds = std::ceil(wgs / 256.0);
+                const double wrnds = std::ceil(wgs / 256.0);
                 const double units = (double)kPwKinds[kind].mp * kPwKinds[kind].mc;
-                const double cost = rounds * (units * (g.cin / 2) * 64.0 + 5000.0) + 1e-3 * units;
+                const double cost = wrnds * (units * (cin_all / 2) * 64.0 + 5000.0) + 1e-3 * units;
                 if (cost < best) {
                     best = cost;
                     *c = PwConfig{groups, kind, wpx, pb_per, cb_per, lds};
@@ -483,22 +613,32 @@ static bool pw_config(const ConvGeom& g, PwConfig* c)
             }
         }
     }
-    // enough workgroups to spread over the chip
-    return found && (long)g.n * c->groups >= 64;
+    return found;
 }
 
 bool pointwise_fits(const ConvGeom& g)
 {
     PwConfig c;
-    return pw_config(g, &c);
+    return pw_config(g, nullptr, &c);
 }
 
-void pointwise_describe(const ConvGeom& g, char* buf, int len)
+bool pointwise_pair_fits(const ConvGeom& g, const ConvGeom& g2)
+{
+    PwConfig c;
+    return pw_config(g, &g2, &c);
+}
+
+void pointwise_describe(const ConvGeom& g, const ConvGeom* g2, char* buf, int len)
 {
     PwConfig c{};
-    pw_config(g, &c);
-    snprintf(buf, len, "pointwise k1 s%d groups=%d wpx=%d splitk=1 kernel=cvx::k_pointwise<%d, %d>",
-             g.stride, c.groups, c.wpx, kPwKinds[c.kind].mp, kPwKinds[c.kind].mc);
+    pw_config(g, g2, &c);
+    if (g2 != nullptr)
+        snprintf(buf, len,
+                 "pointwise k1 s%d + shortcut k1 s%d groups=%d wpx=%d splitk=1 kernel=cvx::k_pointwise<%d, %d, true>",
+                 g.stride, g2->stride, c.groups, c.wpx, kPwKinds[c.kind].mp, kPwKinds[c.kind].mc);
+    else
+        snprintf(buf, len, "pointwise k1 s%d groups=%d wpx=%d splitk=1 kernel=cvx::k_pointwise<%d, %d, false>",
+                 g.stride, c.groups, c.wpx, kPwKinds[c.kind].mp, kPwKinds[c.kind].mc);
 }
 
 bool pointwise_aligned(const float* x, const float* res, const float* y)
@@ -508,69 +648,105 @@ bool pointwise_aligned(const float* x, const float* res, const float* y)
 }
 
 template <int MP, int MC>
-static void launch_pw(dim3 grid, size_t lds, hipStream_t s, const PwArgs& a)
+static void launch_pw(dim3 grid, size_t lds, hipStream_t s, const PwArgs& a, bool two)
 {
-    hipLaunchKernelGGL((k_pointwise<MP, MC>), grid, dim3(kPwThreads), lds, s, a);
+    if (two)
+        hipLaunchKernelGGL((k_pointwise<MP, MC, true>), grid, dim3(kPwThreads), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_pointwise<MP, MC, false>), grid, dim3(kPwThreads), lds, s, a);
 }
 
-hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, const float* scale,
-                            const float* bias, const float* res, float* y, hipStream_t s)
+static void fill_src(const ConvGeom& g, const PwStage& st, const float* x, const float* wp,
+                     const float* scale, PwSrc* sr)
+{
+    sr->x = x;
+    sr->wp = wp;
+    sr->scale = scale;
+    sr->cin = g.cin;
+    sr->HW = g.h * g.w;
+    sr->nchunks = g.cin / 16;
+    sr->rounds = st.rounds;
+    sr->RE = st.re;
+    sr->RQ = st.rq;
+    sr->RPC = st.rpc;
+    sr->RSTR = st.rstr;
+    fastdiv_params(st.rq, &sr->m_rq, &sr->l_rq);
+    fastdiv_params(st.rpc, &sr->m_rpc, &sr->l_rpc);
+    sr->OWD = st.owd;
+    sr->WS = st.ws;
+    sr->S = g.stride;
+    sr->CS = st.cs;
+    fastdiv_params(st.owd, &sr->m_owd, &sr->l_owd);
+    sr->wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+}
+
+// One layer (g2 null), or a layer and a second 1x1 source summed into the same
+// output ahead of the activation (g's residual mode is then not used).
+static hipError_t launch_pw_any(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                                const float* bias, const float* res, const ConvGeom* g2, const float* x2,
+                                const float* wp2, const float* scale2, const float* bias2, float* y,
+                                hipStream_t s)
 {
     PwConfig c;
-    PwStage st;
-    if (!pw_config(g, &c) || !pw_stage(g, &st)) return hipErrorInvalidValue;
-    if (!pointwise_aligned(x, res, y)) return hipErrorInvalidValue;
+    PwStage st, st2{};
+    if (!pw_config(g, g2, &c) || !pw_stage(g, &st)) return hipErrorInvalidValue;
+    if (g2 != nullptr && !pw_stage(*g2, &st2)) return hipErrorInvalidValue;
+    if (!pointwise_aligned(x, g2 ? nullptr : res, y) || (g2 != nullptr && !pointwise_aligned(x2, nullptr, y)))
+        return hipErrorInvalidValue;
     PwArgs a;
-    a.x = x;
-    a.wp = wp;
-    a.scale = scale;
+    fill_src(g, st, x, wp, scale, &a.src[0]);
+    if (g2 != nullptr)
+        fill_src(*g2, st2, x2, wp2, scale2, &a.src[1]);
+    else
+        a.src[1] = a.src[0];  // never staged: every chunk is the first source's
     a.bias = bias;
-    a.res = res;
+    a.bias2 = g2 != nullptr ? bias2 : nullptr;
+    a.res = g2 != nullptr ? nullptr : res;
     a.y = y;
-    a.cin = g.cin;
     a.cout = g.cout;
-    a.HW = g.h * g.w;
     a.OHW = g.oh * g.ow;
     a.groups_co = c.groups;
     a.CO = g.cout / c.groups;
     a.CB = a.CO / 32;
     a.PB = (a.OHW + 31) / 32;
-    a.nchunks = g.cin / 16;
+    a.n1 = g.cin / 16;
+    a.nchunks = a.n1 + (g2 != nullptr ? g2->cin / 16 : 0);
     fastdiv_params(c.groups, &a.m_g, &a.l_g);
-    a.rounds = st.rounds;
-    a.RE = st.re;
-    a.RQ = st.rq;
-    a.RPC = st.rpc;
-    a.RSTR = st.rstr;
-    fastdiv_params(st.rq, &a.m_rq, &a.l_rq);
-    fastdiv_params(st.rpc, &a.m_rpc, &a.l_rpc);
     a.wrounds = (a.CB * 128 + 255) / 256;
-    a.OWD = st.owd;
-    a.WS = st.ws;
-    a.S = g.stride;
-    a.CS = st.cs;
-    fastdiv_params(st.owd, &a.m_owd, &a.l_owd);
     a.wpx = c.wpx;
     a.pb_per = c.pb_per;
     a.cb_per = c.cb_per;
-    a.BUF = st.rounds * 1024 + a.wrounds * 1024;
-    a.WOFF = st.rounds * 1024;
+    const int rounds = std::max(st.rounds, g2 != nullptr ? st2.rounds : 0);
+    a.BUF = rounds * 1024 + a.wrounds * 1024;
+    a.WOFF = rounds * 1024;
     const int tq = a.CO * a.OHW / 4;
     a.SPARE = a.CO * a.OHW;
     a.rq = (tq + 255) / 256;
     // residual loads spread over the chunks' iterations (all but the first)
     a.rq_per = (a.rq + std::max(1, a.nchunks - 1) - 1) / std::max(1, a.nchunks - 1);
-    a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
     a.act = g.act;
-    a.res_mode = g.res_mode;
+    a.res_mode = g2 != nullptr ? CVX_RES_NONE : g.res_mode;
     dim3 grid((unsigned)((long)g.n * c.groups));
     switch (c.kind) {
-    case 0: launch_pw<2, 3>(grid, c.lds, s, a); break;
-    case 1: launch_pw<1, 3>(grid, c.lds, s, a); break;
-    case 2: launch_pw<2, 2>(grid, c.lds, s, a); break;
-    case 3: launch_pw<1, 2>(grid, c.lds, s, a); break;
+    case 0: launch_pw<2, 3>(grid, c.lds, s, a, g2 != nullptr); break;
+    case 1: launch_pw<1, 3>(grid, c.lds, s, a, g2 != nullptr); break;
+    case 2: launch_pw<2, 2>(grid, c.lds, s, a, g2 != nullptr); break;
+    case 3: launch_pw<1, 2>(grid, c.lds, s, a, g2 != nullptr); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_pointwise(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                            const float* bias, const float* res, float* y, hipStream_t s)
+{
+    return launch_pw_any(g, x, wp, scale, bias, res, nullptr, nullptr, nullptr, nullptr, nullptr, y, s);
+}
+
+hipError_t launch_pointwise_pair(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                                 const float* bias, const ConvGeom& g2, const float* x2, const float* wp2,
+                                 const float* scale2, const float* bias2, float* y, hipStream_t s)
+{
+    return launch_pw_any(g, x, wp, scale, bias, nullptr, &g2, x2, wp2, scale2, bias2, y, s);
 }
 
 }  // namespace cvx

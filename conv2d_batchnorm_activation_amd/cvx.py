@@ -81,13 +81,16 @@ lib.cvx_forward_out_shape.argtypes = [_LP, _I, ctypes.POINTER(_I)]
 lib.cvx_forward_out_shape.restype = _I
 lib.cvx_forward_workspace_bytes.argtypes = [_LP, _I, ctypes.POINTER(_I)]
 lib.cvx_forward_workspace_bytes.restype = _Z
+lib.cvx_forward_plan.argtypes = [_LP, _I, ctypes.c_char_p, _I]
+lib.cvx_forward_plan.restype = _I
 lib.cvx_forward.argtypes = [_LP, _I, _P, _P, _P, _Z, _P]
 lib.cvx_forward.restype = _I
 
 #: every entry point include/cvx.h declares
 EXPORTS = ("cvx_status_str", "cvx_version", "cvx_conv_out_shape", "cvx_conv_plan",
            "cvx_conv_workspace_bytes", "cvx_packed_weights_bytes", "cvx_pack_weights", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
-           "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward")
+           "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward_plan",
+           "cvx_forward")
 
 
 class CvxError(RuntimeError):
@@ -202,6 +205,15 @@ def cvx_forward_out_shape(layers) -> tuple:
     out = (_I * 4)()
     _check(lib.cvx_forward_out_shape(arr, n, out), "cvx_forward_out_shape")
     return tuple(out)
+
+
+def cvx_forward_plan(layers) -> list:
+    """Per-layer launch plan of a list: one string per layer (see cvx_forward_plan)."""
+    arr, n = layers if isinstance(layers, tuple) else layer_array(layers)
+    size = 320 * n + 1
+    buf = ctypes.create_string_buffer(size)
+    _check(lib.cvx_forward_plan(arr, n, buf, size), "cvx_forward_plan")
+    return [line.split(" ", 1)[1] for line in buf.value.decode().split("\n")]
 
 
 def cvx_forward_workspace_bytes(layers) -> int:

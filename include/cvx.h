@@ -234,6 +234,16 @@ CVX_API cvx_status cvx_forward_out_shape(const cvx_layer *layers, int n_layers, 
  * status != NULL. */
 CVX_API size_t cvx_forward_workspace_bytes(const cvx_layer *layers, int n_layers, cvx_status *status);
 
+/* Host-only query: the launch plan of a layer list, one line per layer ("i
+ * <text>", lines separated by '\n'): a convolution's cvx_conv_plan text; for a
+ * pointwise layer that computes its block's 1x1 shortcut in the same kernel,
+ * the pair's description and "shortcut=j"; "merged into i" for a layer run
+ * inside layer i's kernel (that shortcut, or an FC after its GAP); "gap",
+ * "gap+fc", "fc" or "preprocess" otherwise.  Validates the list as
+ * cvx_forward_out_shape does; writes at most buf_len bytes (truncated to fit,
+ * always NUL-terminated).  320 bytes per layer always suffice. */
+CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char *buf, int buf_len);
+
 /*
  * cvx_forward -- run an ordered layer list on one stream, with no host
  * synchronisation: layer i reads the output of layer `in` (and the residual from
@@ -241,7 +251,10 @@ CVX_API size_t cvx_forward_workspace_bytes(const cvx_layer *layers, int n_layers
  * last layer writes `output`; the others write into `workspace`.  This is the
  * whole-network launch sequence the pages replay per inference ("YOLO26N
  * Inference Optimisation", "Baseline benchmark" and "nsys kernel-level
- * breakdown": kernels, not copies, take the time).
+ * breakdown": kernels, not copies, take the time).  A 1x1 shortcut (BN, no
+ * activation, packed weights) whose only reader is a later packed 1x1 layer
+ * adding it before its activation runs inside that layer's kernel, as one
+ * product over both inputs' channels; its output is then never written.
  *   input : device; fp32 NCHW, or u8 NHWC frames when layer 0 is CVX_L_PREPROC.
  *   output: device, shape from cvx_forward_out_shape; must not overlap input/workspace.
  *   workspace: device, >= cvx_forward_workspace_bytes(...) bytes, 256-byte aligned.

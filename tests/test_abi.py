@@ -172,7 +172,7 @@ def test_gap_fc_validation():
     assert f(X, 1, 192, 7, 7, W, B, 10, X + 8, None) == -5
 
 
-def _net_layers(wk):
+def _net_layers(wk, w_layout=cvx.CVX_W_OIHW):
     """cvx_layer array for a workload, with fake parameter pointers (planning only)."""
     shapes = []
     out = []
@@ -189,7 +189,8 @@ def _net_layers(wk):
             o = (n, 3, L.dst_h, L.dst_w)
         elif L.kind == wl.KIND_CONV:
             n, c, h, w = s_in
-            d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode)
+            d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
+                              w_layout)
             oh, ow = cvx.cvx_conv_out_shape(d)
             lay.conv = d
             lay.w, lay.scale, lay.bias = W + 0x100000 * i, S + 0x1000 * i, B + 0x1000 * i + 0x800
@@ -228,6 +229,54 @@ def test_forward_shapes_and_workspace(wk_fn, expect):
     assert ws >= largest
     assert ws <= total + 256 * len(inter) + max(
         cvx.cvx_conv_workspace_bytes(l.conv) if l.kind == 0 else 0 for l in layers)
+
+
+def _block_list(n, act_skip, layout=cvx.CVX_W_PACKED):
+    """conv 1x1 -> dw 3x3 -> pw 1x1 + shortcut 1x1 (added before the ReLU) -> GAP,
+    all at 8x8, with fake parameter pointers (planning only)."""
+    def conv(inp, res, c_in, c_out, k, groups, act, res_mode, i):
+        lay = cvx.cvx_layer()
+        lay.kind, lay.in_, lay.res = cvx.CVX_L_CONV, inp, res
+        lay.conv = cvx.make_desc(n, c_in, 8, 8, c_out, k, 1, k // 2, groups, act, res_mode, layout)
+        lay.w, lay.scale, lay.bias = W + 0x100000 * i, S + 0x1000 * i, B + 0x1000 * i + 0x800
+        return lay
+    R, N = cvx.CVX_ACT_RELU, cvx.CVX_ACT_NONE
+    out = [conv(cvx.CVX_INPUT, cvx.CVX_NO_RES, 32, 32, 1, 1, R, cvx.CVX_RES_NONE, 0),
+           conv(0, cvx.CVX_NO_RES, 32, 32, 3, 32, R, cvx.CVX_RES_NONE, 1),
+           conv(0, cvx.CVX_NO_RES, 32, 64, 1, 1, act_skip, cvx.CVX_RES_NONE, 2),
+           conv(1, 2, 32, 64, 1, 1, R, cvx.CVX_RES_BEFORE_ACT, 3)]
+    gap = cvx.cvx_layer()
+    gap.kind, gap.in_, gap.res = cvx.CVX_L_GAP, 3, cvx.CVX_NO_RES
+    gap.conv = cvx.cvx_conv_desc(n, 64, 8, 8, 64, 1, 1, 1, 0, 1, 0, 0)
+    return out + [gap]
+
+
+@pytest.mark.parametrize("n,merged", [(64, True), (8, False)])
+def test_forward_merges_1x1_shortcut(n, merged):
+    """A 1x1 shortcut (BN, no activation) read only by a packed pointwise layer
+    that adds it before its activation runs inside that layer's kernel: its
+    output takes no workspace, while its input stays live one layer longer.
+    First-fit places A, B, C (the shortcut's output) at 0, |A|, 2|A| and then D
+    after C, as B and C are live while D is written; merged, D goes where C was.
+    Below 64 workgroups the pointwise kernel does not take the layers and
+    nothing is merged; an activation on the shortcut also keeps it."""
+    a = 4 * n * 32 * 64            # A = conv 1x1 output, B = dw output: 32 x 8 x 8
+    c = 4 * n * 64 * 64            # C = shortcut output, D = pw output: 64 x 8 x 8
+    kept = 2 * a + 2 * c
+    ws = cvx.cvx_forward_workspace_bytes(_block_list(n, cvx.CVX_ACT_NONE))
+    assert cvx.cvx_forward_workspace_bytes(_block_list(n, cvx.CVX_ACT_RELU)) == kept
+    assert ws == (2 * a + c if merged else kept)
+    plan = cvx.cvx_forward_plan(_block_list(n, cvx.CVX_ACT_NONE))
+    assert len(plan) == 5
+    if merged:
+        assert plan[2] == "merged into 3"
+        assert plan[3].startswith("pointwise k1 s1 + shortcut k1 s1 ") and plan[3].endswith(" shortcut=2")
+        assert "kernel=cvx::k_pointwise<" in plan[3]
+    else:
+        assert "merged" not in plan[2] and "shortcut" not in plan[3]
+    assert plan[4] == "gap kernel=cvx::k_gap_fc"
+    # OIHW weights never take the pointwise kernel
+    assert cvx.cvx_forward_workspace_bytes(_block_list(n, cvx.CVX_ACT_NONE, cvx.CVX_W_OIHW)) == kept
 
 
 def test_forward_list_validation():

@@ -127,6 +127,16 @@ def test_mnist_cnn(batch):
     _forward_check(wl.mnist_cnn(batch))
 
 
+@pytest.mark.parametrize("args", [
+    (64, 32, 10, 64, 2, wl.ACT_SILU),   # 5x5 output (ragged exchange), rows-staged stride-2 shortcut
+    (96, 48, 7, 96, 1, wl.ACT_RELU),    # stride-1 shortcut, 7x7
+    (32, 64, 8, 192, 2, wl.ACT_RELU),   # several channel groups per image
+])
+def test_shortcut_block(args):
+    # the pointwise layer and its shortcut run as one two-source kernel
+    _forward_check(wl.shortcut_block(*args))
+
+
 def test_detector_pipeline_b1():
     _forward_check(wl.detector_pipeline(1))
 

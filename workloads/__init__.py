@@ -145,6 +145,26 @@ def mnist_cnn(batch: int, seed_index: int = 1) -> Workload:
     return Workload(f"mnist_dwsep_b{batch}", x, L)
 
 
+def shortcut_block(batch: int, cin: int, hw: int, cout: int, stride: int, act: int,
+                   seed_index: int = 7) -> Workload:
+    """One block with a projection shortcut, between two 1x1 layers.
+
+    1x1 cin->cin + BN + ReLU; dw3x3 stride s + BN + ReLU; 1x1 stride-s cin->cout
+    shortcut + BN (no activation) of the same input; pw1x1 cin->cout + BN, the
+    shortcut added before `act`; then 1x1 cout->cout + BN (no activation), so
+    the block's output is compared through a full-rank channel mix.
+    """
+    rng = rng_for(seed_index)
+    x = rng.uniform(-1.0, 1.0, (batch, cin, hw, hw)).astype(np.float32)
+    L: List[Layer] = [conv_layer(rng, cin, cin, 1, 1, 0, act=ACT_RELU, name="in1x1")]
+    L.append(conv_layer(rng, cin, cin, 3, stride, 1, groups=cin, act=ACT_RELU, inp=0, name="dw"))
+    L.append(conv_layer(rng, cin, cout, 1, stride, 0, act=ACT_NONE, inp=0, name="skip"))
+    L.append(conv_layer(rng, cin, cout, 1, 1, 0, act=act, res_mode=RES_BEFORE_ACT, inp=1, res=2,
+                        name="pw"))
+    L.append(conv_layer(rng, cout, cout, 1, 1, 0, act=ACT_NONE, inp=3, name="out1x1"))
+    return Workload(f"shortcut_block_b{batch}_{cin}x{hw}_{cout}_s{stride}", x, L)
+
+
 def _stem_layers(rng: np.random.Generator, first_inp: int) -> List[Layer]:
     return [
         conv_layer(rng, 3, 16, 3, 2, 1, act=ACT_SILU, inp=first_inp, name="stem1"),
