@@ -520,7 +520,10 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         __syncthreads();
         if (tid == 0) {
             unsigned long long* c = a.ctr + ((long)(mb * a.n + b) * a.tiles_per_img + tile);
-            unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // a counter left by a finished launch reads 0, so the first attempt
+            // assumes that and skips a round trip; anything else (an arrival of
+            // this launch, or a stale value) comes back in `cur` for the retry
+            unsigned long long cur = 0ull;
             unsigned long long before;
             for (;;) {
                 before = (cur >> 8) == a.epoch ? (cur & 0xffull) : 0ull;
