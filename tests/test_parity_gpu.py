@@ -137,6 +137,17 @@ def test_shortcut_block(args):
     _forward_check(wl.shortcut_block(*args))
 
 
+@pytest.mark.parametrize("args", [
+    (64, 32, 10, 32, 1, wl.ACT_RELU, True),    # 10x10, identity residual
+    (64, 48, 9, 64, 2, wl.ACT_SILU, False),    # odd 9x9 -> 5x5
+    (80, 64, 16, 32, 1, wl.ACT_NONE, False),   # 16x16, no activation on the depthwise layer
+    (64, 32, 18, 32, 2, wl.ACT_RELU, False),   # 18x18 -> 9x9
+])
+def test_dw_block(args):
+    # depthwise-separable blocks with small odd and even planes, chained
+    _forward_check(wl.dw_block(*args))
+
+
 def test_detector_pipeline_b1():
     _forward_check(wl.detector_pipeline(1))
 

@@ -165,6 +165,27 @@ def shortcut_block(batch: int, cin: int, hw: int, cout: int, stride: int, act: i
     return Workload(f"shortcut_block_b{batch}_{cin}x{hw}_{cout}_s{stride}", x, L)
 
 
+def dw_block(batch: int, cin: int, hw: int, cout: int, stride: int, dw_act: int, residual: bool,
+             seed_index: int = 8) -> Workload:
+    """A depthwise-separable block without a projection shortcut, between two 1x1 layers.
+
+    1x1 cin->cin + BN + ReLU; dw3x3 stride s + BN + dw_act; pw1x1 cin->cout +
+    BN + ReLU, with the block input added before the ReLU when `residual`
+    (stride 1, cin == cout); then 1x1 cout->cout + BN (no activation).
+    """
+    rng = rng_for(seed_index)
+    x = rng.uniform(-1.0, 1.0, (batch, cin, hw, hw)).astype(np.float32)
+    L: List[Layer] = [conv_layer(rng, cin, cin, 1, 1, 0, act=ACT_RELU, name="in1x1")]
+    L.append(conv_layer(rng, cin, cin, 3, stride, 1, groups=cin, act=dw_act, inp=0, name="dw"))
+    if residual:
+        L.append(conv_layer(rng, cin, cout, 1, 1, 0, act=ACT_RELU, res_mode=RES_BEFORE_ACT, inp=1, res=0,
+                            name="pw"))
+    else:
+        L.append(conv_layer(rng, cin, cout, 1, 1, 0, act=ACT_RELU, inp=1, name="pw"))
+    L.append(conv_layer(rng, cout, cout, 1, 1, 0, act=ACT_NONE, inp=2, name="out1x1"))
+    return Workload(f"dw_block_b{batch}_{cin}x{hw}_{cout}_s{stride}", x, L)
+
+
 def _stem_layers(rng: np.random.Generator, first_inp: int) -> List[Layer]:
     return [
         conv_layer(rng, 3, 16, 3, 2, 1, act=ACT_SILU, inp=first_inp, name="stem1"),
