@@ -649,6 +649,8 @@ struct ListPlan {
 };
 
 constexpr size_t kAlign = 256;
+constexpr size_t kDistinctBytes = size_t(256) << 20;  // intermediates each in a region of their own
+constexpr int kReuseGap = 2;                          // layers after its last read a buffer waits
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
@@ -763,9 +765,19 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         np.pair = j;
         lp->nodes[sl.in].last_use = std::max(lp->nodes[sl.in].last_use, i);
     }
-    // first-fit placement of intermediate outputs over their live ranges
+    // Placement of intermediate outputs.  A kernel that writes a buffer another
+    // kernel has just read runs markedly slower than one writing memory that
+    // was not read since (MNIST conv1's 38.5 MB output: 16.7 against 10.8 us),
+    // so when all intermediates together fit kDistinctBytes each gets its own
+    // region; past that, first fit over live ranges, where a buffer read by
+    // one of the last kReuseGap layers still counts as busy.
     lp->act_bytes = 0;
     lp->layer_ws = 0;
+    size_t total = 0;
+    for (int i = 0; i < nl - 1; ++i)
+        if (!lp->nodes[i].fuse_next && !lp->nodes[i].merged)
+            total += round_up(lp->nodes[i].out.elems() * sizeof(float));
+    const bool distinct = total <= kDistinctBytes;
     std::vector<int> placed;
     for (int i = 0; i < nl - 1; ++i) {
         NodePlan& np = lp->nodes[i];
@@ -774,17 +786,21 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
             continue;
         }
         const size_t sz = round_up(np.out.elems() * sizeof(float));
-        std::vector<std::pair<size_t, size_t>> busy;
-        for (int j : placed) {
-            const NodePlan& o = lp->nodes[j];
-            if (o.last_use >= i)  // live while layer i writes
-                busy.push_back({o.offset, o.offset + round_up(o.out.elems() * sizeof(float))});
-        }
-        std::sort(busy.begin(), busy.end());
         size_t off = 0;
-        for (auto& b : busy) {
-            if (off + sz <= b.first) break;
-            off = std::max(off, b.second);
+        if (distinct) {
+            off = lp->act_bytes;
+        } else {
+            std::vector<std::pair<size_t, size_t>> busy;
+            for (int j : placed) {
+                const NodePlan& o = lp->nodes[j];
+                if (o.last_use + kReuseGap >= i)  // live while layer i writes, or read just before
+                    busy.push_back({o.offset, o.offset + round_up(o.out.elems() * sizeof(float))});
+            }
+            std::sort(busy.begin(), busy.end());
+            for (auto& b : busy) {
+                if (off + sz <= b.first) break;
+                off = std::max(off, b.second);
+            }
         }
         np.offset = off;
         lp->act_bytes = std::max(lp->act_bytes, off + sz);

@@ -229,9 +229,11 @@ typedef struct cvx_layer {
 CVX_API cvx_status cvx_forward_out_shape(const cvx_layer *layers, int n_layers, int out_shape[4]);
 
 /* Workspace bytes cvx_forward needs: intermediate activations (each 256-byte
- * aligned, reused once no later layer reads them) plus the largest per-layer
- * workspace.  Host only.  Returns 0 and sets *status on an invalid list when
- * status != NULL. */
+ * aligned) plus the largest per-layer workspace.  Intermediates that total at
+ * most 256 MiB each get a region of their own (a kernel writing memory another
+ * kernel has just read runs slower); larger lists reuse a region once no later
+ * layer reads it and two further layers have run.  Host only.  Returns 0 and
+ * sets *status on an invalid list when status != NULL. */
 CVX_API size_t cvx_forward_workspace_bytes(const cvx_layer *layers, int n_layers, cvx_status *status);
 
 /* Host-only query: the launch plan of a layer list, one line per layer ("i

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import workloads as wl
@@ -277,6 +278,31 @@ def test_forward_merges_1x1_shortcut(n, merged):
     assert plan[4] == "gap kernel=cvx::k_gap_fc"
     # OIHW weights never take the pointwise kernel
     assert cvx.cvx_forward_workspace_bytes(_block_list(n, cvx.CVX_ACT_NONE, cvx.CVX_W_OIHW)) == kept
+
+
+def test_forward_workspace_placement():
+    """Intermediates that total at most 256 MiB each get their own region (a
+    kernel writing memory that another kernel has just read runs slower); a
+    larger list reuses regions.  MNIST b=256 (about 140 MB of intermediates)
+    is laid out end to end, b=512 (about 280 MB) is not."""
+    def inter_total(wk):
+        layers, shapes = _net_layers(wk, cvx.CVX_W_PACKED)
+        plan = cvx.cvx_forward_plan(layers)
+        tot = 0
+        for i, sh in enumerate(shapes[:-1]):
+            if plan[i].startswith("merged") or plan[i].startswith("gap+fc"):
+                continue
+            tot += (4 * int(np.prod(sh)) + 255) // 256 * 256
+        return layers, tot
+    layers, tot = inter_total(wl.mnist_cnn(256))
+    assert tot <= 256 << 20
+    assert cvx.cvx_forward_workspace_bytes(layers) == tot
+    layers, tot = inter_total(wl.mnist_cnn(512))
+    assert tot > 256 << 20
+    ws = cvx.cvx_forward_workspace_bytes(layers)
+    assert ws < tot
+    # the largest intermediate plus its input must still fit
+    assert ws >= 2 * 4 * 512 * 48 * 28 * 28
 
 
 def test_forward_list_validation():
