@@ -136,6 +136,7 @@ def per_layer(wk, net, counts, reps: int):
             splitk = int(plan.split("splitk=")[1].split()[0]) if "splitk=" in plan else 1
         else:
             continue
+        marker()
         ms_eager = time_launches(fn, reps)
         inner = 20
         ms = time_graph(capture(fn, inner), inner, max(1, reps // inner))
@@ -154,7 +155,18 @@ def per_layer(wk, net, counts, reps: int):
                                             round(gbs / HBM_PEAK_GBS, 4))})
         log(f"  {L.name:16s} {us:8.2f} us (eager {ms_eager * 1e3:6.2f})  {gflops:9.1f} GFLOP/s  "
             f"{gbs:8.1f} GB/s  {bound} frac {frac:.3f}  [{plan}]")
+    marker()
     return rows
+
+
+MARKER_KERNEL = "spin_kernel"
+
+
+def marker() -> None:
+    """A tiny torch spin kernel on the stream: in a kernel trace it separates the
+    launches of one layer's timing from the next (see --rocprof-summary)."""
+    import torch
+    torch.cuda._sleep(1)
 
 
 def dominant(rows):
@@ -412,7 +424,55 @@ def rocprof_summary(args) -> int:
             print(f"| `{key[0]}` | {key[1]},{key[2]},{key[3]} | {key[4]} | {key[5]} | {key[6]} | "
                   f"{key[7]} | {key[8]} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | "
                   f"{v[len(v) // 2] / 1e3:.2f} |")
+        if args.bench_json:
+            layer_agreement(tr, args.bench_json, args.ref_json)
     return 0
+
+
+def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
+    """Per layer of the bench's layer timing (launches between two markers), the
+    trace's average kernel duration beside the bench's event time, and the
+    dominant kernel's average over the layers of its roofline figure."""
+    with open(bench_json) as fh:
+        res = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    layers = res.get("layers", [])
+    tr = sorted(tr, key=lambda r: int(r["Start_Timestamp"]))
+    segs, cur = [], None
+    for r in tr:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        if MARKER_KERNEL in r["Kernel_Name"]:
+            cur = []
+            segs.append(cur)
+        elif cur is not None and name.startswith("cvx::"):
+            cur.append((name, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    segs = [sg for sg in segs if sg]
+    if len(segs) != len(layers):
+        print(f"\n(layer agreement skipped: {len(segs)} marked segments, {len(layers)} layers)")
+        return
+    print()
+    print("Per layer of the bench's layer timing (the launches between two markers):")
+    print()
+    print("| layer | kernel | launches | trace avg us | bench us (graph of 20) |")
+    print("|---|---|---|---|---|")
+    avg = {}
+    for L, sg in zip(layers, segs):
+        d = [t for _, t in sg]
+        avg[L["layer"]] = sum(d) / len(d) / 1e3
+        print(f"| {L['layer']} | `{sg[0][0]}` | {len(d)} | {avg[L['layer']]:.2f} | {L['us']:.2f} |")
+    roof = res.get("roofline") or {}
+    use = roof.get("measured_layers") or []
+    if use and all(u in avg for u in use):
+        t = sum(avg[u] for u in use) / len(use)
+        print()
+        print(f"Dominant kernel `{roof.get('kernel')}` over {', '.join(use)}: trace average "
+              f"{t:.2f} us per launch (kernel start to end); the traced run's own `avg_launch_us` "
+              f"{roof.get('avg_launch_us')} us (its event times carry the tracer's per-launch cost).")
+        if ref_json:
+            with open(ref_json) as fh:
+                ref = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+            rr = ref.get("roofline") or {}
+            print(f"The untraced bench run of the same build: `avg_launch_us` {rr.get('avg_launch_us')} us "
+                  f"for `{rr.get('kernel')}` (frac {rr.get('frac')}).")
 
 
 def forward_time_ms(net, x, steps: int) -> float:
@@ -513,6 +573,10 @@ def main() -> int:
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="markdown table of a rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
+    ap.add_argument("--bench-json", default="",
+                    help="stdout of the traced bench run (for --rocprof-summary's per-layer agreement)")
+    ap.add_argument("--ref-json", default="",
+                    help="stdout of an untraced bench run of the same build, quoted beside it")
     ap.add_argument("--title", default="detector pipeline 640x640 b=1 (bench.py)",
                     help="workload named in a --rocprof-summary heading")
     args = ap.parse_args()
