@@ -169,7 +169,7 @@ def marker() -> None:
     torch.cuda._sleep(1)
 
 
-def dominant(rows):
+def dominant(rows, with_traffic: bool = True):
     """The kernel (exact template instantiation, as profilers name it) with the
     largest total time over the forward's layers, and its roofline position:
     algorithmic FLOPs (or bytes) per launch over its average launch time.
@@ -197,7 +197,7 @@ def dominant(rows):
         achieved = byts / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": traffic_for(name, [r["layer"] for r in use]),
+    roof.update({"traffic": traffic_for(name, [r["layer"] for r in use]) if with_traffic else None,
                  "kernel": name, "avg_launch_us": round(avg_us, 3),
                  "measured_layers": [r["layer"] for r in use],
                  "all_layers": [r["layer"] for r in group],
@@ -499,8 +499,9 @@ def other_workloads(layer_reps: int, steps: int):
     forward): the MNIST depthwise-separable net at batch 256 (with per-layer
     rows: its depthwise and pointwise layers are large enough to show bandwidth
     rather than launch latency) and at batch 1, the single depthwise layer, and
-    the detector pipeline at batch 8.  Per-layer inputs are reused across the
-    timed launches, so they are cache-resident (hot) figures."""
+    the detector pipeline at batch 8 (per layer too, with the roofline position
+    of its dominant kernel).  Per-layer inputs are reused across the timed
+    launches, so they are cache-resident (hot) figures."""
     import torch
     import workloads as wl
     from conv2d_batchnorm_activation_amd import accounting
@@ -509,7 +510,7 @@ def other_workloads(layer_reps: int, steps: int):
     for name, wk, layers in [("mnist_b256", wl.mnist_cnn(256), True),
                              ("mnist_b1", wl.mnist_cnn(1), False),
                              ("depthwise_48x28x28", wl.depthwise_single(), True),
-                             ("detector_b8", wl.detector_pipeline(8), False)]:
+                             ("detector_b8", wl.detector_pipeline(8), True)]:
         log(f"{name}: timing the forward")
         counts = accounting.layer_counts(wk.layers, wk.x.shape)
         flop = sum(c["flop"] for c in counts)
@@ -528,6 +529,9 @@ def other_workloads(layer_reps: int, steps: int):
                  "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
         if layers:
             entry["layers"] = per_layer(wk, net, counts, layer_reps)
+            # the same roofline position as the headline's, for this workload's
+            # dominant kernel (the traffic record covers the headline only)
+            entry["roofline"] = dominant(entry["layers"], with_traffic=False)
         out[name] = entry
         del net
         torch.cuda.empty_cache()
