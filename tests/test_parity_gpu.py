@@ -148,6 +148,19 @@ def test_dw_block(args):
     _forward_check(wl.dw_block(*args))
 
 
+@pytest.mark.parametrize("args", [
+    (1, 96, 128, 64, 64, 16, 2, wl.ACT_SILU, False),   # downscale, the stem is the list's output
+    (2, 45, 64, 30, 40, 16, 2, wl.ACT_RELU, True),     # batch 2, 15 output rows, a layer after
+    (1, 37, 48, 28, 28, 8, 1, wl.ACT_SILU, True),      # stride 1
+    (1, 20, 16, 40, 32, 16, 2, wl.ACT_NONE, False),    # upscale (clamped first source row)
+    (1, 64, 96, 48, 48, 40, 2, wl.ACT_SILU, True),     # 40 channels: a partial channel block
+    (1, 30, 50, 32, 32, 16, 2, wl.ACT_SILU, True),     # frame rows of 150 bytes
+])
+def test_prologue_then_stem(args):
+    # resize/normalise chained into a 3-channel stem inside one cvx_forward
+    _forward_check(wl.prologue_stem(*args))
+
+
 def test_detector_pipeline_b1():
     _forward_check(wl.detector_pipeline(1))
 

@@ -246,6 +246,22 @@ def detector_pipeline(batch: int, seed_index: int = 4) -> Workload:
     return Workload(f"detector_640_b{batch}", x, L)
 
 
+def prologue_stem(batch: int, src_h: int, src_w: int, dst_h: int, dst_w: int, cout: int,
+                  stride: int, act: int, tail: bool = False, seed_index: int = 9) -> Workload:
+    """u8 frames [N,src_h,src_w,3] -> resize/normalise to [N,3,dst_h,dst_w] ->
+    3x3 pad-1 conv 3->cout (stride 1 or 2) +BN+act, optionally followed by a
+    3x3 stride-1 conv cout->cout (so that the first convolution's output is an
+    intermediate rather than the list's output)."""
+    rng = rng_for(seed_index)
+    x = rng.integers(0, 256, (batch, src_h, src_w, 3), dtype=np.uint8)
+    L: List[Layer] = [Layer(KIND_PREPROC, inp=NET_INPUT, cin=3, cout=3, name="preprocess",
+                            dst_h=dst_h, dst_w=dst_w)]
+    L.append(conv_layer(rng, 3, cout, 3, stride, 1, act=act, inp=0, name="stem"))
+    if tail:
+        L.append(conv_layer(rng, cout, cout, 3, 1, 1, act=act, inp=1, name="tail"))
+    return Workload(f"prologue_{src_h}x{src_w}_{dst_h}x{dst_w}_s{stride}_b{batch}", x, L)
+
+
 def random_conv_case(seed: int, n: int, cin: int, h: int, w: int, cout: int, k: int,
                      stride: int, pad: int, groups: int = 1, act: int = ACT_SILU,
                      res_mode: int = RES_NONE, x_lo: float = -1.0) -> Tuple[np.ndarray, Layer]:
