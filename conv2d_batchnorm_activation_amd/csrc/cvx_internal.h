@@ -126,6 +126,8 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits);
 int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc);
 // workgroups of a configuration that fit one compute unit together
 int packed_occupancy(int kind, int k);
+// workgroup order of a layer: pixel tiles slowest (true) or row blocks slowest
+bool packed_spatial_order(const ConvGeom& g, int nmb);
 
 // igemm helpers used by the planner (defined next to the kernel).
 void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc);

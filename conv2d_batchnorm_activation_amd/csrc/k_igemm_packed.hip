@@ -50,6 +50,9 @@
 //     padding needs no code.
 //   * LDS stage buffer: [chunk j][weights | staged input region].
 #include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include <atomic>
 #include <chrono>
@@ -112,6 +115,9 @@ struct PackedArgs {
     int step_ci, step_r, step_c;    // 256 staged elements in mixed radix (channel, row, element)
     unsigned m_nb, l_nb, m_sp, l_sp, m_tpi, l_tpi;  // divide by n*tiles, splits, tiles per image
     int tr;                     // output rows of a 2-D tile (BN / tc)
+    int spatial;                // workgroup order: pixel tiles slowest (else row blocks slowest)
+    int nms;                    // row blocks x splits
+    unsigned m_ms, l_ms;        // divide by nms
     unsigned wp_bytes;
     int vout;                   // 16-byte epilogue accesses
     int act, res_mode;
@@ -140,16 +146,24 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     const int l32 = lane & 31;
 
     // Workgroup -> (row block, split, image, tile).  Consecutive workgroups are
-    // dealt to the eight XCDs in turn; numbering the tiles XCD by XCD keeps the
-    // tiles of one row block (same weights) and neighbouring pixels (shared
-    // input rows) in one XCD's L2.
+    // dealt to the eight XCDs in turn, and the tiles are numbered XCD by XCD, so
+    // that one XCD's L2 serves a contiguous range of them: with row blocks
+    // slowest, the tiles of one row block (same weights) and neighbouring
+    // pixels; with pixel tiles slowest, every row block of a band of pixels
+    // (same input rows), for layers whose input outweighs their weights.
     int mb, sp, b, tile;
     {
         const unsigned h = blockIdx.x, G8 = gridDim.x;
         const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
         const int L = (int)(xcd * base + min(xcd, rem) + i8);
-        const int ms = pdiv(L, a.m_nb, a.l_nb);
-        const int bt = L - ms * (a.n * a.tiles_per_img);
+        int ms, bt;
+        if (a.spatial) {
+            bt = pdiv(L, a.m_ms, a.l_ms);
+            ms = L - bt * a.nms;
+        } else {
+            ms = pdiv(L, a.m_nb, a.l_nb);
+            bt = L - ms * (a.n * a.tiles_per_img);
+        }
         mb = pdiv(ms, a.m_sp, a.l_sp);
         sp = ms - mb * a.splits;
         b = pdiv(bt, a.m_tpi, a.l_tpi);
@@ -811,6 +825,23 @@ static void launch_packed_k(int kind, bool vec, dim3 grid, size_t lds, hipStream
 
 static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Workgroup order of a layer: the one whose estimated fetches into the eight
+// XCDs' L2 caches are smaller.  Row blocks slowest: each row block's tiles fill
+// about 8/nmb XCDs, so every XCD group reads the whole input and its row
+// blocks' weights; pixel tiles slowest: each XCD reads its band of the input
+// and all the weights.  CVX_PACKED_ORDER=blocks|pixels overrides.
+bool packed_spatial_order(const ConvGeom& g, int nmb)
+{
+    const char* e = getenv("CVX_PACKED_ORDER");
+    if (e && e[0] == 'b') return false;
+    if (e && e[0] == 'p') return true;
+    const double in = (double)g.n * g.cin * g.h * g.w * 4;
+    const double w = (double)g.cout * g.cin * g.k * g.k * 4;
+    const double by_blocks = in * std::min(nmb, 8) + w * std::max(1.0, 8.0 / nmb);
+    const double by_pixels = in + w * 8;
+    return by_pixels < by_blocks;
+}
+
 hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
                                const float* scale, const float* bias, const float* res, float* y,
                                void* ws, hipStream_t s)
@@ -865,6 +896,12 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     }
     fastdiv_params(g.n * a.tiles_per_img, &a.m_nb, &a.l_nb);
     fastdiv_params(splits, &a.m_sp, &a.l_sp);
+    {
+        const int nmb = (g.cout + 31) / 32;
+        a.nms = nmb * splits;
+        fastdiv_params(a.nms, &a.m_ms, &a.l_ms);
+        a.spatial = packed_spatial_order(g, nmb) ? 1 : 0;
+    }
     fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
     a.tr = tc > 0 ? packed_tile_n(kind) / tc : 0;
     a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);

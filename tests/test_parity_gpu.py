@@ -382,6 +382,30 @@ def test_igemm_forced_tiles(force, layout, monkeypatch):
         check(y, oracle_conv(x, L, r), f"forced {force} seed {seed}")
 
 
+ORDERED = [(order, kind, tc, sk) for order in ("blocks", "pixels") for kind in range(3)
+           for tc in (0, 8) for sk in (1, 3)]
+
+
+@pytest.mark.parametrize("force", ORDERED, ids=[f"{o}-t{k}tc{t}sk{s}" for o, k, t, s in ORDERED])
+def test_packed_workgroup_order(force, monkeypatch):
+    # either workgroup order (row blocks slowest, or pixel tiles slowest) is a
+    # permutation of the same tiles, with and without a split reduction
+    order, kind, tc, sk = force
+    monkeypatch.setenv("CVX_PACKED_ORDER", order)
+    monkeypatch.setenv("CVX_IGEMM_TILE", "%d,%d,%d" % (kind, tc, sk))
+    for seed, n, cin, h, w, cout, k, s, p in [(210, 2, 48, 19, 27, 70, 3, 1, 1),
+                                              (211, 1, 40, 23, 21, 100, 3, 2, 1),
+                                              (212, 3, 64, 9, 13, 96, 1, 1, 0)]:
+        x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT)
+        d = cvx.make_desc(n, cin, h, w, cout, k, s, p, 1, wl.ACT_SILU, wl.RES_AFTER_ACT, PACKED)
+        oh, ow = cvx.cvx_conv_out_shape(d)
+        r = wl.residual_for(seed, (n, cout, oh, ow))
+        say(f"order {force} seed {seed}: {cvx.cvx_conv_plan(d)}")
+        y, ok = gpu_conv(x, L, r, PACKED)
+        assert ok, "write outside the output"
+        check(y, oracle_conv(x, L, r), f"order {force} seed {seed}")
+
+
 def _packed_setup(x, L, layout=PACKED):
     n, c, h, w = x.shape
     d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
