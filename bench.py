@@ -98,44 +98,132 @@ def residual_source(s_in, s_out, res_mode) -> str:
     return "input" if tuple(s_in) == tuple(s_out) else "own"
 
 
-def layer_residual(xin, s_out, res_mode):
+def layer_residual(xin, s_out, res_mode, alloc=None):
     import torch
     src = residual_source(xin.shape, s_out, res_mode)
     if src == "none":
         return None
-    return xin if src == "input" else torch.rand(s_out, device=xin.device)
+    if src == "input":
+        return xin
+    return alloc(s_out) if alloc is not None else torch.rand(s_out, device=xin.device)
 
 
-def per_layer(wk, net, counts, reps: int):
-    """Each layer alone, on inputs of its own shape, timed with events."""
+COLD_BYTES = 512 << 20   # a cold leg rotates at least this many bytes of distinct buffers
+MAX_COLD_SETS = 2048
+
+
+class Pool:
+    """Views into one large device buffer of random fp32 values (256-byte aligned),
+    for the cold leg's rotating buffer sets."""
+
+    def __init__(self, nbytes: int):
+        import torch
+        self.buf = torch.empty(nbytes // 4 + 64, device="cuda").uniform_()
+        self.off = 0
+
+    def take(self, shape, dtype=None):
+        import numpy as np
+        import torch
+        n = int(np.prod(shape))
+        if dtype == torch.uint8:
+            nf = (n + 3) // 4
+            t = self.buf[self.off:self.off + nf].view(torch.uint8)[:n].view(*shape)
+        else:
+            nf = n
+            t = self.buf[self.off:self.off + nf].view(*shape)
+        self.off += (nf + 63) // 64 * 64
+        assert self.off <= self.buf.numel(), "cold pool exhausted"
+        return t
+
+
+def layer_setup(wk, net, i, alloc):
+    """Layer i alone on buffers from `alloc(shape, dtype=None)`: (call, plan, kernel,
+    splitk).  The weights, scales and biases are the network's own."""
     import torch
+    from conv2d_batchnorm_activation_amd import cvx
+    L = wk.layers[i]
+    s_in, s_out = net.layer_io[i]
+    if L.kind == cvx.CVX_L_PREPROC:
+        src = alloc(s_in, torch.uint8)
+        dst = alloc(s_out)
+        fn = lambda src=src, dst=dst, L=L: cvx.cvx_preprocess_u8(src, dst, L.pre_mean, L.pre_std)
+        return fn, "preprocess", "cvx::k_preprocess", 1
+    lay = net.layers[i]
+    d = lay.conv
+    xin = alloc(s_in)
+    y = alloc(s_out)
+    res = layer_residual(xin, s_out, L.res_mode, alloc)
+    nws = cvx.cvx_conv_workspace_bytes(d)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+    fn = (lambda d=d, xin=xin, lay=lay, res=res, y=y, ws=ws, nws=nws:
+          cvx.cvx_conv_bn_act(d, xin, lay.w, lay.scale, lay.bias, res, y, ws, nws))
+    plan = cvx.cvx_conv_plan(d)
+    kernel = plan.split("kernel=")[1] if "kernel=" in plan else plan
+    splitk = int(plan.split("splitk=")[1].split()[0]) if "splitk=" in plan else 1
+    return fn, plan, kernel, splitk
+
+
+def hot_alloc(shape, dtype=None):
+    import torch
+    if dtype == torch.uint8:
+        return torch.randint(0, 256, tuple(shape), dtype=torch.uint8, device="cuda")
+    return torch.rand(tuple(shape), device="cuda")
+
+
+def time_rotating(fns, reps: int) -> float:
+    """Average milliseconds per launch over a graph that calls each of `fns` (each
+    on its own buffers) in turn, at least 20 launches, replayed until about `reps`
+    launches have been timed."""
+    inner = max(len(fns), 20)
+    seq = [fns[j % len(fns)] for j in range(inner)]
+    g = capture(lambda: [f() for f in seq], 1)
+    return time_graph(g, inner, max(2, reps // inner))
+
+
+def layer_buffer_bytes(wk, net, i) -> int:
+    """Bytes of the buffers one timed launch of layer i gets: its whole input
+    tensor (a strided 1x1 layer reads only part of it), its output and, when
+    the residual is a tensor of its own, that too; each rounded to 256 bytes."""
+    import numpy as np
+    from conv2d_batchnorm_activation_amd import cvx
+    L = wk.layers[i]
+    s_in, s_out = net.layer_io[i]
+    r = lambda b: (int(b) + 255) // 256 * 256
+    if L.kind == cvx.CVX_L_PREPROC:
+        return r(np.prod(s_in)) + r(4 * np.prod(s_out))
+    own = residual_source(s_in, s_out, L.res_mode) == "own"
+    return r(4 * np.prod(s_in)) + r(4 * np.prod(s_out)) * (2 if own else 1)
+
+
+def cold_layer_us(wk, net, i, reps: int) -> "tuple[float, int, int]":
+    """Layer i timed over rotating buffer sets totalling at least COLD_BYTES (at
+    most MAX_COLD_SETS sets), so that neither the L2 caches nor the 256 MB MALL
+    hold its input or output from one launch to the next: (us per launch,
+    sets, bytes per set)."""
+    import math
+    import torch
+    set_bytes = layer_buffer_bytes(wk, net, i)
+    sets = int(min(MAX_COLD_SETS, max(2, math.ceil(COLD_BYTES / set_bytes))))
+    pool = Pool(sets * (set_bytes + 1024) + (4 << 20))
+    fns = [layer_setup(wk, net, i, pool.take)[0] for _ in range(sets)]
+    ms = time_rotating(fns, max(reps, sets))
+    del fns, pool
+    torch.cuda.empty_cache()
+    return ms * 1e3, sets, set_bytes
+
+
+def per_layer(wk, net, counts, reps: int, cold: bool = True):
+    """Each layer alone, on inputs of its own shape, timed with events: `us` over
+    the same buffers every launch (cache-resident: hot), `us_cold` over rotating
+    buffer sets of at least 512 MB (cold).  Fractions of the HBM peak come from
+    the cold time; fractions of the MFMA peak from the hot time."""
     from conv2d_batchnorm_activation_amd import cvx
     rows = []
     for i, L in enumerate(wk.layers):
-        s_in, s_out = net.layer_io[i]
         c = counts[i]
-        if L.kind == cvx.CVX_L_PREPROC:
-            src = torch.from_numpy(wk.x).cuda()
-            dst = torch.empty(s_out, device="cuda")
-            fn = lambda src=src, dst=dst, L=L: cvx.cvx_preprocess_u8(src, dst, L.pre_mean, L.pre_std)
-            kernel = "cvx::k_preprocess"
-            plan = "preprocess"
-            splitk = 1
-        elif L.kind == cvx.CVX_L_CONV:
-            lay = net.layers[i]
-            d = lay.conv
-            xin = torch.rand(s_in, device="cuda")
-            y = torch.empty(s_out, device="cuda")
-            res = layer_residual(xin, s_out, L.res_mode)
-            nws = cvx.cvx_conv_workspace_bytes(d)
-            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
-            fn = (lambda d=d, xin=xin, lay=lay, res=res, y=y, ws=ws, nws=nws:
-                  cvx.cvx_conv_bn_act(d, xin, lay.w, lay.scale, lay.bias, res, y, ws, nws))
-            plan = cvx.cvx_conv_plan(d)
-            kernel = plan.split("kernel=")[1] if "kernel=" in plan else plan
-            splitk = int(plan.split("splitk=")[1].split()[0]) if "splitk=" in plan else 1
-        else:
+        if L.kind not in (cvx.CVX_L_PREPROC, cvx.CVX_L_CONV):
             continue
+        fn, plan, kernel, splitk = layer_setup(wk, net, i, hot_alloc)
         marker()
         ms_eager = time_launches(fn, reps)
         inner = 20
@@ -144,17 +232,30 @@ def per_layer(wk, net, counts, reps: int):
         gflops = c["flop"] / (ms * 1e-3) / 1e9
         gbs = c["bytes"] / (ms * 1e-3) / 1e9
         bound = "mfma" if c["ai"] >= RIDGE else "hbm"
-        frac = (gflops / (MFMA_F32_PEAK_TFLOPS * 1e3)) if bound == "mfma" else gbs / HBM_PEAK_GBS
+        us_cold, sets, set_bytes = (None, 0, 0)
+        if cold:
+            us_cold, sets, set_bytes = cold_layer_us(wk, net, i, reps)
+        gbs_cold = c["bytes"] / (us_cold * 1e-6) / 1e9 if us_cold else None
+        if bound == "mfma":
+            frac = gflops / (MFMA_F32_PEAK_TFLOPS * 1e3)
+        else:
+            frac = (gbs_cold if gbs_cold is not None else gbs) / HBM_PEAK_GBS
         attainable = min(MFMA_F32_PEAK_TFLOPS * 1e3, c["ai"] * HBM_PEAK_GBS) if c["flop"] else None
         rows.append({"layer": L.name, "plan": plan, "kernel": kernel, "splitk": splitk,
                      "us": round(us, 3), "us_eager": round(ms_eager * 1e3, 3),
+                     "us_cold": round(us_cold, 3) if us_cold else None, "cold_sets": sets,
+                     "cold_rotated_mbytes": round(sets * set_bytes / 1e6, 1),
                      "gflop": c["flop"] / 1e9, "mbytes": c["bytes"] / 1e6, "ai": round(c["ai"], 2),
-                     "gflops": round(gflops, 1), "gbs": round(gbs, 1), "bound": bound,
+                     "gflops": round(gflops, 1), "gbs_hot": round(gbs, 1),
+                     "gbs_cold": round(gbs_cold, 1) if gbs_cold else None, "bound": bound,
                      "frac_of_peak": round(frac, 4),
+                     "frac_of_peak_hot": round((gflops / (MFMA_F32_PEAK_TFLOPS * 1e3)) if bound == "mfma"
+                                               else gbs / HBM_PEAK_GBS, 4),
                      "frac_of_attainable": (round(gflops / attainable, 4) if attainable else
-                                            round(gbs / HBM_PEAK_GBS, 4))})
-        log(f"  {L.name:16s} {us:8.2f} us (eager {ms_eager * 1e3:6.2f})  {gflops:9.1f} GFLOP/s  "
-            f"{gbs:8.1f} GB/s  {bound} frac {frac:.3f}  [{plan}]")
+                                            round((gbs_cold or gbs) / HBM_PEAK_GBS, 4))})
+        cold_txt = f" cold {us_cold:7.2f} us {gbs_cold:7.1f} GB/s" if us_cold else ""
+        log(f"  {L.name:16s} {us:8.2f} us hot (eager {ms_eager * 1e3:6.2f}){cold_txt}  "
+            f"{gflops:9.1f} GFLOP/s  {gbs:8.1f} GB/s hot  {bound} frac {frac:.3f}  [{plan}]")
     marker()
     return rows
 
@@ -475,6 +576,102 @@ def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
                   f"for `{rr.get('kernel')}` (frac {rr.get('frac')}).")
 
 
+def gpu_clocks() -> dict:
+    """Current shader and memory clocks as rocm-smi reports them (for a record
+    against throttling), or an empty dict when the tool is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:  # noqa: BLE001 -- a record only; absent tool or format
+        return {}
+    out = {}
+    for card, v in d.items():
+        if isinstance(v, dict):
+            out[card] = {k: v[k] for k in v if "sclk" in k.lower() or "mclk" in k.lower()
+                         or "fclk" in k.lower()}
+    return out
+
+
+def host_info() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "nproc": affinity, "os_cpu_count": os.cpu_count()}
+
+
+def stats(per_step_ms) -> dict:
+    import numpy as np
+    a = np.asarray(per_step_ms, dtype=np.float64) * 1e3
+    return {"mean_us": round(float(a.mean()), 3), "p50_us": round(float(np.percentile(a, 50)), 3),
+            "p99_us": round(float(np.percentile(a, 99)), 3), "min_us": round(float(a.min()), 3),
+            "cv": round(float(a.std() / a.mean()), 4) if a.mean() > 0 else None, "n": int(a.size)}
+
+
+def timed_steps(fn, steps: int):
+    """`steps` back-to-back calls of `fn` on one stream with an event before and
+    after each: (total ms between the first and last event, per-call ms list).
+    The GPU runs the calls back to back (the host enqueues faster than they
+    run), so a per-call time is that forward's own duration."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        fn()
+        ev[k + 1].record()
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+    return ev[0].elapsed_time(ev[-1]), per
+
+
+def cold_forward_us(net, wk, steps: int) -> dict:
+    """Whole forwards over rotating (frame, workspace, output) sets totalling at
+    least 512 MB (at most 2048 sets: a tiny list rotates less, which the record
+    states), so every intermediate a forward writes and reads is absent from
+    the caches when it starts (the weights, a few MB, are shared)."""
+    import math
+    import torch
+    from conv2d_batchnorm_activation_amd import cvx
+    out_elems = 1
+    for v in net.out_shape:
+        out_elems *= v
+    ws_b = (max(net.ws_bytes, 256) + 255) // 256 * 256
+    set_bytes = wk.x.nbytes + ws_b + out_elems * 4
+    sets = int(min(MAX_COLD_SETS, max(2, math.ceil(COLD_BYTES / set_bytes))))
+    pool = Pool(sets * (set_bytes + 1024) + (4 << 20))
+    u8 = wk.x.dtype.name == "uint8"
+    bufs = [(pool.take(wk.x.shape, torch.uint8 if u8 else None), pool.take(net.out_shape),
+             pool.take((ws_b // 4,))) for _ in range(sets)]
+    k = [0]
+
+    def one():
+        xj, oj, wj = bufs[k[0] % sets]
+        k[0] += 1
+        cvx.cvx_forward(net.arr, xj, oj, wj, net.ws_bytes)
+    for _ in range(sets):
+        one()
+    _, per = timed_steps(one, max(steps, 2 * sets))
+    st = stats(per)
+    st["sets"] = sets
+    st["rotated_mbytes"] = round(sets * set_bytes / 1e6, 1)
+    del bufs, pool
+    torch.cuda.empty_cache()
+    return st
+
+
 def forward_time_ms(net, x, steps: int) -> float:
     """Milliseconds per forward: the forward captured once as a graph, replayed
     `steps` times between two events."""
@@ -510,6 +707,7 @@ def other_workloads(layer_reps: int, steps: int):
     for name, wk, layers in [("mnist_b256", wl.mnist_cnn(256), True),
                              ("mnist_b1", wl.mnist_cnn(1), False),
                              ("depthwise_48x28x28", wl.depthwise_single(), True),
+                             ("dw3x3_64x13x13_res", wl.sweep_layer("h_64x13_dw3x3"), True),
                              ("detector_b8", wl.detector_pipeline(8), True)]:
         log(f"{name}: timing the forward")
         counts = accounting.layer_counts(wk.layers, wk.x.shape)
@@ -519,14 +717,16 @@ def other_workloads(layer_reps: int, steps: int):
         x = torch.from_numpy(wk.x).cuda()
         for _ in range(3):
             net(x)
-        ms = time_launches(lambda: net(x), steps, warm=0)
+        total, per = timed_steps(lambda: net(x), steps)
+        ms = total / steps
         ms_graph = forward_time_ms(net, x, steps)
         log(f"{name}: {ms * 1e3:.1f} us/forward, {ms_graph * 1e3:.1f} us as a graph replay "
             f"({flop / 1e9:.3f} GFLOP, {byts / 1e6:.1f} MB)")
         entry = {"workload": wk.name, "batch": int(wk.x.shape[0]), "us_per_forward": round(ms * 1e3, 2),
                  "us_per_forward_graph": round(ms_graph * 1e3, 2),
                  "gflops": round(flop / (ms * 1e-3) / 1e9, 1),
-                 "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
+                 "gbs": round(byts / (ms * 1e-3) / 1e9, 1), "spread": stats(per),
+                 "cold": cold_forward_us(net, wk, steps)}
         if layers:
             entry["layers"] = per_layer(wk, net, counts, layer_reps)
             # the same roofline position as the headline's, for this workload's
@@ -549,7 +749,7 @@ def cpu_baseline(wk, flop_per_forward: float, budget_s: float):
             break
     dt = (time.perf_counter() - t0) / reps
     return {"value": round(flop_per_forward / dt / 1e9, 3), "unit": "GFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", **host_info(),
             "sample": f"{reps} full forwards of the batch-1 detector pipeline "
                       f"(fp64 direct 7-loop oracle, OpenMP), {dt * 1e3:.1f} ms each",
             "ms_per_forward": round(dt * 1e3, 2)}
@@ -615,30 +815,30 @@ def main() -> int:
     log(f"workload {wk.name}: {len(wk.layers)} layers, {flop / 1e9:.3f} GFLOP, "
         f"{bytes_ / 1e6:.1f} MB algorithmic per forward; workspace {net.ws_bytes / 1e6:.1f} MB")
 
+    clocks_start = gpu_clocks()
     # eager: one cvx_forward call per step (host planning is cached after the first)
     for _ in range(args.warmup):
         net(x)
     torch.cuda.synchronize()
-    ms_eager = time_launches(lambda: net(x), args.steps, warm=0)
-    # graph: the forward captured once, replayed once per step -- what a serving
-    # loop runs; the timed region is exactly `steps` forwards
-    g = capture(lambda: net(x), 1)
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
+    # the timed region: exactly `steps` forwards between two events, with an
+    # event after each forward for the spread
     t_wall = time.perf_counter()
-    s.record()
-    for _ in range(args.steps):
-        g.replay()
-    e.record()
-    e.synchronize()
-    torch.cuda.synchronize()
+    total_ms, per = timed_steps(lambda: net(x), args.steps)
     wall = time.perf_counter() - t_wall
-    ms = s.elapsed_time(e) / args.steps
-    log(f"forward: {ms_eager * 1e3:.1f} us/forward ({args.steps} cvx_forward calls), "
-        f"{ms * 1e3:.1f} us as a graph replay per forward (wall {wall:.3f} s)")
+    ms_eager = total_ms / args.steps
+    spread = stats(per)
+    # two more reruns of the same timed region (run-to-run spread)
+    reruns = [round(ms_eager * 1e3, 3)]
+    for _ in range(2):
+        t, _p = timed_steps(lambda: net(x), args.steps)
+        reruns.append(round(t / args.steps * 1e3, 3))
+    # graph: the forward captured once, replayed once per step
+    ms = forward_time_ms(net, x, args.steps)
+    cold = cold_forward_us(net, wk, args.steps)
+    log(f"forward: {ms_eager * 1e3:.1f} us/forward ({args.steps} cvx_forward calls; p50 "
+        f"{spread['p50_us']} p99 {spread['p99_us']} cv {spread['cv']}; reruns {reruns}), "
+        f"{ms * 1e3:.1f} us as a graph replay per forward, cold {cold['mean_us']} us "
+        f"(wall {wall:.3f} s)")
 
     rows = [] if args.no_layers else per_layer(wk, net, counts, args.layer_reps)
     roof = dominant(rows) if rows else None
@@ -653,10 +853,18 @@ def main() -> int:
         "ms_per_step": round(ms_eager, 5),
         "ms_per_forward": round(ms_eager, 5),
         "ms_per_forward_graph": round(ms, 5),
-        "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events "
-                  "(the library's own launch path); ms_per_forward_graph replays a HIP graph of "
-                  "one forward per step, whose launch boundary adds about 5 us; per-layer times "
-                  "from graphs of 20 back-to-back launches",
+        "forward_spread": spread,
+        "forward_reruns_us": reruns,
+        "forward_cold": cold,
+        "gpu_clocks": {"start": clocks_start, "end": None},
+        "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events, "
+                  "with an event after each forward for the spread (forward_spread: mean, p50, "
+                  "p99, cv of the per-forward times); forward_reruns_us repeats the timed region "
+                  "twice more; ms_per_forward_graph replays a HIP graph of one forward per step, "
+                  "whose launch boundary adds about 5 us; forward_cold rotates frame, workspace "
+                  "and output over sets totalling >= 512 MB. Per-layer `us` from graphs of 20 "
+                  "back-to-back launches on the same buffers (cache-resident: hot), `us_cold` "
+                  "over rotating buffer sets of >= 512 MB; HBM fractions use the cold time",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -674,6 +882,7 @@ def main() -> int:
     }
     if not args.no_others and not args.no_layers:
         result["other_workloads"] = other_workloads(args.layer_reps, args.steps)
+    result["gpu_clocks"]["end"] = gpu_clocks()
     if not args.no_cpu_baseline and args.batch == 1:
         result["cpu_baseline"] = cpu_baseline(wk, flop, args.cpu_budget)
     print(json.dumps(result))

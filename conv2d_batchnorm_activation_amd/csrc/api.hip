@@ -735,6 +735,11 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
             lp->nodes[i].last_use == i + 1) {
             lp->nodes[i].fuse_next = true;
             lp->nodes[i + 1].skipped = true;
+            // the fused kernel (run at i) writes the fc output (node i+1)
+            // while it still reads the pool's input: keep that input live
+            // through i+1 so placement never puts the fc output on it
+            if (L[i].in >= 0)
+                lp->nodes[L[i].in].last_use = std::max(lp->nodes[L[i].in].last_use, i + 1);
         }
     }
     // A 1x1 shortcut convolution (BN, no activation) whose one reader is a
@@ -777,7 +782,10 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
     for (int i = 0; i < nl - 1; ++i)
         if (!lp->nodes[i].fuse_next && !lp->nodes[i].merged)
             total += round_up(lp->nodes[i].out.elems() * sizeof(float));
-    const bool distinct = total <= kDistinctBytes;
+    // CVX_FORWARD_REUSE=1 takes the reuse branch for any size (tests of the
+    // placement at small batches)
+    const char* reuse_env = getenv("CVX_FORWARD_REUSE");
+    const bool distinct = total <= kDistinctBytes && !(reuse_env && reuse_env[0] == '1');
     std::vector<int> placed;
     for (int i = 0; i < nl - 1; ++i) {
         NodePlan& np = lp->nodes[i];

@@ -10,13 +10,14 @@
 //
 // Work decomposition.  A workgroup computes one tile of 32 output channels x
 // 32*NT output pixels with eight waves in two roles:
-//   * four producer waves (one per SIMD) only move data: every stage of CPS
-//     16-channel chunks goes global -> LDS with LDS-direct buffer loads, the
-//     weights as contiguous 1 KB blocks and the input region row by row;
-//   * four consumer waves (one per SIMD) only compute: each takes two of a
-//     chunk's eight channel pairs (wave w: pairs 2w, 2w+1), reads its operands
-//     from LDS and issues the matrix instructions; the four partial tiles are
-//     summed through LDS at the end.
+//   * four producer waves (one per SIMD) only move the input: every stage of
+//     CPS 16-channel chunks goes global -> LDS with LDS-direct buffer loads,
+//     the chunk's staged region row by row;
+//   * four consumer waves (one per SIMD) compute: each takes two of a chunk's
+//     eight channel pairs (wave w: pairs 2w, 2w+1), loads its own share of the
+//     chunk's packed weights global -> registers two stages ahead, reads the
+//     input operands from LDS and issues the matrix instructions; the four
+//     partial tiles are summed through LDS at the end.
 // A unit's vector-memory path takes ~30 clocks per 64-lane load, so a wave that
 // issues loads stalls while the queue drains; with the roles split, only the
 // producers wait there and the consumers' matrix pipes stay busy.  Three LDS
@@ -41,14 +42,15 @@
 //     (4)][slot (5)][lane][4] for 3x3 -- lane l holds output channel
 //     32*block + l%32 and input channels of pairs 2h and 2h+1, its 18 taps (9
 //     per pair) in five 16-byte slots; [block][chunk][h][lane][2] for 1x1.
-//     A (block, chunk) is one contiguous run of 20 KB (3x3) or 2 KB (1x1),
-//     copied to LDS unchanged.  ("YOLO26N Inference Optimisation", "NHWC
+//     A (block, chunk) is one contiguous run of 20 KB (3x3) or 2 KB (1x1);
+//     consumer wave h reads its quarter straight into registers, already in
+//     the operand's lane order.  ("YOLO26N Inference Optimisation", "NHWC
 //     migration", "Weight layout": weights are reordered once for the layout
 //     the kernels read.)
 //   * inputs: 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
 //     positions outside the image use out-of-range offsets and read as zero, so
 //     padding needs no code.
-//   * LDS stage buffer: [chunk j][weights | staged input region].
+//   * LDS stage buffer: [chunk j][staged input region] (REP floats per chunk).
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -764,8 +766,9 @@ int packed_occupancy(int kind, int k)
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;
 }
 
-// Vector-memory instructions the producers issue per chunk: the weights' 1 KB
-// blocks and four per input round.
+// Vector-memory instructions a workgroup issues per chunk: the consumers'
+// weight loads (counted as one per 1 KB of packed weights) and the producers'
+// four per input round.
 int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc)
 {
     const bool vec = g.w % 4 == 0;
