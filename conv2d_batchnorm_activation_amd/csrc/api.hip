@@ -445,6 +445,7 @@ const char* cvx_status_str(cvx_status s)
     case CVX_ERR_WORKSPACE: return "workspace missing or too small";
     case CVX_ERR_HIP: return "HIP runtime error on launch";
     case CVX_ERR_ARG: return "enum or index argument out of range";
+    case CVX_ERR_SCRATCH: return "the list needs more workspace than the static scratch array holds";
     default: return "unknown status";
     }
 }
@@ -977,6 +978,58 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
         if (cs != CVX_OK) return cs;
     }
     return CVX_OK;
+}
+
+}  // extern "C"
+
+// ====================================================== allocation-free forward
+// For callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops, harnesses that forbid it): the intermediates and split
+// partial sums live in one static device array per GPU.  Its device address is
+// looked up once per device, with that device current, and kept; host code
+// never passes the array's own name to a kernel (on the host that name is a
+// stand-in, not a device address).
+namespace {
+
+constexpr size_t kScratchBytes = CVX_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+cvx_status scratch_for_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CVX_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return CVX_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return CVX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cvx_static_scratch_bytes(void) { return kScratchBytes; }
+
+cvx_status cvx_forward_noalloc(const cvx_layer* layers, int n_layers, const void* input,
+                               float* output, void* stream)
+{
+    cvx_status st = CVX_OK;
+    const size_t need = cvx_forward_workspace_bytes(layers, n_layers, &st);
+    if (st != CVX_OK) return st;
+    if (need > kScratchBytes) return CVX_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != CVX_OK) return st;
+    return cvx_forward(layers, n_layers, input, output, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

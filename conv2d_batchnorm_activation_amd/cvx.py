@@ -31,7 +31,7 @@ CVX_INPUT, CVX_NO_RES = -1, -2
 CVX_W_OIHW, CVX_W_PACKED = 0, 1
 STATUS_NAMES = {0: "CVX_OK", -1: "CVX_ERR_NULL", -2: "CVX_ERR_SHAPE", -3: "CVX_ERR_UNSUPPORTED",
                 -4: "CVX_ERR_ALIGN", -5: "CVX_ERR_ALIAS", -6: "CVX_ERR_WORKSPACE",
-                -7: "CVX_ERR_HIP", -8: "CVX_ERR_ARG"}
+                -7: "CVX_ERR_HIP", -8: "CVX_ERR_ARG", -9: "CVX_ERR_SCRATCH"}
 
 
 class cvx_conv_desc(ctypes.Structure):
@@ -85,12 +85,16 @@ lib.cvx_forward_plan.argtypes = [_LP, _I, ctypes.c_char_p, _I]
 lib.cvx_forward_plan.restype = _I
 lib.cvx_forward.argtypes = [_LP, _I, _P, _P, _P, _Z, _P]
 lib.cvx_forward.restype = _I
+lib.cvx_static_scratch_bytes.argtypes = []
+lib.cvx_static_scratch_bytes.restype = _Z
+lib.cvx_forward_noalloc.argtypes = [_LP, _I, _P, _P, _P]
+lib.cvx_forward_noalloc.restype = _I
 
 #: every entry point include/cvx.h declares
 EXPORTS = ("cvx_status_str", "cvx_version", "cvx_conv_out_shape", "cvx_conv_plan",
            "cvx_conv_workspace_bytes", "cvx_packed_weights_bytes", "cvx_pack_weights", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
            "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward_plan",
-           "cvx_forward")
+           "cvx_forward", "cvx_static_scratch_bytes", "cvx_forward_noalloc")
 
 
 class CvxError(RuntimeError):
@@ -231,3 +235,13 @@ def cvx_forward(layers, inp, out, workspace, ws_bytes: Optional[int] = None, str
             workspace.numel() * workspace.element_size()
     _check(lib.cvx_forward(arr, n, _ptr(inp), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "cvx_forward")
+
+
+def cvx_static_scratch_bytes() -> int:
+    return lib.cvx_static_scratch_bytes()
+
+
+def cvx_forward_noalloc(layers, inp, out, stream=None) -> None:
+    arr, n = layers if isinstance(layers, tuple) else layer_array(layers)
+    _check(lib.cvx_forward_noalloc(arr, n, _ptr(inp), _ptr(out), _stream(stream)),
+           "cvx_forward_noalloc")

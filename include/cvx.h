@@ -43,7 +43,9 @@ enum {
     CVX_ERR_ALIAS = -5,       /* the output overlaps an input                      */
     CVX_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required           */
     CVX_ERR_HIP = -7,         /* the HIP runtime reported an error on launch       */
-    CVX_ERR_ARG = -8          /* an enum or index argument is out of range         */
+    CVX_ERR_ARG = -8,         /* an enum or index argument is out of range         */
+    CVX_ERR_SCRATCH = -9      /* cvx_forward_noalloc: the list needs more workspace
+                                 than the static scratch array holds               */
 };
 
 /* Activation applied in the epilogue. ReLU = max(0, v) ("Как я свертки ускорял",
@@ -263,6 +265,36 @@ CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char 
  */
 CVX_API cvx_status cvx_forward(const cvx_layer *layers, int n_layers, const void *input, float *output,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------- allocation-free variant */
+/* Size of the static device scratch array cvx_forward_noalloc uses (32 MiB),
+ * held by each GPU the library runs on until the process ends. */
+#define CVX_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* CVX_STATIC_SCRATCH_BYTES, for callers that load the library dynamically. */
+CVX_API size_t cvx_static_scratch_bytes(void);
+
+/*
+ * cvx_forward_noalloc -- cvx_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same layers, kernels and results as cvx_forward, with
+ * the workspace (intermediate activations, split partial sums and their
+ * arrival counters) taken from a static device array of
+ * CVX_STATIC_SCRATCH_BYTES per GPU instead of a caller buffer.  Calls no
+ * hipMalloc, hipFree or other allocating routine.  The array's device address
+ * is looked up once per device, on the first call with that device current.
+ *   layers, n_layers, input, output, stream: as for cvx_forward.
+ *   Returns CVX_ERR_SCRATCH (nothing launched) when
+ *   cvx_forward_workspace_bytes(layers, n_layers) exceeds CVX_STATIC_SCRATCH_BYTES,
+ *   and every error cvx_forward returns.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: intermediates are written
+ * before they are read, and split arrival counters carry a per-launch tag).
+ * Calls that overlap on one GPU (two streams, or two host threads) race on the
+ * array: serialise them.
+ */
+CVX_API cvx_status cvx_forward_noalloc(const cvx_layer *layers, int n_layers, const void *input,
+                                       float *output, void *stream);
 
 #ifdef __cplusplus
 }

@@ -338,3 +338,21 @@ def test_forward_list_validation():
     assert f(arr, n, X, X, WS, ws, None) == -5        # output == input
     assert f(arr, n, None, Y, WS, ws, None) == -1
     assert f(arr, 0, X, Y, WS, ws, None) == -2
+
+
+def test_forward_noalloc_rejects_lists_beyond_the_scratch():
+    """The allocation-free forward takes its workspace from a static array of
+    CVX_STATIC_SCRATCH_BYTES; a list that needs more is refused on the host
+    with CVX_ERR_SCRATCH before anything is launched, and list errors come
+    back as they do from cvx_forward."""
+    assert cvx.cvx_static_scratch_bytes() == 32 << 20
+    big, _ = _net_layers(wl.mnist_cnn(256), cvx.CVX_W_PACKED)
+    assert cvx.cvx_forward_workspace_bytes(big) > cvx.cvx_static_scratch_bytes()
+    arr, n = cvx.layer_array(big)
+    assert cvx.lib.cvx_forward_noalloc(arr, n, X, Y, None) == -9
+    assert cvx.cvx_status_str(-9) != "unknown status"
+    small, _ = _net_layers(wl.mnist_cnn(1))
+    arr, n = cvx.layer_array(small)
+    arr[3].in_ = 5  # forward reference
+    assert cvx.lib.cvx_forward_noalloc(arr, n, X, Y, None) == -8
+    assert cvx.lib.cvx_forward_noalloc(arr, 0, X, Y, None) == -2
