@@ -162,7 +162,7 @@ bool slices_ok(int nchunks, int sk)
 // trip through memory and the arrival count).  Up to packed_occupancy(kind)
 // workgroups share a compute unit, each slowing the others by ~30%.
 // `max_split` bounds the split (1 when no workspace is at hand).
-bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8)
+bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8, int only_kind = -1)
 {
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
     if (g.cin * g.k * g.k < 16 || g.cin < 4) return false;  // too short a reduction
@@ -174,6 +174,7 @@ bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8)
     double best = 1e300;
     GemmTile bt{-1, 0, 0, 0, 1};
     for (int kind = 0; kind < packed_num_kinds(); ++kind) {
+        if (only_kind >= 0 && kind != only_kind) continue;
         const int bn = packed_tile_n(kind);
         const int nt = bn / 32;
         const int cps = packed_chunks_per_stage(kind, g.k);
@@ -206,7 +207,8 @@ bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8)
     }
     int kind, tc, sk;
     if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < packed_num_kinds() &&
-        sk <= max_split && slices_ok(nchunks, sk) && packed_tile_fits(g, kind, tc, nullptr))
+        (only_kind < 0 || kind == only_kind) && sk <= max_split && slices_ok(nchunks, sk) &&
+        packed_tile_fits(g, kind, tc, nullptr))
         bt = GemmTile{kind, 32, packed_tile_n(kind), tc, sk};
     if (bt.kind < 0) return false;
     p->fam = FAM_IGEMM_PACKED;
@@ -638,6 +640,9 @@ struct NodePlan {
     int pair;            // the merged shortcut this layer computes with its own product, or -1
     int last_use;        // last layer index reading this output
     size_t offset;       // workspace offset of the output (non-final layers)
+    int chain_first;     // first layer of the chain run this layer belongs to, or -1
+    int chain_len;       // (first layer of a run) layers in the run
+    int chain_tc, chain_splits;  // the layer's tile in the chain
 };
 
 struct ListPlan {
@@ -653,6 +658,26 @@ constexpr size_t kAlign = 256;
 constexpr size_t kDistinctBytes = size_t(256) << 20;  // intermediates each in a region of their own
 constexpr int kReuseGap = 2;                          // layers after its last read a buffer waits
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// The tile a chained layer uses: the packed planner's choice among 32 x 32
+// tiles (its tc and split count), or the first 32 x 32 tile the chain takes.
+bool chain_choose(const ConvGeom& g, int* tc, int* splits)
+{
+    Plan p;
+    if (plan_packed(g, &p, 8, 0) && chain_layer_fits(g, p.tile.tc, nullptr)) {
+        *tc = p.tile.tc;
+        *splits = p.tile.splitk;
+        return true;
+    }
+    for (int t : {0, 32, 16, 8, 4}) {
+        if (chain_layer_fits(g, t, nullptr)) {
+            *tc = t;
+            *splits = 1;
+            return true;
+        }
+    }
+    return false;
+}
 
 cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
 {
@@ -818,6 +843,49 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
     for (int i = 0; i < nl; ++i)
         if (L[i].kind == CVX_L_CONV) lp->layer_ws = std::max(lp->layer_ws, lp->nodes[i].p.ws_bytes);
     lp->act_bytes = round_up(lp->act_bytes);
+    // With CVX_CHAIN=1, runs of consecutive dense packed layers become one
+    // chain launch each (k_chain.hip).  Measured on the detector it is slower
+    // than one launch per layer at batch 1 and 8 -- a layer there is one round
+    // of tiles, so the chain's critical path through the layers' rows is the
+    // sum of the tiles' durations plus the signalling -- so it is off by
+    // default.  Only with every intermediate in a region of its own: a
+    // chain's layers run at the same time, so no output may overwrite a buffer
+    // another layer of the run still reads.
+    for (int i = 0; i < nl; ++i) {
+        lp->nodes[i].chain_first = -1;
+        lp->nodes[i].chain_len = 0;
+    }
+    const char* chain_env = getenv("CVX_CHAIN");
+    if (distinct && chain_env && chain_env[0] == '1') {
+        std::vector<char> ok(nl, 0);
+        for (int i = 0; i < nl; ++i) {
+            NodePlan& np = lp->nodes[i];
+            if (L[i].kind != CVX_L_CONV || np.merged || np.pair >= 0 || np.p.fam != FAM_IGEMM_PACKED) continue;
+            ok[i] = chain_choose(np.g, &np.chain_tc, &np.chain_splits) ? 1 : 0;
+        }
+        std::vector<ChainLayerSpec> spec;
+        for (int i = 0; i < nl;) {
+            if (!ok[i]) {
+                ++i;
+                continue;
+            }
+            int j = i;
+            while (j < nl && ok[j] && j - i < kChainMax) ++j;
+            if (j - i >= 2) {
+                spec.assign(j - i, ChainLayerSpec{});
+                for (int k = i; k < j; ++k) {
+                    ChainLayerSpec& c = spec[k - i];
+                    c.g = lp->nodes[k].g;
+                    c.tc = lp->nodes[k].chain_tc;
+                    c.splits = lp->nodes[k].chain_splits;
+                    lp->nodes[k].chain_first = i;
+                }
+                lp->nodes[i].chain_len = j - i;
+                lp->layer_ws = std::max(lp->layer_ws, chain_workspace_bytes(spec.data(), j - i));
+            }
+            i = j;
+        }
+    }
     return CVX_OK;
 }
 
@@ -862,7 +930,11 @@ cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, in
         switch (l.kind) {
         case CVX_L_PREPROC: snprintf(line, sizeof(line), "preprocess"); break;
         case CVX_L_CONV:
-            if (np.merged) {
+            if (np.chain_first >= 0) {
+                const int f = np.chain_first;
+                snprintf(line, sizeof(line), "chain %d-%d k%d s%d tile=0 bm=32 bn=32 tc=%d splitk=%d kernel=cvx::k_chain",
+                         f, f + lp.nodes[f].chain_len - 1, np.g.k, np.g.stride, np.chain_tc, np.chain_splits);
+            } else if (np.merged) {
                 int into = -1;
                 for (int j = i + 1; j < n_layers; ++j)
                     if (lp.nodes[j].pair == i) into = j;
@@ -935,12 +1007,43 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
         return i == CVX_INPUT ? static_cast<const float*>(input) : out_ptr(i);
     };
     void* layer_ws = ws ? ws + lp.act_bytes : nullptr;
+    int chain_end = -1;  // layers before this index ran inside a chain launch
     for (int i = 0; i < n_layers; ++i) {
         const cvx_layer& l = layers[i];
         const NodePlan& np = lp.nodes[i];
-        if (np.skipped || np.merged) continue;
+        if (np.skipped || np.merged || i < chain_end) continue;
         hipError_t e = hipSuccess;
         cvx_status cs = CVX_OK;
+        if (np.chain_first == i && np.chain_len >= 2) {
+            ChainLayerSpec spec[kChainMax];
+            const int n = np.chain_len;
+            bool aligned = true;
+            for (int k = 0; k < n; ++k) {
+                const cvx_layer& lk = layers[i + k];
+                const NodePlan& nk = lp.nodes[i + k];
+                ChainLayerSpec& c = spec[k];
+                c.g = nk.g;
+                c.tc = nk.chain_tc;
+                c.splits = nk.chain_splits;
+                c.x = in_ptr(lk.in);
+                c.wp = lk.w;
+                c.scale = lk.scale;
+                c.bias = lk.bias;
+                c.res = lk.conv.res_mode != CVX_RES_NONE ? in_ptr(lk.res) : nullptr;
+                c.y = out_ptr(i + k);
+                c.in_dep = lk.in >= i && lk.in < i + n ? lk.in - i : -1;
+                c.res_dep = lk.conv.res_mode != CVX_RES_NONE && lk.res >= i && lk.res < i + n ? lk.res - i : -1;
+                for (const void* p : {(const void*)c.x, (const void*)c.y, (const void*)c.res})
+                    if (p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0) aligned = false;
+            }
+            // a list input off a 16-byte boundary: one launch per layer instead
+            if (aligned) {
+                e = launch_chain(spec, n, layer_ws, s);
+                if (e != hipSuccess) return CVX_ERR_HIP;
+                chain_end = i + n;
+                continue;
+            }
+        }
         switch (l.kind) {
         case CVX_L_PREPROC:
             e = launch_preprocess(static_cast<const unsigned char*>(input), np.in.n, np.in.h,

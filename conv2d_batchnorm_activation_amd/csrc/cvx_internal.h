@@ -128,6 +128,34 @@ int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc);
 int packed_occupancy(int kind, int k);
 // workgroup order of a layer: pixel tiles slowest (true) or row blocks slowest
 bool packed_spatial_order(const ConvGeom& g, int nmb);
+// Staged input region of one 16-channel chunk of a tile: rows, LDS floats per
+// row, 16-byte (vec) or 4-byte elements per row and per chunk, 256-lane load
+// rounds, LDS floats per chunk.
+struct PackedStage {
+    int pr, pcw, epr, re, rounds, rep;
+};
+void packed_stage_geometry(const ConvGeom& g, int kind, int tc, bool vec, PackedStage* st);
+// A fresh nonzero tag per launch for counters that outlive a launch.
+unsigned long long packed_next_epoch();
+void fastdiv_params(int d, unsigned* m, unsigned* l);
+
+// ---------------------------------------------------------------- layer chain
+// A run of dense 1x1/3x3 layers with packed weights, run as one launch
+// (k_chain.hip).  Each layer reads its input (and residual) either from a
+// tensor complete before the launch or from an earlier layer of the run.
+constexpr int kChainMax = 10;
+struct ChainLayerSpec {
+    ConvGeom g;
+    int tc, splits;            // 32x32 tiles: tc = 0 flat runs, else 2-D tiles tc columns wide
+    int in_dep, res_dep;       // index in the run of the layer producing x / res, or -1
+    const float *x, *wp, *scale, *bias, *res;
+    float* y;
+};
+// tile geometry the chain supports for this layer (32x32 tiles, 16-byte staging,
+// whole-quad epilogue), its LDS floats per stage buffer when it does
+bool chain_layer_fits(const ConvGeom& g, int tc, int* buf_floats);
+size_t chain_workspace_bytes(const ChainLayerSpec* L, int n);
+hipError_t launch_chain(const ChainLayerSpec* L, int n, void* ws, hipStream_t s);
 
 // igemm helpers used by the planner (defined next to the kernel).
 void igemm_region(const ConvGeom& g, int bn, int tc, int* pr, int* pc);

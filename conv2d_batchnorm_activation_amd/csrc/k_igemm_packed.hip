@@ -708,6 +708,17 @@ static Region packed_region(const ConvGeom& g, int kind, int tc, bool vec)
     return r;
 }
 
+void packed_stage_geometry(const ConvGeom& g, int kind, int tc, bool vec, PackedStage* st)
+{
+    const Region r = packed_region(g, kind, tc, vec);
+    st->pr = r.pr;
+    st->pcw = r.pcw;
+    st->epr = r.epr;
+    st->re = r.re;
+    st->rounds = r.rounds;
+    st->rep = r.rep;
+}
+
 static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
 {
     const int nt = kPacked[kind].nt;
@@ -786,7 +797,7 @@ void packed_kernel_name(const ConvGeom& g, int kind, char* buf, int len)
 
 // A fresh tag per split launch.  The first value mixes the clock and an address,
 // so a workspace's earlier contents practically never hold the same tag.
-static unsigned long long next_epoch()
+unsigned long long packed_next_epoch()
 {
     static std::atomic<unsigned long long> ctr{
         (((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() *
@@ -914,7 +925,7 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
         a.partial = static_cast<float*>(ws);
         a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
                                                       packed_partial_bytes(g, splits));
-        a.epoch = next_epoch();
+        a.epoch = packed_next_epoch();
     } else {
         a.partial = nullptr;
         a.ctr = nullptr;

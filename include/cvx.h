@@ -242,8 +242,9 @@ CVX_API size_t cvx_forward_workspace_bytes(const cvx_layer *layers, int n_layers
  * <text>", lines separated by '\n'): a convolution's cvx_conv_plan text; for a
  * pointwise layer that computes its block's 1x1 shortcut in the same kernel,
  * the pair's description and "shortcut=j"; "merged into i" for a layer run
- * inside layer i's kernel (that shortcut, or an FC after its GAP); "gap",
- * "gap+fc", "fc" or "preprocess" otherwise.  Validates the list as
+ * inside layer i's kernel (that shortcut, or an FC after its GAP); "chain i-j
+ * ..." for a layer of a chain launch (see cvx_forward); "gap", "gap+fc", "fc"
+ * or "preprocess" otherwise.  Validates the list as
  * cvx_forward_out_shape does; writes at most buf_len bytes (truncated to fit,
  * always NUL-terminated).  320 bytes per layer always suffice. */
 CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char *buf, int buf_len);
@@ -259,6 +260,14 @@ CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char 
  * activation, packed weights) whose only reader is a later packed 1x1 layer
  * adding it before its activation runs inside that layer's kernel, as one
  * product over both inputs' channels; its output is then never written.
+ * With the environment variable CVX_CHAIN=1, a run of 2 to 10 consecutive
+ * dense 1x1/3x3 layers with packed weights (rows a multiple of four floats)
+ * runs as one persistent launch whose tiles start once the rows they read are
+ * complete ("Как я свертки ускорял", "Идеи и следующие шаги", item 3: the
+ * whole network in one launch): same results, a larger workspace (the run's
+ * row counters).  It is off by default, as one launch per layer is faster on
+ * the detector workloads.  A wait in it that exceeds its bound poisons the
+ * affected outputs with NaN instead of hanging.
  *   input : device; fp32 NCHW, or u8 NHWC frames when layer 0 is CVX_L_PREPROC.
  *   output: device, shape from cvx_forward_out_shape; must not overlap input/workspace.
  *   workspace: device, >= cvx_forward_workspace_bytes(...) bytes, 256-byte aligned.

@@ -217,7 +217,8 @@ def _net_layers(wk, w_layout=cvx.CVX_W_OIHW):
     (lambda: wl.detector_pipeline(1), (1, 256, 20, 20)),
     (lambda: wl.detector_pipeline(8), (8, 256, 20, 20)),
 ])
-def test_forward_shapes_and_workspace(wk_fn, expect):
+def test_forward_shapes_and_workspace(wk_fn, expect, monkeypatch):
+    monkeypatch.setenv("CVX_CHAIN", "0")  # placement only (the chain's own words: test_chain_plan_on_the_host)
     wk = wk_fn()
     layers, shapes = _net_layers(wk)
     assert cvx.cvx_forward_out_shape(layers) == expect
@@ -253,14 +254,16 @@ def _block_list(n, act_skip, layout=cvx.CVX_W_PACKED):
 
 
 @pytest.mark.parametrize("n,merged", [(64, True), (8, False)])
-def test_forward_merges_1x1_shortcut(n, merged):
+def test_forward_merges_1x1_shortcut(n, merged, monkeypatch):
     """A 1x1 shortcut (BN, no activation) read only by a packed pointwise layer
     that adds it before its activation runs inside that layer's kernel: its
     output takes no workspace, while its input stays live one layer longer.
     First-fit places A, B, C (the shortcut's output) at 0, |A|, 2|A| and then D
     after C, as B and C are live while D is written; merged, D goes where C was.
     Below 64 workgroups the pointwise kernel does not take the layers and
-    nothing is merged; an activation on the shortcut also keeps it."""
+    nothing is merged; an activation on the shortcut also keeps it.  (One
+    launch per layer: a chain launch would add its control words.)"""
+    monkeypatch.setenv("CVX_CHAIN", "0")
     a = 4 * n * 32 * 64            # A = conv 1x1 output, B = dw output: 32 x 8 x 8
     c = 4 * n * 64 * 64            # C = shortcut output, D = pw output: 64 x 8 x 8
     kept = 2 * a + 2 * c
@@ -356,3 +359,23 @@ def test_forward_noalloc_rejects_lists_beyond_the_scratch():
     arr[3].in_ = 5  # forward reference
     assert cvx.lib.cvx_forward_noalloc(arr, n, X, Y, None) == -8
     assert cvx.lib.cvx_forward_noalloc(arr, 0, X, Y, None) == -2
+
+
+def test_chain_plan_on_the_host(monkeypatch):
+    """With CVX_CHAIN=1 the detector's nine dense packed layers (stem2 .. g)
+    plan as one chain launch; by default, and with the forced reuse placement
+    (a chain's layers run concurrently, so no region may be reused inside it),
+    every layer keeps a launch of its own; OIHW weights never chain."""
+    layers, _ = _net_layers(wl.detector_pipeline(1), cvx.CVX_W_PACKED)
+    plan = cvx.cvx_forward_plan(layers)
+    assert not any(p.startswith("chain") for p in plan)
+    ws_plain = cvx.cvx_forward_workspace_bytes(layers)
+    monkeypatch.setenv("CVX_CHAIN", "1")
+    plan = cvx.cvx_forward_plan(layers)
+    assert all(p.startswith("chain 2-10 ") and p.endswith("kernel=cvx::k_chain") for p in plan[2:]), plan
+    assert cvx.cvx_forward_workspace_bytes(layers) >= ws_plain
+    monkeypatch.setenv("CVX_FORWARD_REUSE", "1")
+    assert not any(p.startswith("chain") for p in cvx.cvx_forward_plan(layers))
+    monkeypatch.delenv("CVX_FORWARD_REUSE")
+    layers, _ = _net_layers(wl.detector_pipeline(1), cvx.CVX_W_OIHW)
+    assert not any(p.startswith("chain") for p in cvx.cvx_forward_plan(layers))

@@ -246,6 +246,37 @@ def detector_pipeline(batch: int, seed_index: int = 4) -> Workload:
     return Workload(f"detector_640_b{batch}", x, L)
 
 
+def dense_chain(batch: int, hw: int = 48, seed_index: int = 10) -> Workload:
+    """Eight dense 1x1/3x3 layers in a row (the shapes a chain launch runs),
+    with ragged channel counts (24, 40, 96), ragged tiles (hw/2 and hw/4 wide
+    maps), residuals from the list input, from the layer's own input and from
+    two layers back, added before or after the activation:
+
+      0 3x3 s1 24->24 SiLU  + input (after)      4 3x3 s1 64->64 SiLU  + out 2 (before)
+      1 3x3 s1 24->40 SiLU                       5 3x3 s2 64->96 SiLU
+      2 3x3 s2 40->64 ReLU                       6 1x1 s1 96->96 ReLU  + out 5 (before)
+      3 1x1 s1 64->64 SiLU  + out 2 (after)      7 3x3 s1 96->96 none  + out 5 (after)
+    """
+    rng = rng_for(seed_index)
+    x = rng.uniform(-1.0, 1.0, (batch, 24, hw, hw)).astype(np.float32)
+    S, R = ACT_SILU, ACT_RELU
+    spec = [  # (cin, cout, k, stride, act, res_mode, inp, res)
+        (24, 24, 3, 1, S, RES_AFTER_ACT, NET_INPUT, NET_INPUT),
+        (24, 40, 3, 1, S, RES_NONE, 0, NO_RES),
+        (40, 64, 3, 2, R, RES_NONE, 1, NO_RES),
+        (64, 64, 1, 1, S, RES_AFTER_ACT, 2, 2),
+        (64, 64, 3, 1, S, RES_BEFORE_ACT, 3, 2),
+        (64, 96, 3, 2, S, RES_NONE, 4, NO_RES),
+        (96, 96, 1, 1, R, RES_BEFORE_ACT, 5, 5),
+        (96, 96, 3, 1, ACT_NONE, RES_AFTER_ACT, 6, 5),
+    ]
+    L: List[Layer] = []
+    for i, (cin, cout, k, st, act, rm, inp, res) in enumerate(spec):
+        L.append(conv_layer(rng, cin, cout, k, st, k // 2, act=act, res_mode=rm, inp=inp, res=res,
+                            name=f"d{i}"))
+    return Workload(f"dense_chain_b{batch}_{hw}", x, L)
+
+
 def prologue_stem(batch: int, src_h: int, src_w: int, dst_h: int, dst_w: int, cout: int,
                   stride: int, act: int, tail: bool = False, seed_index: int = 9) -> Workload:
     """u8 frames [N,src_h,src_w,3] -> resize/normalise to [N,3,dst_h,dst_w] ->
