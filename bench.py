@@ -298,7 +298,8 @@ def dominant(rows, with_traffic: bool = True):
         achieved = byts / (avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": traffic_for(name, [r["layer"] for r in use]) if with_traffic else None,
+    plans = {r["layer"]: r["plan"] for r in use}
+    roof.update({"traffic": traffic_for(name, [r["layer"] for r in use], plans) if with_traffic else None,
                  "kernel": name, "avg_launch_us": round(avg_us, 3),
                  "measured_layers": [r["layer"] for r in use],
                  "all_layers": [r["layer"] for r in group],
@@ -340,12 +341,13 @@ def read_record(path: str) -> dict:
     return rec
 
 
-TRAFFIC_FILE = os.path.join(PROFILES, "detector640_b1_traffic.txt")
+TRAFFIC_FILE = os.path.join(PROFILES, "counters_detector640_b1.md")
 
 
-def traffic_for(kernel: str, layers) -> "float | None":
+def traffic_for(kernel: str, layers, plans=None) -> "float | None":
     """Mean measured HBM bytes per launch of `kernel` over `layers`, from the
-    committed counter record, or None (no record, or the sources changed)."""
+    committed counter record, or None (no record, the sources changed, or a
+    layer's plan is no longer the one the counters were taken with)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     want = kernel_sources_hash(kernel)
@@ -357,6 +359,9 @@ def traffic_for(kernel: str, layers) -> "float | None":
             if rec["kernel"] != kernel or rec["source_hash"] != want:
                 continue
             per = rec["traffic_bytes_per_layer"]
+            rp = rec.get("plan_per_layer", {})
+            if plans and any(rp.get(l) != plans.get(l) for l in layers):
+                continue
             if layers and all(l in per for l in layers):
                 return round(sum(per[l] for l in layers) / len(layers), 1)
     return None
@@ -364,122 +369,252 @@ def traffic_for(kernel: str, layers) -> "float | None":
 
 COPY_BYTES = 64 << 20  # the calibration copy: 64 MiB read, 64 MiB written
 
+PMC_WORKLOADS = {
+    "detector_b1": ("detector pipeline 640x640 b=1", lambda wl: wl.detector_pipeline(1)),
+    "detector_b8": ("detector pipeline 640x640 b=8", lambda wl: wl.detector_pipeline(8)),
+    "mnist_b256": ("MNIST depthwise-separable CNN b=256", lambda wl: wl.mnist_cnn(256)),
+}
+
 
 def pmc_probe(args) -> int:
     """Short run for counter passes: one 64 MiB device copy (the calibration),
-    then each layer of the forward alone, `reps` times, in order.  Prints a
-    manifest line (JSON) that --pmc-summary uses to map dispatches to layers."""
+    then each layer of the workload's forward alone, `reps` times, in order, on
+    the same buffers.  Prints a manifest line (JSON) that --pmc-summary uses to
+    map dispatches to layers."""
     import torch
     import workloads as wl
     from conv2d_batchnorm_activation_amd import accounting, cvx
     from conv2d_batchnorm_activation_amd.net import Net
-    wk = wl.detector_pipeline(1)
+    wk = PMC_WORKLOADS[args.workload][1](wl)
     net = Net(wk.layers, wk.x.shape)
     counts = accounting.layer_counts(wk.layers, wk.x.shape)
     calls = []
     for i, L in enumerate(wk.layers):
-        s_in, s_out = net.layer_io[i]
-        if L.kind == cvx.CVX_L_PREPROC:
-            src = torch.from_numpy(wk.x).cuda()
-            dst = torch.empty(s_out, device="cuda")
-            calls.append((L.name, "cvx::k_preprocess", 1, counts[i]["bytes"],
-                          lambda src=src, dst=dst, L=L: cvx.cvx_preprocess_u8(src, dst, L.pre_mean, L.pre_std)))
-        elif L.kind == cvx.CVX_L_CONV:
-            lay = net.layers[i]
-            d = lay.conv
-            xin = torch.rand(s_in, device="cuda")
-            y = torch.empty(s_out, device="cuda")
-            res = layer_residual(xin, s_out, L.res_mode)
-            nws = cvx.cvx_conv_workspace_bytes(d)
-            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
-            plan = cvx.cvx_conv_plan(d)
-            splitk = int(plan.split("splitk=")[1].split()[0])
-            calls.append((L.name, plan.split("kernel=")[1], splitk, counts[i]["bytes"],
-                          lambda d=d, xin=xin, lay=lay, res=res, y=y, ws=ws, nws=nws:
-                          cvx.cvx_conv_bn_act(d, xin, lay.w, lay.scale, lay.bias, res, y, ws, nws)))
+        if L.kind not in (cvx.CVX_L_PREPROC, cvx.CVX_L_CONV):
+            continue
+        fn, plan, kernel, splitk = layer_setup(wk, net, i, hot_alloc)
+        calls.append((L.name, kernel, splitk, counts[i]["bytes"], counts[i]["flop"], fn, plan))
     a = torch.empty(COPY_BYTES // 4, device="cuda").uniform_()
     b = torch.empty_like(a)
+    for c in calls:
+        c[5]()  # plans made and code loaded before the probed dispatches
     torch.cuda.synchronize()
     b.copy_(a)  # calibration: marks the start of the probed dispatches
-    for name, kernel, splitk, byts, fn in calls:
+    for c in calls:
         for _ in range(args.reps):
-            fn()
+            c[5]()
     torch.cuda.synchronize()
-    print(json.dumps({"manifest": [{"layer": n, "kernel": k, "splitk": s, "reps": args.reps,
-                                    "algorithmic_bytes": by} for n, k, s, by, _ in calls]}))
+    print(json.dumps({"workload": args.workload,
+                      "manifest": [{"layer": n, "kernel": k, "splitk": s, "reps": args.reps,
+                                    "algorithmic_bytes": by, "algorithmic_flop": fl, "plan": pl}
+                                   for n, k, s, by, fl, _, pl in calls]}))
     return 0
 
 
-def _dispatches(d: str, counter: str):
-    """[(dispatch id, kernel name, counter value)] from a rocprofv3 counter CSV."""
+def _dispatches(d: str):
+    """{counter: [(dispatch id, kernel name, value)]} from rocprofv3 counter CSVs
+    under d: instances summed, except GRBM counters (one per XCD, all counting
+    the same cycles), whose largest instance is taken."""
     import csv
     import glob
-    out = {}
+    per = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if r["Counter_Name"] != counter:
-                    continue
+                c = r["Counter_Name"]
                 k = int(r["Dispatch_Id"])
-                name, v = out.get(k, (r["Kernel_Name"], 0.0))
-                out[k] = (name, v + float(r["Counter_Value"]))
-    return [(k, n, v) for k, (n, v) in sorted(out.items())]
+                v = float(r["Counter_Value"])
+                name, old = per.setdefault(c, {}).get(k, (r["Kernel_Name"], None))
+                if old is None:
+                    new = v
+                elif c.startswith("GRBM_"):
+                    new = max(old, v)
+                else:
+                    new = old + v
+                per[c][k] = (name, new)
+    return {c: [(k, n, v) for k, (n, v) in sorted(m.items())] for c, m in per.items()}
+
+
+def _trace_dispatches(d: str):
+    """[(dispatch id, kernel name, duration ns)] from a rocprofv3 kernel trace under d."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                            float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))))
+    return sorted(out)
 
 
 def _probe_map(disp, manifest):
     """Counter value per probed layer: the calibration copy is the last copy
-    dispatch moving about COPY_BYTES before the layers; the cvx dispatches after
-    it follow the manifest, one dispatch per call (a split-K layer finishes its
-    tiles inside the same launch)."""
+    dispatch before the layers; the cvx dispatches after it follow the
+    manifest, one dispatch per call (a split-K layer finishes its tiles inside
+    the same launch)."""
     cal = [i for i, (_, n, v) in enumerate(disp) if "copy" in n.lower() and "cvx::" not in n]
     i0 = cal[-1]
-    cal_kib = disp[i0][2]
+    cal_v = disp[i0][2]
     rest = [(n, v) for _, n, v in disp[i0 + 1:] if "cvx::" in n]
     per, names, j = {}, {}, 0
     for m in manifest:
         vals = []
         for _ in range(m["reps"]):
             n, v = rest[j]
-            assert m["kernel"] in n, (m, n)
+            assert m["kernel"].split("<")[0] in n, (m, n)
             vals.append(v)
             j += 1
         per[m["layer"]] = sum(vals) / len(vals)
         names[m["layer"]] = n.split("(")[0].replace("void ", "").strip()  # the variant that ran
-    return cal_kib, per, names
+    return cal_v, per, names
+
+
+SIMDS = 1024  # 256 compute units x 4
+CLOCK_GHZ = 2.4  # MI355X peak engine clock (the peaks above assume it)
 
 
 def pmc_summary(args) -> int:
-    fetch_dir, write_dir = args.pmc_summary
     with open(args.manifest) as fh:
-        manifest = json.loads(fh.read().strip().splitlines()[-1])["manifest"]
-    cf, fetch, names = _probe_map(_dispatches(fetch_dir, "FETCH_SIZE"), manifest)
-    cw, write, _ = _probe_map(_dispatches(write_dir, "WRITE_SIZE"), manifest)
-    ff = COPY_BYTES / (cf * 1024.0)
-    fw = COPY_BYTES / (cw * 1024.0)
-    lines = ["# HBM traffic per launch, detector pipeline 640x640 b=1, each layer alone",
+        info = json.loads(fh.read().strip().splitlines()[-1])
+    manifest = info["manifest"]
+    title = PMC_WORKLOADS.get(info.get("workload", ""), ("", None))[0] or info.get("workload", "")
+    ctr, cal, names = {}, {}, {}
+    for d in args.pmc_summary:
+        for c, disp in _dispatches(d).items():
+            cal[c], ctr[c], nm = _probe_map(disp, manifest)
+            names.update(nm)
+        tr = _trace_dispatches(d)
+        if tr:
+            _, ctr["duration_ns"], nm = _probe_map(tr, manifest)
+            names.update(nm)
+    has = lambda *cs: all(c in ctr for c in cs)
+    lines = [f"# Counters per launch, {title}, each layer alone",
              "",
-             f"Counter passes (rocprofv3 --pmc, one counter block per run): {args.cmd}",
-             "",
-             f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {cf:.0f} KiB "
-             f"(scale {ff:.4f}) and WRITE_SIZE {cw:.0f} KiB (scale {fw:.4f}).",
-             "traffic = FETCH_SIZE*1024*scale_f + WRITE_SIZE*1024*scale_w, averaged over the calls.",
-             "",
-             "| layer | kernel | FETCH KiB | WRITE KiB | traffic bytes | algorithmic bytes | traffic/alg |",
-             "|---|---|---|---|---|---|---|"]
+             f"Counter passes (rocprofv3 --pmc, one counter group per run): {args.cmd}",
+             ""]
+    ff = fw = None
+    if has("FETCH_SIZE", "WRITE_SIZE"):
+        ff = COPY_BYTES / (cal["FETCH_SIZE"] * 1024.0)
+        fw = COPY_BYTES / (cal["WRITE_SIZE"] * 1024.0)
+        lines += [f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {cal['FETCH_SIZE']:.0f} KiB "
+                  f"(scale {ff:.4f}) and WRITE_SIZE {cal['WRITE_SIZE']:.0f} KiB (scale {fw:.4f}).",
+                  "traffic = FETCH_SIZE*1024*scale_f + WRITE_SIZE*1024*scale_w (L2 egress and writes: "
+                  "includes MALL hits, so it is an upper bound on HBM bytes), averaged over the calls."]
+    if has("SQ_VALU_MFMA_BUSY_CYCLES", "duration_ns"):
+        lines += [f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (kernel duration x {CLOCK_GHZ} GHz x 1024 SIMDs): "
+                  "the share of the launch's peak matrix-pipe cycles it kept busy, with the duration from a "
+                  "kernel trace of the same probe (GRBM_GUI_ACTIVE under --pmc also counts the profiler's "
+                  "serialisation of each dispatch, so the profiler's MfmaUtil is not used)."]
+    if has("SQ_INSTS_VALU_MFMA_MOPS_F32"):
+        lines += ["MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_F32 x 512 (fp32 matrix operations issued, padding "
+                  "included) against the layer's algorithmic 2*MAC count."]
+    lines += [""]
+    head = ["layer", "kernel"]
+    if ff is not None:
+        head += ["FETCH KiB", "WRITE KiB", "traffic bytes", "algorithmic bytes", "traffic/alg"]
+    if has("duration_ns"):
+        head += ["trace us"]
+        if ff is not None:
+            head += ["traffic GB/s", "of HBM peak"]
+    if has("SQ_VALU_MFMA_BUSY_CYCLES", "duration_ns"):
+        head += ["MFMA busy"]
+    if has("SQ_INSTS_VALU_MFMA_MOPS_F32"):
+        head += ["MFMA FLOP / alg"]
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES"):
+        if c in ctr:
+            head.append(c)
+    lines += ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
     recs = {}
     for m in manifest:
         L = m["layer"]
-        t = fetch[L] * 1024 * ff + write[L] * 1024 * fw
-        k = names[L]
-        lines.append(f"| {L} | `{k}` | {fetch[L]:.0f} | {write[L]:.0f} | {t:.0f} | "
-                     f"{m['algorithmic_bytes']:.0f} | {t / m['algorithmic_bytes']:.2f} |")
-        r = recs.setdefault(k, {"kernel": k, "source_hash": kernel_sources_hash(k),
-                                "traffic_bytes_per_layer": {}})
-        r["traffic_bytes_per_layer"][L] = round(t, 1)
-    lines.append("")
-    for r in recs.values():
-        lines.append("record: " + json.dumps(r))
+        k = names.get(L, m["kernel"])
+        row = [L, f"`{k}`"]
+        if ff is not None:
+            t = ctr["FETCH_SIZE"][L] * 1024 * ff + ctr["WRITE_SIZE"][L] * 1024 * fw
+            row += [f"{ctr['FETCH_SIZE'][L]:.0f}", f"{ctr['WRITE_SIZE'][L]:.0f}", f"{t:.0f}",
+                    f"{m['algorithmic_bytes']:.0f}", f"{t / m['algorithmic_bytes']:.2f}"]
+            r = recs.setdefault(k, {"kernel": k, "source_hash": kernel_sources_hash(k),
+                                    "traffic_bytes_per_layer": {}, "plan_per_layer": {}})
+            r["traffic_bytes_per_layer"][L] = round(t, 1)
+            r["plan_per_layer"][L] = m.get("plan")
+        if has("duration_ns"):
+            dur = ctr["duration_ns"][L]
+            row += [f"{dur / 1e3:.2f}"]
+            if ff is not None:
+                row += [f"{t / dur:.0f}", f"{t / dur / HBM_PEAK_GBS:.3f}"]
+        if has("SQ_VALU_MFMA_BUSY_CYCLES", "duration_ns"):
+            dur = ctr["duration_ns"][L]
+            row += [f"{ctr['SQ_VALU_MFMA_BUSY_CYCLES'][L] / (dur * CLOCK_GHZ * SIMDS):.3f}"]
+        if has("SQ_INSTS_VALU_MFMA_MOPS_F32"):
+            fl = m.get("algorithmic_flop", 0.0)
+            row += [f"{ctr['SQ_INSTS_VALU_MFMA_MOPS_F32'][L] * 512 / fl:.2f}" if fl else "-"]
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES"):
+            if c in ctr:
+                row.append(f"{ctr[c][L]:.0f}")
+        lines.append("| " + " | ".join(row) + " |")
+    if recs:
+        lines.append("")
+        for r in recs.values():
+            lines.append("record: " + json.dumps(r))
     print("\n".join(lines))
+    return 0
+
+
+def tile_sweep(args) -> int:
+    """Every packed tile configuration (kind x tc x split, forced through
+    CVX_IGEMM_TILE) of every dense packed layer of a workload, each timed alone
+    like the per-layer rows (a graph of 20 launches, hot), against the
+    planner's own choice.  Prints a markdown table (the per-shape tile choice's
+    evidence) and one JSON line per layer."""
+    import torch
+    import workloads as wl
+    from conv2d_batchnorm_activation_amd import cvx
+    from conv2d_batchnorm_activation_amd.net import Net
+    wk = PMC_WORKLOADS[args.workload][1](wl)
+    net = Net(wk.layers, wk.x.shape)
+    rows = []
+    print(f"# Tile sweep, {PMC_WORKLOADS[args.workload][0]}: every packed configuration of each dense layer\n")
+    print(f"Command: {args.cmd}\n")
+    print("Each configuration timed alone as a graph of 20 launches on the same buffers (hot), "
+          f"{args.layer_reps} launches; `default` is the planner's choice.\n")
+    print("| layer | default plan | default us | best plan | best us | default / best | configurations |")
+    print("|---|---|---|---|---|---|---|")
+    for i, L in enumerate(wk.layers):
+        if L.kind != cvx.CVX_L_CONV:
+            continue
+        d = net.layers[i].conv
+        plan0 = cvx.cvx_conv_plan(d)
+        if "igemm_packed" not in plan0:
+            continue
+        def timed():
+            fn, plan, _, _ = layer_setup(wk, net, i, hot_alloc)
+            inner = 20
+            ms = time_graph(capture(fn, inner), inner, max(1, args.layer_reps // inner))
+            return ms * 1e3, plan.split(" kernel")[0]
+        os.environ.pop("CVX_IGEMM_TILE", None)
+        us0, p0 = timed()
+        res = [(us0, p0)]
+        seen = {p0}
+        for kind in range(3):
+            for tc in (0, 4, 8, 16, 32, 64, 128):
+                for sk in (1, 2, 3, 4, 6, 8):
+                    os.environ["CVX_IGEMM_TILE"] = f"{kind},{tc},{sk}"
+                    p = cvx.cvx_conv_plan(d).split(" kernel")[0]
+                    if p in seen or f"tile={kind} " not in p or f"tc={tc} " not in p or f"splitk={sk}" not in p:
+                        continue
+                    seen.add(p)
+                    res.append(timed())
+        os.environ.pop("CVX_IGEMM_TILE", None)
+        best = min(res)
+        print(f"| {L.name} | {p0} | {us0:.2f} | {best[1]} | {best[0]:.2f} | {us0 / best[0]:.3f} | {len(res)} |",
+              flush=True)
+        rows.append({"layer": L.name, "default": p0, "default_us": round(us0, 3), "best": best[1],
+                     "best_us": round(best[0], 3), "all": [[p, round(u, 3)] for u, p in sorted(res)]})
+        torch.cuda.synchronize()
+    print()
+    for r in rows:
+        print("sweep: " + json.dumps(r))
     return 0
 
 
@@ -771,9 +906,14 @@ def main() -> int:
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for rocprofv3 counter passes (prints a manifest line)")
     ap.add_argument("--reps", type=int, default=3, help="calls per layer in --pmc-probe")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two counter passes into the traffic record (stdout)")
+    ap.add_argument("--workload", default="detector_b1", choices=sorted(PMC_WORKLOADS),
+                    help="workload of --pmc-probe")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="turn counter passes (one output directory each) into a table and, with "
+                         "FETCH_SIZE and WRITE_SIZE, the traffic record (stdout)")
     ap.add_argument("--manifest", help="stdout of the --pmc-probe run (for --pmc-summary)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every packed tile configuration of each dense layer of --workload")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="markdown table of a rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--cmd", default="", help="command line recorded in a summary")
@@ -803,6 +943,8 @@ def main() -> int:
         return 1
     if args.pmc_probe:
         return pmc_probe(args)
+    if args.tile_sweep:
+        return tile_sweep(args)
     if args.others_only:
         print(json.dumps({"other_workloads": other_workloads(args.layer_reps, args.steps)}))
         return 0

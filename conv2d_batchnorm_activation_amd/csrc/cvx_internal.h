@@ -139,6 +139,15 @@ void packed_stage_geometry(const ConvGeom& g, int kind, int tc, bool vec, Packed
 unsigned long long packed_next_epoch();
 void fastdiv_params(int d, unsigned* m, unsigned* l);
 
+// ------------------------------------------------------ channels-last layers
+// Dense 1x1/3x3 on NHWC tensors stored as fp32 or fp16 (k_nhwc.hip).
+bool nhwc_supported(const ConvGeom& g, int dtype);
+long nhwc_packed_weight_elems(const ConvGeom& g, int dtype);
+hipError_t launch_pack_nhwc(const ConvGeom& g, int dtype, const float* w, void* wp, hipStream_t s);
+hipError_t launch_conv_nhwc(const ConvGeom& g, int dtype, const void* x, const void* wp, const float* scale,
+                            const float* bias, const void* res, void* y, hipStream_t s);
+void nhwc_describe(const ConvGeom& g, int dtype, char* buf, int len);
+
 // ---------------------------------------------------------------- layer chain
 // A run of dense 1x1/3x3 layers with packed weights, run as one launch
 // (k_chain.hip).  Each layer reads its input (and residual) either from a

@@ -29,6 +29,7 @@ CVX_RES_NONE, CVX_RES_BEFORE_ACT, CVX_RES_AFTER_ACT = 0, 1, 2
 CVX_L_CONV, CVX_L_GAP, CVX_L_FC, CVX_L_PREPROC = 0, 1, 2, 3
 CVX_INPUT, CVX_NO_RES = -1, -2
 CVX_W_OIHW, CVX_W_PACKED = 0, 1
+CVX_DT_F32, CVX_DT_F16 = 0, 1
 STATUS_NAMES = {0: "CVX_OK", -1: "CVX_ERR_NULL", -2: "CVX_ERR_SHAPE", -3: "CVX_ERR_UNSUPPORTED",
                 -4: "CVX_ERR_ALIGN", -5: "CVX_ERR_ALIAS", -6: "CVX_ERR_WORKSPACE",
                 -7: "CVX_ERR_HIP", -8: "CVX_ERR_ARG", -9: "CVX_ERR_SCRATCH"}
@@ -85,6 +86,14 @@ lib.cvx_forward_plan.argtypes = [_LP, _I, ctypes.c_char_p, _I]
 lib.cvx_forward_plan.restype = _I
 lib.cvx_forward.argtypes = [_LP, _I, _P, _P, _P, _Z, _P]
 lib.cvx_forward.restype = _I
+lib.cvx_nhwc_packed_weights_bytes.argtypes = [_DP, _I]
+lib.cvx_nhwc_packed_weights_bytes.restype = _Z
+lib.cvx_nhwc_plan.argtypes = [_DP, _I, ctypes.c_char_p, _I]
+lib.cvx_nhwc_plan.restype = _I
+lib.cvx_nhwc_pack_weights.argtypes = [_DP, _I, _P, _P, _P]
+lib.cvx_nhwc_pack_weights.restype = _I
+lib.cvx_conv_bn_act_nhwc.argtypes = [_DP, _I, _P, _P, _P, _P, _P, _P, _P]
+lib.cvx_conv_bn_act_nhwc.restype = _I
 lib.cvx_static_scratch_bytes.argtypes = []
 lib.cvx_static_scratch_bytes.restype = _Z
 lib.cvx_forward_noalloc.argtypes = [_LP, _I, _P, _P, _P]
@@ -94,7 +103,8 @@ lib.cvx_forward_noalloc.restype = _I
 EXPORTS = ("cvx_status_str", "cvx_version", "cvx_conv_out_shape", "cvx_conv_plan",
            "cvx_conv_workspace_bytes", "cvx_packed_weights_bytes", "cvx_pack_weights", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
            "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward_plan",
-           "cvx_forward", "cvx_static_scratch_bytes", "cvx_forward_noalloc")
+           "cvx_forward", "cvx_nhwc_packed_weights_bytes", "cvx_nhwc_plan", "cvx_nhwc_pack_weights",
+           "cvx_conv_bn_act_nhwc", "cvx_static_scratch_bytes", "cvx_forward_noalloc")
 
 
 class CvxError(RuntimeError):
@@ -245,3 +255,25 @@ def cvx_forward_noalloc(layers, inp, out, stream=None) -> None:
     arr, n = layers if isinstance(layers, tuple) else layer_array(layers)
     _check(lib.cvx_forward_noalloc(arr, n, _ptr(inp), _ptr(out), _stream(stream)),
            "cvx_forward_noalloc")
+
+
+def cvx_nhwc_packed_weights_bytes(desc: cvx_conv_desc, dtype: int) -> int:
+    return lib.cvx_nhwc_packed_weights_bytes(ctypes.byref(desc), dtype)
+
+
+def cvx_nhwc_plan(desc: cvx_conv_desc, dtype: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.cvx_nhwc_plan(ctypes.byref(desc), dtype, buf, 256), "cvx_nhwc_plan")
+    return buf.value.decode()
+
+
+def cvx_nhwc_pack_weights(desc: cvx_conv_desc, dtype: int, w_oihw, w_packed, stream=None) -> None:
+    _check(lib.cvx_nhwc_pack_weights(ctypes.byref(desc), dtype, _ptr(w_oihw), _ptr(w_packed),
+                                     _stream(stream)), "cvx_nhwc_pack_weights")
+
+
+def cvx_conv_bn_act_nhwc(desc: cvx_conv_desc, dtype: int, x, w_packed, scale, bias, residual, y,
+                         stream=None) -> None:
+    _check(lib.cvx_conv_bn_act_nhwc(ctypes.byref(desc), dtype, _ptr(x), _ptr(w_packed), _ptr(scale),
+                                    _ptr(bias), _ptr(residual), _ptr(y), _stream(stream)),
+           "cvx_conv_bn_act_nhwc")

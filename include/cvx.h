@@ -275,6 +275,51 @@ CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char 
 CVX_API cvx_status cvx_forward(const cvx_layer *layers, int n_layers, const void *input, float *output,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------ channels-last variant */
+/* Element type of a channels-last layer's activations and weights.  Sums are
+ * always accumulated in fp32 and the folded BatchNorm, residual and activation
+ * are applied in fp32; CVX_DT_F16 rounds the stored output to IEEE half. */
+enum { CVX_DT_F32 = 0, CVX_DT_F16 = 1 };
+
+/* Bytes of the packed weights cvx_nhwc_pack_weights writes for `d` and
+ * `dtype` (0 when the layer is not supported by the channels-last kernels).
+ * Host only. */
+CVX_API size_t cvx_nhwc_packed_weights_bytes(const cvx_conv_desc *d, int dtype);
+
+/* Host-only query: the channels-last kernel and tile chosen for `d`, like
+ * cvx_conv_plan. */
+CVX_API cvx_status cvx_nhwc_plan(const cvx_conv_desc *d, int dtype, char *buf, int buf_len);
+
+/*
+ * cvx_nhwc_pack_weights -- one-time transform of OIHW fp32 weights into the
+ * order the channels-last kernels read (the weights reordered once to match
+ * the NHWC layout: "YOLO26N Inference Optimisation", "NHWC migration --
+ * detailed scope", "Weight layout"), rounded to `dtype` (fp16 rounds to
+ * nearest even).  Padded with zeros to whole 32-row and 16/32-channel groups.
+ *   w_oihw  : device fp32 [c_out][c_in][kh][kw], read only.
+ *   w_packed: device, cvx_nhwc_packed_weights_bytes(d, dtype) bytes, written.
+ */
+CVX_API cvx_status cvx_nhwc_pack_weights(const cvx_conv_desc *d, int dtype, const float *w_oihw,
+                                         void *w_packed, void *stream);
+
+/*
+ * cvx_conv_bn_act_nhwc -- the fused layer of cvx_conv_bn_act on channels-last
+ * tensors: x [n][h][w][c_in], y and residual [n][oh][ow][c_out], all of
+ * element type `dtype`; the same arithmetic (cross-correlation, folded BN,
+ * residual before or after the activation), fp32 accumulation
+ * ("YOLO26N Inference Optimisation", "NHWC migration -- detailed scope";
+ * "Как я свертки ускорял", "Идеи и следующие шаги", item 1: fp16).
+ * Supported: groups 1, 1x1 or 3x3, stride 1 or 2, c_in a multiple of 4 (fp32)
+ * or 8 (fp16), c_out a multiple of 4; else CVX_ERR_UNSUPPORTED.
+ * d->w_layout is ignored (the weights are cvx_nhwc_pack_weights' output).
+ *   scale, bias: device fp32 [c_out] (cvx_fold_bn).
+ *   x, y, residual: device, 16-byte aligned; y must not overlap the inputs;
+ *   residual required iff d->res_mode != CVX_RES_NONE (may equal x).
+ */
+CVX_API cvx_status cvx_conv_bn_act_nhwc(const cvx_conv_desc *d, int dtype, const void *x,
+                                        const void *w_packed, const float *scale, const float *bias,
+                                        const void *residual, void *y, void *stream);
+
 /* ------------------------------------------------- allocation-free variant */
 /* Size of the static device scratch array cvx_forward_noalloc uses (32 MiB),
  * held by each GPU the library runs on until the process ends. */

@@ -379,3 +379,28 @@ def test_chain_plan_on_the_host(monkeypatch):
     monkeypatch.delenv("CVX_FORWARD_REUSE")
     layers, _ = _net_layers(wl.detector_pipeline(1), cvx.CVX_W_OIHW)
     assert not any(p.startswith("chain") for p in cvx.cvx_forward_plan(layers))
+
+
+def test_nhwc_host_validation():
+    """The channels-last entry points reject unsupported layers and bad
+    arguments on the host, before any launch."""
+    F32, F16 = cvx.CVX_DT_F32, cvx.CVX_DT_F16
+    f = cvx.lib.cvx_conv_bn_act_nhwc
+    d = _desc(c_in=12, c_out=32)  # 12 channels: not whole 16-byte fp16 pieces
+    assert cvx.cvx_nhwc_packed_weights_bytes(d, F16) == 0
+    assert cvx.cvx_nhwc_packed_weights_bytes(d, F32) > 0
+    assert f(ctypes.byref(d), F16, X, W, S, B, None, Y, None) == -3
+    d = _desc(c_in=16, c_out=32, h=8, w=8)
+    assert f(ctypes.byref(d), 7, X, W, S, B, None, Y, None) == -8          # dtype
+    assert f(ctypes.byref(d), F16, X + 4, W, S, B, None, Y, None) == -4    # 16-byte alignment
+    assert f(ctypes.byref(d), F16, None, W, S, B, None, Y, None) == -1
+    assert f(ctypes.byref(d), F16, X, W, S, B, None, X, None) == -5        # y overlaps x
+    dr = _desc(c_in=16, c_out=16, h=8, w=8, res_mode=cvx.CVX_RES_AFTER_ACT)
+    assert f(ctypes.byref(dr), F16, X, W, S, B, None, Y, None) == -1       # residual missing
+    dg = _desc(c_in=16, c_out=16, h=8, w=8, groups=16)
+    assert f(ctypes.byref(dg), F32, X, W, S, B, None, Y, None) == -3       # grouped
+    # sizes: 32-row blocks x 16 (fp32) or 32 (fp16) input channels x taps
+    d = _desc(c_in=64, c_out=64, h=8, w=8)
+    assert cvx.cvx_nhwc_packed_weights_bytes(d, F32) == 2 * 4 * 9 * 32 * 16 * 4
+    assert cvx.cvx_nhwc_packed_weights_bytes(d, F16) == 2 * 2 * 9 * 32 * 32 * 2
+    assert "k_conv_nhwc<_Float16, 3" in cvx.cvx_nhwc_plan(d, F16)
