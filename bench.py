@@ -873,6 +873,71 @@ def other_workloads(layer_reps: int, steps: int):
     return out
 
 
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix
+
+
+def layout_comparison(reps: int):
+    """The detector's dense layers a..g alone at batch 1 and 8, each as the NCHW
+    fp32 layer (packed weights, the production path), the NHWC fp32 layer and
+    the NHWC fp16 layer (fp32 accumulation), timed like the per-layer rows
+    (graphs of 20 launches on the same buffers, hot).  The NHWC variants'
+    inputs are synthetic tensors of the same shapes (timing does not depend on
+    the values)."""
+    import torch
+    import workloads as wl
+    from conv2d_batchnorm_activation_amd import accounting, cvx
+    out = []
+    for batch in (1, 8):
+        for name in [s[0] for s in wl.SWEEP[:7]]:
+            wk = wl.sweep_layer(name, batch=batch)
+            L = wk.layers[0]
+            n, c, h, w = wk.x.shape
+            cnt = accounting.conv_count(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups,
+                                        residual=L.res_mode != 0)
+            row = {"layer": name, "batch": batch, "gflop": round(cnt.flop / 1e9, 4)}
+            dev = "cuda"
+            g_, b_, m_, v_ = (torch.from_numpy(L.params[k]).to(dev) for k in ("gamma", "beta", "mean", "var"))
+            scale = torch.empty(L.cout, device=dev)
+            bias = torch.empty(L.cout, device=dev)
+            cvx.cvx_fold_bn(g_, b_, m_, v_, wl.EPS, scale, bias)
+            wt = torch.from_numpy(L.params["w"]).to(dev)
+            # NCHW fp32, packed weights
+            d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
+                              cvx.CVX_W_PACKED)
+            oh, ow = cvx.cvx_conv_out_shape(d)
+            wp = torch.empty(cvx.cvx_packed_weights_bytes(d) // 4, device=dev)
+            cvx.cvx_pack_weights(d, wt, wp)
+            x = torch.rand((n, c, h, w), device=dev)
+            y = torch.empty((n, L.cout, oh, ow), device=dev)
+            res = x if L.res_mode else None
+            nws = cvx.cvx_conv_workspace_bytes(d)
+            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+            fn = lambda: cvx.cvx_conv_bn_act(d, x, wp, scale, bias, res, y, ws, nws)
+            ms = time_graph(capture(fn, 20), 20, max(1, reps // 20))
+            row["nchw_f32_us"] = round(ms * 1e3, 3)
+            row["nchw_plan"] = cvx.cvx_conv_plan(d).split(" kernel")[0]
+            for dt, tag in ((cvx.CVX_DT_F32, "nhwc_f32"), (cvx.CVX_DT_F16, "nhwc_f16")):
+                tdt = torch.float32 if dt == cvx.CVX_DT_F32 else torch.float16
+                wq = torch.empty(cvx.cvx_nhwc_packed_weights_bytes(d, dt), dtype=torch.uint8, device=dev)
+                cvx.cvx_nhwc_pack_weights(d, dt, wt, wq)
+                xq = torch.rand((n, h, w, c), device=dev).to(tdt)
+                yq = torch.empty((n, oh, ow, L.cout), dtype=tdt, device=dev)
+                rq = xq if L.res_mode else None
+                fq = (lambda d=d, dt=dt, xq=xq, wq=wq, rq=rq, yq=yq:
+                      cvx.cvx_conv_bn_act_nhwc(d, dt, xq, wq, scale, bias, rq, yq))
+                ms = time_graph(capture(fq, 20), 20, max(1, reps // 20))
+                row[tag + "_us"] = round(ms * 1e3, 3)
+                row[tag + "_plan"] = cvx.cvx_nhwc_plan(d, dt).split(" kernel")[0]
+            f = cnt.flop
+            row["nchw_f32_frac_mfma"] = round(f / (row["nchw_f32_us"] * 1e-6) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4)
+            row["nhwc_f32_frac_mfma"] = round(f / (row["nhwc_f32_us"] * 1e-6) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4)
+            row["nhwc_f16_frac_mfma_f16"] = round(f / (row["nhwc_f16_us"] * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)
+            log(f"  b={batch} {name:16s} NCHW f32 {row['nchw_f32_us']:7.2f} us  NHWC f32 {row['nhwc_f32_us']:7.2f} us  "
+                f"NHWC f16 {row['nhwc_f16_us']:7.2f} us")
+            out.append(row)
+    return out
+
+
 def cpu_baseline(wk, flop_per_forward: float, budget_s: float):
     import oracle
     reps = 0
@@ -912,6 +977,8 @@ def main() -> int:
                     help="turn counter passes (one output directory each) into a table and, with "
                          "FETCH_SIZE and WRITE_SIZE, the traffic record (stdout)")
     ap.add_argument("--manifest", help="stdout of the --pmc-probe run (for --pmc-summary)")
+    ap.add_argument("--layouts-only", action="store_true",
+                    help="time only the NCHW / NHWC fp32 / NHWC fp16 comparison of the dense layers")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time every packed tile configuration of each dense layer of --workload")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -947,6 +1014,9 @@ def main() -> int:
         return tile_sweep(args)
     if args.others_only:
         print(json.dumps({"other_workloads": other_workloads(args.layer_reps, args.steps)}))
+        return 0
+    if args.layouts_only:
+        print(json.dumps({"layout_comparison": layout_comparison(args.layer_reps)}))
         return 0
     wk = wl.detector_pipeline(args.batch)
     counts = accounting.layer_counts(wk.layers, wk.x.shape)
@@ -1024,6 +1094,7 @@ def main() -> int:
     }
     if not args.no_others and not args.no_layers:
         result["other_workloads"] = other_workloads(args.layer_reps, args.steps)
+        result["layout_comparison"] = layout_comparison(args.layer_reps)
     result["gpu_clocks"]["end"] = gpu_clocks()
     if not args.no_cpu_baseline and args.batch == 1:
         result["cpu_baseline"] = cpu_baseline(wk, flop, args.cpu_budget)

@@ -92,8 +92,8 @@ __global__ void __launch_bounds__(256) k_direct(const float* __restrict__ x,
 //     group of four columns and single loads for the edge columns; rows and
 //     columns outside the image read through out-of-range offsets as zeros (the
 //     padding), and neighbouring quads share their rows in the caches;
-//   * the workgroup's weights, scale and bias go to LDS once and are read with
-//     lane-uniform addresses (broadcast reads);
+//   * the workgroup's weights, scale and bias are read with lane-uniform
+//     addresses, through the scalar cache;
 //   * a workgroup is one wave, and quads are numbered over batch x rows x
 //     columns, so even a single image gives hundreds of workgroups.
 constexpr int kStemThreads = 64;
@@ -111,23 +111,9 @@ __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__
                                               int res_mode)
 {
     constexpr int KT = CIN * 9;         // taps per output channel
-    constexpr int KP = (KT + 3) & ~3;   // padded to whole 16-byte groups
     constexpr int WC = S == 1 ? 6 : 9;  // window columns of a quad
-    __shared__ __attribute__((aligned(16))) float sw[COB * KP];
-    __shared__ float ssc[COB], sbi[COB];
     const int t = threadIdx.x;
     const int co0 = blockIdx.y * COB;
-    for (int i = t; i < COB * KP; i += kStemThreads) {
-        const int c = i / KP, k = i - c * KP;
-        const int co = co0 + c;
-        sw[i] = (co < cout && k < KT) ? w[(long)co * KT + k] : 0.0f;
-    }
-    if (t < COB) {
-        const int co = min(co0 + t, cout - 1);
-        ssc[t] = scale[co];
-        sbi[t] = bias[co];
-    }
-    __syncthreads();
 
     const int g = blockIdx.x * kStemThreads + t;
     if (g >= nquads) return;
@@ -179,17 +165,18 @@ __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__
 #pragma unroll
         for (int c = 0; c < COB; ++c) r[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // one loop per activation, so the epilogue has no branches
+    // One loop per activation, so the epilogue has no branches.  The
+    // workgroup is one wave and its channels are the same for every lane, so
+    // weights, scale and bias come through the scalar cache (no LDS copy and
+    // no barrier in front of the window loads, which are already in flight).
     auto channels = [&](auto act_fn) {
 #pragma unroll
         for (int c = 0; c < COB; ++c) {
-            float wv[KP];
+            const int cw = min(co0 + c, cout - 1);  // channels past c_out: results dropped
+            const float* wc = w + (long)cw * KT;
+            float wv[KT];
 #pragma unroll
-            for (int k = 0; k < KP; k += 4) {
-                const f32x4 q = *reinterpret_cast<const f32x4*>(sw + c * KP + k);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) wv[k + e] = q[e];
-            }
+            for (int k = 0; k < KT; ++k) wv[k] = wc[k];
             f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ci = 0; ci < CIN; ++ci)
@@ -201,7 +188,7 @@ __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__
 #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[j] = fmaf(wt, win[ci][kh][j * S + kw], acc[j]);
                     }
-            const float sc = ssc[c], bi = sbi[c];
+            const float sc = scale[cw], bi = bias[cw];
             f32x4 o;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -221,9 +208,20 @@ __global__ void __launch_bounds__(kStemThreads) k_stem(const float* __restrict__
         channels([](float v) { return v; });
 }
 
-// Output channels per stem workgroup: 16 when there are enough channels to
-// share each window's loads, else 8 (more workgroups for a 16-channel stem).
-int stem_cob(const ConvGeom& g) { return g.cout >= 32 ? 16 : 8; }
+// Output channels per stem workgroup: the most (16, 8, 4) that still gives
+// the layer about six waves per compute unit (1536), so that a small image's
+// few quads still keep the units busy; each wave's FMA chain is COB x taps
+// long, and fewer channels per wave shortens it at the price of reading the
+// window again for every group (from the caches).
+int stem_cob(const ConvGeom& g)
+{
+    const long waves_per_group = ((long)g.n * g.oh * (g.ow / 4) + kStemThreads - 1) / kStemThreads;
+    for (int cob : {16, 8}) {
+        if (cob > 8 && g.cout < 32) continue;  // a 16-channel group needs 32+ channels to pay off
+        if (waves_per_group * ((g.cout + cob - 1) / cob) >= 1536) return cob;
+    }
+    return 4;
+}
 
 bool stem_shape(const ConvGeom& g)
 {
@@ -266,13 +264,15 @@ hipError_t launch_direct(const ConvGeom& g, const Plan& p, const float* x, const
     const int cout_g = g.cout / g.groups;
     const int ohw = g.oh * g.ow;
     if (p.direct_stem && al16(x) && al16(y) && (res == nullptr || al16(res))) {
-        const bool c16 = stem_cob(g) == 16;
+        const int cob = stem_cob(g);
         if (g.cin == 1) {
-            if (c16) launch_stem_cin<1, 16>(g, s, x, w, scale, bias, res, y);
-            else launch_stem_cin<1, 8>(g, s, x, w, scale, bias, res, y);
+            if (cob == 16) launch_stem_cin<1, 16>(g, s, x, w, scale, bias, res, y);
+            else if (cob == 8) launch_stem_cin<1, 8>(g, s, x, w, scale, bias, res, y);
+            else launch_stem_cin<1, 4>(g, s, x, w, scale, bias, res, y);
         } else {
-            if (c16) launch_stem_cin<3, 16>(g, s, x, w, scale, bias, res, y);
-            else launch_stem_cin<3, 8>(g, s, x, w, scale, bias, res, y);
+            if (cob == 16) launch_stem_cin<3, 16>(g, s, x, w, scale, bias, res, y);
+            else if (cob == 8) launch_stem_cin<3, 8>(g, s, x, w, scale, bias, res, y);
+            else launch_stem_cin<3, 4>(g, s, x, w, scale, bias, res, y);
         }
         return hipGetLastError();
     }

@@ -185,9 +185,13 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
             if constexpr (F16) {
                 const unsigned off = live ? base + (unsigned)((j * 64 + lane) * 16) : kOOB;
                 wv[j] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
-            } else {
-                const unsigned off = live ? base + (unsigned)((j * 64 + lane) * 4) : kOOB;
-                wv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0));
+            } else if (j % 4 == 0) {
+                // a tap's eight pair values are consecutive per lane: two 16-byte loads
+                const int tap = j / 8, q = (j / 4) & 1;
+                const unsigned off = live ? base + (unsigned)(((tap * 64 + lane) * 8 + 4 * q) * 4) : kOOB;
+                const f32x4 v4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wv[j + e] = v4[e];
             }
         }
     };
@@ -280,7 +284,7 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
 
 // OIHW fp32 -> the A operand's lane order per (32-channel block, stage):
 // fp16: [tap][half h][lane][8] holds output channel 32*blk + lane%32, input
-// channels KC*st + 16h + 8*(lane/32) + 0..7; fp32: [tap][pair p][lane] holds
+// channels KC*st + 16h + 8*(lane/32) + 0..7; fp32: [tap][lane][pair p] holds
 // input channel KC*st + 2p + lane/32.  Zero where the channel does not exist.
 template <typename T, int K>
 __global__ void __launch_bounds__(256) k_pack_nhwc(const float* __restrict__ w, int cout, int cin, int nstages,
@@ -304,8 +308,8 @@ __global__ void __launch_bounds__(256) k_pack_nhwc(const float* __restrict__ w, 
         tap = r >> 10;
         ci = KC * st + 16 * h + 8 * (lane >> 5) + e;
     } else {
-        lane = r & 63;
-        const int pp = (r >> 6) & 7;
+        const int pp = r & 7;
+        lane = (r >> 3) & 63;
         tap = r >> 9;
         ci = KC * st + 2 * pp + (lane >> 5);
     }
