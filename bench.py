@@ -212,6 +212,28 @@ def cold_layer_us(wk, net, i, reps: int) -> "tuple[float, int, int]":
     return ms * 1e3, sets, set_bytes
 
 
+def copy_floor_us(nbytes: int, reps: int) -> "tuple[float, float]":
+    """A plain device copy (torch copy_, the runtime's copy) that reads and
+    writes nbytes in total, hot (same buffers) and cold (rotating over at least
+    COLD_BYTES): the rate a bandwidth-bound kernel of that size can reach on
+    this GPU, beside the HBM peak.  (us hot, us cold)."""
+    import math
+    import torch
+    n = max(64, int(nbytes) // 8)  # floats per side
+    a = torch.rand(n, device="cuda")
+    b = torch.empty_like(a)
+    fn = lambda: b.copy_(a)
+    inner = 20
+    hot = time_graph(capture(fn, inner), inner, max(1, reps // inner)) * 1e3
+    sets = int(min(MAX_COLD_SETS, max(2, math.ceil(COLD_BYTES / (8 * n)))))
+    bufs = [(torch.rand(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(sets)]
+    fns = [lambda x=x, y=y: y.copy_(x) for x, y in bufs]
+    cold = time_rotating(fns, max(reps, sets)) * 1e3
+    del bufs, fns, a, b
+    torch.cuda.empty_cache()
+    return hot, cold
+
+
 def per_layer(wk, net, counts, reps: int, cold: bool = True):
     """Each layer alone, on inputs of its own shape, timed with events: `us` over
     the same buffers every launch (cache-resident: hot), `us_cold` over rotating
@@ -241,6 +263,9 @@ def per_layer(wk, net, counts, reps: int, cold: bool = True):
         else:
             frac = (gbs_cold if gbs_cold is not None else gbs) / HBM_PEAK_GBS
         attainable = min(MFMA_F32_PEAK_TFLOPS * 1e3, c["ai"] * HBM_PEAK_GBS) if c["flop"] else None
+        copy_hot = copy_cold = None
+        if bound == "hbm" and cold:
+            copy_hot, copy_cold = copy_floor_us(c["bytes"], reps)
         rows.append({"layer": L.name, "plan": plan, "kernel": kernel, "splitk": splitk,
                      "us": round(us, 3), "us_eager": round(ms_eager * 1e3, 3),
                      "us_cold": round(us_cold, 3) if us_cold else None, "cold_sets": sets,
@@ -252,8 +277,13 @@ def per_layer(wk, net, counts, reps: int, cold: bool = True):
                      "frac_of_peak_hot": round((gflops / (MFMA_F32_PEAK_TFLOPS * 1e3)) if bound == "mfma"
                                                else gbs / HBM_PEAK_GBS, 4),
                      "frac_of_attainable": (round(gflops / attainable, 4) if attainable else
-                                            round((gbs_cold or gbs) / HBM_PEAK_GBS, 4))})
+                                            round((gbs_cold or gbs) / HBM_PEAK_GBS, 4)),
+                     "copy_us": round(copy_hot, 3) if copy_hot else None,
+                     "copy_us_cold": round(copy_cold, 3) if copy_cold else None,
+                     "of_copy_cold": round(copy_cold / us_cold, 3) if copy_cold and us_cold else None})
         cold_txt = f" cold {us_cold:7.2f} us {gbs_cold:7.1f} GB/s" if us_cold else ""
+        if copy_cold:
+            cold_txt += f" (a copy of its bytes: {copy_cold:.2f} us cold)"
         log(f"  {L.name:16s} {us:8.2f} us hot (eager {ms_eager * 1e3:6.2f}){cold_txt}  "
             f"{gflops:9.1f} GFLOP/s  {gbs:8.1f} GB/s hot  {bound} frac {frac:.3f}  [{plan}]")
     marker()
@@ -562,8 +592,9 @@ def pmc_summary(args) -> int:
 
 
 def tile_sweep(args) -> int:
-    """Every packed tile configuration (kind x tc x split, forced through
-    CVX_IGEMM_TILE) of every dense packed layer of a workload, each timed alone
+    """Every packed tile configuration (kind x tc x split, and the persistent
+    form at 256 and 512 workgroups, forced through CVX_IGEMM_TILE) of every
+    dense packed layer of a workload, each timed alone
     like the per-layer rows (a graph of 20 launches, hot), against the
     planner's own choice.  Prints a markdown table (the per-shape tile choice's
     evidence) and one JSON line per layer."""
@@ -598,10 +629,12 @@ def tile_sweep(args) -> int:
         seen = {p0}
         for kind in range(3):
             for tc in (0, 4, 8, 16, 32, 64, 128):
-                for sk in (1, 2, 3, 4, 6, 8):
-                    os.environ["CVX_IGEMM_TILE"] = f"{kind},{tc},{sk}"
+                for sk, pe in [(1, 0), (1, 256), (1, 512), (2, 0), (3, 0), (4, 0), (6, 0), (8, 0)]:
+                    os.environ["CVX_IGEMM_TILE"] = f"{kind},{tc},{sk},{pe}"
                     p = cvx.cvx_conv_plan(d).split(" kernel")[0]
                     if p in seen or f"tile={kind} " not in p or f"tc={tc} " not in p or f"splitk={sk}" not in p:
+                        continue
+                    if pe and f"persist={pe}" not in p:
                         continue
                     seen.add(p)
                     res.append(timed())
@@ -1076,7 +1109,9 @@ def main() -> int:
                   "whose launch boundary adds about 5 us; forward_cold rotates frame, workspace "
                   "and output over sets totalling >= 512 MB. Per-layer `us` from graphs of 20 "
                   "back-to-back launches on the same buffers (cache-resident: hot), `us_cold` "
-                  "over rotating buffer sets of >= 512 MB; HBM fractions use the cold time",
+                  "over rotating buffer sets of >= 512 MB; HBM fractions use the cold time; "
+                  "bandwidth-bound rows also carry copy_us/copy_us_cold, a plain device copy "
+                  "of the same bytes, and of_copy_cold = copy_us_cold / us_cold",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -133,16 +133,21 @@ bool plan_depthwise(const ConvGeom& g, Plan* p)
     return true;
 }
 
-// Tuning and test override: CVX_IGEMM_TILE="kind,tc,splitk" forces a tile
-// configuration when it is valid for this shape (sweeps and coverage tests).
-bool forced_tile(int* kind, int* tc, int* sk)
+// Tuning and test override: CVX_IGEMM_TILE="kind,tc,splitk[,persist]" forces a
+// tile configuration when it is valid for this shape (sweeps and coverage
+// tests); persist > 0 asks for the persistent form with that many workgroups
+// (rounded down to a multiple of 8, at most the tile count).
+bool forced_tile(int* kind, int* tc, int* sk, int* persist)
 {
     const char* env = getenv("CVX_IGEMM_TILE");
-    int k, t, s;
-    if (env == nullptr || sscanf(env, "%d,%d,%d", &k, &t, &s) != 3) return false;
+    int k, t, s, pe = 0;
+    if (env == nullptr) return false;
+    const int got = sscanf(env, "%d,%d,%d,%d", &k, &t, &s, &pe);
+    if (got < 3) return false;
     *kind = k;
     *tc = t;
     *sk = s;
+    *persist = got == 4 ? pe : 0;
     return true;
 }
 
@@ -243,11 +248,17 @@ bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8, int only_kind = 
             packed_tile_fits(g, e->kind, e->tc, nullptr))
             bt = GemmTile{e->kind, 32, packed_tile_n(e->kind), e->tc, e->splitk};
     }
-    int kind, tc, sk;
-    if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < packed_num_kinds() &&
+    int kind, tc, sk, pe;
+    if (forced_tile(&kind, &tc, &sk, &pe) && kind >= 0 && kind < packed_num_kinds() &&
         (only_kind < 0 || kind == only_kind) && sk <= max_split && slices_ok(nchunks, sk) &&
-        packed_tile_fits(g, kind, tc, nullptr))
-        bt = GemmTile{kind, 32, packed_tile_n(kind), tc, sk};
+        packed_tile_fits(g, kind, tc, nullptr)) {
+        bt = GemmTile{kind, 32, packed_tile_n(kind), tc, sk, 0};
+        if (pe > 0 && sk == 1) {
+            const long tiles = packed_num_tiles(g, kind, tc);
+            const int wgs = (int)(std::min<long>(pe, tiles) / 8 * 8);
+            if (packed_persist_fits(g, kind, tc, wgs)) bt.persist = wgs;
+        }
+    }
     if (bt.kind < 0) return false;
     p->fam = FAM_IGEMM_PACKED;
     p->tile = bt;
@@ -298,8 +309,8 @@ bool plan_igemm(const ConvGeom& g, Plan* p)
             }
         }
     }
-    int kind, tc, sk;
-    if (forced_tile(&kind, &tc, &sk) && kind >= 0 && kind < igemm_num_tiles() &&
+    int kind, tc, sk, pe;
+    if (forced_tile(&kind, &tc, &sk, &pe) && kind >= 0 && kind < igemm_num_tiles() &&
         slices_ok(nchunks, sk) && igemm_tile_fits(g, kind, tc, nullptr)) {
         int bm, bn;
         igemm_tile_shape(kind, &bm, &bn);
@@ -327,8 +338,8 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
     if (plan_depthwise(g, p)) return CVX_OK;
     // 1x1 layers over batches of small planes: whole images per workgroup (a
     // forced packed tile keeps the packed kernel, for sweeps and tests)
-    int fk, ft, fs;
-    if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs) && pointwise_fits(g)) {
+    int fk, ft, fs, fp;
+    if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs, &fp) && pointwise_fits(g)) {
         p->fam = FAM_POINTWISE;
         p->ws_bytes = 0;
         return CVX_OK;
@@ -346,7 +357,7 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
 // on every call.  Bounded, and safe to use from several host threads.
 struct PlanKey {
     ConvGeom g;
-    int forced[3];
+    int forced[4];
     bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
 };
 struct PlanKeyHash {
@@ -366,8 +377,8 @@ cvx_status make_plan(const ConvGeom& g, Plan* p)
     PlanKey key;
     memset(&key, 0, sizeof(key));  // padding takes part in the hash and comparison
     key.g = g;
-    key.forced[0] = key.forced[1] = key.forced[2] = -1;
-    forced_tile(&key.forced[0], &key.forced[1], &key.forced[2]);
+    key.forced[0] = key.forced[1] = key.forced[2] = key.forced[3] = -1;
+    forced_tile(&key.forced[0], &key.forced[1], &key.forced[2], &key.forced[3]);
     {
         std::lock_guard<std::mutex> lock(mu);
         auto it = cache.find(key);
@@ -437,9 +448,15 @@ static void describe_plan(const ConvGeom& g, const Plan& p, char* buf, int buf_l
     char kn[96];
     switch (p.fam) {
     case FAM_IGEMM_PACKED:
-        packed_kernel_name(g, p.tile.kind, kn, sizeof(kn));
-        snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
-                 g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
+        if (p.tile.persist > 0) {  // named as launched on 16-byte aligned tensors
+            packed_persist_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+            snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d persist=%d kernel=%s",
+                     g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, p.tile.persist, kn);
+        } else {
+            packed_kernel_name(g, p.tile.kind, kn, sizeof(kn));
+            snprintf(buf, buf_len, "igemm_packed k%d s%d tile=%d bm=%d bn=%d tc=%d splitk=%d kernel=%s",
+                     g.k, g.stride, p.tile.kind, p.tile.bm, p.tile.bn, p.tile.tc, p.tile.splitk, kn);
+        }
         break;
     case FAM_POINTWISE: pointwise_describe(g, nullptr, buf, buf_len); break;
     case FAM_DEPTHWISE:
@@ -676,6 +693,8 @@ struct NodePlan {
     bool skipped;        // FC folded into the preceding GAP
     bool merged;         // 1x1 shortcut computed inside its reader's kernel: no output
     int pair;            // the merged shortcut this layer computes with its own product, or -1
+    bool stem_next;      // stem whose output only the next layer reads: both run as one kernel there
+    bool stem_kept;      // ... whose output still gets a region (a list input may be misaligned at launch)
     int last_use;        // last layer index reading this output
     size_t offset;       // workspace offset of the output (non-final layers)
     int chain_first;     // first layer of the chain run this layer belongs to, or -1
@@ -834,6 +853,27 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         np.pair = j;
         lp->nodes[sl.in].last_use = std::max(lp->nodes[sl.in].last_use, i);
     }
+    // A stem layer (k_stem: 3x3, one or three input channels) with 16 output
+    // channels whose only reader is the next layer, a packed dense 3x3: the two
+    // run as one kernel (k_stem_pair) and the stem's output is not written.
+    // When the stem reads the list input, whose alignment is known only at
+    // launch, its output keeps a region for the two-kernel fallback.
+    // CVX_STEM_PAIR=0 runs them apart.
+    const char* pair_env = getenv("CVX_STEM_PAIR");
+    if (!(pair_env && pair_env[0] == '0')) {
+        for (int i = 0; i + 1 < nl; ++i) {
+            const cvx_layer& l = L[i];
+            const cvx_layer& nx = L[i + 1];
+            NodePlan& np = lp->nodes[i];
+            const NodePlan& nn = lp->nodes[i + 1];
+            if (l.kind != CVX_L_CONV || nx.kind != CVX_L_CONV || nx.in != i || readers[i] != 1) continue;
+            if (np.p.fam != FAM_DIRECT || !np.p.direct_stem || np.merged || np.pair >= 0) continue;
+            if (nn.p.fam != FAM_IGEMM_PACKED || !stem_pair_fits(np.g, nn.g)) continue;
+            np.stem_next = true;
+            np.stem_kept = l.in == CVX_INPUT;
+            if (l.in >= 0) lp->nodes[l.in].last_use = std::max(lp->nodes[l.in].last_use, i + 1);
+        }
+    }
     // Placement of intermediate outputs.  A kernel that writes a buffer another
     // kernel has just read runs markedly slower than one writing memory that
     // was not read since (MNIST conv1's 38.5 MB output: 16.7 against 10.8 us),
@@ -843,9 +883,11 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
     lp->act_bytes = 0;
     lp->layer_ws = 0;
     size_t total = 0;
+    auto unwritten = [&](const NodePlan& n) {
+        return n.fuse_next || n.merged || (n.stem_next && !n.stem_kept);
+    };
     for (int i = 0; i < nl - 1; ++i)
-        if (!lp->nodes[i].fuse_next && !lp->nodes[i].merged)
-            total += round_up(lp->nodes[i].out.elems() * sizeof(float));
+        if (!unwritten(lp->nodes[i])) total += round_up(lp->nodes[i].out.elems() * sizeof(float));
     // CVX_FORWARD_REUSE=1 takes the reuse branch for any size (tests of the
     // placement at small batches)
     const char* reuse_env = getenv("CVX_FORWARD_REUSE");
@@ -853,7 +895,7 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
     std::vector<int> placed;
     for (int i = 0; i < nl - 1; ++i) {
         NodePlan& np = lp->nodes[i];
-        if (np.fuse_next || np.merged) {  // pooled vector / shortcut never materialised
+        if (unwritten(np)) {  // pooled vector / shortcut / paired stem never materialised
             np.offset = 0;
             continue;
         }
@@ -899,6 +941,7 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         for (int i = 0; i < nl; ++i) {
             NodePlan& np = lp->nodes[i];
             if (L[i].kind != CVX_L_CONV || np.merged || np.pair >= 0 || np.p.fam != FAM_IGEMM_PACKED) continue;
+            if (i > 0 && lp->nodes[i - 1].stem_next) continue;  // runs with its stem
             ok[i] = chain_choose(np.g, &np.chain_tc, &np.chain_splits) ? 1 : 0;
         }
         std::vector<ChainLayerSpec> spec;
@@ -981,6 +1024,12 @@ cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, in
                 char d[256];
                 pointwise_describe(np.g, &lp.nodes[np.pair].g, d, sizeof(d));
                 snprintf(line, sizeof(line), "%s shortcut=%d", d, np.pair);
+            } else if (np.stem_next) {
+                snprintf(line, sizeof(line), "merged into %d", i + 1);
+            } else if (i > 0 && lp.nodes[i - 1].stem_next) {
+                char d[256];
+                stem_pair_describe(lp.nodes[i - 1].g, np.g, d, sizeof(d));
+                snprintf(line, sizeof(line), "%s stem=%d", d, i - 1);
             } else {
                 describe_plan(np.g, np.p, line, sizeof(line));
             }
@@ -1052,6 +1101,25 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
         if (np.skipped || np.merged || i < chain_end) continue;
         hipError_t e = hipSuccess;
         cvx_status cs = CVX_OK;
+        if (np.stem_next) {
+            // runs with the next layer, unless its input is off a 16-byte boundary
+            const float* x = in_ptr(l.in);
+            if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) continue;
+            cs = launch_conv(np.g, np.p, x, l.w, l.scale, l.bias, nullptr, out_ptr(i), layer_ws, s);
+            if (cs != CVX_OK) return cs;
+            continue;
+        }
+        if (i > 0 && lp.nodes[i - 1].stem_next) {
+            const cvx_layer& sl = layers[i - 1];
+            const float* x = in_ptr(sl.in);
+            if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) {
+                const float* res = l.conv.res_mode != CVX_RES_NONE ? in_ptr(l.res) : nullptr;
+                e = launch_stem_pair(lp.nodes[i - 1].g, x, sl.w, sl.scale, sl.bias, np.g, l.w, l.scale, l.bias,
+                                     res, out_ptr(i), s);
+                if (e != hipSuccess) return CVX_ERR_HIP;
+                continue;
+            }
+        }
         if (np.chain_first == i && np.chain_len >= 2) {
             ChainLayerSpec spec[kChainMax];
             const int n = np.chain_len;

@@ -32,6 +32,7 @@ struct GemmTile {
     int bm, bn;       // output tile: bm output channels x bn output pixels
     int tc;           // 0: bn consecutive pixels; else 2-D tile of bn/tc rows x tc columns
     int splitk;       // number of K slices (1 = no split); >1 uses the workspace
+    int persist;      // packed family: workgroups of the persistent form (0: one per tile)
 };
 
 struct Plan {
@@ -85,6 +86,7 @@ hipError_t launch_preprocess(const unsigned char* src, int n, int src_h, int src
 // ("cvx::k_igemm_packed<32, 32, 1, 1, 4, 3, 24, 2>").
 void igemm_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
 void packed_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
+void packed_persist_kernel_name(const ConvGeom& g, int tile, char* buf, int len);
 
 hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x, const float* wp,
                                const float* scale, const float* bias, const float* res, float* y,
@@ -106,6 +108,15 @@ hipError_t launch_pointwise_pair(const ConvGeom& g, const float* x, const float*
                                  const float* scale2, const float* bias2, float* y, hipStream_t s);
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s);
+
+// Stem pair (k_stem_pair.hip): a k_stem-shaped layer g1 with 16 output channels
+// and no residual, and the packed 3x3 layer g2 that alone reads its output, in
+// one kernel; x must be 16-byte aligned.
+bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2);
+void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, char* buf, int len);
+hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1, const float* scale1,
+                            const float* bias1, const ConvGeom& g2, const float* wp, const float* scale2,
+                            const float* bias2, const float* res, float* y, hipStream_t s);
 
 hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* partial,
                                 const float* scale, const float* bias, const float* res, float* y,
@@ -135,6 +146,12 @@ struct PackedStage {
     int pr, pcw, epr, re, rounds, rep;
 };
 void packed_stage_geometry(const ConvGeom& g, int kind, int tc, bool vec, PackedStage* st);
+// Persistent form: `wgs` workgroups (a multiple of 8, at most the tile count)
+// each running several tiles; no split, 16-byte staging, two or more stages.
+bool packed_persist_fits(const ConvGeom& g, int kind, int tc, int wgs);
+// workgroups of the persistent form that fit the device at once
+int packed_persist_capacity(const ConvGeom& g, int kind, int tc);
+long packed_num_tiles(const ConvGeom& g, int kind, int tc);
 // A fresh nonzero tag per launch for counters that outlive a launch.
 unsigned long long packed_next_epoch();
 void fastdiv_params(int d, unsigned* m, unsigned* l);

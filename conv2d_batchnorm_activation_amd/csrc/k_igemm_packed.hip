@@ -120,6 +120,7 @@ struct PackedArgs {
     int spatial;                // workgroup order: pixel tiles slowest (else row blocks slowest)
     int nms;                    // row blocks x splits
     unsigned m_ms, l_ms;        // divide by nms
+    int nv;                     // persistent form: tiles x row blocks (the workgroups it stands for)
     unsigned wp_bytes;
     int vout;                   // 16-byte epilogue accesses
     int act, res_mode;
@@ -582,6 +583,425 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     }
 }
 
+// Persistent form (no split, 16-byte staging).  A layer with more tiles than
+// the device holds at once runs as fewer workgroups (a multiple of 8), each
+// taking tiles h = blockIdx + k*gridDim numbered as the one-tile-per-workgroup
+// launch numbers workgroup h (so a tile still lands on the XCD its neighbours
+// use).  The stages of a workgroup's tiles form one stream: the producers stage
+// the next tile's first chunks while the consumers finish the current tile, so
+// a tile's start-up (argument fetch, address set-up, the first stage's landing)
+// is paid once per workgroup instead of once per tile.  The partial-sum
+// exchange has its own LDS region past the three stage buffers, and costs one
+// barrier per tile: tile k ends at stream stage e = (k+1)*ns - 1, and its
+// exchange barrier falls between barriers e and e+1 of the stream.
+template <int K, int NT, int CPS>
+__global__ void __launch_bounds__(kThreads) k_igemm_persist(PackedArgs a)
+{
+    constexpr int NR = kRoundsVec;
+    constexpr int KK = K * K;
+    constexpr int G = 4;  // floats per staged element
+    constexpr int BN = 32 * NT;
+    constexpr int PITCH = BN + (NT < 4 ? 4 : 0);
+    constexpr int WF = K == 3 ? kBCFloats3 : kBCFloats1;
+
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    warm_kernargs<sizeof(PackedArgs)>();
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5;
+    const int l32 = lane & 31;
+
+    const int NV = a.nv;
+    const int GR = (int)gridDim.x;
+    const int ntiles = (NV - (int)blockIdx.x + GR - 1) / GR;  // >= 1: the host keeps gridDim <= NV
+    const int ns = (a.nchunks + CPS - 1) / CPS;               // stages per tile, >= 2 (host)
+    const int S = ntiles * ns;
+    const int OHW = a.OH * a.OW;
+    const int HW = a.H * a.W;
+    const int CHF = a.REP;
+    const int BUF = CPS * CHF;
+    const int XB = 3 * BUF;  // the exchange region
+
+    struct Tile {
+        int mb, b, q0, q_end, oh_ref, gx0;
+    };
+    auto decode = [&](int k) {
+        Tile t;
+        const unsigned h = blockIdx.x + (unsigned)(k * GR);
+        const unsigned xcd = h & 7u, i8 = h >> 3, base = (unsigned)NV >> 3, rem = (unsigned)NV & 7u;
+        const int L = (int)(xcd * base + min(xcd, rem) + i8);
+        int bt;
+        if (a.spatial) {
+            bt = pdiv(L, a.m_ms, a.l_ms);
+            t.mb = L - bt * a.nms;
+        } else {
+            t.mb = pdiv(L, a.m_nb, a.l_nb);
+            bt = L - t.mb * (a.n * a.tiles_per_img);
+        }
+        t.b = pdiv(bt, a.m_tpi, a.l_tpi);
+        const int tile = bt - t.b * a.tiles_per_img;
+        int ix0;
+        if (a.tc == 0) {
+            t.q0 = tile * BN;
+            t.q_end = min(t.q0 + BN, OHW);
+            t.oh_ref = pdiv(t.q0, a.m_ow, a.l_ow);
+            ix0 = (a.run_in_row ? (t.q0 - t.oh_ref * a.OW) * a.stride : 0) - a.pad;
+        } else {
+            const int band = pdiv(tile, a.m_tw, a.l_tw);
+            const int tw = tile - band * a.tiles_w;
+            t.oh_ref = band * a.tr;
+            ix0 = tw * a.tc * a.stride - a.pad;
+            t.q0 = tw * a.tc;
+            t.q_end = 0;
+        }
+        t.gx0 = ix0 & ~3;
+        return t;
+    };
+
+    if (wave >= 4) {
+        // ---------------------------------------------------------- producers
+        const int ptid = tid - 256;
+        const int pw = wave - 4;
+        // Staged element e = ptid + 256*i of a chunk: its row r and element c of
+        // the region, and its offset from the region's origin (channel 0, row
+        // iy0, column gx0) -- the same for every tile; the tile adds its origin.
+        int er[NR], ec[NR], elin[NR];
+        {
+            int ci = pdiv(ptid, a.m_rc, a.l_rc);
+            const int rem = ptid - ci * (a.PR * a.EPR);
+            int r = pdiv(rem, a.m_c, a.l_c);
+            int c = rem - r * a.EPR;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const bool live = i < a.rounds && ptid + 256 * i < a.RE;
+                er[i] = live ? r : -0x40000000;  // a row no tile has
+                ec[i] = c;
+                elin[i] = ci * HW + r * a.W + G * c;
+                c += a.step_c;
+                const bool cc = c >= a.EPR;
+                c -= cc ? a.EPR : 0;
+                r += a.step_r + (cc ? 1 : 0);
+                const bool rc = r >= a.PR;
+                r -= rc ? a.PR : 0;
+                ci += a.step_ci + (rc ? 1 : 0);
+            }
+        }
+        unsigned goff[NR];
+        const float* xim = a.x;
+        auto setup = [&](const Tile& t) {
+            const int iy0 = t.oh_ref * a.stride - a.pad;
+            const int org = iy0 * a.W + t.gx0;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int iy = iy0 + er[i], gx = t.gx0 + G * ec[i];
+                const bool ok = ((unsigned)iy < (unsigned)a.H) & (gx >= 0) & (gx + G <= a.W);
+                goff[i] = ok ? 4u * (unsigned)(elin[i] + org) : kOOB;
+            }
+            xim = a.x + (long)t.b * a.cin * HW;
+        };
+        int ist = 0, it = 0;  // stage (within its tile) and tile of the next issue
+        setup(decode(0));
+        auto issue = [&](int sb) {
+            if (ist == ns) {
+                ist = 0;
+                ++it;
+                setup(decode(it));
+            }
+#pragma unroll
+            for (int j = 0; j < CPS; ++j) {
+                const int chunk = ist * CPS + j;
+                int cbase = sb + j * CHF;
+                // (no scalar pin here)
+
+                const int left = chunk < a.nchunks ? min(kCh, a.cin - chunk * kCh) : 0;
+                const rsrc_t rc = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if (i >= a.rounds) break;
+                    auto* d = (__attribute__((address_space(3))) void*)(smem + cbase + 256 * G * i + pw * 64 * G);
+                    lds_load16(rc, d, goff[i]);
+                }
+            }
+            ++ist;
+        };
+        // Barrier g of the stream follows the landing of stage g+1; stage g+1 goes
+        // into the buffer of stage g-2, which the consumers left by barrier g-1.
+        issue(0);
+        if (S > 1) issue(BUF);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        int sb = 2 * BUF, in_tile = 1;  // in_tile: stream stage g's index within its tile
+        for (int g = 1; g < S; ++g) {
+            if (g + 1 < S) issue(sb);
+            sb = sb == 2 * BUF ? 0 : sb + BUF;
+            if (in_tile == ns) {
+                lds_barrier();  // the exchange of the tile that ended at stage g-1
+                in_tile = 0;
+            }
+            ++in_tile;
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        lds_barrier();  // the last tile's exchange
+        return;
+    }
+
+    // -------------------------------------------------------------- consumers
+    const int erow = 8 * wave + (lane >> 3);  // epilogue: channel of the tile, as in k_igemm_packed
+    const int RS = a.PR * a.PCW;
+    const rsrc_t rsc = make_rsrc(a.scale, 4u * (unsigned)a.cout);
+    const rsrc_t rbi = make_rsrc(a.bias, 4u * (unsigned)a.cout);
+    const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
+    const unsigned plane_b = 4u * (unsigned)OHW;
+    const unsigned out_bytes = 4u * (unsigned)(a.n * a.cout * OHW);
+    const bool want_res = a.res_mode != CVX_RES_NONE;
+    const rsrc_t rr = make_rsrc(a.res, want_res ? out_bytes : 0u);
+    const rsrc_t ry = make_rsrc(a.y, out_bytes);
+    auto wrow_of = [&](int mb) {
+        return 4u * (unsigned)(mb * a.nchunks * WF + wave * (WF / 4)) + (K == 3 ? 16u : 8u) * (unsigned)lane;
+    };
+
+    Tile tcur = decode(0);
+    int kcur = 0;
+    unsigned wr_cur = wrow_of(tcur.mb);
+    unsigned wr_nxt = ntiles > 1 ? wrow_of(decode(1).mb) : 0u;
+
+    int loff[NT];
+    auto set_loff = [&](const Tile& t) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int j = nt * 32 + l32;
+            int oh, ow;
+            if (a.tc == 0) {
+                const int qc = min(t.q0 + j, t.q_end - 1);
+                oh = pdiv(qc, a.m_ow, a.l_ow);
+                ow = qc - oh * a.OW;
+            } else {
+                const int jr = pdiv(j, a.m_tc, a.l_tc);
+                oh = min(t.oh_ref + jr, a.OH - 1);
+                ow = min(t.q0 + (j - jr * a.tc), a.OW - 1);
+            }
+            loff[nt] = (oh - t.oh_ref) * a.stride * a.PCW + ow * a.stride - a.pad - t.gx0;
+        }
+    };
+    set_loff(tcur);
+
+    // epilogue offset of pixel e of this lane's quad k in tile t, or kOOB
+    auto at = [&](const Tile& t, int k, int e) {
+        const int p = 32 * k + 4 * (lane & 7) + e;
+        bool ok;
+        int q;
+        if (a.tc == 0) {
+            q = t.q0 + p;
+            ok = q < t.q_end;
+        } else {
+            const int jr = pdiv(p, a.m_tc, a.l_tc);
+            const int oh = t.oh_ref + jr, ow = t.q0 + (p - jr * a.tc);
+            ok = oh < a.OH && ow < a.OW;
+            q = oh * a.OW + ow;
+        }
+        const int eco = t.mb * 32 + erow;
+        return ok && eco < a.cout ? (unsigned)(t.b * a.cout + eco) * plane_b + 4u * (unsigned)q : kOOB;
+    };
+    auto load_quad = [&](const rsrc_t& r, const Tile& t, int k) {
+        f32x4 v;
+        if (a.vout) {
+            v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(t, k, 0), 0, 0));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(t, k, e), 0, 0));
+        }
+        return v;
+    };
+    auto store_quad = [&](const Tile& t, int k, f32x4 v) {
+        if (a.vout) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry, (int)at(t, k, 0), 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = v[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), ry, (int)at(t, k, e), 0, 0);
+            }
+        }
+    };
+    float sc, bi;
+    f32x4 rv[NT];
+    auto load_tile_consts = [&](const Tile& t) {
+        const int eco = t.mb * 32 + erow;
+        const unsigned o = eco < a.cout ? 4u * (unsigned)eco : kOOB;
+        sc = bload(rsc, o);
+        bi = bload(rbi, o);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) rv[k] = load_quad(rr, t, k);
+    };
+
+    struct AT {
+        f32x4 q[K == 3 ? 4 : 0 + 1];
+        f32x2 t;
+        __device__ float operator[](int f) const { return K == 3 ? (f < 16 ? q[f / 4][f % 4] : t[f - 16]) : t[f]; }
+    };
+    // weights of stage s of the tile whose weight row is `wo_base` (kOOB: none)
+    auto load_w = [&](unsigned wo_base, bool valid, int s, AT (&av)[CPS]) {
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) {
+            const int chunk = s * CPS + j;
+            const unsigned wo = valid && chunk < a.nchunks ? wo_base + 4u * (unsigned)(chunk * WF) : kOOB;
+            if constexpr (K == 3) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    av[j].q[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wo + 1024u * q), 0, 0));
+                av[j].t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(wo + 4096u), 0, 0));
+            } else {
+                av[j].t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)wo, 0, 0));
+            }
+        }
+    };
+    auto read_b = [&](int sb, int q, float (&bv)[KK][NT]) {
+        const int j = q >> 1, pp = q & 1;
+        int base = sb + j * CHF + (2 * (2 * wave + pp) + hi) * RS;
+        asm volatile("" : "+v"(base));
+        const float* xa = smem + base;
+#pragma unroll
+        for (int tap = 0; tap < KK; ++tap) {
+            const int toff = (tap / K) * a.PCW + (tap % K);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
+        }
+    };
+
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+
+    constexpr int NQ = CPS * 2;
+    float b0[KK][NT], b1[KK][NT];
+    AT a0[CPS], a1[CPS];
+    // Stage st of the current tile at buffer sb (the stream's next stage at nsb,
+    // read ahead when it belongs to the same tile), weights `ac`; then `ac` takes
+    // the weights of the stream's stage two ahead (this tile's, the next tile's,
+    // or zeros past the last).
+    auto stage = [&](int st, AT (&ac)[CPS], int sb, int nsb, bool more) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float (&cur)[KK][NT] = (q & 1) ? b1 : b0;
+            float (&nxt)[KK][NT] = (q & 1) ? b0 : b1;
+            const int j = q >> 1, pp = q & 1;
+            if (q + 1 < NQ)
+                read_b(sb, q + 1, nxt);
+            else if (more)
+                read_b(nsb, 0, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int tap = 0; tap < KK; ++tap) {
+                const float wv = ac[j][K == 3 ? 9 * pp + tap : pp];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[tap][nt], wv, acc[nt], 0, 0, 0);
+            }
+        }
+        if (st + 2 < ns)
+            load_w(wr_cur, true, st + 2, ac);
+        else
+            load_w(wr_nxt, kcur + 1 < ntiles, st + 2 - ns, ac);
+    };
+    // After the last stage of the current tile: exchange, read the next tile's
+    // first operands (its stage landed at the previous barrier), epilogue and
+    // stores, then the next tile's constants and residual.
+    auto tile_end = [&](int nsb) {
+        {
+            float* red = smem + XB + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(red + 32 * nt + 8 * g) =
+                        f32x4{acc[nt][4 * g], acc[nt][4 * g + 1], acc[nt][4 * g + 2], acc[nt][4 * g + 3]};
+        }
+        lds_barrier();
+        f32x4 v[NT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            const int off = XB + erow * PITCH + 32 * k + 4 * (lane & 7);
+            v[k] = *reinterpret_cast<const f32x4*>(smem + off);
+#pragma unroll
+            for (int s = 1; s < 4; ++s) v[k] += *reinterpret_cast<const f32x4*>(smem + s * 32 * PITCH + off);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+        const bool has_next = kcur + 1 < ntiles;
+        Tile tn = tcur;
+        if (has_next) {
+            tn = decode(kcur + 1);
+            set_loff(tn);
+            read_b(nsb, 0, b0);
+        }
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            f32x4 z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t = fmaf(sc, v[k][e], bi);
+                if (a.res_mode == CVX_RES_BEFORE_ACT) t += rv[k][e];
+                t = apply_act_fast(t, a.act);
+                if (a.res_mode == CVX_RES_AFTER_ACT) t += rv[k][e];
+                z[e] = t;
+            }
+            store_quad(tcur, k, z);
+        }
+        if (has_next) {
+            tcur = tn;
+            load_tile_consts(tcur);
+            wr_cur = wr_nxt;
+            if (kcur + 2 < ntiles) wr_nxt = wrow_of(decode(kcur + 2).mb);
+        }
+        ++kcur;
+    };
+
+    load_w(wr_cur, true, 0, a0);
+    load_w(wr_cur, true, 1, a1);
+    load_tile_consts(tcur);
+    lds_barrier();
+    read_b(0, 0, b0);
+    {
+        int sb = 0, st = 0;
+        for (int g = 0; g < S; g += 2) {
+            if (g > 0) lds_barrier();
+            {
+                const int nsb = sb == 2 * BUF ? 0 : sb + BUF;
+                const bool more = st + 1 < ns;
+                stage(st, a0, sb, nsb, more);
+                if (more) {
+                    ++st;
+                } else {
+                    tile_end(nsb);
+                    st = 0;
+                }
+                sb = nsb;
+            }
+            if (g + 1 < S) {
+                lds_barrier();
+                const int nsb = sb == 2 * BUF ? 0 : sb + BUF;
+                const bool more = st + 1 < ns;
+                stage(st, a1, sb, nsb, more);
+                if (more) {
+                    ++st;
+                } else {
+                    tile_end(nsb);
+                    st = 0;
+                }
+                sb = nsb;
+            }
+        }
+    }
+}
+
 // One-time weight transform, OIHW -> the packed order above; zero where the row,
 // channel or tap does not exist.
 __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ w, int cout, int cin,
@@ -727,6 +1147,33 @@ static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
     return stage > red ? stage : red;
 }
 
+static size_t packed_persist_lds(const ConvGeom& g, int kind, const Region& r)
+{
+    const int nt = kPacked[kind].nt;
+    const size_t stage = 3 * (size_t)packed_chunks_per_stage(kind, g.k) * r.rep * sizeof(float);
+    const size_t red = (size_t)4 * 32 * (32 * nt + (nt < 4 ? 4 : 0)) * sizeof(float);
+    return stage + red;
+}
+
+long packed_num_tiles(const ConvGeom& g, int kind, int tc)
+{
+    return (long)g.n * packed_tiles_per_image(g, kind, tc) * ((g.cout + 31) / 32);
+}
+
+bool packed_persist_fits(const ConvGeom& g, int kind, int tc, int wgs)
+{
+    // tiles of 32 or 64 pixels (at 128 the compiler keeps the accumulators in scratch)
+    if (kind < 0 || kind >= kNumPacked || kPacked[kind].nt > 2) return false;
+    if (!packed_tile_fits(g, kind, tc, nullptr)) return false;
+    if (g.w % 4 != 0) return false;  // 16-byte staging only
+    const int cps = packed_chunks_per_stage(kind, g.k);
+    const int nchunks = (g.cin + kCh - 1) / kCh;
+    if ((nchunks + cps - 1) / cps < 2) return false;
+    const Region r = packed_region(g, kind, tc, true);
+    if (packed_persist_lds(g, kind, r) + 256 > kMaxLdsBytes) return false;
+    return wgs >= 8 && wgs % 8 == 0 && wgs <= packed_num_tiles(g, kind, tc);
+}
+
 bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
 {
     if (kind < 0 || kind >= kNumPacked) return false;
@@ -787,12 +1234,32 @@ int packed_loads_per_chunk(const ConvGeom& g, int kind, int tc)
     return (g.k == 3 ? kBCFloats3 : kBCFloats1) / 256 + 4 * r.rounds;
 }
 
+int packed_persist_capacity(const ConvGeom& g, int kind, int tc)
+{
+    // registers per lane of k_igemm_persist as the compiler reports them for
+    // gfx950 (1x1: NT = 1, 2; 3x3: NT = 1, 2); two waves per SIMD per workgroup
+    static constexpr int kRegs[2][2] = {{71, 113}, {106, 160}};
+    const int nt = kPacked[kind].nt;
+    if (nt > 2) return 0;
+    const Region r = packed_region(g, kind, tc, true);
+    const size_t lds = packed_persist_lds(g, kind, r) + 256;
+    int occ = 512 / kRegs[g.k == 3 ? 1 : 0][nt - 1] / 2;
+    occ = std::min<int>(std::min(occ, 2), (int)(kMaxLdsBytes / lds));
+    return 256 * std::max(occ, 1);
+}
+
 void packed_kernel_name(const ConvGeom& g, int kind, char* buf, int len)
 {
     const PackedKind& t = kPacked[kind];
     const bool vec = g.w % 4 == 0;  // as launched on 16-byte aligned tensors
     snprintf(buf, len, "cvx::k_igemm_packed<%d, %d, %d, %d>", g.k, t.nt,
              packed_chunks_per_stage(kind, g.k), vec ? 1 : 0);
+}
+
+void packed_persist_kernel_name(const ConvGeom& g, int kind, char* buf, int len)
+{
+    const PackedKind& t = kPacked[kind];
+    snprintf(buf, len, "cvx::k_igemm_persist<%d, %d, %d>", g.k, t.nt, packed_chunks_per_stage(kind, g.k));
 }
 
 // A fresh tag per split launch.  The first value mixes the clock and an address,
@@ -816,10 +1283,16 @@ static void launch_packed_cfg(dim3 grid, size_t lds, hipStream_t s, const Packed
 }
 
 template <int K, int KIND>
-static void launch_packed_kind(bool vec, dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
+static void launch_packed_kind(bool vec, bool persist, dim3 grid, size_t lds, hipStream_t s, const PackedArgs& a)
 {
     constexpr PackedKind t = kPacked[KIND];
     constexpr int cps = K == 3 ? t.cps3 : t.cps1;
+    if constexpr (t.nt <= 2) {
+        if (persist) {
+            hipLaunchKernelGGL((k_igemm_persist<K, t.nt, cps>), grid, dim3(kThreads), lds, s, a);
+            return;
+        }
+    }
     if (vec)
         launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
     else
@@ -827,13 +1300,13 @@ static void launch_packed_kind(bool vec, dim3 grid, size_t lds, hipStream_t s, c
 }
 
 template <int K>
-static void launch_packed_k(int kind, bool vec, dim3 grid, size_t lds, hipStream_t s,
+static void launch_packed_k(int kind, bool vec, bool persist, dim3 grid, size_t lds, hipStream_t s,
                             const PackedArgs& a)
 {
     switch (kind) {
-    case 0: launch_packed_kind<K, 0>(vec, grid, lds, s, a); break;
-    case 1: launch_packed_kind<K, 1>(vec, grid, lds, s, a); break;
-    case 2: launch_packed_kind<K, 2>(vec, grid, lds, s, a); break;
+    case 0: launch_packed_kind<K, 0>(vec, persist, grid, lds, s, a); break;
+    case 1: launch_packed_kind<K, 1>(vec, persist, grid, lds, s, a); break;
+    case 2: launch_packed_kind<K, 2>(vec, persist, grid, lds, s, a); break;
     }
 }
 
@@ -867,7 +1340,9 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     if (splits < 1 || (splits > 1 && ws == nullptr)) return hipErrorInvalidValue;
     const bool vec = g.w % 4 == 0 && al16(x);
     const Region r = packed_region(g, kind, tc, vec);
-    const size_t lds = packed_lds(g, kind, r);
+    // the persistent form needs 16-byte staging; otherwise one workgroup per tile
+    const bool persist = p.tile.persist > 0 && splits == 1 && vec && packed_persist_fits(g, kind, tc, p.tile.persist);
+    const size_t lds = persist ? packed_persist_lds(g, kind, r) : packed_lds(g, kind, r);
     PackedArgs a;
     a.x = x;
     a.wp = wp;
@@ -934,11 +1409,13 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     // 16-byte epilogue accesses when a lane's quad of pixels is contiguous and aligned
     const bool quads = tc > 0 ? (tc % 4 == 0 && g.ow % 4 == 0) : (g.oh * g.ow) % 4 == 0;
     a.vout = quads && al16(y) && (res == nullptr || al16(res)) && (ws == nullptr || al16(ws)) ? 1 : 0;
-    dim3 grid((unsigned)((long)g.n * a.tiles_per_img * ((g.cout + 31) / 32) * splits));
+    const long tiles = (long)g.n * a.tiles_per_img * ((g.cout + 31) / 32);
+    a.nv = (int)tiles;
+    dim3 grid((unsigned)(persist ? (long)p.tile.persist : tiles * splits));
     if (g.k == 1)
-        launch_packed_k<1>(kind, vec, grid, lds, s, a);
+        launch_packed_k<1>(kind, vec, persist, grid, lds, s, a);
     else
-        launch_packed_k<3>(kind, vec, grid, lds, s, a);
+        launch_packed_k<3>(kind, vec, persist, grid, lds, s, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,497 @@
+// k_stem_pair.hip -- the first two convolutions of a detector stem as one
+// kernel: a direct 3x3 convolution of a few input channels into 16 channels
+// (folded BN, activation), whose output only the next layer reads, and that
+// next layer, a dense 3x3 convolution on fp32 matrix cores (folded BN,
+// residual, activation) -- "YOLO26N Inference Optimisation", "Baseline
+// benchmark" (the stem's two Conv2d+BN+SiLU blocks) and "Improvements"
+// (fusing what a layer writes into what the next one reads).
+//
+// Run apart, the two layers are each one round of workgroups whose latency
+// (argument fetch, first loads, store drain) nothing overlaps, and the 16
+// channels in between go through memory.  Here a workgroup computes one tile of
+// the second layer (32 output channels x 32*NT pixels, a block of TR rows x TC
+// columns) and makes its input itself:
+//   1. all eight waves copy the first layer's input window (every channel, the
+//      rows and columns the tile's 3x3 windows of 3x3 windows reach) to LDS
+//      with 16-byte LDS-direct loads; outside the image they read zeros (the
+//      first layer's padding);
+//   2. all eight waves compute the first layer's 16 output channels over the
+//      region the tile's 3x3 windows cover (four columns and four channels a
+//      lane; weights, scales and biases uniform per wave, through the scalar
+//      cache) and store them to LDS in the layout the matrix loop reads,
+//      writing zeros outside the image (the second layer's padding);
+//   3. four consumer waves run the second layer's reduction (16 channels x 9
+//      taps) on v_mfma_f32_32x32x2_f32, as k_igemm_packed does for one chunk,
+//      sum their partial tiles through LDS and apply the epilogue.
+// The first layer's outputs are recomputed where the regions of neighbouring
+// tiles overlap (about a quarter more of them), which costs less than writing
+// and reading the 16 channels and running a second round of workgroups.
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "bufio.h"
+#include "cvx_internal.h"
+#include "epilogue.h"
+
+namespace cvx {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSPThreads = 512;
+constexpr int kC1 = 16;              // channels between the two layers: one chunk
+constexpr int kWinRounds = 6;        // 512-lane rounds of 16-byte window loads, at most
+constexpr int kMaxCin1 = 4;
+constexpr int kBCFloats = 4 * 5 * 256;  // packed 3x3 floats per (32-row block, chunk)
+
+__device__ __forceinline__ int sp_div(int n, unsigned m, unsigned l)
+{
+    return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> l);
+}
+
+__device__ __forceinline__ void sp_lds_load16(rsrc_t r, __attribute__((address_space(3))) void* d, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
+}
+
+}  // namespace
+
+struct StemPairArgs {
+    const float* x;       // layer 1 input [n][cin1][H1][W1]
+    const float* w1;      // layer 1 weights [16][cin1][3][3]
+    const float* scale1;
+    const float* bias1;
+    const float* wp;      // layer 2 packed 3x3 weights (c_in 16: one chunk per row block)
+    const float* scale2;
+    const float* bias2;
+    const float* res;
+    float* y;
+    int n, cin1, H1, W1, S1;  // layer 1
+    int H2, W2;               // layer 1 output = layer 2 input
+    int S2, OH, OW, cout;     // layer 2
+    int act1, act2, res_mode;
+    int tc, tr, tiles_w, tiles_per_img, nmb;
+    unsigned m_tc, l_tc, m_tw, l_tw, m_tpi, l_tpi, m_nb, l_nb;
+    int PR, PCW;              // staged layer-1 output region per channel: PR rows x PCW floats
+    int NQ;                   // quads of four columns per channel: PR * PCW / 4
+    unsigned m_q4, l_q4;      // divide by PCW / 4
+    int WR, WCW;              // layer-1 input window per channel: WR rows x WCW floats
+    int win_elems, win_rounds;  // 16-byte elements of the window, 512-lane rounds
+    unsigned m_we, l_we;      // divide by WCW / 4
+    unsigned m_wc, l_wc;      // divide by WR * WCW / 4 (elements per channel)
+    unsigned x_bytes, wp_bytes;
+    int vout;
+};
+
+template <int NT, int S1>
+__global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
+{
+    constexpr int BN = 32 * NT;
+    constexpr int PITCH = BN + 4;
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    warm_kernargs<sizeof(StemPairArgs)>();
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5;
+    const int l32 = lane & 31;
+
+    // workgroup -> (row block, image, tile), dealt to the XCDs in turn
+    int mb, b, tile;
+    {
+        const unsigned h = blockIdx.x, G8 = gridDim.x;
+        const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
+        const int L = (int)(xcd * base + min(xcd, rem) + i8);
+        mb = sp_div(L, a.m_nb, a.l_nb);
+        const int bt = L - mb * (a.n * a.tiles_per_img);
+        b = sp_div(bt, a.m_tpi, a.l_tpi);
+        tile = bt - b * a.tiles_per_img;
+    }
+    const int band = sp_div(tile, a.m_tw, a.l_tw);
+    const int tw = tile - band * a.tiles_w;
+    const int oh_ref = band * a.tr;
+    const int ow0 = tw * a.tc;
+    const int gx0 = (ow0 * a.S2 - 1) & ~3;   // first staged column of the region (16-byte aligned)
+    const int iy0 = oh_ref * a.S2 - 1;       // first staged row of the region
+    const int RS = a.PR * a.PCW;             // LDS floats per region channel
+    const int WIN = kC1 * RS;                // the window (then the exchange) after the region
+    const int wx0 = S1 * gx0 - 4;            // first window column (16-byte aligned)
+    const int wy0 = S1 * iy0 - 1;            // first window row
+
+    // ---- 1. the first layer's input window -> LDS (all waves)
+    {
+        const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+        const int epr = a.WCW >> 2;  // 16-byte elements per window row
+#pragma unroll
+        for (int i = 0; i < kWinRounds; ++i) {
+            if (i >= a.win_rounds) break;
+            const int e = tid + kSPThreads * i;
+            const int ci = sp_div(e, a.m_wc, a.l_wc);
+            const int rem = e - ci * (a.WR * epr);
+            const int r = sp_div(rem, a.m_we, a.l_we);
+            const int c4 = rem - r * epr;
+            const int iy = wy0 + r, ix = wx0 + 4 * c4;
+            const bool ok = e < a.win_elems && (unsigned)iy < (unsigned)a.H1 && ix >= 0 && ix + 4 <= a.W1;
+            const unsigned off = ok ? 4u * (unsigned)(((b * a.cin1 + ci) * a.H1 + iy) * a.W1 + ix) : kOOB;
+            // lane l of the wave writes 16 bytes at d + 16 l: element e lands at WIN + 4 e
+            sp_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + WIN + 4 * (kSPThreads * i + 64 * wave)), off);
+        }
+    }
+    // the loads below are counted after these: keep the compiler from moving any
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // consumers: the second layer's weights (one chunk of row block mb, this
+    // wave's quarter, in the operand's lane order), scale, bias and residual
+    const bool consumer = wave < 4;
+    const int erow = 8 * (wave & 3) + (lane >> 3);
+    const int eco = mb * 32 + erow;
+    const bool row_ok = eco < a.cout;
+    f32x4 wq[4];
+    f32x2 wt;
+    float sc2 = 0.0f, bi2 = 0.0f;
+    f32x4 rv[NT];
+    const unsigned plane_b = 4u * (unsigned)(a.OH * a.OW);
+    const unsigned out_bytes = 4u * (unsigned)(a.n * a.cout * a.OH * a.OW);
+    // output offset of pixel e of this lane's quad k, or kOOB
+    auto at = [&](int k, int e) {
+        const int p = 32 * k + 4 * (lane & 7) + e;
+        const int jr = sp_div(p, a.m_tc, a.l_tc);
+        const int oh = oh_ref + jr, ow = ow0 + (p - jr * a.tc);
+        const bool ok = oh < a.OH && ow < a.OW && row_ok;
+        return ok ? (unsigned)(b * a.cout + eco) * plane_b + 4u * (unsigned)(oh * a.OW + ow) : kOOB;
+    };
+    if (consumer) {
+        const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
+        const unsigned wo = 4u * (unsigned)(mb * kBCFloats + (wave & 3) * (kBCFloats / 4)) + 16u * (unsigned)lane;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            wq[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wo + 1024u * s), 0, 0));
+        wt = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(wo + 4096u), 0, 0));
+        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
+        sc2 = bload(make_rsrc(a.scale2, 4u * (unsigned)a.cout), o);
+        bi2 = bload(make_rsrc(a.bias2, 4u * (unsigned)a.cout), o);
+        const rsrc_t rr = make_rsrc(a.res, a.res_mode != CVX_RES_NONE ? out_bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            if (a.vout) {
+                rv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)at(k, 0), 0, 0));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rv[k][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (int)at(k, e), 0, 0));
+            }
+        }
+        // the window's loads were issued first and complete in order
+        wait_vm_at_most(5 + 2 + (a.vout ? NT : 4 * NT));
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    lds_barrier();
+
+    // ---- 2. the first layer over the region (all waves): wave w takes
+    // channels 4 (w & 3) .. +3 and half (w >> 2) of the region's quads
+    {
+        const int cg = wave & 3;
+        const int QH = (a.NQ + 1) >> 1;
+        const int q_lo = (wave >> 2) * QH;
+        const int q_hi = min(a.NQ, q_lo + QH);
+        const int KT = a.cin1 * 9;
+        // the wave's four channels' weights, uniform: read through the scalar
+        // cache where they are used
+        const float* w1c = a.w1 + (4 * cg) * KT;
+        float s1[4], b1[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s1[c] = a.scale1[4 * cg + c];
+            b1[c] = a.bias1[4 * cg + c];
+        }
+        const int q4 = a.PCW >> 2;
+        for (int q = q_lo + lane; q < q_hi; q += 64) {
+            const int r = sp_div(q, a.m_q4, a.l_q4);
+            const int x = 4 * (q - r * q4);
+            const int yy = iy0 + r;
+            f32x4 acc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ci = 0; ci < kMaxCin1; ++ci) {
+                if (ci >= a.cin1) break;
+#pragma unroll
+                for (int kh = 0; kh < 3; ++kh) {
+                    // window columns S1*(x+j) + kw + 3 (j < 4, kw < 3) of row S1*r + kh
+                    const float* wr = smem + WIN + (ci * a.WR + S1 * r + kh) * a.WCW + S1 * x + 3;
+                    float win[S1 == 2 ? 9 : 6];
+                    win[0] = wr[0];
+                    const f32x4 m0 = *reinterpret_cast<const f32x4*>(wr + 1);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) win[1 + e] = m0[e];
+                    if constexpr (S1 == 2) {
+                        const f32x4 m1 = *reinterpret_cast<const f32x4*>(wr + 5);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) win[5 + e] = m1[e];
+                    } else {
+                        win[5] = wr[5];
+                    }
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float wv = w1c[c * KT + ci * 9 + kh * 3 + kw];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) acc[c][j] = fmaf(wv, win[S1 * j + kw], acc[c][j]);
+                        }
+                }
+            }
+            // outside the first layer's output: zeros (the second layer's padding)
+            const bool rok = (unsigned)yy < (unsigned)a.H2;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int xx = gx0 + x + j;
+                    const float v = apply_act_fast(fmaf(s1[c], acc[c][j], b1[c]), a.act1);
+                    o[j] = rok && (unsigned)xx < (unsigned)a.W2 ? v : 0.0f;
+                }
+                *reinterpret_cast<f32x4*>(smem + (4 * cg + c) * RS + r * a.PCW + x) = o;
+            }
+        }
+    }
+    lds_barrier();
+
+    if (!consumer) {
+        __syncthreads();  // the consumers' exchange
+        return;
+    }
+
+    // ---- 3. the second layer: one chunk of 16 channels x 9 taps; wave h takes
+    // channel pairs 2h and 2h+1 (lane: channel 2 (2h + pp) + hi)
+    int loff[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int j = nt * 32 + l32;
+        const int jr = sp_div(j, a.m_tc, a.l_tc);
+        const int oh = min(oh_ref + jr, a.OH - 1);
+        const int ow = min(ow0 + (j - jr * a.tc), a.OW - 1);
+        loff[nt] = (oh - oh_ref) * a.S2 * a.PCW + ow * a.S2 - 1 - gx0;
+    }
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+    auto wsel = [&](int f) { return f < 16 ? wq[f / 4][f % 4] : wt[f - 16]; };
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const float* xa = smem + (2 * (2 * wave + pp) + hi) * RS;
+        float bv[9][NT];
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap) {
+            const int toff = (tap / 3) * a.PCW + (tap % 3);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
+        }
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap) {
+            const float wv = wsel(9 * pp + tap);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[tap][nt], wv, acc[nt], 0, 0, 0);
+        }
+    }
+
+    // partial tiles of the four waves through LDS (the window region is free),
+    // then wave w sums channels 8w .. 8w+7 of the tile
+    {
+        float* red = smem + WIN + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4*>(red + 32 * nt + 8 * g) =
+                    f32x4{acc[nt][4 * g], acc[nt][4 * g + 1], acc[nt][4 * g + 2], acc[nt][4 * g + 3]};
+    }
+    __syncthreads();
+    const rsrc_t ry = make_rsrc(a.y, out_bytes);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int off = WIN + erow * PITCH + 32 * k + 4 * (lane & 7);
+        f32x4 v = *reinterpret_cast<const f32x4*>(smem + off);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) v += *reinterpret_cast<const f32x4*>(smem + s * 32 * PITCH + off);
+        f32x4 z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = fmaf(sc2, v[e], bi2);
+            if (a.res_mode == CVX_RES_BEFORE_ACT) t += rv[k][e];
+            t = apply_act_fast(t, a.act2);
+            if (a.res_mode == CVX_RES_AFTER_ACT) t += rv[k][e];
+            z[e] = t;
+        }
+        if (a.vout) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, z), ry, (int)at(k, 0), 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = z[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), ry, (int)at(k, e), 0, 0);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+void fastdiv_params(int d, unsigned* m, unsigned* l);
+
+namespace {
+
+struct PairGeom {
+    int nt, tc, tr, tiles_w, tiles_per_img, nmb;
+    int PR, PCW, WR, WCW, win_elems, win_rounds;
+    size_t lds;
+};
+
+// The region of layer-1 outputs a tile of layer 2 reads, and the window of
+// layer-1 inputs that region needs.
+bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, int nt, int tc, PairGeom* pg)
+{
+    const int bn = 32 * nt;
+    if (tc <= 0 || bn % tc != 0 || (tc * g2.stride) % 4 != 0) return false;
+    pg->nt = nt;
+    pg->tc = tc;
+    pg->tr = bn / tc;
+    pg->tiles_w = (g2.ow + tc - 1) / tc;
+    pg->tiles_per_img = ((g2.oh + pg->tr - 1) / pg->tr) * pg->tiles_w;
+    pg->nmb = (g2.cout + 31) / 32;
+    pg->PR = (pg->tr - 1) * g2.stride + 3;
+    // columns from gx0 = (ow0*S2 - 1) & ~3 = ow0*S2 - 4 to ow0*S2 - 1 + (tc-1)*S2 + 2
+    pg->PCW = ((3 + (tc - 1) * g2.stride + 3) + 3) & ~3;
+    pg->WR = g1.stride * (pg->PR - 1) + 3;
+    pg->WCW = (g1.stride * pg->PCW - g1.stride + 6 + 3) & ~3;
+    pg->win_elems = g1.cin * pg->WR * (pg->WCW / 4);
+    pg->win_rounds = (pg->win_elems + kSPThreads - 1) / kSPThreads;
+    if (pg->win_rounds > kWinRounds) return false;
+    const size_t region = (size_t)kC1 * pg->PR * pg->PCW;
+    // every lane of a window round writes its 16 bytes (zeros past the window)
+    const size_t win = (size_t)4 * kSPThreads * pg->win_rounds;
+    const size_t xch = (size_t)4 * 32 * (bn + 4);
+    pg->lds = (region + std::max(win, xch)) * sizeof(float);
+    return pg->lds + 256 <= kMaxLdsBytes;
+}
+
+bool pair_choose(const ConvGeom& g1, const ConvGeom& g2, PairGeom* pg)
+{
+    // 64-pixel tiles of 4 rows x 16 columns recompute the fewest layer-1
+    // outputs per layer-2 output; then 2 x 32, 8 x 8, and 32-pixel tiles
+    const int forced_nt = getenv("CVX_STEM_PAIR_TILE") ? atoi(getenv("CVX_STEM_PAIR_TILE")) / 100 : 0;
+    const int forced_tc = getenv("CVX_STEM_PAIR_TILE") ? atoi(getenv("CVX_STEM_PAIR_TILE")) % 100 : 0;
+    if (forced_nt > 0 && pair_geom(g1, g2, forced_nt, forced_tc, pg)) return true;
+    const int cand[][2] = {{2, 16}, {2, 32}, {2, 8}, {1, 16}, {1, 8}, {1, 32}};
+    for (const auto& c : cand)
+        if (pair_geom(g1, g2, c[0], c[1], pg)) return true;
+    return false;
+}
+
+}  // namespace
+
+bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2)
+{
+    if (!stem_shape(g1) || g1.cout != kC1 || g1.cin > kMaxCin1 || g1.res_mode != CVX_RES_NONE) return false;
+    if (g2.groups != 1 || g2.k != 3 || g2.pad != 1 || (g2.stride != 1 && g2.stride != 2)) return false;
+    if (g2.cin != kC1 || g2.n != g1.n || g2.h != g1.oh || g2.w != g1.ow) return false;
+    if (g2.w_layout != CVX_W_PACKED) return false;
+    if ((long)g2.n * g2.cout * g2.oh * g2.ow * 4 >= 0x7fffffffL) return false;
+    PairGeom pg;
+    return pair_choose(g1, g2, &pg);
+}
+
+void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, char* buf, int len)
+{
+    PairGeom pg;
+    if (!pair_choose(g1, g2, &pg)) {
+        snprintf(buf, len, "unsupported");
+        return;
+    }
+    snprintf(buf, len, "stem_pair k3 s%d+s%d bn=%d tc=%d kernel=cvx::k_stem_pair<%d, %d>", g1.stride, g2.stride,
+             32 * pg.nt, pg.tc, pg.nt, g1.stride);
+}
+
+hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1, const float* scale1,
+                            const float* bias1, const ConvGeom& g2, const float* wp, const float* scale2,
+                            const float* bias2, const float* res, float* y, hipStream_t s)
+{
+    PairGeom pg;
+    if (!pair_choose(g1, g2, &pg)) return hipErrorInvalidValue;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return hipErrorInvalidValue;
+    StemPairArgs a;
+    a.x = x;
+    a.w1 = w1;
+    a.scale1 = scale1;
+    a.bias1 = bias1;
+    a.wp = wp;
+    a.scale2 = scale2;
+    a.bias2 = bias2;
+    a.res = res;
+    a.y = y;
+    a.n = g1.n;
+    a.cin1 = g1.cin;
+    a.H1 = g1.h;
+    a.W1 = g1.w;
+    a.S1 = g1.stride;
+    a.H2 = g1.oh;
+    a.W2 = g1.ow;
+    a.S2 = g2.stride;
+    a.OH = g2.oh;
+    a.OW = g2.ow;
+    a.cout = g2.cout;
+    a.act1 = g1.act;
+    a.act2 = g2.act;
+    a.res_mode = g2.res_mode;
+    a.tc = pg.tc;
+    a.tr = pg.tr;
+    a.tiles_w = pg.tiles_w;
+    a.tiles_per_img = pg.tiles_per_img;
+    a.nmb = pg.nmb;
+    fastdiv_params(pg.tc, &a.m_tc, &a.l_tc);
+    fastdiv_params(pg.tiles_w, &a.m_tw, &a.l_tw);
+    fastdiv_params(pg.tiles_per_img, &a.m_tpi, &a.l_tpi);
+    fastdiv_params(g1.n * pg.tiles_per_img, &a.m_nb, &a.l_nb);
+    a.PR = pg.PR;
+    a.PCW = pg.PCW;
+    a.NQ = pg.PR * pg.PCW / 4;
+    fastdiv_params(pg.PCW / 4, &a.m_q4, &a.l_q4);
+    a.WR = pg.WR;
+    a.WCW = pg.WCW;
+    a.win_elems = pg.win_elems;
+    a.win_rounds = pg.win_rounds;
+    fastdiv_params(pg.WCW / 4, &a.m_we, &a.l_we);
+    fastdiv_params(pg.WR * pg.WCW / 4, &a.m_wc, &a.l_wc);
+    a.x_bytes = (unsigned)((long)g1.n * g1.cin * g1.h * g1.w * 4);
+    a.wp_bytes = (unsigned)(packed_weight_floats(g2) * 4);
+    const bool quads = pg.tc % 4 == 0 && g2.ow % 4 == 0;
+    const bool al_y = (reinterpret_cast<uintptr_t>(y) & 15u) == 0;
+    const bool al_r = res == nullptr || (reinterpret_cast<uintptr_t>(res) & 15u) == 0;
+    a.vout = quads && al_y && al_r ? 1 : 0;
+    dim3 grid((unsigned)((long)g1.n * pg.tiles_per_img * pg.nmb));
+    if (pg.nt == 2) {
+        if (g1.stride == 2)
+            hipLaunchKernelGGL((k_stem_pair<2, 2>), grid, dim3(kSPThreads), pg.lds, s, a);
+        else
+            hipLaunchKernelGGL((k_stem_pair<2, 1>), grid, dim3(kSPThreads), pg.lds, s, a);
+    } else {
+        if (g1.stride == 2)
+            hipLaunchKernelGGL((k_stem_pair<1, 2>), grid, dim3(kSPThreads), pg.lds, s, a);
+        else
+            hipLaunchKernelGGL((k_stem_pair<1, 1>), grid, dim3(kSPThreads), pg.lds, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cvx

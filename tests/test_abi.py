@@ -366,6 +366,7 @@ def test_chain_plan_on_the_host(monkeypatch):
     plan as one chain launch; by default, and with the forced reuse placement
     (a chain's layers run concurrently, so no region may be reused inside it),
     every layer keeps a launch of its own; OIHW weights never chain."""
+    monkeypatch.setenv("CVX_STEM_PAIR", "0")  # stem2 chains instead of pairing with stem1
     layers, _ = _net_layers(wl.detector_pipeline(1), cvx.CVX_W_PACKED)
     plan = cvx.cvx_forward_plan(layers)
     assert not any(p.startswith("chain") for p in plan)

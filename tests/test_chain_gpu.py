@@ -28,8 +28,10 @@ def setup_module(module):
 
 @pytest.fixture(autouse=True)
 def chain_on(monkeypatch):
-    # the chain launch is opt-in (one launch per layer measured faster)
+    # the chain launch is opt-in (one launch per layer measured faster); the
+    # detector's stem2 chains instead of running with stem1 as one kernel
     monkeypatch.setenv("CVX_CHAIN", "1")
+    monkeypatch.setenv("CVX_STEM_PAIR", "0")
 
 
 def _run(wk, expect_chain=True):

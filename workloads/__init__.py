@@ -293,6 +293,23 @@ def prologue_stem(batch: int, src_h: int, src_w: int, dst_h: int, dst_w: int, co
     return Workload(f"prologue_{src_h}x{src_w}_{dst_h}x{dst_w}_s{stride}_b{batch}", x, L)
 
 
+def stem_pair_case(seed: int, n: int, cin: int, h: int, w: int, s1: int, s2: int, cout: int,
+                   act1: int = ACT_SILU, act2: int = ACT_SILU, res_mode: int = RES_NONE) -> Workload:
+    """A stem layer (3x3 pad 1, cin -> 16, stride s1) and the 3x3 pad-1 layer
+    16 -> cout (stride s2) that alone reads it; with a residual, a 1x1 layer of
+    stride s1*s2 on the input provides it (layer 0), the stem is layer 1."""
+    rng = np.random.default_rng(1000 + seed)
+    x = rng.uniform(0.0, 1.0, (n, cin, h, w)).astype(np.float32)
+    L: List[Layer] = []
+    if res_mode != RES_NONE:
+        L.append(conv_layer(rng, cin, cout, 1, s1 * s2, 0, act=ACT_NONE, name="res_src"))
+    first = len(L)
+    L.append(conv_layer(rng, cin, 16, 3, s1, 1, act=act1, inp=NET_INPUT, name="stem1"))
+    L.append(conv_layer(rng, 16, cout, 3, s2, 1, act=act2, inp=first, res_mode=res_mode,
+                        res=0 if res_mode != RES_NONE else NO_RES, name="stem2"))
+    return Workload(f"stem_pair_{seed}", x, L)
+
+
 def random_conv_case(seed: int, n: int, cin: int, h: int, w: int, cout: int, k: int,
                      stride: int, pad: int, groups: int = 1, act: int = ACT_SILU,
                      res_mode: int = RES_NONE, x_lo: float = -1.0) -> Tuple[np.ndarray, Layer]:
