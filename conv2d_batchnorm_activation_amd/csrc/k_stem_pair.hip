@@ -16,10 +16,11 @@
 //      with 16-byte LDS-direct loads; outside the image they read zeros (the
 //      first layer's padding);
 //   2. all eight waves compute the first layer's 16 output channels over the
-//      region the tile's 3x3 windows cover (four columns and four channels a
-//      lane; weights, scales and biases uniform per wave, through the scalar
-//      cache) and store them to LDS in the layout the matrix loop reads,
-//      writing zeros outside the image (the second layer's padding);
+//      region the tile's 3x3 windows cover, on matrix cores
+//      (v_mfma_f32_16x16x4_f32: 16 pixels x 16 channels a block, the taps
+//      read from the LDS window), apply its BN and activation and store them
+//      to LDS in the layout the matrix loop reads, writing zeros outside the
+//      image (the second layer's padding);
 //   3. four consumer waves run the second layer's reduction (16 channels x 9
 //      taps) on v_mfma_f32_32x32x2_f32, as k_igemm_packed does for one chunk,
 //      sum their partial tiles through LDS and apply the epilogue.
@@ -78,8 +79,7 @@ struct StemPairArgs {
     int tc, tr, tiles_w, tiles_per_img, nmb;
     unsigned m_tc, l_tc, m_tw, l_tw, m_tpi, l_tpi, m_nb, l_nb;
     int PR, PCW;              // staged layer-1 output region per channel: PR rows x PCW floats
-    int NQ;                   // quads of four columns per channel: PR * PCW / 4
-    unsigned m_q4, l_q4;      // divide by PCW / 4
+    unsigned m_pcw, l_pcw;    // divide by PCW
     int WR, WCW;              // layer-1 input window per channel: WR rows x WCW floats
     int win_elems, win_rounds;  // 16-byte elements of the window, 512-lane rounds
     unsigned m_we, l_we;      // divide by WCW / 4
@@ -143,9 +143,26 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             sp_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + WIN + 4 * (kSPThreads * i + 64 * wave)), off);
         }
     }
-    // the loads below are counted after these: keep the compiler from moving any
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+
+    // the first layer's operands of this lane for phase 2 (all waves): its
+    // weight of each step (channel l%16, tap 4s + l/16; zero past c_in x 9),
+    // where that tap sits in the window, and its channel's scale and bias --
+    // loaded now, so that their latency hides under the window's
+    const int KT = a.cin1 * 9;
+    const int steps = (KT + 3) >> 2;
+    const int co1 = lane & 15;
+    const int kg = lane >> 4;
+    float bw[kMaxCin1 * 9 / 4 + 1];
+    int aoff[kMaxCin1 * 9 / 4 + 1];
+#pragma unroll
+    for (int st = 0; st < kMaxCin1 * 9 / 4 + 1; ++st) {
+        const int k = 4 * st + kg;
+        const bool live = st < steps && k < KT;
+        bw[st] = live ? a.w1[co1 * KT + k] : 0.0f;
+        const int ci = k / 9, t = k - 9 * (k / 9);
+        aoff[st] = live ? (ci * a.WR + t / 3) * a.WCW + t % 3 + 3 : 0;
+    }
+    const float s1 = a.scale1[co1], b1 = a.bias1[co1];
 
     // consumers: the second layer's weights (one chunk of row block mb, this
     // wave's quarter, in the operand's lane order), scale, bias and residual
@@ -188,79 +205,46 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
                     rv[k][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (int)at(k, e), 0, 0));
             }
         }
-        // the window's loads were issued first and complete in order
-        wait_vm_at_most(5 + 2 + (a.vout ? NT : 4 * NT));
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);
     }
+    // the window has landed (and with it every operand load above)
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
 
-    // ---- 2. the first layer over the region (all waves): wave w takes
-    // channels 4 (w & 3) .. +3 and half (w >> 2) of the region's quads
+    // ---- 2. the first layer over the region (all waves), on matrix cores:
+    // v_mfma_f32_16x16x4_f32 with the region's pixels as rows (16 consecutive
+    // of its flat [row][column] order per block), the 16 channels as columns
+    // and K = c_in x 9 taps, four per instruction (lane l: pixel l%16 of the
+    // block, tap 4s + l/16 of step s; the weights' lane: channel l%16, same
+    // tap).  A lane's four sums are four consecutive pixels of channel l%16,
+    // which go to the region as one 16-byte store.  Taps past c_in x 9 have
+    // zero weights.  Wave w takes blocks w, w+8, ...
     {
-        const int cg = wave & 3;
-        const int QH = (a.NQ + 1) >> 1;
-        const int q_lo = (wave >> 2) * QH;
-        const int q_hi = min(a.NQ, q_lo + QH);
-        const int KT = a.cin1 * 9;
-        // the wave's four channels' weights, uniform: read through the scalar
-        // cache where they are used
-        const float* w1c = a.w1 + (4 * cg) * KT;
-        float s1[4], b1[4];
+        const int nblk = (RS + 15) >> 4;
+        for (int blk = wave; blk < nblk; blk += 8) {
+            // the A operand's pixel of this lane: flat index, clamped into the region
+            const int f = min(16 * blk + (lane & 15), RS - 1);
+            const int r = sp_div(f, a.m_pcw, a.l_pcw);
+            const int x = f - r * a.PCW;
+            const float* wb = smem + WIN + S1 * r * a.WCW + S1 * x;
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            s1[c] = a.scale1[4 * cg + c];
-            b1[c] = a.bias1[4 * cg + c];
-        }
-        const int q4 = a.PCW >> 2;
-        for (int q = q_lo + lane; q < q_hi; q += 64) {
-            const int r = sp_div(q, a.m_q4, a.l_q4);
-            const int x = 4 * (q - r * q4);
-            const int yy = iy0 + r;
-            f32x4 acc[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ci = 0; ci < kMaxCin1; ++ci) {
-                if (ci >= a.cin1) break;
-#pragma unroll
-                for (int kh = 0; kh < 3; ++kh) {
-                    // window columns S1*(x+j) + kw + 3 (j < 4, kw < 3) of row S1*r + kh
-                    const float* wr = smem + WIN + (ci * a.WR + S1 * r + kh) * a.WCW + S1 * x + 3;
-                    float win[S1 == 2 ? 9 : 6];
-                    win[0] = wr[0];
-                    const f32x4 m0 = *reinterpret_cast<const f32x4*>(wr + 1);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) win[1 + e] = m0[e];
-                    if constexpr (S1 == 2) {
-                        const f32x4 m1 = *reinterpret_cast<const f32x4*>(wr + 5);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) win[5 + e] = m1[e];
-                    } else {
-                        win[5] = wr[5];
-                    }
-#pragma unroll
-                    for (int kw = 0; kw < 3; ++kw)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const float wv = w1c[c * KT + ci * 9 + kh * 3 + kw];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[c][j] = fmaf(wv, win[S1 * j + kw], acc[c][j]);
-                        }
-                }
+            for (int st = 0; st < kMaxCin1 * 9 / 4 + 1; ++st) {
+                if (st >= steps) break;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wb[aoff[st]], bw[st], acc, 0, 0, 0);
             }
-            // outside the first layer's output: zeros (the second layer's padding)
-            const bool rok = (unsigned)yy < (unsigned)a.H2;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            // sums: channel co1, flat pixels fo .. fo+3 (one region row: PCW % 4 == 0)
+            const int fo = 16 * blk + 4 * kg;
+            if (fo < RS) {
+                const int ro = sp_div(fo, a.m_pcw, a.l_pcw);
+                const int xo = fo - ro * a.PCW;
+                const bool rok = (unsigned)(iy0 + ro) < (unsigned)a.H2;
                 f32x4 o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int xx = gx0 + x + j;
-                    const float v = apply_act_fast(fmaf(s1[c], acc[c][j], b1[c]), a.act1);
-                    o[j] = rok && (unsigned)xx < (unsigned)a.W2 ? v : 0.0f;
+                for (int v = 0; v < 4; ++v) {
+                    const float t = apply_act_fast(fmaf(s1, acc[v], b1), a.act1);
+                    o[v] = rok && (unsigned)(gx0 + xo + v) < (unsigned)a.W2 ? t : 0.0f;
                 }
-                *reinterpret_cast<f32x4*>(smem + (4 * cg + c) * RS + r * a.PCW + x) = o;
+                *reinterpret_cast<f32x4*>(smem + co1 * RS + fo) = o;
             }
         }
     }
@@ -465,8 +449,7 @@ hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1,
     fastdiv_params(g1.n * pg.tiles_per_img, &a.m_nb, &a.l_nb);
     a.PR = pg.PR;
     a.PCW = pg.PCW;
-    a.NQ = pg.PR * pg.PCW / 4;
-    fastdiv_params(pg.PCW / 4, &a.m_q4, &a.l_q4);
+    fastdiv_params(pg.PCW, &a.m_pcw, &a.l_pcw);
     a.WR = pg.WR;
     a.WCW = pg.WCW;
     a.win_elems = pg.win_elems;

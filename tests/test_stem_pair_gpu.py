@@ -4,10 +4,10 @@ as one kernel by cvx_forward, the stem's output never written.  Against the
 fp64 oracle at |gpu - oracle| <= 1e-4*max(1,|oracle|), for both strides of
 each layer, ragged tiles and row blocks, several images, every tile the
 kernel takes, residual placements of the second layer, and a list input off a
-16-byte boundary (the two-kernel fallback).  The pair keeps every summation
-in the order the two separate kernels use, so its output is also compared bit
-for bit with CVX_STEM_PAIR=0."""
-import numpy as np
+16-byte boundary (the two-kernel fallback).  The two-kernel path
+(CVX_STEM_PAIR=0) is checked against the oracle beside it: the pair computes
+the stem on matrix cores, in another summation order, so the two agree to
+rounding, not bit for bit."""
 import pytest
 import torch
 
@@ -59,10 +59,11 @@ def test_stem_pair_matches_oracle(case, tile, monkeypatch):
         nt, tc = int(tile) // 100, int(tile) % 100
         if f"bn={32 * nt} tc={tc} " not in plan[1]:
             pytest.skip(f"tile {tile} does not fit this shape: {plan[1]}")
-    check(got, oracle.forward(wk.layers, wk.x), f"stem pair {case} tile {tile}")
+    ref = oracle.forward(wk.layers, wk.x)
+    check(got, ref, f"stem pair {case} tile {tile}")
     apart, plan0 = _forward(wk, monkeypatch, False)
     assert "k_stem<" in plan0[0] and "k_igemm_packed" in plan0[1], plan0
-    assert np.array_equal(got, apart), "fused and two-kernel results differ"
+    check(apart, ref, f"two kernels {case}")
 
 
 MODES = [(a1, a2, r) for a1, a2 in ((wl.ACT_SILU, wl.ACT_SILU), (wl.ACT_RELU, wl.ACT_NONE))
@@ -77,8 +78,6 @@ def test_stem_pair_residual_and_activations(mode, monkeypatch):
     say(f"stem pair modes {mode}: {plan}")
     assert plan[1] == "merged into 2" and "k_stem_pair" in plan[2], plan
     check(got, oracle.forward(wk.layers, wk.x), f"stem pair modes {mode}")
-    apart, _ = _forward(wk, monkeypatch, False)
-    assert np.array_equal(got, apart)
 
 
 def test_stem_pair_misaligned_input_falls_back(monkeypatch):
@@ -97,12 +96,9 @@ def test_stem_pair_misaligned_input_falls_back(monkeypatch):
 @pytest.mark.parametrize("batch", [1, 2])
 def test_detector_stem_pair_in_pipeline(batch, monkeypatch):
     """The detector pipeline: prologue -> (stem1, stem2 as one kernel) -> the
-    rest; the whole forward against the oracle, and bit for bit against the
-    pipeline with the two stem kernels apart."""
+    rest; the whole forward against the oracle."""
     wk = wl.detector_pipeline(batch)
     got, plan = _forward(wk, monkeypatch, True)
     assert plan[1] == "merged into 2" and "k_stem_pair" in plan[2], plan
     say(f"detector b{batch} with the stem pair")
     check(got, oracle.forward(wk.layers, wk.x), f"detector b{batch} stem pair")
-    apart, _ = _forward(wk, monkeypatch, False)
-    assert np.array_equal(got, apart)
