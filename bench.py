@@ -241,6 +241,7 @@ def per_layer(wk, net, counts, reps: int, cold: bool = True):
     the cold time; fractions of the MFMA peak from the hot time."""
     from conv2d_batchnorm_activation_amd import cvx
     rows = []
+    fplan = cvx.cvx_forward_plan(net.arr)
     for i, L in enumerate(wk.layers):
         c = counts[i]
         if L.kind not in (cvx.CVX_L_PREPROC, cvx.CVX_L_CONV):
@@ -280,14 +281,98 @@ def per_layer(wk, net, counts, reps: int, cold: bool = True):
                                             round((gbs_cold or gbs) / HBM_PEAK_GBS, 4)),
                      "copy_us": round(copy_hot, 3) if copy_hot else None,
                      "copy_us_cold": round(copy_cold, 3) if copy_cold else None,
-                     "of_copy_cold": round(copy_cold / us_cold, 3) if copy_cold and us_cold else None})
+                     "of_copy_cold": round(copy_cold / us_cold, 3) if copy_cold and us_cold else None,
+                     # a layer the forward runs inside another kernel (a stem pair) is timed
+                     # here alone for reference; the pair has a row of its own below
+                     "in_forward": not (fplan[i].startswith("merged into") or fplan[i].startswith("stem_pair")),
+                     "forward_plan": fplan[i]})
         cold_txt = f" cold {us_cold:7.2f} us {gbs_cold:7.1f} GB/s" if us_cold else ""
         if copy_cold:
             cold_txt += f" (a copy of its bytes: {copy_cold:.2f} us cold)"
         log(f"  {L.name:16s} {us:8.2f} us hot (eager {ms_eager * 1e3:6.2f}){cold_txt}  "
             f"{gflops:9.1f} GFLOP/s  {gbs:8.1f} GB/s hot  {bound} frac {frac:.3f}  [{plan}]")
+    for i, line in enumerate(fplan):
+        if line.startswith("stem_pair") and not wk.layers[i].res_mode:
+            marker()
+            rows.append(stem_pair_row(wk, counts, i - 1, line, reps, cold))
     marker()
     return rows
+
+
+def stem_pair_row(wk, counts, i, line, reps: int, cold: bool):
+    """Layers i (a stem) and i+1, which the forward runs as one kernel
+    (k_stem_pair), timed as that kernel: a two-layer list on an input of the
+    stem's input shape, hot (a graph of 20 forwards on the same buffers) and
+    cold (rotating sets of at least COLD_BYTES).  Algorithmic counts: both
+    layers' FLOPs; the stem's input, the second layer's output and residual and
+    both layers' weights (the 16 channels in between never leave the chip)."""
+    import dataclasses
+    import math
+    import numpy as np
+    import torch
+    import workloads as wl
+    from conv2d_batchnorm_activation_amd.net import Net
+    L1, L2 = wk.layers[i], wk.layers[i + 1]
+    s1 = dataclasses.replace(L1, inp=wl.NET_INPUT)
+    s2 = dataclasses.replace(L2, inp=0)
+    net = Net([s1, s2], _layer_input_shape(wk, i))
+    shape = net.input_shape
+    c1, c2 = counts[i], counts[i + 1]
+    flop = c1["flop"] + c2["flop"]
+    out_b = 4.0 * float(np.prod(net.out_shape))
+    byts = 4.0 * float(np.prod(shape)) + out_b * (2 if L2.res_mode else 1) + \
+        4.0 * (L1.params["w"].size + L2.params["w"].size + 2 * L1.cout + 2 * L2.cout)
+    x = torch.rand(shape, device="cuda")
+    fn = lambda: net(x)
+    inner = 20
+    us = time_graph(capture(fn, inner), inner, max(1, reps // inner)) * 1e3
+    us_cold = None
+    sets = 0
+    if cold:
+        set_bytes = 4 * int(np.prod(shape)) + int(out_b) + net.ws_bytes
+        sets = int(min(MAX_COLD_SETS, max(2, math.ceil(COLD_BYTES / set_bytes))))
+        bufs = [(torch.rand(shape, device="cuda"), torch.empty(net.out_shape, device="cuda"),
+                 torch.empty(max(net.ws_bytes, 256), dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+        from conv2d_batchnorm_activation_amd import cvx
+        fns = [lambda b=b: cvx.cvx_forward(net.arr, b[0], b[1], b[2], net.ws_bytes) for b in bufs]
+        us_cold = time_rotating(fns, max(reps, sets)) * 1e3
+        del bufs, fns
+        torch.cuda.empty_cache()
+    gflops = flop / (us * 1e-6) / 1e9
+    ai = flop / byts
+    bound = "mfma" if ai >= RIDGE else "hbm"
+    gbs_cold = byts / (us_cold * 1e-6) / 1e9 if us_cold else None
+    frac = gflops / (MFMA_F32_PEAK_TFLOPS * 1e3) if bound == "mfma" else (gbs_cold or byts / (us * 1e-6) / 1e9) / HBM_PEAK_GBS
+    kernel = line.split("kernel=")[1].split()[0] if "kernel=" in line else line
+    log(f"  {L1.name + '+' + L2.name:16s} {us:8.2f} us hot" + (f" cold {us_cold:7.2f} us" if us_cold else "") +
+        f"  {gflops:9.1f} GFLOP/s  {bound} frac {frac:.3f}  [{line}]")
+    return {"layer": f"{L1.name}+{L2.name}", "plan": line, "kernel": kernel, "splitk": 1,
+            "us": round(us, 3), "us_cold": round(us_cold, 3) if us_cold else None, "cold_sets": sets,
+            "gflop": flop / 1e9, "mbytes": byts / 1e6, "ai": round(ai, 2), "gflops": round(gflops, 1),
+            "gbs_hot": round(byts / (us * 1e-6) / 1e9, 1), "gbs_cold": round(gbs_cold, 1) if gbs_cold else None,
+            "bound": bound, "frac_of_peak": round(frac, 4), "in_forward": True, "forward_plan": line}
+
+
+def _layer_input_shape(wk, i):
+    """The input shape of layer i of a workload (its producer's output shape)."""
+    from conv2d_batchnorm_activation_amd.net import Net  # noqa: F401
+    import workloads as wl
+    shapes = []
+    for L in wk.layers[:i + 1]:
+        s_in = wk.x.shape if L.inp == wl.NET_INPUT else shapes[L.inp]
+        if L.kind == wl.KIND_PREPROC:
+            n = s_in[0]
+            out = (n, 3, L.dst_h, L.dst_w)
+        elif L.kind == wl.KIND_CONV:
+            n, _, h, w = s_in
+            oh = (h + 2 * L.pad - L.k) // L.stride + 1
+            ow = (w + 2 * L.pad - L.k) // L.stride + 1
+            out = (n, L.cout, oh, ow)
+        else:
+            out = (s_in[0], L.cout if L.kind == wl.KIND_FC else s_in[1], 1, 1)
+        shapes.append(out)
+    L = wk.layers[i]
+    return tuple(wk.x.shape if L.inp == wl.NET_INPUT else shapes[L.inp])
 
 
 MARKER_KERNEL = "spin_kernel"
@@ -310,6 +395,8 @@ def dominant(rows, with_traffic: bool = True):
     (all of its layers when it has none of those)."""
     by = {}
     for r in rows:
+        if not r.get("in_forward", True):
+            continue  # timed alone for reference; the forward runs it inside another kernel
         k = by.setdefault(r["kernel"], [])
         k.append(r)
     name, group = max(by.items(), key=lambda kv: sum(r["us"] for r in kv[1]))
@@ -840,22 +927,25 @@ def cold_forward_us(net, wk, steps: int) -> dict:
     return st
 
 
-def forward_time_ms(net, x, steps: int) -> float:
-    """Milliseconds per forward: the forward captured once as a graph, replayed
-    `steps` times between two events."""
+def forward_time_ms(net, x, steps: int, per_graph: int = 1) -> float:
+    """Milliseconds per forward: `per_graph` forwards captured as one graph,
+    replayed until `steps` forwards ran, between two events.  With one forward
+    per graph each replay adds the graph launch's own cost (about 5 us); with
+    ten, a tiny forward's figure is the GPU's time, not the host's enqueue."""
     import torch
-    g = capture(lambda: net(x), 1)
+    g = capture(lambda: net(x), per_graph)
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(steps):
+    for _ in range(reps):
         g.replay()
     e.record()
     e.synchronize()
-    return s.elapsed_time(e) / steps
+    return s.elapsed_time(e) / (reps * per_graph)
 
 
 def other_workloads(layer_reps: int, steps: int):
@@ -888,10 +978,13 @@ def other_workloads(layer_reps: int, steps: int):
         total, per = timed_steps(lambda: net(x), steps)
         ms = total / steps
         ms_graph = forward_time_ms(net, x, steps)
-        log(f"{name}: {ms * 1e3:.1f} us/forward, {ms_graph * 1e3:.1f} us as a graph replay "
+        ms_graph10 = forward_time_ms(net, x, steps, per_graph=10)
+        log(f"{name}: {ms * 1e3:.1f} us/forward, {ms_graph * 1e3:.1f} us as a graph replay, "
+            f"{ms_graph10 * 1e3:.1f} us per forward in graphs of ten "
             f"({flop / 1e9:.3f} GFLOP, {byts / 1e6:.1f} MB)")
         entry = {"workload": wk.name, "batch": int(wk.x.shape[0]), "us_per_forward": round(ms * 1e3, 2),
                  "us_per_forward_graph": round(ms_graph * 1e3, 2),
+                 "us_per_forward_graph10": round(ms_graph10 * 1e3, 2),
                  "gflops": round(flop / (ms * 1e-3) / 1e9, 1),
                  "gbs": round(byts / (ms * 1e-3) / 1e9, 1), "spread": stats(per),
                  "cold": cold_forward_us(net, wk, steps)}
