@@ -680,6 +680,21 @@ cvx_status cvx_gap_fc(const float* x, int n, int c, int h, int w, const float* f
 // ============================================================ layer lists
 namespace {
 
+// The stem prologue of list layer `l` (a CVX_L_PREPROC over contiguous frames).
+StemPrologue prologue_of(const cvx_layer& l, const void* frames)
+{
+    StemPrologue pre;
+    pre.src = static_cast<const unsigned char*>(frames);
+    pre.src_h = l.conv.h;
+    pre.src_w = l.conv.w;
+    pre.row_bytes = 3L * l.conv.w;
+    for (int c = 0; c < 3; ++c) {
+        pre.mean[c] = l.mean[c];
+        pre.stdv[c] = l.std[c];
+    }
+    return pre;
+}
+
 struct Shape {
     int n, c, h, w;
     size_t elems() const { return (size_t)n * c * h * w; }
@@ -695,6 +710,7 @@ struct NodePlan {
     int pair;            // the merged shortcut this layer computes with its own product, or -1
     bool stem_next;      // stem whose output only the next layer reads: both run as one kernel there
     bool stem_kept;      // ... whose output still gets a region (a list input may be misaligned at launch)
+    bool pre_into_pair;  // prologue whose output only a paired stem reads: the pair resizes the frame itself
     int last_use;        // last layer index reading this output
     size_t offset;       // workspace offset of the output (non-final layers)
     int chain_first;     // first layer of the chain run this layer belongs to, or -1
@@ -868,10 +884,18 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
             const NodePlan& nn = lp->nodes[i + 1];
             if (l.kind != CVX_L_CONV || nx.kind != CVX_L_CONV || nx.in != i || readers[i] != 1) continue;
             if (np.p.fam != FAM_DIRECT || !np.p.direct_stem || np.merged || np.pair >= 0) continue;
-            if (nn.p.fam != FAM_IGEMM_PACKED || !stem_pair_fits(np.g, nn.g)) continue;
+            if (nn.p.fam != FAM_IGEMM_PACKED || !stem_pair_fits(np.g, nn.g, nullptr)) continue;
             np.stem_next = true;
             np.stem_kept = l.in == CVX_INPUT;
             if (l.in >= 0) lp->nodes[l.in].last_use = std::max(lp->nodes[l.in].last_use, i + 1);
+            // the prologue before it, read by nothing else: the pair resizes and
+            // normalises the frame itself (CVX_STEM_PAIR_U8=0 keeps it apart).
+            // Its output keeps a region, for frames off a 16-byte boundary.
+            const char* u8_env = getenv("CVX_STEM_PAIR_U8");
+            if (i == 1 && l.in == 0 && L[0].kind == CVX_L_PREPROC && readers[0] == 1 && !(u8_env && u8_env[0] == '0')) {
+                const StemPrologue pre = prologue_of(L[0], nullptr);
+                if (stem_pair_fits(np.g, nn.g, &pre)) lp->nodes[0].pre_into_pair = true;
+            }
         }
     }
     // Placement of intermediate outputs.  A kernel that writes a buffer another
@@ -1009,7 +1033,12 @@ cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, in
         const NodePlan& np = lp.nodes[i];
         char line[320];
         switch (l.kind) {
-        case CVX_L_PREPROC: snprintf(line, sizeof(line), "preprocess"); break;
+        case CVX_L_PREPROC:
+            if (np.pre_into_pair)
+                snprintf(line, sizeof(line), "merged into 2");
+            else
+                snprintf(line, sizeof(line), "preprocess");
+            break;
         case CVX_L_CONV:
             if (np.chain_first >= 0) {
                 const int f = np.chain_first;
@@ -1028,7 +1057,9 @@ cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, in
                 snprintf(line, sizeof(line), "merged into %d", i + 1);
             } else if (i > 0 && lp.nodes[i - 1].stem_next) {
                 char d[256];
-                stem_pair_describe(lp.nodes[i - 1].g, np.g, d, sizeof(d));
+                const bool u8 = i == 2 && lp.nodes[0].pre_into_pair;
+                const StemPrologue pre = u8 ? prologue_of(layers[0], nullptr) : StemPrologue{};
+                stem_pair_describe(lp.nodes[i - 1].g, np.g, u8 ? &pre : nullptr, d, sizeof(d));
                 snprintf(line, sizeof(line), "%s stem=%d", d, i - 1);
             } else {
                 describe_plan(np.g, np.p, line, sizeof(line));
@@ -1095,6 +1126,9 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
     };
     void* layer_ws = ws ? ws + lp.act_bytes : nullptr;
     int chain_end = -1;  // layers before this index ran inside a chain launch
+    // frames the stem pair can read itself: 16-byte aligned (rows are whole
+    // 16-byte runs, checked when planning)
+    const bool frames_fused = lp.nodes[0].pre_into_pair && (reinterpret_cast<uintptr_t>(input) & 15u) == 0;
     for (int i = 0; i < n_layers; ++i) {
         const cvx_layer& l = layers[i];
         const NodePlan& np = lp.nodes[i];
@@ -1109,13 +1143,16 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
             if (cs != CVX_OK) return cs;
             continue;
         }
+        if (np.pre_into_pair && frames_fused) continue;  // the stem pair resizes the frame
         if (i > 0 && lp.nodes[i - 1].stem_next) {
             const cvx_layer& sl = layers[i - 1];
             const float* x = in_ptr(sl.in);
             if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) {
                 const float* res = l.conv.res_mode != CVX_RES_NONE ? in_ptr(l.res) : nullptr;
-                e = launch_stem_pair(lp.nodes[i - 1].g, x, sl.w, sl.scale, sl.bias, np.g, l.w, l.scale, l.bias,
-                                     res, out_ptr(i), s);
+                const bool u8 = i == 2 && lp.nodes[0].pre_into_pair && frames_fused;
+                const StemPrologue pre = u8 ? prologue_of(layers[0], input) : StemPrologue{};
+                e = launch_stem_pair(lp.nodes[i - 1].g, x, u8 ? &pre : nullptr, sl.w, sl.scale, sl.bias, np.g, l.w,
+                                     l.scale, l.bias, res, out_ptr(i), s);
                 if (e != hipSuccess) return CVX_ERR_HIP;
                 continue;
             }

@@ -111,12 +111,20 @@ hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hip
 
 // Stem pair (k_stem_pair.hip): a k_stem-shaped layer g1 with 16 output channels
 // and no residual, and the packed 3x3 layer g2 that alone reads its output, in
-// one kernel; x must be 16-byte aligned.
-bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2);
-void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, char* buf, int len);
-hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1, const float* scale1,
-                            const float* bias1, const ConvGeom& g2, const float* wp, const float* scale2,
-                            const float* bias2, const float* res, float* y, hipStream_t s);
+// one kernel.  Layer 1's input is x (16-byte aligned), or, with `pre`, a u8 HWC
+// frame the kernel resizes and normalises into it as the stem prologue does
+// (frame 16-byte aligned, rows a multiple of 16 bytes).
+struct StemPrologue {
+    const unsigned char* src;
+    int src_h, src_w;
+    long row_bytes;
+    float mean[3], stdv[3];
+};
+bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre);
+void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, char* buf, int len);
+hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const StemPrologue* pre, const float* w1,
+                            const float* scale1, const float* bias1, const ConvGeom& g2, const float* wp,
+                            const float* scale2, const float* bias2, const float* res, float* y, hipStream_t s);
 
 hipError_t launch_splitk_finish(const ConvGeom& g, int splitk, const float* partial,
                                 const float* scale, const float* bias, const float* res, float* y,

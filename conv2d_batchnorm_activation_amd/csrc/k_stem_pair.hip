@@ -28,6 +28,7 @@
 // tiles overlap (about a quarter more of them), which costs less than writing
 // and reading the 16 channels and running a second round of workgroups.
 #include <stdio.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -47,6 +48,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSPThreads = 512;
 constexpr int kC1 = 16;              // channels between the two layers: one chunk
 constexpr int kWinRounds = 6;        // 512-lane rounds of 16-byte window loads, at most
+constexpr int kSrcRounds = 6;        // 512-lane rounds of 16-byte frame loads (u8 source), at most
 constexpr int kMaxCin1 = 4;
 constexpr int kBCFloats = 4 * 5 * 256;  // packed 3x3 floats per (32-row block, chunk)
 
@@ -86,9 +88,45 @@ struct StemPairArgs {
     unsigned m_wc, l_wc;      // divide by WR * WCW / 4 (elements per channel)
     unsigned x_bytes, wp_bytes;
     int vout;
+    // u8 source: layer 1's input is a u8 HWC frame, resized (half-pixel
+    // bilinear) and normalised here, as the stem prologue does
+    const unsigned char* src;
+    int src_h, src_w;
+    unsigned row_bytes, img_bytes;
+    unsigned m_dh, l_dh, m_dw, l_dw;  // divide by 2 * H1, 2 * W1
+    float inv_dh, inv_dw;             // 1 / (2 * H1), 1 / (2 * W1)
+    float na[3], nb[3];               // /255 and the normalisation: v * na + nb
+    int SRB;                          // bytes of a staged frame row segment (multiple of 16)
+    int src_elems, src_rounds;        // 16-byte elements staged, 512-lane rounds
+    unsigned m_srb, l_srb;            // divide by SRB / 16
+    unsigned m_wcw, l_wcw;            // divide by WCW
 };
 
-template <int NT, int S1>
+// Source row (or column) pair and weight of destination index d for the
+// half-pixel bilinear resize, from integers: (2d + 1) * src - dst over 2 * dst,
+// clamped at 0 and at the last row (the prologue's arithmetic).
+struct SrcAxis {
+    int i0, i1;
+    float f;
+};
+__device__ __forceinline__ SrcAxis sp_axis(int d, int src, int dst, unsigned m, unsigned l, float inv)
+{
+    const int num = (2 * d + 1) * src - dst;
+    SrcAxis a;
+    if (num <= 0) {
+        a.i0 = 0;
+        a.f = 0.0f;
+    } else {
+        const unsigned q = (__umulhi((unsigned)num, m) + (unsigned)num) >> l;
+        a.i0 = (int)q;
+        a.f = (float)((unsigned)num - q * (2u * (unsigned)dst)) * inv;
+    }
+    if (a.i0 > src - 1) a.i0 = src - 1;
+    a.i1 = a.i0 + 1 < src ? a.i0 + 1 : src - 1;
+    return a;
+}
+
+template <int NT, int S1, bool U8>
 __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
 {
     constexpr int BN = 32 * NT;
@@ -124,8 +162,33 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     const int wx0 = S1 * gx0 - 4;            // first window column (16-byte aligned)
     const int wy0 = S1 * iy0 - 1;            // first window row
 
-    // ---- 1. the first layer's input window -> LDS (all waves)
-    {
+    // ---- 1. the first layer's input window -> LDS (all waves).  From a u8
+    // frame: the two frame rows each window row interpolates between, over the
+    // window's span of frame columns, go to LDS (16-byte LDS-direct loads),
+    // then are resized and normalised into the window below.
+    const int SRC = WIN * 4 + 4 * a.cin1 * a.WR * a.WCW;  // byte offset of the staged frame rows
+    int sb0 = 0;                                          // first staged frame byte of a row
+    if constexpr (U8) {
+        const int x_lo = max(wx0, 0);
+        sb0 = (3 * sp_axis(x_lo, a.src_w, a.W1, a.m_dw, a.l_dw, a.inv_dw).i0) & ~15;
+        const rsrc_t rs = make_rsrc(a.src + (long)b * a.img_bytes, a.img_bytes);
+        const int epr = a.SRB >> 4;
+        unsigned char* sm = reinterpret_cast<unsigned char*>(smem);
+#pragma unroll
+        for (int i = 0; i < kSrcRounds; ++i) {
+            if (i >= a.src_rounds) break;
+            const int e = tid + kSPThreads * i;
+            const int rr = sp_div(e, a.m_srb, a.l_srb);  // staged row: window row rr/2, its row pair (rr&1)
+            const int j = e - rr * epr;
+            const int y = wy0 + (rr >> 1);
+            const bool ok = e < a.src_elems && (unsigned)y < (unsigned)a.H1;
+            const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
+            const int srow = (rr & 1) ? ay.i1 : ay.i0;
+            const unsigned off = ok ? (unsigned)srow * a.row_bytes + (unsigned)(sb0 + 16 * j) : kOOB;
+            // lane l of the wave writes 16 bytes at d + 16 l: element e lands at SRC + 16 e
+            sp_lds_load16(rs, (__attribute__((address_space(3))) void*)(sm + SRC + 16 * (kSPThreads * i + 64 * wave)), off);
+        }
+    } else {
         const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
         const int epr = a.WCW >> 2;  // 16-byte elements per window row
 #pragma unroll
@@ -206,9 +269,37 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             }
         }
     }
-    // the window has landed (and with it every operand load above)
+    // the window (or the frame rows) has landed, and with it every operand load above
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
+    if constexpr (U8) {
+        // resize and normalise the frame rows into the window: a thread takes
+        // a window pixel (row r, column col) and its three channels; outside the
+        // resized image, zeros (the first layer's padding)
+        const unsigned char* sm = reinterpret_cast<const unsigned char*>(smem) + SRC;
+        const int n_px = a.WR * a.WCW;
+        for (int idx = tid; idx < n_px; idx += kSPThreads) {
+            const int r = sp_div(idx, a.m_wcw, a.l_wcw);
+            const int col = idx - r * a.WCW;
+            const int y = wy0 + r, x = wx0 + col;
+            const bool ok = (unsigned)y < (unsigned)a.H1 && (unsigned)x < (unsigned)a.W1;
+            const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
+            const SrcAxis ax = sp_axis(ok ? x : 0, a.src_w, a.W1, a.m_dw, a.l_dw, a.inv_dw);
+            const unsigned char* r0 = sm + (2 * r) * a.SRB;
+            const unsigned char* r1 = r0 + a.SRB;
+            const int c0 = ok ? 3 * ax.i0 - sb0 : 0, c1 = ok ? 3 * ax.i1 - sb0 : 0;
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) {
+                const float p00 = (float)r0[c0 + ch], p01 = (float)r0[c1 + ch];
+                const float p10 = (float)r1[c0 + ch], p11 = (float)r1[c1 + ch];
+                const float top = fmaf(ax.f, p01 - p00, p00);
+                const float bot = fmaf(ax.f, p11 - p10, p10);
+                const float v = fmaf(fmaf(ay.f, bot - top, top), a.na[ch], a.nb[ch]);
+                smem[WIN + (ch * a.WR + r) * a.WCW + col] = ok ? v : 0.0f;
+            }
+        }
+        lds_barrier();
+    }
 
     // ---- 2. the first layer over the region (all waves), on matrix cores:
     // v_mfma_f32_16x16x4_f32 with the region's pixels as rows (16 consecutive
@@ -339,12 +430,23 @@ namespace {
 struct PairGeom {
     int nt, tc, tr, tiles_w, tiles_per_img, nmb;
     int PR, PCW, WR, WCW, win_elems, win_rounds;
+    int SRB, src_elems, src_rounds;  // u8 source only
     size_t lds;
 };
 
+// Source column index pair of destination column d (host copy of sp_axis's
+// integer part).
+int host_axis_i0(int d, int src, int dst)
+{
+    const long num = (long)(2 * d + 1) * src - dst;
+    long q = num <= 0 ? 0 : num / (2L * dst);
+    return (int)std::min<long>(q, src - 1);
+}
+
 // The region of layer-1 outputs a tile of layer 2 reads, and the window of
-// layer-1 inputs that region needs.
-bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, int nt, int tc, PairGeom* pg)
+// layer-1 inputs that region needs; with a u8 source (pre != null), the frame
+// rows the window interpolates from, their widest byte span over the tiles.
+bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, int nt, int tc, PairGeom* pg)
 {
     const int bn = 32 * nt;
     if (tc <= 0 || bn % tc != 0 || (tc * g2.stride) % 4 != 0) return false;
@@ -361,60 +463,109 @@ bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, int nt, int tc, PairGeom*
     pg->WCW = (g1.stride * pg->PCW - g1.stride + 6 + 3) & ~3;
     pg->win_elems = g1.cin * pg->WR * (pg->WCW / 4);
     pg->win_rounds = (pg->win_elems + kSPThreads - 1) / kSPThreads;
-    if (pg->win_rounds > kWinRounds) return false;
+    pg->SRB = pg->src_elems = pg->src_rounds = 0;
     const size_t region = (size_t)kC1 * pg->PR * pg->PCW;
-    // every lane of a window round writes its 16 bytes (zeros past the window)
-    const size_t win = (size_t)4 * kSPThreads * pg->win_rounds;
     const size_t xch = (size_t)4 * 32 * (bn + 4);
-    pg->lds = (region + std::max(win, xch)) * sizeof(float);
+    size_t after;  // floats after the region
+    if (pre == nullptr) {
+        if (pg->win_rounds > kWinRounds) return false;
+        // every lane of a window round writes its 16 bytes (zeros past the window)
+        after = std::max((size_t)4 * kSPThreads * pg->win_rounds, xch);
+    } else {
+        // widest frame byte span of a window's columns, from its 16-byte aligned start
+        int srb = 16;
+        for (int tw = 0; tw < pg->tiles_w; ++tw) {
+            const int gx0 = (tw * tc * g2.stride - 1) & ~3;
+            const int wx0 = g1.stride * gx0 - 4;
+            const int x_lo = std::max(wx0, 0), x_hi = std::min(wx0 + pg->WCW - 1, g1.w - 1);
+            if (x_hi < x_lo) continue;
+            const int b0 = (3 * host_axis_i0(x_lo, pre->src_w, g1.w)) & ~15;
+            const int i1 = std::min(host_axis_i0(x_hi, pre->src_w, g1.w) + 1, pre->src_w - 1);
+            srb = std::max(srb, ((3 * i1 + 3 + 15) & ~15) - b0);
+        }
+        pg->SRB = srb;
+        pg->src_elems = 2 * pg->WR * (srb / 16);
+        pg->src_rounds = (pg->src_elems + kSPThreads - 1) / kSPThreads;
+        if (pg->src_rounds > kSrcRounds) return false;
+        // the window (written by the interpolation), then the staged frame rows
+        // (every lane of a round writes its 16 bytes)
+        const size_t win = (size_t)g1.cin * pg->WR * pg->WCW;
+        const size_t src = (size_t)4 * kSPThreads * pg->src_rounds;  // floats
+        after = std::max(win + src, xch);
+    }
+    pg->lds = (region + after) * sizeof(float);
     return pg->lds + 256 <= kMaxLdsBytes;
 }
 
-bool pair_choose(const ConvGeom& g1, const ConvGeom& g2, PairGeom* pg)
+bool pair_choose(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, PairGeom* pg)
 {
     // 64-pixel tiles of 4 rows x 16 columns recompute the fewest layer-1
     // outputs per layer-2 output; then 2 x 32, 8 x 8, and 32-pixel tiles
-    const int forced_nt = getenv("CVX_STEM_PAIR_TILE") ? atoi(getenv("CVX_STEM_PAIR_TILE")) / 100 : 0;
-    const int forced_tc = getenv("CVX_STEM_PAIR_TILE") ? atoi(getenv("CVX_STEM_PAIR_TILE")) % 100 : 0;
-    if (forced_nt > 0 && pair_geom(g1, g2, forced_nt, forced_tc, pg)) return true;
+    const char* env = getenv("CVX_STEM_PAIR_TILE");
+    const int forced_nt = env ? atoi(env) / 100 : 0;
+    const int forced_tc = env ? atoi(env) % 100 : 0;
+    if (forced_nt > 0 && pair_geom(g1, g2, pre, forced_nt, forced_tc, pg)) return true;
     const int cand[][2] = {{2, 16}, {2, 32}, {2, 8}, {1, 16}, {1, 8}, {1, 32}};
     for (const auto& c : cand)
-        if (pair_geom(g1, g2, c[0], c[1], pg)) return true;
+        if (pair_geom(g1, g2, pre, c[0], c[1], pg)) return true;
     return false;
 }
 
-}  // namespace
-
-bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2)
+bool pair_shapes(const ConvGeom& g1, const ConvGeom& g2)
 {
     if (!stem_shape(g1) || g1.cout != kC1 || g1.cin > kMaxCin1 || g1.res_mode != CVX_RES_NONE) return false;
     if (g2.groups != 1 || g2.k != 3 || g2.pad != 1 || (g2.stride != 1 && g2.stride != 2)) return false;
     if (g2.cin != kC1 || g2.n != g1.n || g2.h != g1.oh || g2.w != g1.ow) return false;
     if (g2.w_layout != CVX_W_PACKED) return false;
-    if ((long)g2.n * g2.cout * g2.oh * g2.ow * 4 >= 0x7fffffffL) return false;
-    PairGeom pg;
-    return pair_choose(g1, g2, &pg);
+    return (long)g2.n * g2.cout * g2.oh * g2.ow * 4 < 0x7fffffffL;
 }
 
-void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, char* buf, int len)
+}  // namespace
+
+bool stem_pair_fits(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre)
+{
+    if (!pair_shapes(g1, g2)) return false;
+    if (pre != nullptr) {
+        if (g1.cin != 3 || pre->src_h < 1 || pre->src_w < 1) return false;
+        if ((3L * pre->src_w) % 16 != 0) return false;  // whole 16-byte frame rows
+        if ((long)g1.n * pre->src_h * pre->src_w * 3 >= 0x7fffffffL) return false;
+        if ((2L * g1.h + 1) * pre->src_h >= 0x7fffffffL || (2L * g1.w + 1) * pre->src_w >= 0x7fffffffL) return false;
+    }
+    PairGeom pg;
+    return pair_choose(g1, g2, pre, &pg);
+}
+
+void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, char* buf, int len)
 {
     PairGeom pg;
-    if (!pair_choose(g1, g2, &pg)) {
+    if (!pair_choose(g1, g2, pre, &pg)) {
         snprintf(buf, len, "unsupported");
         return;
     }
-    snprintf(buf, len, "stem_pair k3 s%d+s%d bn=%d tc=%d kernel=cvx::k_stem_pair<%d, %d>", g1.stride, g2.stride,
-             32 * pg.nt, pg.tc, pg.nt, g1.stride);
+    snprintf(buf, len, "stem_pair k3 s%d+s%d bn=%d tc=%d%s kernel=cvx::k_stem_pair<%d, %d, %s>", g1.stride,
+             g2.stride, 32 * pg.nt, pg.tc, pre ? " from=u8" : "", pg.nt, g1.stride, pre ? "true" : "false");
 }
 
-hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1, const float* scale1,
-                            const float* bias1, const ConvGeom& g2, const float* wp, const float* scale2,
-                            const float* bias2, const float* res, float* y, hipStream_t s)
+template <int NT, int S1>
+static void launch_pair_u8(bool u8, dim3 grid, size_t lds, hipStream_t s, const StemPairArgs& a)
+{
+    if (u8)
+        hipLaunchKernelGGL((k_stem_pair<NT, S1, true>), grid, dim3(kSPThreads), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_stem_pair<NT, S1, false>), grid, dim3(kSPThreads), lds, s, a);
+}
+
+hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const StemPrologue* pre, const float* w1,
+                            const float* scale1, const float* bias1, const ConvGeom& g2, const float* wp,
+                            const float* scale2, const float* bias2, const float* res, float* y, hipStream_t s)
 {
     PairGeom pg;
-    if (!pair_choose(g1, g2, &pg)) return hipErrorInvalidValue;
-    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return hipErrorInvalidValue;
+    if (!pair_choose(g1, g2, pre, &pg)) return hipErrorInvalidValue;
+    if (pre == nullptr && (reinterpret_cast<uintptr_t>(x) & 15u) != 0) return hipErrorInvalidValue;
+    if (pre != nullptr && ((reinterpret_cast<uintptr_t>(pre->src) & 15u) != 0 || pre->row_bytes % 16 != 0))
+        return hipErrorInvalidValue;
     StemPairArgs a;
+    memset(&a, 0, sizeof(a));
     a.x = x;
     a.w1 = w1;
     a.scale1 = scale1;
@@ -456,23 +607,44 @@ hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const float* w1,
     a.win_rounds = pg.win_rounds;
     fastdiv_params(pg.WCW / 4, &a.m_we, &a.l_we);
     fastdiv_params(pg.WR * pg.WCW / 4, &a.m_wc, &a.l_wc);
+    fastdiv_params(pg.WCW, &a.m_wcw, &a.l_wcw);
     a.x_bytes = (unsigned)((long)g1.n * g1.cin * g1.h * g1.w * 4);
     a.wp_bytes = (unsigned)(packed_weight_floats(g2) * 4);
+    if (pre != nullptr) {
+        a.src = pre->src;
+        a.src_h = pre->src_h;
+        a.src_w = pre->src_w;
+        a.row_bytes = (unsigned)pre->row_bytes;
+        a.img_bytes = (unsigned)((long)pre->src_h * pre->row_bytes);
+        fastdiv_params(2 * g1.h, &a.m_dh, &a.l_dh);
+        fastdiv_params(2 * g1.w, &a.m_dw, &a.l_dw);
+        a.inv_dh = (float)(1.0 / (2.0 * g1.h));
+        a.inv_dw = (float)(1.0 / (2.0 * g1.w));
+        for (int c = 0; c < 3; ++c) {
+            a.na[c] = (float)(1.0 / (255.0 * (double)pre->stdv[c]));
+            a.nb[c] = (float)(-(double)pre->mean[c] / (double)pre->stdv[c]);
+        }
+        a.SRB = pg.SRB;
+        a.src_elems = pg.src_elems;
+        a.src_rounds = pg.src_rounds;
+        fastdiv_params(pg.SRB / 16, &a.m_srb, &a.l_srb);
+    }
     const bool quads = pg.tc % 4 == 0 && g2.ow % 4 == 0;
     const bool al_y = (reinterpret_cast<uintptr_t>(y) & 15u) == 0;
     const bool al_r = res == nullptr || (reinterpret_cast<uintptr_t>(res) & 15u) == 0;
     a.vout = quads && al_y && al_r ? 1 : 0;
     dim3 grid((unsigned)((long)g1.n * pg.tiles_per_img * pg.nmb));
+    const bool u8 = pre != nullptr;
     if (pg.nt == 2) {
         if (g1.stride == 2)
-            hipLaunchKernelGGL((k_stem_pair<2, 2>), grid, dim3(kSPThreads), pg.lds, s, a);
+            launch_pair_u8<2, 2>(u8, grid, pg.lds, s, a);
         else
-            hipLaunchKernelGGL((k_stem_pair<2, 1>), grid, dim3(kSPThreads), pg.lds, s, a);
+            launch_pair_u8<2, 1>(u8, grid, pg.lds, s, a);
     } else {
         if (g1.stride == 2)
-            hipLaunchKernelGGL((k_stem_pair<1, 2>), grid, dim3(kSPThreads), pg.lds, s, a);
+            launch_pair_u8<1, 2>(u8, grid, pg.lds, s, a);
         else
-            hipLaunchKernelGGL((k_stem_pair<1, 1>), grid, dim3(kSPThreads), pg.lds, s, a);
+            launch_pair_u8<1, 1>(u8, grid, pg.lds, s, a);
     }
     return hipGetLastError();
 }

@@ -4,7 +4,11 @@ as one kernel by cvx_forward, the stem's output never written.  Against the
 fp64 oracle at |gpu - oracle| <= 1e-4*max(1,|oracle|), for both strides of
 each layer, ragged tiles and row blocks, several images, every tile the
 kernel takes, residual placements of the second layer, and a list input off a
-16-byte boundary (the two-kernel fallback).  The two-kernel path
+16-byte boundary (the two-kernel fallback); and with the stem prologue
+folded in (the pair resizes and normalises the u8 frame itself), at several
+resize ratios, against the oracle and beside the separate prologue
+(CVX_STEM_PAIR_U8=0), with a frame off a 16-byte boundary taking the
+separate prologue.  The two-kernel path
 (CVX_STEM_PAIR=0) is checked against the oracle beside it: the pair computes
 the stem on matrix cores, in another summation order, so the two agree to
 rounding, not bit for bit."""
@@ -102,3 +106,38 @@ def test_detector_stem_pair_in_pipeline(batch, monkeypatch):
     assert plan[1] == "merged into 2" and "k_stem_pair" in plan[2], plan
     say(f"detector b{batch} with the stem pair")
     check(got, oracle.forward(wk.layers, wk.x), f"detector b{batch} stem pair")
+
+
+# (seed, batch, src_h, src_w, dst_h, dst_w, stride 1, stride 2, c_out 2)
+U8_CASES = [(430, 1, 720, 1280, 640, 640, 2, 2, 32),   # the detector's stem: 1.125 x 2 downscale
+            (431, 2, 45, 64, 30, 40, 2, 1, 32),
+            (432, 1, 20, 16, 40, 32, 2, 2, 48),        # upscale (clamped first source row)
+            (433, 1, 100, 160, 48, 80, 1, 2, 32),      # stride-1 stem
+            (434, 3, 96, 144, 64, 80, 2, 2, 40)]
+
+
+@pytest.mark.parametrize("case", U8_CASES, ids=[f"seed{c[0]}" for c in U8_CASES])
+def test_prologue_in_stem_pair(case, monkeypatch):
+    wk = wl.prologue_stem_pair(*case)
+    ref = oracle.forward(wk.layers, wk.x)
+    got, plan = _forward(wk, monkeypatch, True)
+    say(f"prologue+stem pair {case}: {plan}")
+    assert plan[0] == "merged into 2" and plan[1] == "merged into 2" and "from=u8" in plan[2], plan
+    check(got, ref, f"prologue+stem pair {case}")
+    monkeypatch.setenv("CVX_STEM_PAIR_U8", "0")
+    apart, plan0 = _forward(wk, monkeypatch, True)
+    assert plan0[0] == "preprocess" and "from=u8" not in plan0[2], plan0
+    check(apart, ref, f"prologue apart {case}")
+
+
+def test_prologue_in_stem_pair_misaligned_frame(monkeypatch):
+    """A frame off a 16-byte boundary: the prologue runs apart (its output
+    keeps a region for that), then the pair on its output."""
+    wk = wl.prologue_stem_pair(440, 1, 48, 64, 32, 32, 2, 2, 32)
+    flat = torch.empty(wk.x.size + 4, dtype=torch.uint8, device=DEV)
+    x = flat[4:].view(wk.x.shape)
+    x.copy_(torch.from_numpy(wk.x).to(DEV))
+    assert x.data_ptr() % 16 != 0
+    got, plan = _forward(wk, monkeypatch, True, x=x)
+    assert "from=u8" in plan[2], plan
+    check(got, oracle.forward(wk.layers, wk.x), "prologue+stem pair, misaligned frame")

@@ -293,6 +293,19 @@ def prologue_stem(batch: int, src_h: int, src_w: int, dst_h: int, dst_w: int, co
     return Workload(f"prologue_{src_h}x{src_w}_{dst_h}x{dst_w}_s{stride}_b{batch}", x, L)
 
 
+def prologue_stem_pair(seed: int, n: int, src_h: int, src_w: int, dst_h: int, dst_w: int, s1: int,
+                       s2: int, cout: int) -> Workload:
+    """u8 frames [N,src_h,src_w,3] -> resize/normalise to [N,3,dst_h,dst_w] ->
+    stem 3x3 3->16 (stride s1) +BN+SiLU -> 3x3 16->cout (stride s2) +BN+SiLU."""
+    rng = np.random.default_rng(1000 + seed)
+    x = rng.integers(0, 256, (n, src_h, src_w, 3), dtype=np.uint8)
+    L: List[Layer] = [Layer(KIND_PREPROC, inp=NET_INPUT, cin=3, cout=3, name="preprocess",
+                            dst_h=dst_h, dst_w=dst_w)]
+    L.append(conv_layer(rng, 3, 16, 3, s1, 1, act=ACT_SILU, inp=0, name="stem1"))
+    L.append(conv_layer(rng, 16, cout, 3, s2, 1, act=ACT_SILU, inp=1, name="stem2"))
+    return Workload(f"prologue_pair_{seed}", x, L)
+
+
 def stem_pair_case(seed: int, n: int, cin: int, h: int, w: int, s1: int, s2: int, cout: int,
                    act1: int = ACT_SILU, act2: int = ACT_SILU, res_mode: int = RES_NONE) -> Workload:
     """A stem layer (3x3 pad 1, cin -> 16, stride s1) and the 3x3 pad-1 layer
