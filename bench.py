@@ -302,10 +302,12 @@ def per_layer(wk, net, counts, reps: int, cold: bool = True):
 def stem_pair_row(wk, counts, i, line, reps: int, cold: bool):
     """Layers i (a stem) and i+1, which the forward runs as one kernel
     (k_stem_pair), timed as that kernel: a two-layer list on an input of the
-    stem's input shape, hot (a graph of 20 forwards on the same buffers) and
-    cold (rotating sets of at least COLD_BYTES).  Algorithmic counts: both
-    layers' FLOPs; the stem's input, the second layer's output and residual and
-    both layers' weights (the 16 channels in between never leave the chip)."""
+    stem's input shape (with "from=u8", the prologue before them too, on the
+    u8 frames), hot (a graph of 20 forwards on the same buffers) and cold
+    (rotating sets of at least COLD_BYTES).  Algorithmic counts: the layers'
+    FLOPs; the first layer's input, the second layer's output and residual and
+    the weights (what the kernel passes between the layers never leaves the
+    chip)."""
     import dataclasses
     import math
     import numpy as np
@@ -313,25 +315,35 @@ def stem_pair_row(wk, counts, i, line, reps: int, cold: bool):
     import workloads as wl
     from conv2d_batchnorm_activation_amd.net import Net
     L1, L2 = wk.layers[i], wk.layers[i + 1]
-    s1 = dataclasses.replace(L1, inp=wl.NET_INPUT)
-    s2 = dataclasses.replace(L2, inp=0)
-    net = Net([s1, s2], _layer_input_shape(wk, i))
-    shape = net.input_shape
-    c1, c2 = counts[i], counts[i + 1]
-    flop = c1["flop"] + c2["flop"]
+    u8 = "from=u8" in line
+    if u8:
+        first = i - 1
+        sub = [dataclasses.replace(wk.layers[first], inp=wl.NET_INPUT), dataclasses.replace(L1, inp=0),
+               dataclasses.replace(L2, inp=1)]
+        shape = tuple(wk.x.shape)
+        in_b = float(np.prod(shape))  # u8 frames
+    else:
+        first = i
+        sub = [dataclasses.replace(L1, inp=wl.NET_INPUT), dataclasses.replace(L2, inp=0)]
+        shape = _layer_input_shape(wk, i)
+        in_b = 4.0 * float(np.prod(shape))
+    net = Net(sub, shape)
+    flop = sum(counts[j]["flop"] for j in range(first, i + 2))
     out_b = 4.0 * float(np.prod(net.out_shape))
-    byts = 4.0 * float(np.prod(shape)) + out_b * (2 if L2.res_mode else 1) + \
+    byts = in_b + out_b * (2 if L2.res_mode else 1) + \
         4.0 * (L1.params["w"].size + L2.params["w"].size + 2 * L1.cout + 2 * L2.cout)
-    x = torch.rand(shape, device="cuda")
+    rand_in = (lambda: torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda")) if u8 else \
+        (lambda: torch.rand(shape, device="cuda"))
+    x = rand_in()
     fn = lambda: net(x)
     inner = 20
     us = time_graph(capture(fn, inner), inner, max(1, reps // inner)) * 1e3
     us_cold = None
     sets = 0
     if cold:
-        set_bytes = 4 * int(np.prod(shape)) + int(out_b) + net.ws_bytes
+        set_bytes = int(in_b) + int(out_b) + net.ws_bytes
         sets = int(min(MAX_COLD_SETS, max(2, math.ceil(COLD_BYTES / set_bytes))))
-        bufs = [(torch.rand(shape, device="cuda"), torch.empty(net.out_shape, device="cuda"),
+        bufs = [(rand_in(), torch.empty(net.out_shape, device="cuda"),
                  torch.empty(max(net.ws_bytes, 256), dtype=torch.uint8, device="cuda")) for _ in range(sets)]
         from conv2d_batchnorm_activation_amd import cvx
         fns = [lambda b=b: cvx.cvx_forward(net.arr, b[0], b[1], b[2], net.ws_bytes) for b in bufs]
@@ -344,9 +356,10 @@ def stem_pair_row(wk, counts, i, line, reps: int, cold: bool):
     gbs_cold = byts / (us_cold * 1e-6) / 1e9 if us_cold else None
     frac = gflops / (MFMA_F32_PEAK_TFLOPS * 1e3) if bound == "mfma" else (gbs_cold or byts / (us * 1e-6) / 1e9) / HBM_PEAK_GBS
     kernel = line.split("kernel=")[1].split()[0] if "kernel=" in line else line
-    log(f"  {L1.name + '+' + L2.name:16s} {us:8.2f} us hot" + (f" cold {us_cold:7.2f} us" if us_cold else "") +
+    name = "+".join(wk.layers[j].name for j in range(first, i + 2))
+    log(f"  {name:16s} {us:8.2f} us hot" + (f" cold {us_cold:7.2f} us" if us_cold else "") +
         f"  {gflops:9.1f} GFLOP/s  {bound} frac {frac:.3f}  [{line}]")
-    return {"layer": f"{L1.name}+{L2.name}", "plan": line, "kernel": kernel, "splitk": 1,
+    return {"layer": name, "plan": line, "kernel": kernel, "splitk": 1,
             "us": round(us, 3), "us_cold": round(us_cold, 3) if us_cold else None, "cold_sets": sets,
             "gflop": flop / 1e9, "mbytes": byts / 1e6, "ai": round(ai, 2), "gflops": round(gflops, 1),
             "gbs_hot": round(byts / (us * 1e-6) / 1e9, 1), "gbs_cold": round(gbs_cold, 1) if gbs_cold else None,
@@ -1172,11 +1185,12 @@ def main() -> int:
         reruns.append(round(t / args.steps * 1e3, 3))
     # graph: the forward captured once, replayed once per step
     ms = forward_time_ms(net, x, args.steps)
+    ms10 = forward_time_ms(net, x, args.steps, per_graph=10)
     cold = cold_forward_us(net, wk, args.steps)
     log(f"forward: {ms_eager * 1e3:.1f} us/forward ({args.steps} cvx_forward calls; p50 "
         f"{spread['p50_us']} p99 {spread['p99_us']} cv {spread['cv']}; reruns {reruns}), "
-        f"{ms * 1e3:.1f} us as a graph replay per forward, cold {cold['mean_us']} us "
-        f"(wall {wall:.3f} s)")
+        f"{ms * 1e3:.1f} us as a graph replay per forward, {ms10 * 1e3:.1f} us per forward in graphs "
+        f"of ten, cold {cold['mean_us']} us (wall {wall:.3f} s)")
 
     rows = [] if args.no_layers else per_layer(wk, net, counts, args.layer_reps)
     roof = dominant(rows) if rows else None
@@ -1191,6 +1205,7 @@ def main() -> int:
         "ms_per_step": round(ms_eager, 5),
         "ms_per_forward": round(ms_eager, 5),
         "ms_per_forward_graph": round(ms, 5),
+        "ms_per_forward_graph10": round(ms10, 5),
         "forward_spread": spread,
         "forward_reruns_us": reruns,
         "forward_cold": cold,
@@ -1199,7 +1214,9 @@ def main() -> int:
                   "with an event after each forward for the spread (forward_spread: mean, p50, "
                   "p99, cv of the per-forward times); forward_reruns_us repeats the timed region "
                   "twice more; ms_per_forward_graph replays a HIP graph of one forward per step, "
-                  "whose launch boundary adds about 5 us; forward_cold rotates frame, workspace "
+                  "whose launch boundary adds about 5 us (ms_per_forward_graph10: graphs of ten "
+                  "forwards, which also removes most of the gaps between kernels); forward_cold "
+                  "rotates frame, workspace "
                   "and output over sets totalling >= 512 MB. Per-layer `us` from graphs of 20 "
                   "back-to-back launches on the same buffers (cache-resident: hot), `us_cold` "
                   "over rotating buffer sets of >= 512 MB; HBM fractions use the cold time; "
