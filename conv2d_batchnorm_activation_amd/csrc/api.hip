@@ -656,6 +656,16 @@ cvx_status cvx_preprocess_u8(const unsigned char* src, int n, int src_h, int src
     return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;
 }
 
+cvx_status cvx_workgroup_xcds(int* xcd, int n_workgroups, void* stream)
+{
+    if (!xcd) return CVX_ERR_NULL;
+    if (n_workgroups < 1 || n_workgroups > (1 << 20)) return CVX_ERR_SHAPE;
+    if (!aligned4(xcd)) return CVX_ERR_ALIGN;
+    return launch_workgroup_xcds(xcd, n_workgroups, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CVX_OK
+               : CVX_ERR_HIP;
+}
+
 cvx_status cvx_gap_fc(const float* x, int n, int c, int h, int w, const float* fc_w,
                       const float* fc_b, int out_f, float* out, void* stream)
 {

@@ -157,6 +157,8 @@ void packed_stage_geometry(const ConvGeom& g, int kind, int tc, bool vec, Packed
 // Persistent form: `wgs` workgroups (a multiple of 8, at most the tile count)
 // each running several tiles; no split, 16-byte staging, two or more stages.
 bool packed_persist_fits(const ConvGeom& g, int kind, int tc, int wgs);
+bool packed_split_xcd(hipStream_t s);
+hipError_t launch_workgroup_xcds(int* xcd, int n, hipStream_t s);
 // workgroups of the persistent form that fit the device at once
 int packed_persist_capacity(const ConvGeom& g, int kind, int tc);
 long packed_num_tiles(const ConvGeom& g, int kind, int tc);

@@ -58,6 +58,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <type_traits>
 
 #include "bufio.h"
@@ -118,9 +119,10 @@ struct PackedArgs {
     unsigned m_nb, l_nb, m_sp, l_sp, m_tpi, l_tpi;  // divide by n*tiles, splits, tiles per image
     int tr;                     // output rows of a 2-D tile (BN / tc)
     int spatial;                // workgroup order: pixel tiles slowest (else row blocks slowest)
-    int nms;                    // row blocks x splits
+    int nms;                    // row blocks x splits (row blocks alone when xsplit)
     unsigned m_ms, l_ms;        // divide by nms
-    int nv;                     // persistent form: tiles x row blocks (the workgroups it stands for)
+    int nv;                     // tiles x row blocks (the persistent form: the workgroups it stands for)
+    int xsplit;                 // the slices of a tile run on one XCD and meet in its L2
     unsigned wp_bytes;
     int vout;                   // 16-byte epilogue accesses
     int act, res_mode;
@@ -158,7 +160,17 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     {
         const unsigned h = blockIdx.x, G8 = gridDim.x;
         const unsigned xcd = h & 7u, i8 = h >> 3, base = G8 >> 3, rem = G8 & 7u;
-        const int L = (int)(xcd * base + min(xcd, rem) + i8);
+        int L = (int)(xcd * base + min(xcd, rem) + i8);
+        // XCD-local slices: the grid is a multiple of 8 x splits, so each XCD's
+        // range of L holds whole groups of `splits` consecutive values, one
+        // group per tile; the last groups are padding
+        int sl = 0;
+        if (a.xsplit) {
+            if (L >= a.nv * a.splits) return;
+            const int u = pdiv(L, a.m_sp, a.l_sp);
+            sl = L - u * a.splits;
+            L = u;
+        }
         int ms, bt;
         if (a.spatial) {
             bt = pdiv(L, a.m_ms, a.l_ms);
@@ -167,8 +179,13 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
             ms = pdiv(L, a.m_nb, a.l_nb);
             bt = L - ms * (a.n * a.tiles_per_img);
         }
-        mb = pdiv(ms, a.m_sp, a.l_sp);
-        sp = ms - mb * a.splits;
+        if (a.xsplit) {
+            mb = ms;
+            sp = sl;
+        } else {
+            mb = pdiv(ms, a.m_sp, a.l_sp);
+            sp = ms - mb * a.splits;
+        }
         b = pdiv(bt, a.m_tpi, a.l_tpi);
         tile = bt - b * a.tiles_per_img;
     }
@@ -413,36 +430,25 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         }
         return ok && row_ok ? (unsigned)(b * a.cout + eco) * plane_b + 4u * (unsigned)q : kOOB;
     };
-    // `dev` marks accesses coherent across the whole device (the sc1 cache
-    // policy): they bypass an XCD's own L2, so a partial sum written on one XCD is
-    // read correctly on another.
-    auto load_quad = [&](const rsrc_t& r, int k, bool dev = false) {
+    auto load_quad = [&](const rsrc_t& r, int k) {
         f32x4 v;
         if (a.vout) {
-            v = __builtin_bit_cast(f32x4, dev ? __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(k, 0), 0, kSC1)
-                                              : __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(k, 0), 0, 0));
+            v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)at(k, 0), 0, 0));
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = __builtin_bit_cast(float, dev ? __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(k, e), 0, kSC1)
-                                                     : __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(k, e), 0, 0));
+                v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)at(k, e), 0, 0));
         }
         return v;
     };
-    auto store_quad = [&](const rsrc_t& r, int k, f32x4 v, bool dev = false) {
+    auto store_quad = [&](const rsrc_t& r, int k, f32x4 v) {
         if (a.vout) {
-            if (dev)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)at(k, 0), 0, kSC1);
-            else
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)at(k, 0), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)at(k, 0), 0, 0);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float f = v[e];  // a scalar copy: bit_cast of a vector element takes element 0
-                if (dev)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, (int)at(k, e), 0, kSC1);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, (int)at(k, e), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, f), r, (int)at(k, e), 0, 0);
             }
         }
     };
@@ -513,18 +519,32 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 
     if (!single) {
         // Split reduction: publish this slice's sums, count arrivals at the tile's
-        // counter, and let the last arrival finish the tile.  The sums are stored
-        // and read with device-coherent accesses, and every wave waits for its
-        // stores to complete before the workgroup's arrival is counted, so the
-        // last arrival reads every slice.  Counters carry the launch's epoch in
-        // their upper bits, so whatever a counter held before (another launch's
-        // value, or anything at all in a fresh workspace) reads as zero arrivals;
-        // the last arrival resets it to 0.
-        const unsigned part_b = out_bytes;
+        // counter, and let the last arrival finish the tile.  Every wave waits for
+        // its stores to complete before the workgroup's arrival is counted, so
+        // the last arrival reads every slice.  Each tile owns a region of whole
+        // cache lines, [slice][32 rows][BN pixels]: no workgroup ever reads a
+        // line holding another tile's sums, so no compute unit's own cache can
+        // hold a stale copy of one.  With `xsplit` all slices of the tile run
+        // on one XCD and the sums meet in its L2 (plain stores and loads);
+        // otherwise they are stored and read with device-coherent accesses.  Counters carry the launch's epoch in their
+        // upper bits, so whatever a counter held before (another launch's
+        // value, or anything at all in a fresh workspace) reads as zero
+        // arrivals; the last arrival resets it to 0.
+        constexpr int SF = 32 * BN;  // floats of one slice of a tile
+        const long tix = (long)(mb * a.n + b) * a.tiles_per_img + tile;
+        float* const tp = a.partial + tix * a.splits * SF;
+        const int pofs = 4 * (erow * BN + 4 * (lane & 7));  // + 128 bytes per quad k
+        const bool dev = !a.xsplit;
         {
-            const rsrc_t rps = make_rsrc(a.partial + (long)sp * (part_b / 4), part_b);
+            const rsrc_t rps = make_rsrc(tp + (long)sp * SF, 4u * SF);
 #pragma unroll
-            for (int k = 0; k < NT; ++k) store_quad(rps, k, v[k], true);
+            for (int k = 0; k < NT; ++k) {
+                const u32x4 q = __builtin_bit_cast(u32x4, v[k]);
+                if (dev)
+                    __builtin_amdgcn_raw_buffer_store_b128(q, rps, pofs + 128 * k, 0, kSC1);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(q, rps, pofs + 128 * k, 0, 0);
+            }
         }
         // whichever workgroup finishes the tile needs these (and the residual,
         // already here): fetched by all, while the stores drain
@@ -536,7 +556,7 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            unsigned long long* c = a.ctr + ((long)(mb * a.n + b) * a.tiles_per_img + tile);
+            unsigned long long* c = a.ctr + tix;
             // a counter left by a finished launch reads 0, so the first attempt
             // assumes that and skips a round trip; anything else (an arrival of
             // this launch, or a stale value) comes back in `cur` for the retry
@@ -559,9 +579,18 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
 #pragma unroll
         for (int k = 0; k < NT; ++k) tot[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int s = 0; s < a.splits; ++s) {
-            const rsrc_t rps = make_rsrc(a.partial + (long)s * (part_b / 4), part_b);
+            const rsrc_t rps = make_rsrc(tp + (long)s * SF, 4u * SF);
 #pragma unroll
-            for (int k = 0; k < NT; ++k) tot[k] += s == sp ? v[k] : load_quad(rps, k, true);
+            for (int k = 0; k < NT; ++k) {
+                f32x4 q;
+                if (s == sp)
+                    q = v[k];
+                else if (dev)
+                    q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rps, pofs + 128 * k, 0, kSC1));
+                else
+                    q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rps, pofs + 128 * k, 0, 0));
+                tot[k] += q;
+            }
         }
 #pragma unroll
         for (int k = 0; k < NT; ++k) v[k] = tot[k];
@@ -1199,16 +1228,18 @@ bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
 }
 
 // Split-K partial sums, then one 8-byte arrival counter per output tile.
-static size_t packed_partial_bytes(const ConvGeom& g, int splits)
+// Split partial sums: one region per tile, [slice][32 rows][tile pixels].
+static size_t packed_partial_bytes(const ConvGeom& g, int kind, int tc, int splits)
 {
-    return ((size_t)splits * g.n * g.cout * g.oh * g.ow * sizeof(float) + 255) & ~(size_t)255;
+    const size_t tiles = (size_t)g.n * packed_tiles_per_image(g, kind, tc) * ((g.cout + 31) / 32);
+    return (tiles * splits * 32 * packed_tile_n(kind) * sizeof(float) + 255) & ~(size_t)255;
 }
 
 size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
 {
     if (splits <= 1) return 0;
     const size_t tiles = (size_t)g.n * packed_tiles_per_image(g, kind, tc) * ((g.cout + 31) / 32);
-    return packed_partial_bytes(g, splits) + tiles * sizeof(unsigned long long);
+    return packed_partial_bytes(g, kind, tc, splits) + tiles * sizeof(unsigned long long);
 }
 
 // Workgroups per compute unit the compiled kernels allow: each puts two waves
@@ -1312,6 +1343,64 @@ static void launch_packed_k(int kind, bool vec, bool persist, dim3 grid, size_t 
 
 static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Placement report: the XCD each workgroup ran on (the XCC_ID hardware
+// register, bits 0..3).
+__global__ void __launch_bounds__(64) k_workgroup_xcds(int* __restrict__ xcd, int n)
+{
+    const int id = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
+    if (threadIdx.x == 0 && (int)blockIdx.x < n) xcd[blockIdx.x] = id;
+}
+
+hipError_t launch_workgroup_xcds(int* xcd, int n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_workgroup_xcds, dim3((unsigned)n), dim3(64), 0, s, xcd, n);
+    return hipGetLastError();
+}
+
+// Whether the slices of a split tile run on one XCD and reduce through its L2.
+// The device deals consecutive workgroups to its XCDs in turn (workgroup i to
+// XCD i mod 8, or mod a divisor of 8 on a partition with fewer XCDs), so a
+// launch whose workgroups are numbered as the kernel numbers them puts a
+// tile's slices on one XCD and one L2.  The first split launch on a device
+// checks this once: 2048 workgroups report their XCD, and every workgroup must
+// share it with the workgroup whose index agrees modulo 8.  Until the check
+// has run (it needs a synchronisation, so it is skipped while the stream is
+// being captured into a graph), and wherever it fails, the reduction goes
+// through device-coherent memory.  CVX_SPLIT_XCD=0 selects that path always.
+__device__ int g_placement[2048];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_split_xcd[kMaxDevices];  // 0 not checked, 1 holds, 2 does not
+std::mutex g_split_mu;
+}  // namespace
+
+bool packed_split_xcd(hipStream_t s)
+{
+    const char* e = getenv("CVX_SPLIT_XCD");
+    if (e && e[0] == '0') return false;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    const int st = g_split_xcd[dev].load();
+    if (st != 0) return st == 1;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    std::lock_guard<std::mutex> lock(g_split_mu);
+    if (g_split_xcd[dev].load() != 0) return g_split_xcd[dev].load() == 1;
+    constexpr int n = 2048;
+    void* dptr = nullptr;
+    static int host[n];
+    if (hipGetSymbolAddress(&dptr, HIP_SYMBOL(g_placement)) != hipSuccess || dptr == nullptr) return false;
+    if (launch_workgroup_xcds(static_cast<int*>(dptr), n, s) != hipSuccess) return false;
+    if (hipMemcpyAsync(host, dptr, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return false;
+    bool ok = true;
+    for (int i = 8; i < n; ++i) ok = ok && host[i] == host[i & 7];
+    g_split_xcd[dev].store(ok ? 1 : 2);
+    return ok;
+}
+
 // Workgroup order of a layer: the one whose estimated fetches into the eight
 // XCDs' L2 caches are smaller.  Row blocks slowest: each row block's tiles fill
 // about 8/nmb XCDs, so every XCD group reads the whole input and its row
@@ -1385,9 +1474,10 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     }
     fastdiv_params(g.n * a.tiles_per_img, &a.m_nb, &a.l_nb);
     fastdiv_params(splits, &a.m_sp, &a.l_sp);
+    a.xsplit = splits > 1 && packed_split_xcd(s) ? 1 : 0;
     {
         const int nmb = (g.cout + 31) / 32;
-        a.nms = nmb * splits;
+        a.nms = a.xsplit ? nmb : nmb * splits;
         fastdiv_params(a.nms, &a.m_ms, &a.l_ms);
         a.spatial = packed_spatial_order(g, nmb) ? 1 : 0;
     }
@@ -1399,7 +1489,7 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     if (splits > 1) {
         a.partial = static_cast<float*>(ws);
         a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
-                                                      packed_partial_bytes(g, splits));
+                                                      packed_partial_bytes(g, kind, tc, splits));
         a.epoch = packed_next_epoch();
     } else {
         a.partial = nullptr;
@@ -1411,7 +1501,9 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     a.vout = quads && al16(y) && (res == nullptr || al16(res)) && (ws == nullptr || al16(ws)) ? 1 : 0;
     const long tiles = (long)g.n * a.tiles_per_img * ((g.cout + 31) / 32);
     a.nv = (int)tiles;
-    dim3 grid((unsigned)(persist ? (long)p.tile.persist : tiles * splits));
+    // XCD-local slices: a multiple of 8 x splits workgroups (the rest exit at once)
+    const long wgs = a.xsplit ? (tiles * splits + 8L * splits - 1) / (8L * splits) * (8L * splits) : tiles * splits;
+    dim3 grid((unsigned)(persist ? (long)p.tile.persist : wgs));
     if (g.k == 1)
         launch_packed_k<1>(kind, vec, persist, grid, lds, s, a);
     else

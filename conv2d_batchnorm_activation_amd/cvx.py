@@ -98,13 +98,16 @@ lib.cvx_static_scratch_bytes.argtypes = []
 lib.cvx_static_scratch_bytes.restype = _Z
 lib.cvx_forward_noalloc.argtypes = [_LP, _I, _P, _P, _P]
 lib.cvx_forward_noalloc.restype = _I
+lib.cvx_workgroup_xcds.argtypes = [_P, _I, _P]
+lib.cvx_workgroup_xcds.restype = _I
 
 #: every entry point include/cvx.h declares
 EXPORTS = ("cvx_status_str", "cvx_version", "cvx_conv_out_shape", "cvx_conv_plan",
            "cvx_conv_workspace_bytes", "cvx_packed_weights_bytes", "cvx_pack_weights", "cvx_fold_bn", "cvx_conv_bn_act", "cvx_preprocess_u8",
            "cvx_gap_fc", "cvx_forward_out_shape", "cvx_forward_workspace_bytes", "cvx_forward_plan",
            "cvx_forward", "cvx_nhwc_packed_weights_bytes", "cvx_nhwc_plan", "cvx_nhwc_pack_weights",
-           "cvx_conv_bn_act_nhwc", "cvx_static_scratch_bytes", "cvx_forward_noalloc")
+           "cvx_conv_bn_act_nhwc", "cvx_static_scratch_bytes", "cvx_forward_noalloc",
+           "cvx_workgroup_xcds")
 
 
 class CvxError(RuntimeError):
@@ -245,6 +248,11 @@ def cvx_forward(layers, inp, out, workspace, ws_bytes: Optional[int] = None, str
             workspace.numel() * workspace.element_size()
     _check(lib.cvx_forward(arr, n, _ptr(inp), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "cvx_forward")
+
+
+def cvx_workgroup_xcds(out, stream=None) -> None:
+    """XCD index of each of out.numel() workgroups of one launch (int32 device tensor)."""
+    _check(lib.cvx_workgroup_xcds(_ptr(out), out.numel(), _stream(stream)), "cvx_workgroup_xcds")
 
 
 def cvx_static_scratch_bytes() -> int:

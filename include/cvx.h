@@ -320,6 +320,22 @@ CVX_API cvx_status cvx_conv_bn_act_nhwc(const cvx_conv_desc *d, int dtype, const
                                         const void *w_packed, const float *scale, const float *bias,
                                         const void *residual, void *y, void *stream);
 
+/* ------------------------------------------------------ placement report */
+/*
+ * cvx_workgroup_xcds -- where a launch's workgroups run.  Launches n_workgroups
+ * workgroups of 64 threads on `stream`; workgroup i writes to xcd[i] the index
+ * of the XCD (the die, with its own L2 cache) that ran it.  A diagnostic, not a
+ * step of the operation: the split reduction of the implicit-GEMM kernel puts
+ * the slices of a tile on workgroups whose indices agree modulo 8, and relies on
+ * such workgroups sharing an XCD; this call lets a caller confirm that on its
+ * device.  Asynchronous.
+ *   xcd: device, n_workgroups ints, 4-byte aligned, written.
+ *   n_workgroups: 1 .. 1048576.
+ * Errors: CVX_ERR_NULL, CVX_ERR_SHAPE (count out of range), CVX_ERR_ALIGN,
+ * CVX_ERR_HIP (launch failed).
+ */
+CVX_API cvx_status cvx_workgroup_xcds(int *xcd, int n_workgroups, void *stream);
+
 /* ------------------------------------------------- allocation-free variant */
 /* Size of the static device scratch array cvx_forward_noalloc uses (32 MiB),
  * held by each GPU the library runs on until the process ends. */

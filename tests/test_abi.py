@@ -173,6 +173,14 @@ def test_gap_fc_validation():
     assert f(X, 1, 192, 7, 7, W, B, 10, X + 8, None) == -5
 
 
+def test_workgroup_xcds_validation():
+    f = cvx.lib.cvx_workgroup_xcds
+    assert f(None, 8, None) == -1
+    assert f(Y, 0, None) == -2
+    assert f(Y, (1 << 20) + 1, None) == -2
+    assert f(Y + 2, 8, None) == -4
+
+
 def _net_layers(wk, w_layout=cvx.CVX_W_OIHW):
     """cvx_layer array for a workload, with fake parameter pointers (planning only)."""
     shapes = []
