@@ -526,10 +526,11 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         // line holding another tile's sums, so no compute unit's own cache can
         // hold a stale copy of one.  With `xsplit` all slices of the tile run
         // on one XCD and the sums meet in its L2 (plain stores and loads);
-        // otherwise they are stored and read with device-coherent accesses.  Counters carry the launch's epoch in their
-        // upper bits, so whatever a counter held before (another launch's
-        // value, or anything at all in a fresh workspace) reads as zero
-        // arrivals; the last arrival resets it to 0.
+        // otherwise they are stored and read with device-coherent accesses.
+        // Counters carry the launch's epoch in their upper bits, so whatever a
+        // counter held before (another launch's value, or anything at all in a
+        // fresh workspace) reads as zero arrivals; the last arrival resets it
+        // to 0.
         constexpr int SF = 32 * BN;  // floats of one slice of a tile
         const long tix = (long)(mb * a.n + b) * a.tiles_per_img + tile;
         float* const tp = a.partial + tix * a.splits * SF;
