@@ -171,9 +171,11 @@ constexpr TileEntry kTileTable[] = {
     {1, 16, 320, 320, 32, 3, 2, 1, 1, 32, 1},   // stem2  7.55 -> 7.20 us
     {1, 64, 80, 80, 128, 3, 2, 1, 0, 16, 1},    // b      6.21 -> 6.07
     {1, 128, 40, 40, 128, 3, 1, 1, 0, 8, 1},    // d      8.66 -> 8.35
+    {1, 128, 40, 40, 256, 3, 2, 1, 0, 8, 2},    // e      8.40 -> 7.76 (slices meeting in one XCD's L2)
     {1, 256, 20, 20, 256, 3, 1, 1, 0, 0, 2},    // g     10.79 -> 10.39
     // batch 8
     {8, 16, 320, 320, 32, 3, 2, 1, 1, 32, 1},   // stem2 42.58 -> 39.77
+    {8, 32, 160, 160, 64, 3, 2, 1, 0, 16, 1},   // bridge 30.87 -> 29.99
     {8, 64, 80, 80, 128, 3, 2, 1, 0, 8, 1},     // b     27.98 -> 27.04
     {8, 128, 40, 40, 128, 1, 1, 0, 1, 16, 1},   // c     14.23 -> 12.23
     {8, 128, 40, 40, 128, 3, 1, 1, 0, 0, 1},    // d     45.76 -> 42.18
