@@ -821,20 +821,39 @@ def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
     print()
     print("Per layer of the bench's layer timing (the launches between two markers):")
     print()
-    print("| layer | kernel | launches | trace avg us | bench us (graph of 20) |")
-    print("|---|---|---|---|---|")
+    # a layer's launches in order: warm-up and `reps` eager calls, then the
+    # graph replays on the same buffers (hot, what `us` times), then the cold sets
+    reps = int(res.get("layer_reps", 200))
+    # the bench's own hot figure, from the untraced run when there is one (the
+    # traced run's event times carry the tracer's per-launch cost)
+    ref_us = {}
+    if ref_json:
+        with open(ref_json) as fh:
+            ref0 = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+        ref_us = {r["layer"]: r["us"] for r in ref0.get("layers", [])}
+    hot0 = 3 + reps
+    hot1 = hot0 + 20 * (2 + max(1, reps // 20))
+    col = "untraced bench us (graph of 20, hot)" if ref_us else "bench us (graph of 20, hot)"
+    print(f"| layer | kernel (the segment's most frequent) | launches | trace avg us, all | trace avg us, hot graph launches | {col} |")
+    print("|---|---|---|---|---|---|")
     avg = {}
     for L, sg in zip(layers, segs):
-        d = [t for _, t in sg]
-        avg[L["layer"]] = sum(d) / len(d) / 1e3
-        print(f"| {L['layer']} | `{sg[0][0]}` | {len(d)} | {avg[L['layer']]:.2f} | {L['us']:.2f} |")
+        counts = {}
+        for n, _ in sg:
+            counts[n] = counts.get(n, 0) + 1
+        k = max(counts, key=counts.get)
+        d = [t for n, t in sg if n == k]
+        hot = d[hot0:hot1] if len(d) >= hot1 else d
+        avg[L["layer"]] = sum(hot) / len(hot) / 1e3
+        print(f"| {L['layer']} | `{k}` | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {avg[L['layer']]:.2f} | "
+              f"{ref_us.get(L['layer'], L['us']):.2f} |")
     roof = res.get("roofline") or {}
     use = roof.get("measured_layers") or []
     if use and all(u in avg for u in use):
         t = sum(avg[u] for u in use) / len(use)
         print()
-        print(f"Dominant kernel `{roof.get('kernel')}` over {', '.join(use)}: trace average "
-              f"{t:.2f} us per launch (kernel start to end); the traced run's own `avg_launch_us` "
+        print(f"Dominant kernel `{roof.get('kernel')}` over {', '.join(use)}: trace average over the hot "
+              f"graph launches {t:.2f} us per launch (kernel start to end); the traced run's own `avg_launch_us` "
               f"{roof.get('avg_launch_us')} us (its event times carry the tracer's per-launch cost).")
         if ref_json:
             with open(ref_json) as fh:
@@ -1209,6 +1228,7 @@ def main() -> int:
         "forward_spread": spread,
         "forward_reruns_us": reruns,
         "forward_cold": cold,
+        "layer_reps": args.layer_reps,
         "gpu_clocks": {"start": clocks_start, "end": None},
         "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events, "
                   "with an event after each forward for the spread (forward_spread: mean, p50, "
