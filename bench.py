@@ -1031,13 +1031,13 @@ def other_workloads(layer_reps: int, steps: int):
     return out
 
 
-F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 and bf16 matrix (the same rate)
 
 
 def layout_comparison(reps: int):
     """The detector's dense layers a..g alone at batch 1 and 8, each as the NCHW
     fp32 layer (packed weights, the production path), the NHWC fp32 layer and
-    the NHWC fp16 layer (fp32 accumulation), timed like the per-layer rows
+    the NHWC fp16 and bf16 layers (fp32 accumulation), timed like the per-layer rows
     (graphs of 20 launches on the same buffers, hot).  The NHWC variants'
     inputs are synthetic tensors of the same shapes (timing does not depend on
     the values)."""
@@ -1074,8 +1074,9 @@ def layout_comparison(reps: int):
             ms = time_graph(capture(fn, 20), 20, max(1, reps // 20))
             row["nchw_f32_us"] = round(ms * 1e3, 3)
             row["nchw_plan"] = cvx.cvx_conv_plan(d).split(" kernel")[0]
-            for dt, tag in ((cvx.CVX_DT_F32, "nhwc_f32"), (cvx.CVX_DT_F16, "nhwc_f16")):
-                tdt = torch.float32 if dt == cvx.CVX_DT_F32 else torch.float16
+            for dt, tag, tdt in ((cvx.CVX_DT_F32, "nhwc_f32", torch.float32),
+                                 (cvx.CVX_DT_F16, "nhwc_f16", torch.float16),
+                                 (cvx.CVX_DT_BF16, "nhwc_bf16", torch.bfloat16)):
                 wq = torch.empty(cvx.cvx_nhwc_packed_weights_bytes(d, dt), dtype=torch.uint8, device=dev)
                 cvx.cvx_nhwc_pack_weights(d, dt, wt, wq)
                 xq = torch.rand((n, h, w, c), device=dev).to(tdt)
@@ -1090,8 +1091,10 @@ def layout_comparison(reps: int):
             row["nchw_f32_frac_mfma"] = round(f / (row["nchw_f32_us"] * 1e-6) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4)
             row["nhwc_f32_frac_mfma"] = round(f / (row["nhwc_f32_us"] * 1e-6) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4)
             row["nhwc_f16_frac_mfma_f16"] = round(f / (row["nhwc_f16_us"] * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)
+            row["nhwc_bf16_frac_mfma_bf16"] = round(f / (row["nhwc_bf16_us"] * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS,
+                                                    4)
             log(f"  b={batch} {name:16s} NCHW f32 {row['nchw_f32_us']:7.2f} us  NHWC f32 {row['nhwc_f32_us']:7.2f} us  "
-                f"NHWC f16 {row['nhwc_f16_us']:7.2f} us")
+                f"NHWC f16 {row['nhwc_f16_us']:7.2f} us  NHWC bf16 {row['nhwc_bf16_us']:7.2f} us")
             out.append(row)
     return out
 

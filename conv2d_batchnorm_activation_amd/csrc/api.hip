@@ -1241,19 +1241,22 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
 }  // extern "C"
 
 // ============================================================ channels-last
+static bool nhwc_dtype_known(int dt) { return dt == CVX_DT_F32 || dt == CVX_DT_F16 || dt == CVX_DT_BF16; }
+static size_t nhwc_dtype_bytes(int dt) { return dt == CVX_DT_F32 ? 4 : 2; }
+
 extern "C" {
 
 size_t cvx_nhwc_packed_weights_bytes(const cvx_conv_desc* d, int dtype)
 {
     ConvGeom g;
     if (geom_from_desc(d, &g) != CVX_OK || !nhwc_supported(g, dtype)) return 0;
-    return (size_t)nhwc_packed_weight_elems(g, dtype) * (dtype == CVX_DT_F16 ? 2 : 4);
+    return (size_t)nhwc_packed_weight_elems(g, dtype) * nhwc_dtype_bytes(dtype);
 }
 
 cvx_status cvx_nhwc_plan(const cvx_conv_desc* d, int dtype, char* buf, int buf_len)
 {
     if (buf == nullptr || buf_len < 1) return CVX_ERR_NULL;
-    if (dtype != CVX_DT_F32 && dtype != CVX_DT_F16) return CVX_ERR_ARG;
+    if (!nhwc_dtype_known(dtype)) return CVX_ERR_ARG;
     ConvGeom g;
     cvx_status st = geom_from_desc(d, &g);
     if (st != CVX_OK) return st;
@@ -1265,14 +1268,14 @@ cvx_status cvx_nhwc_plan(const cvx_conv_desc* d, int dtype, char* buf, int buf_l
 cvx_status cvx_nhwc_pack_weights(const cvx_conv_desc* d, int dtype, const float* w_oihw, void* w_packed,
                                  void* stream)
 {
-    if (dtype != CVX_DT_F32 && dtype != CVX_DT_F16) return CVX_ERR_ARG;
+    if (!nhwc_dtype_known(dtype)) return CVX_ERR_ARG;
     ConvGeom g;
     cvx_status st = geom_from_desc(d, &g);
     if (st != CVX_OK) return st;
     if (!w_oihw || !w_packed) return CVX_ERR_NULL;
     if (!nhwc_supported(g, dtype)) return CVX_ERR_UNSUPPORTED;
     if (!aligned4(w_oihw) || (reinterpret_cast<uintptr_t>(w_packed) & 15u) != 0) return CVX_ERR_ALIGN;
-    const size_t nb = (size_t)nhwc_packed_weight_elems(g, dtype) * (dtype == CVX_DT_F16 ? 2 : 4);
+    const size_t nb = (size_t)nhwc_packed_weight_elems(g, dtype) * nhwc_dtype_bytes(dtype);
     if (overlap(span(w_packed, nb), span(w_oihw, elems_oihw(g) * sizeof(float)))) return CVX_ERR_ALIAS;
     return launch_pack_nhwc(g, dtype, w_oihw, w_packed, static_cast<hipStream_t>(stream)) == hipSuccess
                ? CVX_OK
@@ -1282,7 +1285,7 @@ cvx_status cvx_nhwc_pack_weights(const cvx_conv_desc* d, int dtype, const float*
 cvx_status cvx_conv_bn_act_nhwc(const cvx_conv_desc* d, int dtype, const void* x, const void* w_packed,
                                 const float* scale, const float* bias, const void* residual, void* y, void* stream)
 {
-    if (dtype != CVX_DT_F32 && dtype != CVX_DT_F16) return CVX_ERR_ARG;
+    if (!nhwc_dtype_known(dtype)) return CVX_ERR_ARG;
     ConvGeom g;
     cvx_status st = geom_from_desc(d, &g);
     if (st != CVX_OK) return st;
@@ -1296,7 +1299,7 @@ cvx_status cvx_conv_bn_act_nhwc(const cvx_conv_desc* d, int dtype, const void* x
     if (!aligned4(scale) || !aligned4(bias)) return CVX_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(scale) & 15u) != 0 || (reinterpret_cast<uintptr_t>(bias) & 15u) != 0)
         return CVX_ERR_ALIGN;  // read four channels at a time
-    const size_t sz = dtype == CVX_DT_F16 ? 2 : 4;
+    const size_t sz = nhwc_dtype_bytes(dtype);
     const Range yr = span(y, elems_out(g) * sz);
     if (overlap(yr, span(x, elems_in(g) * sz)) ||
         overlap(yr, span(w_packed, (size_t)nhwc_packed_weight_elems(g, dtype) * sz)) ||

@@ -1,6 +1,6 @@
 // k_nhwc.hip -- dense 1x1 / 3x3 convolution + folded BatchNorm + activation
-// (+ residual) on channels-last tensors, stored as fp32 or fp16, accumulated
-// in fp32.
+// (+ residual) on channels-last tensors, stored as fp32, fp16 or bf16,
+// accumulated in fp32.
 //
 // The pages name two next steps for the convolutions: moving the activations
 // to NHWC with the weights reordered to match ("YOLO26N Inference
@@ -17,8 +17,10 @@
 // consecutive channels, which NHWC stores contiguously.
 //   * fp32: v_mfma_f32_32x32x2_f32, K = 2 channels per instruction (lane l:
 //     channel 2p + l/32 of pair p);
-//   * fp16: v_mfma_f32_32x32x16_f16, K = 16 channels (lane l: channels
-//     8*(l/32) .. +7).
+//   * fp16 / bf16: v_mfma_f32_32x32x16_f16 / _bf16, K = 16 channels (lane
+//     l: channels 8*(l/32) .. +7); the two 16-bit types share the layout,
+//     the staging and the tiles, and differ in the instruction and in the
+//     conversions (both round to nearest even).
 // A workgroup (four waves) computes WM x 32 output pixels (a block of TR rows
 // x TC columns) x WN x 32 output channels; wave (wm, wn) one 32 x 32 block.
 // Each stage stages KC input channels of the tile's input window in LDS as
@@ -46,6 +48,9 @@ namespace {
 typedef _Float16 half_t;
 typedef half_t h8 __attribute__((ext_vector_type(8)));
 typedef half_t h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16_t;
+typedef bf16_t b8 __attribute__((ext_vector_type(8)));
+typedef bf16_t b4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -93,7 +98,7 @@ __device__ __forceinline__ void lds16(rsrc_t r, __attribute__((address_space(3))
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
 }
 
-// Packed weight floats (or halves) per (32-channel block, stage): KK taps x
+// Packed weight floats (or 16-bit values) per (32-channel block, stage): KK taps x
 // KC input channels x 32 output channels, in the A operand's lane order.
 template <typename T, int K>
 constexpr int wstage_elems()
@@ -104,7 +109,10 @@ constexpr int wstage_elems()
 template <typename T, int K, int WM, int WN>
 __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
 {
-    constexpr bool F16 = sizeof(T) == 2;
+    constexpr bool F16 = sizeof(T) == 2;       // a 16-bit type: fp16 or bf16
+    constexpr bool BF = std::is_same<T, bf16_t>::value;
+    typedef typename std::conditional<BF, b8, h8>::type V8;
+    typedef typename std::conditional<BF, b4, h4>::type V4;
     constexpr int KC = F16 ? 32 : 16;          // input channels per stage
     constexpr int PER = 16 / (int)sizeof(T);   // channels per 16-byte piece
     constexpr int KK = K * K;
@@ -174,7 +182,7 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
     // Weights: A operand rows m = lane % 32 (output channel co + m).
     const rsrc_t rw = make_rsrc(a.wp, a.w_bytes);
     const int blk = co / 32;
-    typedef typename std::conditional<F16, h8, float>::type AV;
+    typedef typename std::conditional<F16, V8, float>::type AV;
     constexpr int NA = F16 ? KK * 2 : KK * 8;  // A values per lane per stage
     AV w0[NA], w1[NA];
     auto load_w = [&](int st, AV (&wv)[NA]) {
@@ -184,7 +192,7 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
         for (int j = 0; j < NA; ++j) {
             if constexpr (F16) {
                 const unsigned off = live ? base + (unsigned)((j * 64 + lane) * 16) : kOOB;
-                wv[j] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+                wv[j] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
             } else if (j % 4 == 0) {
                 // a tap's eight pair values are consecutive per lane: two 16-byte loads
                 const int tap = j / 8, q = (j / 4) & 1;
@@ -207,8 +215,11 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
             if constexpr (F16) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {  // two 16-channel halves of the stage
-                    const h8 bv = *reinterpret_cast<const h8*>(sb + toff + 32 * h + 16 * hi);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[tap * 2 + h], bv, acc, 0, 0, 0);
+                    const V8 bv = *reinterpret_cast<const V8*>(sb + toff + 32 * h + 16 * hi);
+                    if constexpr (BF)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[tap * 2 + h], bv, acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[tap * 2 + h], bv, acc, 0, 0, 0);
                 }
             } else {
 #pragma unroll
@@ -256,7 +267,7 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
         const f32x4 bi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, (int)coff, 0, 0));
         f32x4 rv;
         if constexpr (F16) {
-            const h4 r4 = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(rr, (int)eoff, 0, 0));
+            const V4 r4 = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(rr, (int)eoff, 0, 0));
 #pragma unroll
             for (int i = 0; i < 4; ++i) rv[i] = (float)r4[i];
         } else {
@@ -272,9 +283,9 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
             z[i] = t;
         }
         if constexpr (F16) {
-            h4 o;
+            V4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (half_t)z[i];
+            for (int i = 0; i < 4; ++i) o[i] = (T)z[i];
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), ry, (int)eoff, 0, 0);
         } else {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, z), ry, (int)eoff, 0, 0);
@@ -283,7 +294,7 @@ __global__ void __launch_bounds__(256) k_conv_nhwc(NhwcArgs a)
 }
 
 // OIHW fp32 -> the A operand's lane order per (32-channel block, stage):
-// fp16: [tap][half h][lane][8] holds output channel 32*blk + lane%32, input
+// fp16 / bf16: [tap][half h][lane][8] holds output channel 32*blk + lane%32, input
 // channels KC*st + 16h + 8*(lane/32) + 0..7; fp32: [tap][lane][pair p] holds
 // input channel KC*st + 2p + lane/32.  Zero where the channel does not exist.
 template <typename T, int K>
@@ -326,9 +337,9 @@ struct NhwcTile {
 }  // namespace
 
 // ------------------------------------------------------------------ host side
-static bool nhwc_dtype_ok(int dt) { return dt == CVX_DT_F32 || dt == CVX_DT_F16; }
-static int dt_size(int dt) { return dt == CVX_DT_F16 ? 2 : 4; }
-static int dt_kc(int dt) { return dt == CVX_DT_F16 ? 32 : 16; }
+static bool nhwc_dtype_ok(int dt) { return dt == CVX_DT_F32 || dt == CVX_DT_F16 || dt == CVX_DT_BF16; }
+static int dt_size(int dt) { return dt == CVX_DT_F32 ? 4 : 2; }
+static int dt_kc(int dt) { return dt == CVX_DT_F32 ? 16 : 32; }
 
 long nhwc_packed_weight_elems(const ConvGeom& g, int dt)
 {
@@ -391,6 +402,13 @@ hipError_t launch_pack_nhwc(const ConvGeom& g, int dt, const float* w, void* wp,
         else
             hipLaunchKernelGGL((k_pack_nhwc<half_t, 1>), grid, dim3(256), 0, s, w, g.cout, g.cin, nst, total,
                                static_cast<half_t*>(wp));
+    } else if (dt == CVX_DT_BF16) {
+        if (g.k == 3)
+            hipLaunchKernelGGL((k_pack_nhwc<bf16_t, 3>), grid, dim3(256), 0, s, w, g.cout, g.cin, nst, total,
+                               static_cast<bf16_t*>(wp));
+        else
+            hipLaunchKernelGGL((k_pack_nhwc<bf16_t, 1>), grid, dim3(256), 0, s, w, g.cout, g.cin, nst, total,
+                               static_cast<bf16_t*>(wp));
     } else {
         if (g.k == 3)
             hipLaunchKernelGGL((k_pack_nhwc<float, 3>), grid, dim3(256), 0, s, w, g.cout, g.cin, nst, total,
@@ -411,8 +429,8 @@ void nhwc_describe(const ConvGeom& g, int dt, char* buf, int len)
         return;
     }
     snprintf(buf, len, "nhwc k%d s%d %s wm=%d wn=%d tr=%d tc=%d kernel=cvx::k_conv_nhwc<%s, %d, %d, %d>", g.k,
-             g.stride, dt == CVX_DT_F16 ? "f16" : "f32", t.wm, t.wn, t.tr, t.tc,
-             dt == CVX_DT_F16 ? "_Float16" : "float", g.k, t.wm, t.wn);
+             g.stride, dt == CVX_DT_F16 ? "f16" : dt == CVX_DT_BF16 ? "bf16" : "f32", t.wm, t.wn, t.tr, t.tc,
+             dt == CVX_DT_F16 ? "_Float16" : dt == CVX_DT_BF16 ? "__bf16" : "float", g.k, t.wm, t.wn);
 }
 
 template <typename T, int K>
@@ -478,6 +496,11 @@ hipError_t launch_conv_nhwc(const ConvGeom& g, int dt, const void* x, const void
             launch_nhwc_k<half_t, 3>(t, grid, lds, s, a);
         else
             launch_nhwc_k<half_t, 1>(t, grid, lds, s, a);
+    } else if (dt == CVX_DT_BF16) {
+        if (g.k == 3)
+            launch_nhwc_k<bf16_t, 3>(t, grid, lds, s, a);
+        else
+            launch_nhwc_k<bf16_t, 1>(t, grid, lds, s, a);
     } else {
         if (g.k == 3)
             launch_nhwc_k<float, 3>(t, grid, lds, s, a);

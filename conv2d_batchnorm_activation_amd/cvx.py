@@ -29,7 +29,7 @@ CVX_RES_NONE, CVX_RES_BEFORE_ACT, CVX_RES_AFTER_ACT = 0, 1, 2
 CVX_L_CONV, CVX_L_GAP, CVX_L_FC, CVX_L_PREPROC = 0, 1, 2, 3
 CVX_INPUT, CVX_NO_RES = -1, -2
 CVX_W_OIHW, CVX_W_PACKED = 0, 1
-CVX_DT_F32, CVX_DT_F16 = 0, 1
+CVX_DT_F32, CVX_DT_F16, CVX_DT_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "CVX_OK", -1: "CVX_ERR_NULL", -2: "CVX_ERR_SHAPE", -3: "CVX_ERR_UNSUPPORTED",
                 -4: "CVX_ERR_ALIGN", -5: "CVX_ERR_ALIAS", -6: "CVX_ERR_WORKSPACE",
                 -7: "CVX_ERR_HIP", -8: "CVX_ERR_ARG", -9: "CVX_ERR_SCRATCH"}

@@ -278,8 +278,11 @@ CVX_API cvx_status cvx_forward(const cvx_layer *layers, int n_layers, const void
 /* ------------------------------------------------ channels-last variant */
 /* Element type of a channels-last layer's activations and weights.  Sums are
  * always accumulated in fp32 and the folded BatchNorm, residual and activation
- * are applied in fp32; CVX_DT_F16 rounds the stored output to IEEE half. */
-enum { CVX_DT_F32 = 0, CVX_DT_F16 = 1 };
+ * are applied in fp32; CVX_DT_F16 rounds the stored output to IEEE half and
+ * CVX_DT_BF16 to bfloat16 (8-bit exponent, 8-bit significand), both to
+ * nearest even.  bf16 keeps fp32's range, so activations that would overflow
+ * half stay finite, at a coarser step (2^-8 of the value). */
+enum { CVX_DT_F32 = 0, CVX_DT_F16 = 1, CVX_DT_BF16 = 2 };
 
 /* Bytes of the packed weights cvx_nhwc_pack_weights writes for `d` and
  * `dtype` (0 when the layer is not supported by the channels-last kernels).
@@ -294,8 +297,9 @@ CVX_API cvx_status cvx_nhwc_plan(const cvx_conv_desc *d, int dtype, char *buf, i
  * cvx_nhwc_pack_weights -- one-time transform of OIHW fp32 weights into the
  * order the channels-last kernels read (the weights reordered once to match
  * the NHWC layout: "YOLO26N Inference Optimisation", "NHWC migration --
- * detailed scope", "Weight layout"), rounded to `dtype` (fp16 rounds to
- * nearest even).  Padded with zeros to whole 32-row and 16/32-channel groups.
+ * detailed scope", "Weight layout"), rounded to `dtype` (fp16 and bf16 round
+ * to nearest even).  Padded with zeros to whole 32-row and 16/32-channel
+ * groups.
  *   w_oihw  : device fp32 [c_out][c_in][kh][kw], read only.
  *   w_packed: device, cvx_nhwc_packed_weights_bytes(d, dtype) bytes, written.
  */
@@ -310,7 +314,8 @@ CVX_API cvx_status cvx_nhwc_pack_weights(const cvx_conv_desc *d, int dtype, cons
  * ("YOLO26N Inference Optimisation", "NHWC migration -- detailed scope";
  * "Как я свертки ускорял", "Идеи и следующие шаги", item 1: fp16).
  * Supported: groups 1, 1x1 or 3x3, stride 1 or 2, c_in a multiple of 4 (fp32)
- * or 8 (fp16), c_out a multiple of 4; else CVX_ERR_UNSUPPORTED.
+ * or 8 (fp16, bf16), c_out a multiple of 4; else CVX_ERR_UNSUPPORTED.
+ * An unknown dtype is CVX_ERR_ARG.
  * d->w_layout is ignored (the weights are cvx_nhwc_pack_weights' output).
  *   scale, bias: device fp32 [c_out] (cvx_fold_bn).
  *   x, y, residual: device, 16-byte aligned; y must not overlap the inputs;

@@ -413,3 +413,24 @@ def test_nhwc_host_validation():
     assert cvx.cvx_nhwc_packed_weights_bytes(d, F32) == 2 * 4 * 9 * 32 * 16 * 4
     assert cvx.cvx_nhwc_packed_weights_bytes(d, F16) == 2 * 2 * 9 * 32 * 32 * 2
     assert "k_conv_nhwc<_Float16, 3" in cvx.cvx_nhwc_plan(d, F16)
+    # bf16 shares fp16's 16-bit layout: same sizes, limits and checks
+    BF16 = cvx.CVX_DT_BF16
+    assert cvx.cvx_nhwc_packed_weights_bytes(d, BF16) == cvx.cvx_nhwc_packed_weights_bytes(d, F16)
+    assert "k_conv_nhwc<__bf16, 3" in cvx.cvx_nhwc_plan(d, BF16)
+    assert cvx.cvx_nhwc_packed_weights_bytes(_desc(c_in=12, c_out=32), BF16) == 0
+    assert f(ctypes.byref(d), BF16, X + 4, W, S, B, None, Y, None) == -4
+    assert f(ctypes.byref(d), 3, X, W, S, B, None, Y, None) == -8
+    assert cvx.lib.cvx_nhwc_pack_weights(ctypes.byref(d), 3, W, X, None) == -8
+
+
+def test_bf16_rounding_of_the_test_inputs_is_nearest_even():
+    """The channels-last bf16 tests round their fp32 inputs and weights to
+    bf16 with torch's CPU conversion, and the packing kernel rounds weights to
+    nearest even; the two must agree on ties.  bf16 keeps 7 significand bits:
+    between 1 and 2 its step is 2^-7, so 1 + 2^-8 is a tie."""
+    import torch
+    v = torch.tensor([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -20,
+                      1 + 2.0 ** -8 - 2.0 ** -20, 3.0e38], dtype=torch.float32)
+    got = v.to(torch.bfloat16).to(torch.float32).tolist()
+    assert got[:5] == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7, 1.0]
+    assert np.isfinite(got[5]) and abs(got[5] - 3.0e38) <= 3.0e38 * 2.0 ** -8  # fp32's range

@@ -1,5 +1,5 @@
 """GPU parity of the channels-last layer (cvx_conv_bn_act_nhwc): NHWC tensors
-stored as fp32 or fp16, fp32 accumulation, against the fp64 oracle.
+stored as fp32, fp16 or bf16, fp32 accumulation, against the fp64 oracle.
 
 The oracle works in NCHW; the tests transpose NCHW <-> NHWC on the host.  For
 fp16 the layer reads fp16 activations, residual and weights, so the oracle is
@@ -9,7 +9,11 @@ products then differ from the fp64 result by rounding only, and the stored
 output adds one fp16 rounding (at most half an ulp: 2^-11 of the value).  The
 bar is |gpu - oracle| <= 1e-4*max(1,|oracle|) + 2^-11*|oracle| for fp16 and
 the usual 1e-4*max(1,|oracle|) for fp32, element by element, with NaN guard
-bands around every output."""
+bands around every output.  bf16 is the same argument with 7 stored
+significand bits instead of 10: the host rounds inputs, residual and weights
+to bf16 with torch's CPU conversion (round to nearest even, checked on ties in
+test_abi.py), and the stored output's half ulp is at most 2^-8 of the
+value, so the bar is 1e-4*max(1,|oracle|) + 2^-8*|oracle|."""
 import numpy as np
 import pytest
 import torch
@@ -22,9 +26,11 @@ pytestmark = pytest.mark.gpu
 
 from conv2d_batchnorm_activation_amd import cvx  # noqa: E402
 
-F32, F16 = cvx.CVX_DT_F32, cvx.CVX_DT_F16
-TORCH_DT = {F32: torch.float32, F16: torch.float16}
-NP_DT = {F32: np.float32, F16: np.float16}
+F32, F16, BF16 = cvx.CVX_DT_F32, cvx.CVX_DT_F16, cvx.CVX_DT_BF16
+TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+# half an ulp of the stored output, relative to the value
+OUT_ROUND = {F32: 0.0, F16: 2.0 ** -11, BF16: 2.0 ** -8}
+DTS, DT_IDS = [F32, F16, BF16], ["f32", "f16", "bf16"]
 
 
 def setup_module(module):
@@ -37,7 +43,7 @@ def check_dt(got, ref, dt, what):
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
-    tol = 1e-4 * np.maximum(1.0, np.abs(r)) + (2.0 ** -11 * np.abs(r) if dt == F16 else 0.0)
+    tol = 1e-4 * np.maximum(1.0, np.abs(r)) + OUT_ROUND[dt] * np.abs(r)
     bad = np.abs(g - r) > tol
     if bad.any():
         idx = np.unravel_index(int(np.argmax(np.abs(g - r) - tol)), g.shape)
@@ -79,7 +85,9 @@ def run_nhwc(x, L, residual, dt):
 
 
 def rounded(a, dt):
-    return a.astype(NP_DT[dt]).astype(np.float32)
+    """fp32 copy of `a` rounded to dt's values (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(TORCH_DT[dt]).to(torch.float32).numpy()
 
 
 def oracle_ref(x, L, residual, dt):
@@ -98,7 +106,7 @@ def case(x, L, residual, dt, what):
     check_dt(y, oracle_ref(x, L, residual, dt), dt, what)
 
 
-@pytest.mark.parametrize("dt", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("dt", DTS, ids=DT_IDS)
 @pytest.mark.parametrize("name", [s[0] for s in wl.SWEEP[:7]])
 def test_nhwc_sweep_layer(name, dt):
     # the detector's dense layers a..g at their own shapes, residual = own input
@@ -123,7 +131,7 @@ NHWC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dt", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("dt", DTS, ids=DT_IDS)
 @pytest.mark.parametrize("c", NHWC_CASES, ids=[f"case{c[0]}" for c in NHWC_CASES])
 def test_nhwc_cases(c, dt):
     seed, n, cin, h, w, cout, k, s, p, act, rm = c
@@ -132,3 +140,14 @@ def test_nhwc_cases(c, dt):
     oh, ow = cvx.cvx_conv_out_shape(d)
     r = wl.residual_for(seed, (n, cout, oh, ow)) if rm else None
     case(x, L, r, dt, f"case {seed} {dt}")
+
+
+def test_nhwc_bf16_keeps_fp32_range():
+    """Outputs far beyond fp16's largest finite value (65504) stay finite and
+    within the bar in bf16, whose exponent is fp32's."""
+    seed, n, cin, h, w, cout = 320, 1, 64, 12, 12, 64
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, 3, 1, 1, 1, wl.ACT_NONE, wl.RES_NONE)
+    x = x * np.float32(65536.0)
+    ref = oracle_ref(rounded(x, BF16), L, None, BF16)
+    assert np.abs(ref).max() > 1e5, "the case must leave fp16's range"
+    case(x, L, None, BF16, "bf16 range")
