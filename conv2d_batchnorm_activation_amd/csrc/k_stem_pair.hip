@@ -126,9 +126,14 @@ __device__ __forceinline__ SrcAxis sp_axis(int d, int src, int dst, unsigned m, 
     return a;
 }
 
-template <int NT, int S1, bool U8>
+template <int NT, int S1, int C1, bool U8>
 __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
 {
+    // the first layer's reduction: C1 channels x 9 taps, four per matrix
+    // instruction (a compile-time count, so that its operands sit in fixed
+    // registers and every LDS read of a block can be issued ahead)
+    constexpr int KT = C1 * 9;
+    constexpr int STEPS = (KT + 3) / 4;
     constexpr int BN = 32 * NT;
     constexpr int PITCH = BN + 4;
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -157,8 +162,13 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     const int ow0 = tw * a.tc;
     const int gx0 = (ow0 * a.S2 - 1) & ~3;   // first staged column of the region (16-byte aligned)
     const int iy0 = oh_ref * a.S2 - 1;       // first staged row of the region
+    // LDS: the first layer's input window from 0, its output region after it
+    // (the staged frame rows, dead once resized, share the region's space),
+    // and the consumers' exchange from 0 again once the region has been read
     const int RS = a.PR * a.PCW;             // LDS floats per region channel
-    const int WIN = kC1 * RS;                // the window (then the exchange) after the region
+    constexpr int WIN = 0;                   // the window
+    const int REG = a.cin1 * a.WR * a.WCW;   // the region (a multiple of 4 floats)
+    constexpr int XO = 0;                    // the exchange
     const int wx0 = S1 * gx0 - 4;            // first window column (16-byte aligned)
     const int wy0 = S1 * iy0 - 1;            // first window row
 
@@ -166,7 +176,7 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     // frame: the two frame rows each window row interpolates between, over the
     // window's span of frame columns, go to LDS (16-byte LDS-direct loads),
     // then are resized and normalised into the window below.
-    const int SRC = WIN * 4 + 4 * a.cin1 * a.WR * a.WCW;  // byte offset of the staged frame rows
+    const int SRC = 4 * REG;                              // byte offset of the staged frame rows
     int sb0 = 0;                                          // first staged frame byte of a row
     if constexpr (U8) {
         const int x_lo = max(wx0, 0);
@@ -203,6 +213,8 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             const bool ok = e < a.win_elems && (unsigned)iy < (unsigned)a.H1 && ix >= 0 && ix + 4 <= a.W1;
             const unsigned off = ok ? 4u * (unsigned)(((b * a.cin1 + ci) * a.H1 + iy) * a.W1 + ix) : kOOB;
             // lane l of the wave writes 16 bytes at d + 16 l: element e lands at WIN + 4 e
+            // (a round's lanes past the window write zeros into the region, which
+            // the first layer rewrites whole)
             sp_lds_load16(rx, (__attribute__((address_space(3))) void*)(smem + WIN + 4 * (kSPThreads * i + 64 * wave)), off);
         }
     }
@@ -211,16 +223,14 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     // weight of each step (channel l%16, tap 4s + l/16; zero past c_in x 9),
     // where that tap sits in the window, and its channel's scale and bias --
     // loaded now, so that their latency hides under the window's
-    const int KT = a.cin1 * 9;
-    const int steps = (KT + 3) >> 2;
     const int co1 = lane & 15;
     const int kg = lane >> 4;
-    float bw[kMaxCin1 * 9 / 4 + 1];
-    int aoff[kMaxCin1 * 9 / 4 + 1];
+    float bw[STEPS];
+    int aoff[STEPS];
 #pragma unroll
-    for (int st = 0; st < kMaxCin1 * 9 / 4 + 1; ++st) {
+    for (int st = 0; st < STEPS; ++st) {
         const int k = 4 * st + kg;
-        const bool live = st < steps && k < KT;
+        const bool live = k < KT;
         bw[st] = live ? a.w1[co1 * KT + k] : 0.0f;
         const int ci = k / 9, t = k - 9 * (k / 9);
         aoff[st] = live ? (ci * a.WR + t / 3) * a.WCW + t % 3 + 3 : 0;
@@ -288,10 +298,20 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             const unsigned char* r0 = sm + (2 * r) * a.SRB;
             const unsigned char* r1 = r0 + a.SRB;
             const int c0 = ok ? 3 * ax.i0 - sb0 : 0, c1 = ok ? 3 * ax.i1 - sb0 : 0;
+            // all twelve bytes first: the window stores below could alias them
+            // as far as the compiler knows, and would otherwise wait on each
+            unsigned char px[4][3];
 #pragma unroll
             for (int ch = 0; ch < 3; ++ch) {
-                const float p00 = (float)r0[c0 + ch], p01 = (float)r0[c1 + ch];
-                const float p10 = (float)r1[c0 + ch], p11 = (float)r1[c1 + ch];
+                px[0][ch] = r0[c0 + ch];
+                px[1][ch] = r0[c1 + ch];
+                px[2][ch] = r1[c0 + ch];
+                px[3][ch] = r1[c1 + ch];
+            }
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) {
+                const float p00 = (float)px[0][ch], p01 = (float)px[1][ch];
+                const float p10 = (float)px[2][ch], p11 = (float)px[3][ch];
                 const float top = fmaf(ax.f, p01 - p00, p00);
                 const float bot = fmaf(ax.f, p11 - p10, p10);
                 const float v = fmaf(fmaf(ay.f, bot - top, top), a.na[ch], a.nb[ch]);
@@ -318,11 +338,11 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             const int x = f - r * a.PCW;
             const float* wb = smem + WIN + S1 * r * a.WCW + S1 * x;
             f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            float av[STEPS];
 #pragma unroll
-            for (int st = 0; st < kMaxCin1 * 9 / 4 + 1; ++st) {
-                if (st >= steps) break;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wb[aoff[st]], bw[st], acc, 0, 0, 0);
-            }
+            for (int st = 0; st < STEPS; ++st) av[st] = wb[aoff[st]];
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bw[st], acc, 0, 0, 0);
             // sums: channel co1, flat pixels fo .. fo+3 (one region row: PCW % 4 == 0)
             const int fo = 16 * blk + 4 * kg;
             if (fo < RS) {
@@ -335,13 +355,14 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
                     const float t = apply_act_fast(fmaf(s1, acc[v], b1), a.act1);
                     o[v] = rok && (unsigned)(gx0 + xo + v) < (unsigned)a.W2 ? t : 0.0f;
                 }
-                *reinterpret_cast<f32x4*>(smem + co1 * RS + fo) = o;
+                *reinterpret_cast<f32x4*>(smem + REG + co1 * RS + fo) = o;
             }
         }
     }
     lds_barrier();
 
     if (!consumer) {
+        __syncthreads();  // the region read: the exchange overwrites it
         __syncthreads();  // the consumers' exchange
         return;
     }
@@ -365,7 +386,7 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     auto wsel = [&](int f) { return f < 16 ? wq[f / 4][f % 4] : wt[f - 16]; };
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-        const float* xa = smem + (2 * (2 * wave + pp) + hi) * RS;
+        const float* xa = smem + REG + (2 * (2 * wave + pp) + hi) * RS;
         float bv[9][NT];
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
@@ -382,10 +403,12 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
         }
     }
 
-    // partial tiles of the four waves through LDS (the window region is free),
-    // then wave w sums channels 8w .. 8w+7 of the tile
+    // partial tiles of the four waves through LDS (over the window and the
+    // region, once every wave has read its part of the region), then wave w
+    // sums channels 8w .. 8w+7 of the tile
+    __syncthreads();
     {
-        float* red = smem + WIN + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
+        float* red = smem + XO + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -397,7 +420,7 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     const rsrc_t ry = make_rsrc(a.y, out_bytes);
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-        const int off = WIN + erow * PITCH + 32 * k + 4 * (lane & 7);
+        const int off = XO + erow * PITCH + 32 * k + 4 * (lane & 7);
         f32x4 v = *reinterpret_cast<const f32x4*>(smem + off);
 #pragma unroll
         for (int s = 1; s < 4; ++s) v += *reinterpret_cast<const f32x4*>(smem + s * 32 * PITCH + off);
@@ -464,13 +487,15 @@ bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, 
     pg->win_elems = g1.cin * pg->WR * (pg->WCW / 4);
     pg->win_rounds = (pg->win_elems + kSPThreads - 1) / kSPThreads;
     pg->SRB = pg->src_elems = pg->src_rounds = 0;
+    // floats: the window from 0, the region after it, the exchange from 0
     const size_t region = (size_t)kC1 * pg->PR * pg->PCW;
     const size_t xch = (size_t)4 * 32 * (bn + 4);
-    size_t after;  // floats after the region
+    const size_t win = (size_t)g1.cin * pg->WR * pg->WCW;
+    size_t total;
     if (pre == nullptr) {
         if (pg->win_rounds > kWinRounds) return false;
         // every lane of a window round writes its 16 bytes (zeros past the window)
-        after = std::max((size_t)4 * kSPThreads * pg->win_rounds, xch);
+        total = std::max(std::max(win + region, (size_t)4 * kSPThreads * pg->win_rounds), xch);
     } else {
         // widest frame byte span of a window's columns, from its 16-byte aligned start
         int srb = 16;
@@ -487,13 +512,12 @@ bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, 
         pg->src_elems = 2 * pg->WR * (srb / 16);
         pg->src_rounds = (pg->src_elems + kSPThreads - 1) / kSPThreads;
         if (pg->src_rounds > kSrcRounds) return false;
-        // the window (written by the interpolation), then the staged frame rows
-        // (every lane of a round writes its 16 bytes)
-        const size_t win = (size_t)g1.cin * pg->WR * pg->WCW;
+        // the staged frame rows share the region's space (every lane of a
+        // round writes its 16 bytes)
         const size_t src = (size_t)4 * kSPThreads * pg->src_rounds;  // floats
-        after = std::max(win + src, xch);
+        total = std::max(win + std::max(region, src), xch);
     }
-    pg->lds = (region + after) * sizeof(float);
+    pg->lds = total * sizeof(float);
     return pg->lds + 256 <= kMaxLdsBytes;
 }
 
@@ -542,17 +566,23 @@ void stem_pair_describe(const ConvGeom& g1, const ConvGeom& g2, const StemProlog
         snprintf(buf, len, "unsupported");
         return;
     }
-    snprintf(buf, len, "stem_pair k3 s%d+s%d bn=%d tc=%d%s kernel=cvx::k_stem_pair<%d, %d, %s>", g1.stride,
-             g2.stride, 32 * pg.nt, pg.tc, pre ? " from=u8" : "", pg.nt, g1.stride, pre ? "true" : "false");
+    snprintf(buf, len, "stem_pair k3 s%d+s%d bn=%d tc=%d%s kernel=cvx::k_stem_pair<%d, %d, %d, %s>", g1.stride,
+             g2.stride, 32 * pg.nt, pg.tc, pre ? " from=u8" : "", pg.nt, g1.stride, g1.cin, pre ? "true" : "false");
 }
 
 template <int NT, int S1>
-static void launch_pair_u8(bool u8, dim3 grid, size_t lds, hipStream_t s, const StemPairArgs& a)
+static void launch_pair_u8(bool u8, int cin1, dim3 grid, size_t lds, hipStream_t s, const StemPairArgs& a)
 {
-    if (u8)
-        hipLaunchKernelGGL((k_stem_pair<NT, S1, true>), grid, dim3(kSPThreads), lds, s, a);
-    else
-        hipLaunchKernelGGL((k_stem_pair<NT, S1, false>), grid, dim3(kSPThreads), lds, s, a);
+    if (u8) {  // a u8 frame has three channels
+        hipLaunchKernelGGL((k_stem_pair<NT, S1, 3, true>), grid, dim3(kSPThreads), lds, s, a);
+        return;
+    }
+    switch (cin1) {
+    case 1: hipLaunchKernelGGL((k_stem_pair<NT, S1, 1, false>), grid, dim3(kSPThreads), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_stem_pair<NT, S1, 2, false>), grid, dim3(kSPThreads), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_stem_pair<NT, S1, 3, false>), grid, dim3(kSPThreads), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_stem_pair<NT, S1, 4, false>), grid, dim3(kSPThreads), lds, s, a); break;
+    }
 }
 
 hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const StemPrologue* pre, const float* w1,
@@ -637,14 +667,14 @@ hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const StemProlog
     const bool u8 = pre != nullptr;
     if (pg.nt == 2) {
         if (g1.stride == 2)
-            launch_pair_u8<2, 2>(u8, grid, pg.lds, s, a);
+            launch_pair_u8<2, 2>(u8, g1.cin, grid, pg.lds, s, a);
         else
-            launch_pair_u8<2, 1>(u8, grid, pg.lds, s, a);
+            launch_pair_u8<2, 1>(u8, g1.cin, grid, pg.lds, s, a);
     } else {
         if (g1.stride == 2)
-            launch_pair_u8<1, 2>(u8, grid, pg.lds, s, a);
+            launch_pair_u8<1, 2>(u8, g1.cin, grid, pg.lds, s, a);
         else
-            launch_pair_u8<1, 1>(u8, grid, pg.lds, s, a);
+            launch_pair_u8<1, 1>(u8, g1.cin, grid, pg.lds, s, a);
     }
     return hipGetLastError();
 }
