@@ -198,6 +198,24 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             // lane l of the wave writes 16 bytes at d + 16 l: element e lands at SRC + 16 e
             sp_lds_load16(rs, (__attribute__((address_space(3))) void*)(sm + SRC + 16 * (kSPThreads * i + 64 * wave)), off);
         }
+        // while the rows are in flight: the resize's column and row terms, once
+        // per window column and row (the interpolation below then looks them
+        // up): column -> {first and second source byte in the staged row,
+        // weight, inside the image}; row -> {weight, inside the image}
+        const int TB = SRC + 16 * kSPThreads * a.src_rounds;
+        if (tid < a.WCW) {
+            const int x = wx0 + tid;
+            const bool ok = (unsigned)x < (unsigned)a.W1;
+            const SrcAxis ax = sp_axis(ok ? x : 0, a.src_w, a.W1, a.m_dw, a.l_dw, a.inv_dw);
+            *reinterpret_cast<int4*>(sm + TB + 16 * tid) =
+                int4{ok ? 3 * ax.i0 - sb0 : 0, ok ? 3 * ax.i1 - sb0 : 0, __float_as_int(ax.f), ok ? 1 : 0};
+        } else if (tid - a.WCW < a.WR) {
+            const int r = tid - a.WCW;
+            const int y = wy0 + r;
+            const bool ok = (unsigned)y < (unsigned)a.H1;
+            const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
+            *reinterpret_cast<int2*>(sm + TB + 16 * a.WCW + 8 * r) = int2{__float_as_int(ay.f), ok ? 1 : 0};
+        }
     } else {
         const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
         const int epr = a.WCW >> 2;  // 16-byte elements per window row
@@ -287,17 +305,18 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
         // a window pixel (row r, column col) and its three channels; outside the
         // resized image, zeros (the first layer's padding)
         const unsigned char* sm = reinterpret_cast<const unsigned char*>(smem) + SRC;
+        const unsigned char* tb = reinterpret_cast<const unsigned char*>(smem) + SRC + 16 * kSPThreads * a.src_rounds;
         const int n_px = a.WR * a.WCW;
         for (int idx = tid; idx < n_px; idx += kSPThreads) {
             const int r = sp_div(idx, a.m_wcw, a.l_wcw);
             const int col = idx - r * a.WCW;
-            const int y = wy0 + r, x = wx0 + col;
-            const bool ok = (unsigned)y < (unsigned)a.H1 && (unsigned)x < (unsigned)a.W1;
-            const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
-            const SrcAxis ax = sp_axis(ok ? x : 0, a.src_w, a.W1, a.m_dw, a.l_dw, a.inv_dw);
+            const int4 cx = *reinterpret_cast<const int4*>(tb + 16 * col);
+            const int2 cy = *reinterpret_cast<const int2*>(tb + 16 * a.WCW + 8 * r);
+            const bool ok = (cx.w & cy.y) != 0;
+            const SrcAxis ax{0, 0, __int_as_float(cx.z)}, ay{0, 0, __int_as_float(cy.x)};
             const unsigned char* r0 = sm + (2 * r) * a.SRB;
             const unsigned char* r1 = r0 + a.SRB;
-            const int c0 = ok ? 3 * ax.i0 - sb0 : 0, c1 = ok ? 3 * ax.i1 - sb0 : 0;
+            const int c0 = ok ? cx.x : 0, c1 = ok ? cx.y : 0;
             // all twelve bytes first: the window stores below could alias them
             // as far as the compiler knows, and would otherwise wait on each
             unsigned char px[4][3];
@@ -513,8 +532,10 @@ bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, 
         pg->src_rounds = (pg->src_elems + kSPThreads - 1) / kSPThreads;
         if (pg->src_rounds > kSrcRounds) return false;
         // the staged frame rows share the region's space (every lane of a
-        // round writes its 16 bytes)
-        const size_t src = (size_t)4 * kSPThreads * pg->src_rounds;  // floats
+        // round writes its 16 bytes), then the resize's column and row tables
+        // (16 bytes a column, 8 a row, filled by one thread each)
+        if (pg->WCW + pg->WR > kSPThreads) return false;
+        const size_t src = (size_t)4 * kSPThreads * pg->src_rounds + 4 * pg->WCW + 2 * pg->WR;  // floats
         total = std::max(win + std::max(region, src), xch);
     }
     pg->lds = total * sizeof(float);
