@@ -225,6 +225,25 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         // image (or past the region).  Found once by division, then stepped by 256
         // elements in mixed radix with selects (full-rate operations, no branches).
         const int iy0 = oh_ref * a.stride - a.pad;
+        const float* xim = a.x + (long)b * a.cin * HW;
+        auto chunk_rsrc = [&](int chunk) {
+            const int left = chunk < c_end ? min(kCh, a.cin - chunk * kCh) : 0;
+            return make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+        };
+        auto lds_dst = [&](int cbase, int i) {
+            return (__attribute__((address_space(3))) void*)(smem + cbase + 256 * G * i + pw * 64 * G);
+        };
+        auto load_elem = [&](const rsrc_t& rc, int cbase, int i, unsigned off) {
+            if constexpr (VEC)
+                lds_load16(rc, lds_dst(cbase, i), off);
+            else
+                lds_load4(rc, lds_dst(cbase, i), off);
+        };
+        // Stage 0 goes out round by round as the offsets are found, so the
+        // first loads do not wait for all of them.
+        rsrc_t rc0[CPS];
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) rc0[j] = chunk_rsrc(c_begin + j);
         unsigned goff[NR];
         {
             int ci = pdiv(ptid, a.m_rc, a.l_rc);
@@ -242,6 +261,10 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
                     const unsigned lin = __umul24((unsigned)ci, (unsigned)HW) +
                                          __umul24((unsigned)iy, (unsigned)a.W) + (unsigned)gx;
                     goff[i] = ok ? 4u * lin : kOOB;
+                    if (nstages > 0) {
+#pragma unroll
+                        for (int j = 0; j < CPS; ++j) load_elem(rc0[j], j * CHF, i, goff[i]);
+                    }
                     c += a.step_c;
                     const bool cc = c >= a.EPR;
                     c -= cc ? a.EPR : 0;
@@ -252,31 +275,22 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
                 }
             }
         }
-        const float* xim = a.x + (long)b * a.cin * HW;
         auto issue_x = [&](int st, int sb) {
 #pragma unroll
             for (int j = 0; j < CPS; ++j) {
-                const int chunk = c_begin + st * CPS + j;
                 int cbase = sb + j * CHF;
                 asm volatile("" : "+s"(cbase));
-                const int left = chunk < c_end ? min(kCh, a.cin - chunk * kCh) : 0;
-                const rsrc_t rc = make_rsrc(xim + (long)chunk * kCh * HW, 4u * (unsigned)(left * HW));
+                const rsrc_t rc = chunk_rsrc(c_begin + st * CPS + j);
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
                     if (i >= a.rounds) break;
-                    auto* d = (__attribute__((address_space(3))) void*)(smem + cbase + 256 * G * i +
-                                                                         pw * 64 * G);
-                    if constexpr (VEC)
-                        lds_load16(rc, d, goff[i]);
-                    else
-                        lds_load4(rc, d, goff[i]);
+                    load_elem(rc, cbase, i, goff[i]);
                 }
             }
         };
         // Barrier s (s = 0 .. nstages-1) follows the landing of stage s+1; stage
         // s+2 then goes into the buffer of stage s-1, which the consumers have
-        // left by barrier s.
-        if (nstages > 0) issue_x(0, 0);
+        // left by barrier s.  (Stage 0 is in flight already.)
         if (nstages > 1) issue_x(1, BUF);
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();
@@ -301,11 +315,6 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     const bool row_ok = eco < a.cout;
     const bool single = a.partial == nullptr;
     float sc = 0.0f, bi = 0.0f;
-    if (single) {
-        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
-        sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
-        bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
-    }
 
     // LDS offset of each of this lane's pixels (tap 0) in a staged channel
     const int RS = a.PR * a.PCW;  // LDS floats per staged channel
@@ -467,12 +476,17 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     // stage s-1 (whose buffer now takes stage s+2).  The barrier orders LDS only,
     // so the weight loads in flight stay in flight.
     // Every global load of the loop is issued unconditionally, in a fixed order
-    // (weights of stages 0 and 1, the residual, then stage st+2's weights at the
-    // end of stage st), so each wait for a stage's weights leaves the later loads
-    // in flight.
+    // (weights of stages 0 and 1, the residual, the scale and bias, then stage
+    // st+2's weights at the end of stage st), so each wait for a stage's weights
+    // leaves the later loads in flight.
     load_a(0, a0);
     load_a(1, a1);
     load_res();
+    if (single) {  // needed only by the epilogue: behind the stages' first loads
+        const unsigned o = row_ok ? 4u * (unsigned)eco : kOOB;
+        sc = bload(make_rsrc(a.scale, 4u * (unsigned)a.cout), o);
+        bi = bload(make_rsrc(a.bias, 4u * (unsigned)a.cout), o);
+    }
     lds_barrier();
     if (nstages > 0) read_b(0, 0, b0);
     {
