@@ -1100,6 +1100,33 @@ def layout_comparison(reps: int):
     return out
 
 
+def batch_scaling(t1_us: float, tb_us: float, batch: int) -> dict:
+    """Throughput-scaling of a batch against batch 1: images per second at
+    batch B over B times the batch-1 rate, thr(B) / (B * thr(1)), which is
+    t(1) / t(B) (1.0 when a batch of B takes no longer than one image), and
+    the plain throughput ratio thr(B) / thr(1)."""
+    eff = t1_us / tb_us
+    return {"batch": batch, "us_b1": t1_us, "us_batch": tb_us, "efficiency": round(eff, 4),
+            "throughput_ratio": round(batch * eff, 3)}
+
+
+def batch_scalings(result: dict) -> dict:
+    """The detector at b=8 and the MNIST net at b=256 against their batch-1
+    forwards, from the graphs-of-ten figures (GPU time: the back-to-back figure
+    of a tiny forward is the host's enqueue rate)."""
+    ow = result.get("other_workloads", {})
+    out = {}
+    d8 = ow.get("detector_b8")
+    if d8 and result.get("ms_per_forward_graph10"):
+        out["detector_b8"] = batch_scaling(round(result["ms_per_forward_graph10"] * 1e3, 2),
+                                           d8["us_per_forward_graph10"], d8["batch"])
+    m1, m256 = ow.get("mnist_b1"), ow.get("mnist_b256")
+    if m1 and m256:
+        out["mnist_b256"] = batch_scaling(m1["us_per_forward_graph10"], m256["us_per_forward_graph10"],
+                                          m256["batch"])
+    return out
+
+
 def cpu_baseline(wk, flop_per_forward: float, budget_s: float):
     import oracle
     reps = 0
@@ -1263,6 +1290,7 @@ def main() -> int:
     }
     if not args.no_others and not args.no_layers:
         result["other_workloads"] = other_workloads(args.layer_reps, args.steps)
+        result["batch_scaling"] = batch_scalings(result)
         result["layout_comparison"] = layout_comparison(args.layer_reps)
     result["gpu_clocks"]["end"] = gpu_clocks()
     if not args.no_cpu_baseline and args.batch == 1:

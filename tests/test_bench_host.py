@@ -45,3 +45,18 @@ def test_timed_layers_get_a_residual_of_the_output_shape():
                 assert src == "own"
                 seen_own += 1
     assert seen_own == 2  # b0.pw and b2.pw of the MNIST net
+
+
+def test_batch_scaling_is_t1_over_tb():
+    """thr(B) / (B * thr(1)) = t(1) / t(B): a batch of 8 that takes four times
+    one image's time runs at efficiency 0.25 and twice the batch-1 throughput."""
+    r = bench.batch_scaling(70.0, 280.0, 8)
+    assert r["efficiency"] == 0.25 and r["throughput_ratio"] == 2.0
+    res = {"ms_per_forward_graph10": 0.07,
+           "other_workloads": {"detector_b8": {"batch": 8, "us_per_forward_graph10": 280.0},
+                               "mnist_b1": {"batch": 1, "us_per_forward_graph10": 50.0},
+                               "mnist_b256": {"batch": 256, "us_per_forward_graph10": 100.0}}}
+    out = bench.batch_scalings(res)
+    assert out["detector_b8"]["efficiency"] == 0.25
+    assert out["mnist_b256"]["efficiency"] == 0.5 and out["mnist_b256"]["throughput_ratio"] == 128.0
+    assert bench.batch_scalings({}) == {}
