@@ -391,6 +391,33 @@ def _layer_input_shape(wk, i):
 MARKER_KERNEL = "spin_kernel"
 
 
+def forward_launches(wk, plan) -> list:
+    """The forward's launches in order: (layers they compute, joined with '+',
+    kernel), one per plan line that is not merged into a later one."""
+    import re
+    out = []
+    for i, line in enumerate(plan):
+        if line.startswith("merged into"):
+            continue
+        names = [wk.layers[j].name for j in range(len(plan)) if plan[j] == f"merged into {i}"] + [wk.layers[i].name]
+        m = re.search(r"kernel=(cvx::\w+(?:<[^>]*>)?)", line)
+        out.append(("+".join(names), m.group(1) if m else ""))
+    return out
+
+
+def forward_probe(wk, net, x, forwards: int = 20) -> dict:
+    """`forwards` back-to-back forwards right after the per-layer timing's last
+    marker, closed by a marker of their own: in a kernel trace they give each
+    layer's duration inside the forward, beside its duration alone."""
+    import torch
+    from conv2d_batchnorm_activation_amd import cvx
+    for _ in range(forwards):
+        net(x)
+    marker()
+    torch.cuda.synchronize()
+    return {"forwards": forwards, "launches": forward_launches(wk, cvx.cvx_forward_plan(net.arr))}
+
+
 def marker() -> None:
     """A tiny torch spin kernel on the stream: in a kernel trace it separates the
     launches of one layer's timing from the next (see --rocprof-summary)."""
@@ -799,6 +826,32 @@ def rocprof_summary(args) -> int:
     return 0
 
 
+def in_forward_table(probe: dict, seg, alone: dict) -> None:
+    """Each launch of the forward probe (its forwards back to back) against the
+    same layer's hot launches timed alone."""
+    launches = probe["launches"]
+    n = probe["forwards"]
+    print()
+    if len(seg) != n * len(launches) or any(seg[k][0] != launches[k % len(launches)][1] for k in range(len(seg))):
+        print(f"(in-forward table skipped: {len(seg)} launches in the probe, {n} x {len(launches)} expected)")
+        return
+    print(f"Per layer inside the forward ({n} back-to-back forwards, trace durations) against the same "
+          "launch alone (hot graph launches above):")
+    print()
+    print("| layer | kernel | in forward avg us | alone avg us | in forward / alone |")
+    print("|---|---|---|---|---|")
+    tot_in = tot_alone = 0.0
+    for p, (name, kernel) in enumerate(launches):
+        d = [seg[k][1] for k in range(p, len(seg), len(launches))]
+        t = sum(d) / len(d) / 1e3
+        a = alone.get(name)
+        tot_in += t
+        tot_alone += a or 0.0
+        print(f"| {name} | `{kernel}` | {t:.2f} | {a:.2f} | {t / a:.2f} |" if a else
+              f"| {name} | `{kernel}` | {t:.2f} | - | - |")
+    print(f"| sum | | {tot_in:.2f} | {tot_alone:.2f} | {tot_in / tot_alone:.2f} |" if tot_alone else "")
+
+
 def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
     """Per layer of the bench's layer timing (launches between two markers), the
     trace's average kernel duration beside the bench's event time, and the
@@ -816,9 +869,13 @@ def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
         elif cur is not None and name.startswith("cvx::"):
             cur.append((name, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     segs = [sg for sg in segs if sg]
-    if len(segs) != len(layers):
-        print(f"\n(layer agreement skipped: {len(segs)} marked segments, {len(layers)} layers)")
+    probe = res.get("forward_probe")
+    want = len(layers) + (1 if probe else 0)
+    if len(segs) != want:
+        print(f"\n(layer agreement skipped: {len(segs)} marked segments, {want} expected)")
         return
+    probe_seg = segs[len(layers)] if probe else None
+    segs = segs[:len(layers)]
     print()
     print("Per layer of the bench's layer timing (the launches between two markers):")
     print()
@@ -862,6 +919,8 @@ def layer_agreement(tr, bench_json: str, ref_json: str = "") -> None:
             rr = ref.get("roofline") or {}
             print(f"The untraced bench run of the same build: `avg_launch_us` {rr.get('avg_launch_us')} us "
                   f"for `{rr.get('kernel')}` (frac {rr.get('frac')}).")
+    if probe_seg:
+        in_forward_table(probe, probe_seg, avg)
 
 
 def gpu_clocks() -> dict:
@@ -1243,6 +1302,7 @@ def main() -> int:
         f"of ten, cold {cold['mean_us']} us (wall {wall:.3f} s)")
 
     rows = [] if args.no_layers else per_layer(wk, net, counts, args.layer_reps)
+    probe = forward_probe(wk, net, x) if rows else None
     roof = dominant(rows) if rows else None
 
     result = {
@@ -1260,6 +1320,7 @@ def main() -> int:
         "forward_reruns_us": reruns,
         "forward_cold": cold,
         "layer_reps": args.layer_reps,
+        "forward_probe": probe,
         "gpu_clocks": {"start": clocks_start, "end": None},
         "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events, "
                   "with an event after each forward for the spread (forward_spread: mean, p50, "

@@ -74,3 +74,53 @@ def test_layer_agreement_skips_on_count_mismatch(tmp_path, capsys):
     p.write_text(json.dumps({"layers": [{"layer": "a", "us": 1.0}, {"layer": "b", "us": 1.0}]}))
     bench.layer_agreement(tr, str(p))
     assert "layer agreement skipped" in capsys.readouterr().out
+
+
+def test_in_forward_table_from_the_probe_segment(tmp_path, capsys):
+    """A forward probe after the per-layer segments: its launches, in plan
+    order, are averaged per position and set beside each layer's hot launches
+    alone; a probe whose launch count does not match the plan is skipped."""
+    ka = "void cvx::k_stem_pair<2, 2, 3, true>(cvx::StemPairArgs)"
+    kb = "void cvx::k_igemm_packed<3, 1, 1, 1>(cvx::PackedArgs)"
+    spin = "at::cuda::(anonymous namespace)::spin_kernel(long)"
+    t = 0
+    tr = []
+    for k, d in ((ka, 4000), (kb, 2000)):  # the two layers alone: 3 launches each
+        tr.append(_row(spin, t, 10)); t += 20
+        for _ in range(3):
+            tr.append(_row(k, t, d)); t += d + 10
+    tr.append(_row(spin, t, 10)); t += 20  # per-layer timing's last marker: the probe follows
+    for _ in range(2):
+        for k, d in ((ka, 5000), (kb, 3000)):
+            tr.append(_row(k, t, d)); t += d + 10
+    tr.append(_row(spin, t, 10))
+    res = {"layer_reps": 0, "layers": [{"layer": "pre+stem", "us": 4.0}, {"layer": "bridge", "us": 2.0}],
+           "forward_probe": {"forwards": 2, "launches": [["pre+stem", "cvx::k_stem_pair<2, 2, 3, true>"],
+                                                         ["bridge", "cvx::k_igemm_packed<3, 1, 1, 1>"]]}}
+    p = tmp_path / "bench.json"
+    p.write_text(json.dumps(res) + "\n")
+    bench.layer_agreement(tr, str(p))
+    out = capsys.readouterr().out
+    assert "| pre+stem | `cvx::k_stem_pair<2, 2, 3, true>` | 5.00 | 4.00 | 1.25 |" in out
+    assert "| bridge | `cvx::k_igemm_packed<3, 1, 1, 1>` | 3.00 | 2.00 | 1.50 |" in out
+    assert "| sum | | 8.00 | 6.00 | 1.33 |" in out
+    res["forward_probe"]["forwards"] = 3
+    p.write_text(json.dumps(res) + "\n")
+    bench.layer_agreement(tr, str(p))
+    assert "in-forward table skipped" in capsys.readouterr().out
+
+
+def test_forward_launches_follow_the_plan():
+    """One launch per plan line that is not merged into a later one, named by
+    every layer it computes."""
+    class L:
+        def __init__(self, name):
+            self.name = name
+
+    class W:
+        layers = [L("preprocess"), L("stem1"), L("stem2"), L("bridge")]
+
+    plan = ["merged into 2", "merged into 2", "stem_pair k3 s2+s2 kernel=cvx::k_stem_pair<2, 2, 3, true> stem=1",
+            "igemm_packed k3 s2 tile=0 splitk=1 kernel=cvx::k_igemm_packed<3, 1, 1, 1>"]
+    assert bench.forward_launches(W, plan) == [("preprocess+stem1+stem2", "cvx::k_stem_pair<2, 2, 3, true>"),
+                                               ("bridge", "cvx::k_igemm_packed<3, 1, 1, 1>")]
