@@ -14,7 +14,11 @@
 //   1. all eight waves copy the first layer's input window (every channel, the
 //      rows and columns the tile's 3x3 windows of 3x3 windows reach) to LDS
 //      with 16-byte LDS-direct loads; outside the image they read zeros (the
-//      first layer's padding);
+//      first layer's padding).  With U8 the input is a u8 frame instead: the
+//      two frame rows each window row interpolates between are staged, then
+//      resized (half-pixel bilinear) and normalised into the window, so the
+//      normalised image is never written ("A fused Ampere preprocess kernel",
+//      "The theory");
 //   2. all eight waves compute the first layer's 16 output channels over the
 //      region the tile's 3x3 windows cover, on matrix cores
 //      (v_mfma_f32_16x16x4_f32: 16 pixels x 16 channels a block, the taps
