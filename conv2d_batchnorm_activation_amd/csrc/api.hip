@@ -336,6 +336,22 @@ void plan_direct(const ConvGeom& g, Plan* p)
     p->ws_bytes = 0;
 }
 
+// CVX_GEMM1X1=0 never takes the 1x1 GEMM kernel, =1 takes it for every layer
+// it fits (tests and sweeps); unset, for layers with at least kGemm1x1Waves
+// output blocks.
+int gemm1x1_mode()
+{
+    const char* e = getenv("CVX_GEMM1X1");
+    return e == nullptr ? -1 : (e[0] == '1' ? 1 : 0);
+}
+constexpr long kGemm1x1Waves = 1024;
+
+bool gemm1x1_wanted(const ConvGeom& g)
+{
+    const int m = gemm1x1_mode();
+    return m == 1 || (m < 0 && gemm1x1_waves(g) >= kGemm1x1Waves);
+}
+
 cvx_status plan_uncached(const ConvGeom& g, Plan* p)
 {
     *p = Plan{};
@@ -345,6 +361,14 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
     int fk, ft, fs, fp;
     if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs, &fp) && pointwise_fits(g)) {
         p->fam = FAM_POINTWISE;
+        p->ws_bytes = 0;
+        return CVX_OK;
+    }
+    // 1x1 stride-1 layers with enough 32 x 32 output blocks to give every SIMD
+    // one: a wave per block over the whole reduction (a forced packed tile
+    // keeps the packed kernel)
+    if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs, &fp) && gemm1x1_fits(g) && gemm1x1_wanted(g)) {
+        p->fam = FAM_GEMM1X1;
         p->ws_bytes = 0;
         return CVX_OK;
     }
@@ -362,6 +386,7 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
 struct PlanKey {
     ConvGeom g;
     int forced[4];
+    int g1x1;  // CVX_GEMM1X1
     bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
 };
 struct PlanKeyHash {
@@ -383,6 +408,7 @@ cvx_status make_plan(const ConvGeom& g, Plan* p)
     key.g = g;
     key.forced[0] = key.forced[1] = key.forced[2] = key.forced[3] = -1;
     forced_tile(&key.forced[0], &key.forced[1], &key.forced[2], &key.forced[3]);
+    key.g1x1 = gemm1x1_mode();
     {
         std::lock_guard<std::mutex> lock(mu);
         auto it = cache.find(key);
@@ -408,6 +434,7 @@ cvx_status launch_conv(const ConvGeom& g, const Plan& p, const float* x, const f
     case FAM_DIRECT: e = launch_direct(g, p, x, w, scale, bias, res, y, s); break;
     case FAM_IGEMM: e = launch_igemm(g, p, x, w, scale, bias, res, y, ws, s); break;
     case FAM_IGEMM_PACKED: e = launch_igemm_packed(g, p, x, w, scale, bias, res, y, ws, s); break;
+    case FAM_GEMM1X1: e = launch_gemm1x1(g, x, w, scale, bias, res, y, s); break;
     case FAM_POINTWISE:
         if (pointwise_aligned(x, res, y)) {
             e = launch_pointwise(g, x, w, scale, bias, res, y, s);
@@ -434,7 +461,8 @@ size_t elems_packed(const ConvGeom& g)
     ConvGeom gp = g;
     gp.w_layout = CVX_W_PACKED;
     Plan p;
-    if (make_plan(gp, &p) == CVX_OK && (p.fam == FAM_IGEMM_PACKED || p.fam == FAM_POINTWISE))
+    if (make_plan(gp, &p) == CVX_OK &&
+        (p.fam == FAM_IGEMM_PACKED || p.fam == FAM_POINTWISE || p.fam == FAM_GEMM1X1))
         return (size_t)packed_weight_floats(gp);
     return elems_oihw(g);
 }
@@ -463,6 +491,7 @@ static void describe_plan(const ConvGeom& g, const Plan& p, char* buf, int buf_l
         }
         break;
     case FAM_POINTWISE: pointwise_describe(g, nullptr, buf, buf_len); break;
+    case FAM_GEMM1X1: gemm1x1_describe(g, buf, buf_len); break;
     case FAM_DEPTHWISE:
         if (p.dw_toh == -1) {  // named as launched on 16-byte aligned tensors
             const int hw = g.h * g.w;
@@ -577,7 +606,7 @@ cvx_status cvx_pack_weights(const cvx_conv_desc* d, const float* w_oihw, float* 
     gp.w_layout = CVX_W_PACKED;
     Plan pp;
     make_plan(gp, &pp);
-    const bool packed = pp.fam == FAM_IGEMM_PACKED || pp.fam == FAM_POINTWISE;
+    const bool packed = pp.fam == FAM_IGEMM_PACKED || pp.fam == FAM_POINTWISE || pp.fam == FAM_GEMM1X1;
     hipError_t e = packed ? launch_pack_weights(g, w_oihw, w_packed, s)
                                               : launch_copy(w_oihw, w_packed, (long)no, s);
     return e == hipSuccess ? CVX_OK : CVX_ERR_HIP;

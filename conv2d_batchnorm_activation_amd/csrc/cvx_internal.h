@@ -17,6 +17,7 @@ enum Family : int {
     FAM_IGEMM = 2,      // implicit GEMM on fp32 MFMA (dense 1x1 and 3x3), OIHW weights
     FAM_IGEMM_PACKED = 3,  // the same, weights pre-packed in MFMA operand order
     FAM_POINTWISE = 4,  // 1x1 over batches of small planes, whole images per workgroup (packed weights)
+    FAM_GEMM1X1 = 5,    // 1x1 stride 1 as a GEMM per image, a wave per 32x32 block over all of c_in (packed weights)
 };
 
 // Geometry of one convolution, derived from a validated cvx_conv_desc.
@@ -108,6 +109,14 @@ hipError_t launch_pointwise_pair(const ConvGeom& g, const float* x, const float*
                                  const float* scale2, const float* bias2, float* y, hipStream_t s);
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s);
+
+// 1x1 GEMM family (k_gemm1x1.hip): stride 1, no padding, packed 1x1 weights,
+// c_in >= 16.  gemm1x1_waves is the number of 32 x 32 output blocks (one wave each).
+bool gemm1x1_fits(const ConvGeom& g);
+long gemm1x1_waves(const ConvGeom& g);
+void gemm1x1_describe(const ConvGeom& g, char* buf, int len);
+hipError_t launch_gemm1x1(const ConvGeom& g, const float* x, const float* wp, const float* scale,
+                          const float* bias, const float* res, float* y, hipStream_t s);
 
 // Stem pair (k_stem_pair.hip): a k_stem-shaped layer g1 with 16 output channels
 // and no residual, and the packed 3x3 layer g2 that alone reads its output, in

@@ -434,3 +434,28 @@ def test_bf16_rounding_of_the_test_inputs_is_nearest_even():
     got = v.to(torch.bfloat16).to(torch.float32).tolist()
     assert got[:5] == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7, 1.0]
     assert np.isfinite(got[5]) and abs(got[5] - 3.0e38) <= 3.0e38 * 2.0 ** -8  # fp32's range
+
+
+def test_gemm1x1_plan_on_the_host(monkeypatch):
+    """A 1x1 stride-1 layer with packed weights takes the 1x1 GEMM kernel when
+    it has at least 1024 32 x 32 output blocks (the detector's c at batch 8,
+    not at batch 1), always with CVX_GEMM1X1=1 and never with =0; the packed
+    weights are the same size either way (one layout for both kernels)."""
+    P = cvx.CVX_W_PACKED
+    c8 = _desc(n=8, c_in=128, h=40, w=40, c_out=128, k=1, pad=0, w_layout=P)
+    c1 = _desc(n=1, c_in=128, h=40, w=40, c_out=128, k=1, pad=0, w_layout=P)
+    monkeypatch.delenv("CVX_GEMM1X1", raising=False)
+    assert cvx.cvx_conv_plan(c8).startswith("gemm1x1 k1 s1 waves=1600 ")
+    assert cvx.cvx_conv_plan(c1).startswith("igemm_packed")
+    nb = cvx.cvx_packed_weights_bytes(c8)
+    monkeypatch.setenv("CVX_GEMM1X1", "1")
+    assert cvx.cvx_conv_plan(c1).startswith("gemm1x1")
+    assert cvx.cvx_packed_weights_bytes(c1) == nb
+    # 3x3, strided and OIHW layers never take it
+    assert not cvx.cvx_conv_plan(_desc(n=8, w_layout=P)).startswith("gemm1x1")
+    assert not cvx.cvx_conv_plan(_desc(n=8, c_in=128, h=40, w=40, c_out=128, k=1, pad=0, stride=2,
+                                       w_layout=P)).startswith("gemm1x1")
+    assert not cvx.cvx_conv_plan(_desc(n=8, c_in=128, h=40, w=40, c_out=128, k=1, pad=0)).startswith("gemm1x1")
+    monkeypatch.setenv("CVX_GEMM1X1", "0")
+    assert cvx.cvx_conv_plan(c8).startswith("igemm_packed")
+    assert cvx.cvx_packed_weights_bytes(c8) == nb
