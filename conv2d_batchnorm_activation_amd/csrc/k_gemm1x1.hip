@@ -18,7 +18,7 @@
 // are shared through the caches).  Per 16-channel chunk a wave issues four
 // 8-byte weight loads (the packed 1x1 layout of cvx_pack_weights: lane l's
 // values for output channel l%32 and the chunk's eight channel pairs) and
-// eight input loads, four chunks ahead of the matrix instructions; past the
+// eight input loads, two chunks ahead of the matrix instructions; past the
 // last chunk the loads read zeros (out-of-range offsets), which keeps every
 // wait count exact.  Lane l ends with pixel l%32 of output channels
 // 8g + 4*(l/32) + 0..3 (g = 0..3): the epilogue stores 128-byte runs.
@@ -130,12 +130,10 @@ __global__ void __launch_bounds__(kG1Threads) k_gemm1x1(Gemm1x1Args a)
         for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o[q], o[8 + q], acc, 0, 0, 0);
     };
 
-    // epilogue operands, issued behind the first four chunks' loads
-    Ops o0, o1, o2, o3;
+    // epilogue operands, issued behind the first two chunks' loads
+    Ops o0, o1;
     load(0, o0);
     load(1, o1);
-    load(2, o2);
-    load(3, o3);
     const int co0 = 32 * mb + 4 * hi;  // this lane's channels: co0 + 8 g + 0..3
     f32x4 sc[4], bi[4];
     {
@@ -171,17 +169,13 @@ __global__ void __launch_bounds__(kG1Threads) k_gemm1x1(Gemm1x1Args a)
         for (int j = 0; j < 16; ++j) rv[j] = bload(rr, yoff(j));
     }
 
-    // four chunks in flight: a chunk's loads have three chunks' matrix work
-    // (about 1.5k clocks) to land
-    for (int c = 0; c < a.nchunks; c += 4) {
+    // two chunks in flight (four measured no faster: the loads are not what
+    // the loop waits on)
+    for (int c = 0; c < a.nchunks; c += 2) {
         compute(o0);
-        load(c + 4, o0);
+        load(c + 2, o0);
         compute(o1);
-        load(c + 5, o1);
-        compute(o2);
-        load(c + 6, o2);
-        compute(o3);
-        load(c + 7, o3);
+        load(c + 3, o1);
     }
 
     const rsrc_t ry = make_rsrc(a.y, a.y_bytes);
