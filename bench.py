@@ -722,7 +722,8 @@ def pmc_summary(args) -> int:
 def tile_sweep(args) -> int:
     """Every packed tile configuration (kind x tc x split, and the persistent
     form at 256 and 512 workgroups, forced through CVX_IGEMM_TILE) of every
-    dense packed layer of a workload, each timed alone
+    dense packed layer of a workload, and for a 1x1 stride-1 layer the 1x1
+    GEMM kernel (CVX_GEMM1X1=1), each timed alone
     like the per-layer rows (a graph of 20 launches, hot), against the
     planner's own choice.  Prints a markdown table (the per-shape tile choice's
     evidence) and one JSON line per layer."""
@@ -733,7 +734,8 @@ def tile_sweep(args) -> int:
     wk = PMC_WORKLOADS[args.workload][1](wl)
     net = Net(wk.layers, wk.x.shape)
     rows = []
-    print(f"# Tile sweep, {PMC_WORKLOADS[args.workload][0]}: every packed configuration of each dense layer\n")
+    print(f"# Tile sweep, {PMC_WORKLOADS[args.workload][0]}: every packed configuration of each dense layer "
+          "(and the 1x1 GEMM kernel for 1x1 stride-1 layers)\n")
     print(f"Command: {args.cmd}\n")
     print("Each configuration timed alone as a graph of 20 launches on the same buffers (hot), "
           f"{args.layer_reps} launches; `default` is the planner's choice.\n")
@@ -744,7 +746,7 @@ def tile_sweep(args) -> int:
             continue
         d = net.layers[i].conv
         plan0 = cvx.cvx_conv_plan(d)
-        if "igemm_packed" not in plan0:
+        if "igemm_packed" not in plan0 and not plan0.startswith("gemm1x1"):
             continue
         def timed():
             fn, plan, _, _ = layer_setup(wk, net, i, hot_alloc)
@@ -755,6 +757,17 @@ def tile_sweep(args) -> int:
         us0, p0 = timed()
         res = [(us0, p0)]
         seen = {p0}
+        if p0.startswith("igemm_packed k1 s1 "):  # the 1x1 GEMM kernel as an alternative
+            prev = os.environ.get("CVX_GEMM1X1")
+            os.environ["CVX_GEMM1X1"] = "1"
+            p = cvx.cvx_conv_plan(d).split(" kernel")[0]
+            if p.startswith("gemm1x1") and p not in seen:
+                seen.add(p)
+                res.append(timed())
+            if prev is None:
+                os.environ.pop("CVX_GEMM1X1", None)
+            else:
+                os.environ["CVX_GEMM1X1"] = prev
         for kind in range(3):
             for tc in (0, 4, 8, 16, 32, 64, 128):
                 for sk, pe in [(1, 0), (1, 256), (1, 512), (2, 0), (3, 0), (4, 0), (6, 0), (8, 0)]:

@@ -344,7 +344,7 @@ int gemm1x1_mode()
     const char* e = getenv("CVX_GEMM1X1");
     return e == nullptr ? -1 : (e[0] == '1' ? 1 : 0);
 }
-constexpr long kGemm1x1Waves = 1024;
+constexpr long kGemm1x1Waves = 768;  // the detector's c and f at b=8 (1600, 832), not at b=1 (200, 104)
 
 bool gemm1x1_wanted(const ConvGeom& g)
 {
@@ -364,7 +364,7 @@ cvx_status plan_uncached(const ConvGeom& g, Plan* p)
         p->ws_bytes = 0;
         return CVX_OK;
     }
-    // 1x1 stride-1 layers with enough 32 x 32 output blocks to give every SIMD
+    // 1x1 stride-1 layers with enough 32 x 32 output blocks to give most SIMDs
     // one: a wave per block over the whole reduction (a forced packed tile
     // keeps the packed kernel)
     if (g.w_layout == CVX_W_PACKED && !forced_tile(&fk, &ft, &fs, &fp) && gemm1x1_fits(g) && gemm1x1_wanted(g)) {

@@ -438,8 +438,8 @@ def test_bf16_rounding_of_the_test_inputs_is_nearest_even():
 
 def test_gemm1x1_plan_on_the_host(monkeypatch):
     """A 1x1 stride-1 layer with packed weights takes the 1x1 GEMM kernel when
-    it has at least 1024 32 x 32 output blocks (the detector's c at batch 8,
-    not at batch 1), always with CVX_GEMM1X1=1 and never with =0; the packed
+    it has at least 768 32 x 32 output blocks (the detector's c and f at batch
+    8, not at batch 1), always with CVX_GEMM1X1=1 and never with =0; the packed
     weights are the same size either way (one layout for both kernels)."""
     P = cvx.CVX_W_PACKED
     c8 = _desc(n=8, c_in=128, h=40, w=40, c_out=128, k=1, pad=0, w_layout=P)
@@ -447,6 +447,8 @@ def test_gemm1x1_plan_on_the_host(monkeypatch):
     monkeypatch.delenv("CVX_GEMM1X1", raising=False)
     assert cvx.cvx_conv_plan(c8).startswith("gemm1x1 k1 s1 waves=1600 ")
     assert cvx.cvx_conv_plan(c1).startswith("igemm_packed")
+    f8 = _desc(n=8, c_in=256, h=20, w=20, c_out=256, k=1, pad=0, w_layout=P)
+    assert cvx.cvx_conv_plan(f8).startswith("gemm1x1 k1 s1 waves=832 ")
     nb = cvx.cvx_packed_weights_bytes(c8)
     monkeypatch.setenv("CVX_GEMM1X1", "1")
     assert cvx.cvx_conv_plan(c1).startswith("gemm1x1")

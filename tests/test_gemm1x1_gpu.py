@@ -9,7 +9,7 @@ partial channel chunks (c_in not a multiple of 16), c_out not a multiple of
 32 or of 4 (the scale and bias then load one channel at a time), several
 images per launch, every activation and residual placement, and misaligned
 scale and bias; the detector's own 1x1 layers run at batch 1 and 8 (at
-batch 8, c takes the kernel without being forced).
+batch 8 they take the kernel without being forced).
 """
 import numpy as np
 import pytest
@@ -61,13 +61,10 @@ def test_gemm1x1_cases(c, gemm1x1):
     check(y, oracle_conv(x, L, r), f"gemm1x1 case {seed}")
 
 
-@pytest.mark.parametrize("name,default", [("c_128x40_1x1", True), ("f_256x20_1x1", False)])
-def test_gemm1x1_detector_b8_layers(name, default, monkeypatch):
-    """The detector's 1x1 layers at batch 8, on every image: c (1600 output
-    blocks) takes the kernel by default, f (832, under the 1024 the planner
-    asks for) only when forced."""
-    if not default:
-        monkeypatch.setenv("CVX_GEMM1X1", "1")
+@pytest.mark.parametrize("name", ["c_128x40_1x1", "f_256x20_1x1"])
+def test_gemm1x1_detector_b8_layers(name):
+    """The detector's 1x1 layers at batch 8 (1600 and 832 output blocks) take
+    the kernel by default; every image against the oracle."""
     wk = wl.sweep_layer(name, batch=8)
     L = wk.layers[0]
     n, c, h, w = wk.x.shape
