@@ -177,14 +177,16 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
     const int wy0 = S1 * iy0 - 1;            // first window row
 
     // ---- 1. the first layer's input window -> LDS (all waves).  From a u8
-    // frame: the two frame rows each window row interpolates between, over the
-    // window's span of frame columns, go to LDS (16-byte LDS-direct loads),
-    // then are resized and normalised into the window below.
+    // frame: the frame rows the window rows interpolate between (each once,
+    // from the first window row's upper one on), over the window's span of
+    // frame columns, go to LDS (16-byte LDS-direct loads), then are resized
+    // and normalised into the window below.
     const int SRC = 4 * REG;                              // byte offset of the staged frame rows
     int sb0 = 0;                                          // first staged frame byte of a row
     if constexpr (U8) {
         const int x_lo = max(wx0, 0);
         sb0 = (3 * sp_axis(x_lo, a.src_w, a.W1, a.m_dw, a.l_dw, a.inv_dw).i0) & ~15;
+        const int sy0 = sp_axis(max(wy0, 0), a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh).i0;  // first staged row
         const rsrc_t rs = make_rsrc(a.src + (long)b * a.img_bytes, a.img_bytes);
         const int epr = a.SRB >> 4;
         unsigned char* sm = reinterpret_cast<unsigned char*>(smem);
@@ -192,20 +194,19 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
         for (int i = 0; i < kSrcRounds; ++i) {
             if (i >= a.src_rounds) break;
             const int e = tid + kSPThreads * i;
-            const int rr = sp_div(e, a.m_srb, a.l_srb);  // staged row: window row rr/2, its row pair (rr&1)
+            const int rr = sp_div(e, a.m_srb, a.l_srb);  // staged row: frame row sy0 + rr
             const int j = e - rr * epr;
-            const int y = wy0 + (rr >> 1);
-            const bool ok = e < a.src_elems && (unsigned)y < (unsigned)a.H1;
-            const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
-            const int srow = (rr & 1) ? ay.i1 : ay.i0;
+            const int srow = sy0 + rr;
+            const bool ok = e < a.src_elems && srow < a.src_h;
             const unsigned off = ok ? (unsigned)srow * a.row_bytes + (unsigned)(sb0 + 16 * j) : kOOB;
             // lane l of the wave writes 16 bytes at d + 16 l: element e lands at SRC + 16 e
             sp_lds_load16(rs, (__attribute__((address_space(3))) void*)(sm + SRC + 16 * (kSPThreads * i + 64 * wave)), off);
         }
         // while the rows are in flight: the resize's column and row terms, once
         // per window column and row (the interpolation below then looks them
-        // up): column -> {first and second source byte in the staged row,
-        // weight, inside the image}; row -> {weight, inside the image}
+        // up): column -> {first and second source byte in a staged row,
+        // weight, inside the image}; row -> {weight, inside the image, byte
+        // offsets of its two staged rows}
         const int TB = SRC + 16 * kSPThreads * a.src_rounds;
         if (tid < a.WCW) {
             const int x = wx0 + tid;
@@ -218,7 +219,8 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             const int y = wy0 + r;
             const bool ok = (unsigned)y < (unsigned)a.H1;
             const SrcAxis ay = sp_axis(ok ? y : 0, a.src_h, a.H1, a.m_dh, a.l_dh, a.inv_dh);
-            *reinterpret_cast<int2*>(sm + TB + 16 * a.WCW + 8 * r) = int2{__float_as_int(ay.f), ok ? 1 : 0};
+            *reinterpret_cast<int4*>(sm + TB + 16 * a.WCW + 16 * r) =
+                int4{__float_as_int(ay.f), ok ? 1 : 0, ok ? (ay.i0 - sy0) * a.SRB : 0, ok ? (ay.i1 - sy0) * a.SRB : 0};
         }
     } else {
         const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
@@ -315,11 +317,11 @@ __global__ void __launch_bounds__(kSPThreads) k_stem_pair(StemPairArgs a)
             const int r = sp_div(idx, a.m_wcw, a.l_wcw);
             const int col = idx - r * a.WCW;
             const int4 cx = *reinterpret_cast<const int4*>(tb + 16 * col);
-            const int2 cy = *reinterpret_cast<const int2*>(tb + 16 * a.WCW + 8 * r);
+            const int4 cy = *reinterpret_cast<const int4*>(tb + 16 * a.WCW + 16 * r);
             const bool ok = (cx.w & cy.y) != 0;
             const SrcAxis ax{0, 0, __int_as_float(cx.z)}, ay{0, 0, __int_as_float(cy.x)};
-            const unsigned char* r0 = sm + (2 * r) * a.SRB;
-            const unsigned char* r1 = r0 + a.SRB;
+            const unsigned char* r0 = sm + cy.z;
+            const unsigned char* r1 = sm + cy.w;
             const int c0 = ok ? cx.x : 0, c1 = ok ? cx.y : 0;
             // all twelve bytes first: the window stores below could alias them
             // as far as the compiler knows, and would otherwise wait on each
@@ -532,14 +534,27 @@ bool pair_geom(const ConvGeom& g1, const ConvGeom& g2, const StemPrologue* pre, 
             srb = std::max(srb, ((3 * i1 + 3 + 15) & ~15) - b0);
         }
         pg->SRB = srb;
-        pg->src_elems = 2 * pg->WR * (srb / 16);
+        // frame rows a tile's window interpolates between, widest over the
+        // bands of tiles: from the first in-image window row's upper row to the
+        // last one's lower row
+        int nr = 1;
+        const int tiles_h = (g2.oh + pg->tr - 1) / pg->tr;
+        for (int band = 0; band < tiles_h; ++band) {
+            const int wy0 = g1.stride * (band * pg->tr * g2.stride - 1) - 1;
+            const int y_lo = std::max(wy0, 0), y_hi = std::min(wy0 + pg->WR - 1, g1.h - 1);
+            if (y_hi < y_lo) continue;
+            const int r0 = host_axis_i0(y_lo, pre->src_h, g1.h);
+            const int r1 = std::min(host_axis_i0(y_hi, pre->src_h, g1.h) + 1, pre->src_h - 1);
+            nr = std::max(nr, r1 - r0 + 1);
+        }
+        pg->src_elems = nr * (srb / 16);
         pg->src_rounds = (pg->src_elems + kSPThreads - 1) / kSPThreads;
         if (pg->src_rounds > kSrcRounds) return false;
         // the staged frame rows share the region's space (every lane of a
         // round writes its 16 bytes), then the resize's column and row tables
-        // (16 bytes a column, 8 a row, filled by one thread each)
+        // (16 bytes a column or row, filled by one thread each)
         if (pg->WCW + pg->WR > kSPThreads) return false;
-        const size_t src = (size_t)4 * kSPThreads * pg->src_rounds + 4 * pg->WCW + 2 * pg->WR;  // floats
+        const size_t src = (size_t)4 * kSPThreads * pg->src_rounds + 4 * pg->WCW + 4 * pg->WR;  // floats
         total = std::max(win + std::max(region, src), xch);
     }
     pg->lds = total * sizeof(float);
