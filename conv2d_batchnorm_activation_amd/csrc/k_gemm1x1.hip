@@ -14,13 +14,14 @@
 //
 // A wave computes 32 output channels x 32 pixels over the whole reduction, so
 // no partial sums cross waves; a workgroup is four waves, four consecutive
-// 32-pixel blocks of one 32-channel row block (the weights one row block reads
-// are shared through the caches).  Per 16-channel chunk a wave issues four
-// 8-byte weight loads (the packed 1x1 layout of cvx_pack_weights: lane l's
-// values for output channel l%32 and the chunk's eight channel pairs) and
-// eight input loads, two chunks ahead of the matrix instructions; past the
-// last chunk the loads read zeros (out-of-range offsets), which keeps every
-// wait count exact.  Lane l ends with pixel l%32 of output channels
+// 32-pixel blocks of one 32-channel row block, whose weights (c_in up to 256)
+// go to LDS once, with 16-byte LDS-direct loads of the contiguous packed block
+// (the 1x1 layout of cvx_pack_weights, where lane l's values for output
+// channel l%32 and a chunk's eight channel pairs are four 8-byte pieces).  Per
+// 16-channel chunk a wave issues eight input loads, two chunks ahead of the
+// matrix instructions, and reads the chunk's weights from LDS; past the last
+// chunk the loads read zeros (out-of-range offsets), which keeps every wait
+// count exact.  Lane l ends with pixel l%32 of output channels
 // 8g + 4*(l/32) + 0..3 (g = 0..3): the epilogue stores 128-byte runs.
 #include <stdio.h>
 
@@ -39,6 +40,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kG1Threads = 256;  // four waves
 constexpr int kG1Ch = 16;        // input channels per chunk
 constexpr int kG1WF = 512;       // packed weight floats per (32-row block, chunk)
+constexpr int kG1MaxChunks = 16;  // c_in <= 256: a row block's weights, 32 KB, in LDS
+constexpr int kG1MaxWRounds = kG1MaxChunks / 2;  // 256-lane rounds of 16-byte pieces
 
 __device__ __forceinline__ int g1div(int n, unsigned m, unsigned l)
 {
@@ -61,7 +64,8 @@ struct Gemm1x1Args {
     int total_pblocks;    // n * pblocks
     unsigned m_pb, l_pb;  // divide by pblocks
     unsigned m_mb, l_mb;  // divide by mblocks
-    unsigned x_bytes, y_bytes, wp_bytes;
+    unsigned x_bytes, y_bytes;
+    int wrounds;          // rounds of the weights' LDS-direct copy: ceil(nchunks / 2)
     int vsb;              // scale and bias 16-byte aligned (four channels a load)
     int act, res_mode;
 };
@@ -87,53 +91,74 @@ __global__ void __launch_bounds__(kG1Threads) k_gemm1x1(Gemm1x1Args a)
         mb = L - pg * a.mblocks;
     }
     const int pbk = 4 * pg + wave;                // this wave's 32-pixel block
-    if (pbk >= a.total_pblocks) return;           // no barriers: a wave may leave
-    const int img = g1div(pbk, a.m_pb, a.l_pb);
+    const bool live = pbk < a.total_pblocks;      // past the end: loads read nothing, and the
+                                                  // wave leaves after the barrier
+    const int img = live ? g1div(pbk, a.m_pb, a.l_pb) : 0;
     const int p = 32 * (pbk - img * a.pblocks) + l32;
-    const bool p_ok = p < a.hw;
+    const bool p_ok = live && p < a.hw;
+
+    // The row block's weights, every chunk, go to LDS once for the four waves
+    // (16-byte LDS-direct loads of the contiguous packed block: chunk c at
+    // float 512 c, lane l's pairs (2h, 2h+1) at + 128 h + 2 l).
+    extern __shared__ __attribute__((aligned(16))) float wl[];
+    {
+        const rsrc_t rw = make_rsrc(a.wp + (long)mb * a.nchunks * kG1WF, 4u * (unsigned)(a.nchunks * kG1WF));
+        const int pieces = a.nchunks * (kG1WF / 4);
+#pragma unroll
+        for (int i = 0; i < kG1MaxWRounds; ++i) {
+            if (i >= a.wrounds) break;
+            const int e = threadIdx.x + kG1Threads * i;
+            const unsigned off = e < pieces ? 16u * (unsigned)e : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(wl + 4 * (kG1Threads * i + 64 * wave)), 16, off, 0,
+                0, 0);
+        }
+    }
 
     // input: channel ci of this lane's pixel at ((img * cin + ci) * hw + p) * 4
     const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
     const unsigned xrow = 4u * (unsigned)a.hw;
     const unsigned xbase = p_ok ? 4u * (unsigned)(img * a.cin * a.hw + p) + (unsigned)hi * xrow : kOOB;
-    // weights: chunk c of row block mb at float (mb * nchunks + c) * 512, lane l's
-    // pairs (2h, 2h+1) at + 128 h + 2 l
-    const rsrc_t rw = make_rsrc(a.wp, a.wp_bytes);
-    const unsigned wbase = 4u * (unsigned)(mb * a.nchunks * kG1WF) + 8u * (unsigned)lane;
-
     // Out-of-range offsets are formed by setting bit 31 (every offset in range
     // is below 2^31), not by selects: the compiler turns a select on the
     // uniform chunk test into branches that wait for all loads in flight.
-    typedef float Ops[16];  // [0..7]: weights of pairs 0..7, [8..15]: inputs of pairs 0..7
+    typedef float Ops[8];  // inputs of the chunk's pairs 0..7
     auto load = [&](int c, Ops& o) {
         const unsigned dead = (unsigned)(c >= a.nchunks) << 31;
-        const unsigned wo = (wbase + 4u * (unsigned)(c * kG1WF)) | dead;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const f32x2 v = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(wo + 512u * h), 0, 0));
-            o[2 * h] = v[0];
-            o[2 * h + 1] = v[1];
-        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int ci = kG1Ch * c + 2 * q + hi;
             const unsigned xo = (xbase + (unsigned)(kG1Ch * c + 2 * q) * xrow) | dead |
                                 ((unsigned)(ci >= a.cin) << 31);
-            o[8 + q] = bload(rx, xo);
+            o[q] = bload(rx, xo);
         }
     };
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    auto compute = [&](const Ops& o) {
+    // chunk c's weights from LDS (a chunk past the end reads the last chunk's,
+    // against zero inputs)
+    auto compute = [&](int c, const Ops& o) {
+        const float* wc = wl + kG1WF * min(c, a.nchunks - 1) + 2 * lane;
+        float wv[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o[q], o[8 + q], acc, 0, 0, 0);
+        for (int h = 0; h < 4; ++h) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(wc + 128 * h);
+            wv[2 * h] = v[0];
+            wv[2 * h + 1] = v[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[q], o[q], acc, 0, 0, 0);
     };
 
-    // epilogue operands, issued behind the first two chunks' loads
+    // the first two chunks' inputs go out behind the weights; the weights are
+    // waited for (the inputs stay in flight), then the epilogue operands
     Ops o0, o1;
     load(0, o0);
     load(1, o1);
+    wait_vm_at_most(16);
+    lds_barrier();
+    if (!live) return;
     const int co0 = 32 * mb + 4 * hi;  // this lane's channels: co0 + 8 g + 0..3
     f32x4 sc[4], bi[4];
     {
@@ -172,9 +197,9 @@ __global__ void __launch_bounds__(kG1Threads) k_gemm1x1(Gemm1x1Args a)
     // two chunks in flight (four measured no faster: the loads are not what
     // the loop waits on)
     for (int c = 0; c < a.nchunks; c += 2) {
-        compute(o0);
+        compute(c, o0);
         load(c + 2, o0);
-        compute(o1);
+        compute(c + 1, o1);
         load(c + 3, o1);
     }
 
@@ -195,7 +220,7 @@ void fastdiv_params(int d, unsigned* m, unsigned* l);
 bool gemm1x1_fits(const ConvGeom& g)
 {
     if (g.groups != 1 || g.k != 1 || g.stride != 1 || g.pad != 0 || g.w_layout != CVX_W_PACKED) return false;
-    if (g.cin < 16) return false;
+    if (g.cin < 16 || (g.cin + kG1Ch - 1) / kG1Ch > kG1MaxChunks) return false;
     const long hw = (long)g.h * g.w;
     const long xb = (long)g.n * g.cin * hw * 4, yb = (long)g.n * g.cout * hw * 4;
     return xb < 0x7fffffffL && yb < 0x7fffffffL && packed_weight_floats(g) * 4 < 0x7fffffffL &&
@@ -236,7 +261,7 @@ hipError_t launch_gemm1x1(const ConvGeom& g, const float* x, const float* wp, co
     fastdiv_params(a.mblocks, &a.m_mb, &a.l_mb);
     a.x_bytes = (unsigned)((long)g.n * g.cin * a.hw * 4);
     a.y_bytes = (unsigned)((long)g.n * g.cout * a.hw * 4);
-    a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+    a.wrounds = (a.nchunks + 1) / 2;
     a.vsb = (reinterpret_cast<uintptr_t>(scale) & 15u) == 0 && (reinterpret_cast<uintptr_t>(bias) & 15u) == 0 &&
                     g.cout % 4 == 0
                 ? 1
@@ -246,7 +271,8 @@ hipError_t launch_gemm1x1(const ConvGeom& g, const float* x, const float* wp, co
     const long groups = ((long)a.total_pblocks + 3) / 4;
     const long wgs = groups * a.mblocks;
     if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gemm1x1, dim3((unsigned)wgs), dim3(kG1Threads), 0, s, a);
+    const size_t lds = (size_t)a.wrounds * kG1Threads * 16;
+    hipLaunchKernelGGL(k_gemm1x1, dim3((unsigned)wgs), dim3(kG1Threads), lds, s, a);
     return hipGetLastError();
 }
 
