@@ -768,7 +768,7 @@ def tile_sweep(args) -> int:
                 os.environ.pop("CVX_GEMM1X1", None)
             else:
                 os.environ["CVX_GEMM1X1"] = prev
-        for kind in range(3):
+        for kind in range(4):  # 32 x 32, 64, 128 pixels, and the 16-pixel tile
             for tc in (0, 4, 8, 16, 32, 64, 128):
                 for sk, pe in [(1, 0), (1, 256), (1, 512), (2, 0), (3, 0), (4, 0), (6, 0), (8, 0)]:
                     os.environ["CVX_IGEMM_TILE"] = f"{kind},{tc},{sk},{pe}"

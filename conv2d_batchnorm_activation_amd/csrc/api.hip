@@ -172,8 +172,8 @@ constexpr TileEntry kTileTable[] = {
     {1, 16, 320, 320, 32, 3, 2, 1, 1, 16, 1},   // stem2  7.70 -> 7.33 us (when not paired with stem1)
     {1, 64, 80, 80, 128, 3, 2, 1, 0, 16, 1},    // b      6.21 -> 6.07
     {1, 128, 40, 40, 128, 3, 1, 1, 0, 8, 1},    // d      8.66 -> 8.35
-    {1, 128, 40, 40, 256, 3, 2, 1, 0, 8, 2},    // e      8.40 -> 7.76 (slices meeting in one XCD's L2)
-    {1, 256, 20, 20, 256, 3, 1, 1, 0, 0, 2},    // g     10.79 -> 10.39
+    {1, 128, 40, 40, 256, 3, 2, 1, 3, 8, 1},    // e      7.88 -> 6.85 (16-pixel tile; 32x32 needed a split)
+    {1, 256, 20, 20, 256, 3, 1, 1, 3, 0, 1},    // g     10.23 -> 9.31 (16-pixel tile; 32x32 needed a split)
     // batch 8
     {8, 16, 320, 320, 32, 3, 2, 1, 0, 16, 1},   // stem2 40.38 -> 37.07 (when not paired with stem1)
     {8, 32, 160, 160, 64, 3, 2, 1, 0, 16, 1},   // bridge 30.87 -> 29.99
@@ -198,10 +198,10 @@ const TileEntry* table_tile(const ConvGeom& g)
 // set-up, the cross-wave exchange and the epilogue) plus its first stage's loads,
 // which nothing overlaps; after that the producers load stage s+1 while the
 // consumers compute stage s, so a stage costs the larger of its matrix time
-// (2 pairs x taps x NT x 64 clocks per SIMD and chunk) and its load time
-// (~30 clocks per vector-memory instruction the unit issues), plus a barrier.
-// A split into s slices adds ~4000 + 800*NT*s clocks (the partial sums' round
-// trip through memory and the arrival count).  Up to packed_occupancy(kind)
+// (taps x 64 clocks per SIMD and chunk for every 16 pixels of the tile) and
+// its load time (~30 clocks per vector-memory instruction the unit issues),
+// plus a barrier.  A split into s slices adds ~4000 + 800*s*(tile pixels / 32)
+// clocks (the partial sums' round trip through memory and the arrival count).  Up to packed_occupancy(kind)
 // workgroups share a compute unit, each slowing the others by ~30%.
 // `max_split` bounds the split (1 when no workspace is at hand).
 bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8, int only_kind = -1)
@@ -218,7 +218,7 @@ bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8, int only_kind = 
     for (int kind = 0; kind < packed_num_kinds(); ++kind) {
         if (only_kind >= 0 && kind != only_kind) continue;
         const int bn = packed_tile_n(kind);
-        const int nt = bn / 32;
+        const double nt = bn / 32.0;
         const int cps = packed_chunks_per_stage(kind, g.k);
         for (int tc = bn; tc >= 0; tc = tc > 4 ? tc / 2 : tc - 4) {
             size_t lds = 0;
@@ -226,7 +226,7 @@ bool plan_packed(const ConvGeom& g, Plan* p, int max_split = 8, int only_kind = 
             const int occ = std::max(1, std::min<int>(packed_occupancy(kind, g.k),
                                                       (int)(kMaxLdsBytes / std::max<size_t>(lds, 1))));
             const double loads = cps * kLoadClk * packed_loads_per_chunk(g, kind, tc);
-            const double stage = std::max(cps * 2.0 * kk * nt * 64.0, loads) + kBarrierClk;
+            const double stage = std::max(cps * kk * 64.0 * (bn / 16), loads) + kBarrierClk;
             const long tiles = (long)g.n * packed_tiles_per_image(g, kind, tc) * mblocks;
             for (int sk = 1; sk <= max_split; ++sk) {
                 if (!slices_ok(nchunks, sk)) continue;

@@ -37,6 +37,16 @@
 // consecutive pixels of one output channel: the exchange and the epilogue move
 // them 16 bytes at a time.
 //
+// The 16-pixel tile (NT = 0, 3x3 only) halves a workgroup's work for layers
+// whose 32-pixel tiles number fewer than the compute units, which would
+// otherwise split the reduction and pay its partial-sum round trip.  It runs
+// on v_mfma_f32_16x16x4_f32 (half the work of the 32x32x2 instruction in half
+// the clocks): consumer wave h takes channels 4h..4h+3 of every chunk (A lane
+// l: pixel l%16, channel 4h + l/16) and issues two instructions per tap, one
+// per half of the 32 output channels (B lane l: channel 16*half + l%16), two
+// chunks to a stage.  Its weights are a second copy of the block in that lane
+// order, stored after the first.
+//
 // Layouts:
 //   * packed weights: [32-row block][16-channel chunk][pair of channel pairs h
 //     (4)][slot (5)][lane][4] for 3x3 -- lane l holds output channel
@@ -44,7 +54,9 @@
 //     per pair) in five 16-byte slots; [block][chunk][h][lane][2] for 1x1.
 //     A (block, chunk) is one contiguous run of 20 KB (3x3) or 2 KB (1x1);
 //     consumer wave h reads its quarter straight into registers, already in
-//     the operand's lane order.  ("YOLO26N Inference Optimisation", "NHWC
+//     the operand's lane order.  3x3 weights then repeat in the 16-pixel
+//     tile's order: same shape, lane l holding output channel 32*block +
+//     16*half + l%16 and input channel 4h + l/16, its 18 values 9*half + tap.  ("YOLO26N Inference Optimisation", "NHWC
 //     migration", "Weight layout": weights are reordered once for the layout
 //     the kernels read.)
 //   * inputs: 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
@@ -136,7 +148,10 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     constexpr int NR = VEC ? kRoundsVec : kRoundsScalar;
     constexpr int KK = K * K;
     constexpr int G = VEC ? 4 : 1;     // floats per staged element
-    constexpr int BN = 32 * NT;
+    constexpr bool H16 = NT == 0;      // the 16-pixel tile
+    static_assert(!H16 || (K == 3 && CPS % 2 == 0), "16-pixel tile: 3x3, chunks in pairs");
+    constexpr int NB = H16 ? 1 : NT;   // input operands a lane reads per tap
+    constexpr int BN = H16 ? 16 : 32 * NT;
     constexpr int PITCH = BN + (NT < 4 ? 4 : 0);  // LDS row pitch of the partial-sum exchange
     constexpr int WF = K == 3 ? kBCFloats3 : kBCFloats1;  // weight floats per chunk
 
@@ -313,15 +328,17 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     const int erow = 8 * wave + (lane >> 3);
     const int eco = co0 + erow;
     const bool row_ok = eco < a.cout;
+    // the 16-pixel tile's rows have four quads: lanes 8i+4..8i+7 hold none
+    const bool quad_ok = !H16 || (lane & 7) < 4;
     const bool single = a.partial == nullptr;
     float sc = 0.0f, bi = 0.0f;
 
     // LDS offset of each of this lane's pixels (tap 0) in a staged channel
     const int RS = a.PR * a.PCW;  // LDS floats per staged channel
-    int loff[NT];
+    int loff[NB];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int j = nt * 32 + l32;
+    for (int nt = 0; nt < NB; ++nt) {
+        const int j = H16 ? (lane & 15) : nt * 32 + l32;
         int oh, ow;
         if (a.tc == 0) {
             const int qc = min(q0 + j, q_end - 1);
@@ -335,11 +352,15 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         loff[nt] = (oh - oh_ref) * a.stride * a.PCW + ow * a.stride - a.pad - gx0;
     }
 
-    f32x16 acc[NT];
+    // 32x32 blocks: one accumulator per pixel block; 16-pixel tile: one per
+    // half of the output channels
+    typedef typename std::conditional<H16, f32x4, f32x16>::type AccT;
+    constexpr int NACC = H16 ? 2 : NT;
+    AccT acc[NACC];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int i = 0; i < NACC; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+        for (int r = 0; r < (H16 ? 4 : 16); ++r) acc[i][r] = 0.0f;
 
     // Matrix work, pair by pair: for each chunk, this wave's weights (its
     // h = wave block of the chunk) and, for each of its two channel pairs, KK
@@ -375,22 +396,24 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
             }
         }
     };
-    auto read_b = [&](int sb, int q, float (&bv)[KK][NT]) {
-        const int j = q >> 1, pp = q & 1;
+    // Input operands of step q of a stage: a channel pair (q/2 = chunk, q%2 =
+    // pair) or, for the 16-pixel tile, a chunk (this wave's four channels).
+    auto read_b = [&](int sb, int q, float (&bv)[KK][NB]) {
         // formed here: hoisting these addresses would hold one register per
         // (chunk, pair, buffer)
-        int base = sb + j * CHF + (2 * (2 * wave + pp) + hi) * RS;
+        int base = H16 ? sb + q * CHF + (4 * wave + (lane >> 4)) * RS
+                       : sb + (q >> 1) * CHF + (2 * (2 * wave + (q & 1)) + hi) * RS;
         asm volatile("" : "+v"(base));
         const float* xa = smem + base;
 #pragma unroll
         for (int tap = 0; tap < KK; ++tap) {
             const int toff = (tap / K) * a.PCW + (tap % K);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
+            for (int nt = 0; nt < NB; ++nt) bv[tap][nt] = xa[loff[nt] + toff];
         }
     };
-    constexpr int NQ = CPS * 2;
-    float b0[KK][NT], b1[KK][NT];
+    constexpr int NQ = H16 ? CPS : CPS * 2;
+    float b0[KK][NB], b1[KK][NB];
     AT a0[CPS], a1[CPS];
     // One stage at buffer `sb`, the next stage's at `nsb` (when `more`), with
     // weight registers `ac`; once its matrix instructions are issued those
@@ -399,20 +422,28 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     auto stage = [&](int st, AT (&ac)[CPS], int sb, int nsb, bool more) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            float (&cur)[KK][NT] = (q & 1) ? b1 : b0;
-            float (&nxt)[KK][NT] = (q & 1) ? b0 : b1;
-            const int j = q >> 1, pp = q & 1;
+            float (&cur)[KK][NB] = (q & 1) ? b1 : b0;
+            float (&nxt)[KK][NB] = (q & 1) ? b0 : b1;
             if (q + 1 < NQ)
                 read_b(sb, q + 1, nxt);
             else if (more)
                 read_b(nsb, 0, nxt);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (H16) {
 #pragma unroll
-            for (int tap = 0; tap < KK; ++tap) {
-                const float wv = ac[j][K == 3 ? 9 * pp + tap : pp];
+                for (int tap = 0; tap < KK; ++tap) {
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][tap], acc[0], 0, 0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][9 + tap], acc[1], 0, 0, 0);
+                }
+            } else {
+                const int j = q >> 1, pp = q & 1;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[tap][nt], wv, acc[nt], 0, 0, 0);
+                for (int tap = 0; tap < KK; ++tap) {
+                    const float wv = ac[j][K == 3 ? 9 * pp + tap : pp];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[tap][nt], wv, acc[nt], 0, 0, 0);
+                }
             }
         }
         load_a(st + 2, ac);  // past the end: zeros, issued anyway (keeps wait counts exact)
@@ -426,15 +457,15 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     const unsigned out_bytes = 4u * (unsigned)(a.n * a.cout * OHW);
     auto at = [&](int k, int e) {
         const int p = 32 * k + 4 * (lane & 7) + e;
-        bool ok;
+        bool ok = quad_ok;
         int q;
         if (a.tc == 0) {
             q = q0 + p;
-            ok = q < q_end;
+            ok = ok && q < q_end;
         } else {
             const int jr = pdiv(p, a.m_tc, a.l_tc);
             const int oh = oh_ref + jr, ow = q0 + (p - jr * a.tc);
-            ok = oh < a.OH && ow < a.OW;
+            ok = ok && oh < a.OH && ow < a.OW;
             q = oh * a.OW + ow;
         }
         return ok && row_ok ? (unsigned)(b * a.cout + eco) * plane_b + 4u * (unsigned)q : kOOB;
@@ -461,15 +492,15 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
             }
         }
     };
-    f32x4 rv[NT];
+    f32x4 rv[NB];
 #pragma unroll
-    for (int k = 0; k < NT; ++k) rv[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < NB; ++k) rv[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const bool want_res = a.res_mode != CVX_RES_NONE;
     // without a residual the descriptor is empty and the loads return zeros
     auto load_res = [&]() {
         const rsrc_t rr = make_rsrc(a.res, want_res ? out_bytes : 0u);
 #pragma unroll
-        for (int k = 0; k < NT; ++k) rv[k] = load_quad(rr, k);
+        for (int k = 0; k < NB; ++k) rv[k] = load_quad(rr, k);
     };
 
     // Barrier s: the producers have landed stage s+1, this wave has finished
@@ -511,8 +542,13 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     // BN x 32 tile as [channel][pixel], then wave w sums channels 8w..8w+7 of the
     // four tiles in wave order.  Lane (hi, l32) holds channel l32 and the pixel
     // runs 32*nt + 8*g + 4*hi + 0..3, g = 0..3.
+    // (16-pixel tile: lane l holds channels 16*half + l%16, pixels 4*(l/16) + 0..3.)
     __syncthreads();
-    {
+    if constexpr (H16) {
+        float* red = smem + wave * 32 * PITCH + (lane & 15) * PITCH + 4 * (lane >> 4);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) *reinterpret_cast<f32x4*>(red + 16 * PITCH * half) = acc[half];
+    } else {
         float* red = smem + wave * 32 * PITCH + l32 * PITCH + 4 * hi;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -522,10 +558,11 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
                     f32x4{acc[nt][4 * g], acc[nt][4 * g + 1], acc[nt][4 * g + 2], acc[nt][4 * g + 3]};
     }
     __syncthreads();
-    f32x4 v[NT];
+    f32x4 v[NB];
 #pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        const int off = erow * PITCH + 32 * k + 4 * (lane & 7);
+    for (int k = 0; k < NB; ++k) {
+        // (lanes without a quad read their neighbour's: inside the row, unused)
+        const int off = erow * PITCH + 32 * k + 4 * (lane & (H16 ? 3 : 7));
         v[k] = *reinterpret_cast<const f32x4*>(smem + off);
 #pragma unroll
         for (int s = 1; s < 4; ++s) v[k] += *reinterpret_cast<const f32x4*>(smem + s * 32 * PITCH + off);
@@ -548,12 +585,13 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         constexpr int SF = 32 * BN;  // floats of one slice of a tile
         const long tix = (long)(mb * a.n + b) * a.tiles_per_img + tile;
         float* const tp = a.partial + tix * a.splits * SF;
-        const int pofs = 4 * (erow * BN + 4 * (lane & 7));  // + 128 bytes per quad k
+        // + 128 bytes per quad k; lanes without a quad store and load nothing
+        const int pofs = quad_ok ? 4 * (erow * BN + 4 * (lane & 7)) : 4 * SF;
         const bool dev = !a.xsplit;
         {
             const rsrc_t rps = make_rsrc(tp + (long)sp * SF, 4u * SF);
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
+            for (int k = 0; k < NB; ++k) {
                 const u32x4 q = __builtin_bit_cast(u32x4, v[k]);
                 if (dev)
                     __builtin_amdgcn_raw_buffer_store_b128(q, rps, pofs + 128 * k, 0, kSC1);
@@ -590,13 +628,13 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
         }
         __syncthreads();
         if (!s_last) return;
-        f32x4 tot[NT];
+        f32x4 tot[NB];
 #pragma unroll
-        for (int k = 0; k < NT; ++k) tot[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = 0; k < NB; ++k) tot[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int s = 0; s < a.splits; ++s) {
             const rsrc_t rps = make_rsrc(tp + (long)s * SF, 4u * SF);
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
+            for (int k = 0; k < NB; ++k) {
                 f32x4 q;
                 if (s == sp)
                     q = v[k];
@@ -608,12 +646,12 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
             }
         }
 #pragma unroll
-        for (int k = 0; k < NT; ++k) v[k] = tot[k];
+        for (int k = 0; k < NB; ++k) v[k] = tot[k];
     }
 
     const rsrc_t ry = make_rsrc(a.y, out_bytes);
 #pragma unroll
-    for (int k = 0; k < NT; ++k) {
+    for (int k = 0; k < NB; ++k) {
         f32x4 z;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1047,13 +1085,16 @@ __global__ void __launch_bounds__(kThreads) k_igemm_persist(PackedArgs a)
 }
 
 // One-time weight transform, OIHW -> the packed order above; zero where the row,
-// channel or tap does not exist.
+// channel or tap does not exist.  3x3: `copy` floats in the 32x32 blocks' lane
+// order, then as many in the 16-pixel tile's.
 __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ w, int cout, int cin,
-                                                      int k, int nchunks, long total,
+                                                      int k, int nchunks, long copy, long total,
                                                       float* __restrict__ wp)
 {
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
+    const long at = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (at >= total) return;
+    const bool h16 = at >= copy;
+    const long idx = h16 ? at - copy : at;
     int co, ci, tap = 0;
     bool live = true;
     if (k == 3) {
@@ -1066,12 +1107,17 @@ __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ 
         const long g3 = g2 >> 2;
         const int chunk = (int)(g3 % nchunks);
         const int blk = (int)(g3 / nchunks);
-        const int f = 4 * slot + j;  // 0..19: 9*(pair within h) + tap; 18 and 19 unused
+        const int f = 4 * slot + j;  // 0..19: 9*(pair within h, or half) + tap; 18 and 19 unused
         live = f < 18;
         const int pp = f / 9;
         tap = f - 9 * pp;
-        co = blk * 32 + (lane & 31);
-        ci = chunk * kCh + 2 * (2 * h + pp) + (lane >> 5);
+        if (h16) {
+            co = blk * 32 + 16 * pp + (lane & 15);
+            ci = chunk * kCh + 4 * h + (lane >> 4);
+        } else {
+            co = blk * 32 + (lane & 31);
+            ci = chunk * kCh + 2 * (2 * h + pp) + (lane >> 5);
+        }
     } else {
         const int j = (int)(idx & 1);
         const int lane = (int)((idx >> 1) & 63);
@@ -1085,35 +1131,39 @@ __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ 
     }
     float v = 0.0f;
     if (live && co < cout && ci < cin) v = w[((long)co * cin + ci) * (k * k) + tap];
-    wp[idx] = v;
+    wp[at] = v;
 }
 
 // ------------------------------------------------------------------ host side
 // Compiled configurations: NT pixel blocks per wave, and chunks per pipeline
-// stage for 3x3 and 1x1.  The tile is 32 x 32*NT.
+// stage for 3x3 and 1x1.  The tile is 32 x 32*NT; NT = 0 is the 16-pixel tile
+// (3x3 only).
 struct PackedKind {
     int nt, cps3, cps1;
 };
-static constexpr PackedKind kPacked[] = {{1, 1, 4}, {2, 1, 4}, {4, 1, 2}};
+static constexpr PackedKind kPacked[] = {{1, 1, 4}, {2, 1, 4}, {4, 1, 2}, {0, 2, 0}};
 constexpr int kNumPacked = sizeof(kPacked) / sizeof(kPacked[0]);
 
 int packed_num_kinds() { return kNumPacked; }
 int packed_chunks_per_stage(int kind, int k) { return k == 3 ? kPacked[kind].cps3 : kPacked[kind].cps1; }
-int packed_tile_n(int kind) { return 32 * kPacked[kind].nt; }
+int packed_tile_n(int kind) { return kPacked[kind].nt > 0 ? 32 * kPacked[kind].nt : 16; }
 
-long packed_weight_floats(const ConvGeom& g)
+// One copy of the packed weights (one lane order)
+static long packed_copy_floats(const ConvGeom& g)
 {
     const long blocks = (g.cout + 31) / 32;
     const long nchunks = (g.cin + kCh - 1) / kCh;
     return blocks * nchunks * (g.k == 3 ? kBCFloats3 : kBCFloats1);
 }
 
+long packed_weight_floats(const ConvGeom& g) { return (g.k == 3 ? 2 : 1) * packed_copy_floats(g); }
+
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s)
 {
     const long total = packed_weight_floats(g);
     dim3 grid((unsigned)((total + 255) / 256));
     hipLaunchKernelGGL(k_pack_weights, grid, dim3(256), 0, s, w, g.cout, g.cin, g.k,
-                       (g.cin + kCh - 1) / kCh, total, wp);
+                       (g.cin + kCh - 1) / kCh, packed_copy_floats(g), total, wp);
     return hipGetLastError();
 }
 
@@ -1187,7 +1237,7 @@ static size_t packed_lds(const ConvGeom& g, int kind, const Region& r)
 {
     const int nt = kPacked[kind].nt;
     const size_t stage = 3 * (size_t)packed_chunks_per_stage(kind, g.k) * r.rep * sizeof(float);
-    const size_t red = (size_t)4 * 32 * (32 * nt + (nt < 4 ? 4 : 0)) * sizeof(float);
+    const size_t red = (size_t)4 * 32 * (packed_tile_n(kind) + (nt < 4 ? 4 : 0)) * sizeof(float);
     return stage > red ? stage : red;
 }
 
@@ -1207,7 +1257,7 @@ long packed_num_tiles(const ConvGeom& g, int kind, int tc)
 bool packed_persist_fits(const ConvGeom& g, int kind, int tc, int wgs)
 {
     // tiles of 32 or 64 pixels (at 128 the compiler keeps the accumulators in scratch)
-    if (kind < 0 || kind >= kNumPacked || kPacked[kind].nt > 2) return false;
+    if (kind < 0 || kind >= kNumPacked || kPacked[kind].nt > 2 || kPacked[kind].nt < 1) return false;
     if (!packed_tile_fits(g, kind, tc, nullptr)) return false;
     if (g.w % 4 != 0) return false;  // 16-byte staging only
     const int cps = packed_chunks_per_stage(kind, g.k);
@@ -1222,6 +1272,7 @@ bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
 {
     if (kind < 0 || kind >= kNumPacked) return false;
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
+    if (packed_chunks_per_stage(kind, g.k) == 0) return false;  // the 16-pixel tile: 3x3 only
     const int bn = packed_tile_n(kind);
     if (tc < 0 || (tc > 0 && (tc > bn || bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
     const long lim = 0x7fffffffL;
@@ -1263,9 +1314,9 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
 // two (LDS).
 int packed_occupancy(int kind, int k)
 {
-    static constexpr int kRegs[2][kNumPacked] = {{56, 81, 123},    // 1x1: NT = 1, 2, 4
-                                                 {87, 127, 207}};  // 3x3
-    const int regs = kRegs[k == 3 ? 1 : 0][kind];
+    static constexpr int kRegs[2][kNumPacked] = {{56, 81, 123, 0},     // 1x1: NT = 1, 2, 4 (no 16-pixel tile)
+                                                 {87, 127, 207, 118}};  // 3x3, and the 16-pixel tile
+    const int regs = std::max(1, kRegs[k == 3 ? 1 : 0][kind]);
     const int occ = 512 / regs / 2;
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;
 }
@@ -1286,7 +1337,7 @@ int packed_persist_capacity(const ConvGeom& g, int kind, int tc)
     // gfx950 (1x1: NT = 1, 2; 3x3: NT = 1, 2); two waves per SIMD per workgroup
     static constexpr int kRegs[2][2] = {{71, 113}, {106, 160}};
     const int nt = kPacked[kind].nt;
-    if (nt > 2) return 0;
+    if (nt > 2 || nt < 1) return 0;
     const Region r = packed_region(g, kind, tc, true);
     const size_t lds = packed_persist_lds(g, kind, r) + 256;
     int occ = 512 / kRegs[g.k == 3 ? 1 : 0][nt - 1] / 2;
@@ -1333,16 +1384,18 @@ static void launch_packed_kind(bool vec, bool persist, dim3 grid, size_t lds, hi
 {
     constexpr PackedKind t = kPacked[KIND];
     constexpr int cps = K == 3 ? t.cps3 : t.cps1;
-    if constexpr (t.nt <= 2) {
-        if (persist) {
-            hipLaunchKernelGGL((k_igemm_persist<K, t.nt, cps>), grid, dim3(kThreads), lds, s, a);
-            return;
+    if constexpr (cps > 0) {
+        if constexpr (t.nt >= 1 && t.nt <= 2) {
+            if (persist) {
+                hipLaunchKernelGGL((k_igemm_persist<K, t.nt, cps>), grid, dim3(kThreads), lds, s, a);
+                return;
+            }
         }
+        if (vec)
+            launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
+        else
+            launch_packed_cfg<K, t.nt, cps, 0>(grid, lds, s, a);
     }
-    if (vec)
-        launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
-    else
-        launch_packed_cfg<K, t.nt, cps, 0>(grid, lds, s, a);
 }
 
 template <int K>
@@ -1353,6 +1406,7 @@ static void launch_packed_k(int kind, bool vec, bool persist, dim3 grid, size_t 
     case 0: launch_packed_kind<K, 0>(vec, persist, grid, lds, s, a); break;
     case 1: launch_packed_kind<K, 1>(vec, persist, grid, lds, s, a); break;
     case 2: launch_packed_kind<K, 2>(vec, persist, grid, lds, s, a); break;
+    case 3: launch_packed_kind<K, 3>(vec, persist, grid, lds, s, a); break;
     }
 }
 
@@ -1449,7 +1503,7 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     const size_t lds = persist ? packed_persist_lds(g, kind, r) : packed_lds(g, kind, r);
     PackedArgs a;
     a.x = x;
-    a.wp = wp;
+    a.wp = kPacked[kind].nt == 0 ? wp + packed_copy_floats(g) : wp;  // the 16-pixel tile's copy
     a.scale = scale;
     a.bias = bias;
     a.res = res;
@@ -1498,7 +1552,7 @@ hipError_t launch_igemm_packed(const ConvGeom& g, const Plan& p, const float* x,
     }
     fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
     a.tr = tc > 0 ? packed_tile_n(kind) / tc : 0;
-    a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+    a.wp_bytes = (unsigned)(packed_copy_floats(g) * 4);
     a.act = g.act;
     a.res_mode = g.res_mode;
     if (splits > 1) {

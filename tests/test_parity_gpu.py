@@ -344,8 +344,10 @@ def test_gap_fc():
 
 
 def test_packed_weights_layout():
-    """The packed form holds every OIHW weight exactly once (the rest is zero
-    padding), for 3x3 and 1x1 shapes with ragged row, channel and tap groups."""
+    """The packed form holds every OIHW weight exactly once per copy (the rest
+    is zero padding): one copy for 1x1, two equal halves for 3x3 (the 32x32
+    blocks' lane order, then the 16-pixel tile's), for shapes with ragged row,
+    channel and tap groups."""
     for (cout, cin, k) in [(70, 40, 3), (33, 19, 1), (256, 256, 3), (10, 192, 1)]:
         d = cvx.make_desc(1, cin, 12, 12, cout, k, 1, k // 2, 1, 0, 0, PACKED)
         w = np.random.default_rng(cout).normal(size=(cout, cin, k, k)).astype(np.float32)
@@ -355,8 +357,11 @@ def test_packed_weights_layout():
         torch.cuda.synchronize()
         got = wp.cpu().numpy()
         assert not np.isnan(got).any()
-        nz = np.sort(got[got != 0.0])
-        assert np.array_equal(nz, np.sort(w[w != 0.0].ravel()))
+        copies = 2 if k == 3 else 1
+        assert got.size % copies == 0
+        for part in np.split(got, copies):
+            nz = np.sort(part[part != 0.0])
+            assert np.array_equal(nz, np.sort(w[w != 0.0].ravel()))
 
 
 def test_deterministic_across_runs():
@@ -385,7 +390,8 @@ def test_forward_repeat_is_stable():
     assert torch.equal(a, b)
 
 
-# every compiled tile configuration, both pixel layouts, with and without a split
+# every compiled tile configuration (kinds 0-2: 32 x 32, 64 and 128 pixels; 3:
+# the 16-pixel tile, 3x3 only), both pixel layouts, with and without a split
 # reduction, on shapes with ragged edges in both dimensions
 FORCED = [(kind, tc, sk) for kind in range(4) for tc in (0, 4, 8, 16, 32) for sk in (1, 3)]
 
@@ -408,7 +414,7 @@ def test_igemm_forced_tiles(force, layout, monkeypatch):
         check(y, oracle_conv(x, L, r), f"forced {force} seed {seed}")
 
 
-ORDERED = [(order, kind, tc, sk) for order in ("blocks", "pixels") for kind in range(3)
+ORDERED = [(order, kind, tc, sk) for order in ("blocks", "pixels") for kind in range(4)
            for tc in (0, 8) for sk in (1, 3)]
 
 
@@ -430,6 +436,29 @@ def test_packed_workgroup_order(force, monkeypatch):
         y, ok = gpu_conv(x, L, r, PACKED)
         assert ok, "write outside the output"
         check(y, oracle_conv(x, L, r), f"order {force} seed {seed}")
+
+
+# the 16-pixel tile on the detector's 3x3 layers at batch 1, full size: flat
+# runs and 2-D tiles, stride 1 and 2, with and without a split reduction
+H16_LAYERS = [("b_64x80_3x3s2", "3,16,1"), ("d_128x40_3x3", "3,8,1"), ("e_128x40_3x3s2", "3,8,1"),
+              ("e_128x40_3x3s2", "3,0,2"), ("g_256x20_3x3", "3,0,1"), ("g_256x20_3x3", "3,4,2")]
+
+
+@pytest.mark.parametrize("name,force", H16_LAYERS, ids=[f"{n[0]}-{f}" for n, f in H16_LAYERS])
+def test_packed_16_pixel_tile_layers(name, force, monkeypatch):
+    monkeypatch.setenv("CVX_IGEMM_TILE", force)
+    wk = wl.sweep_layer(name)
+    L = wk.layers[0]
+    n, c, h, w = wk.x.shape
+    d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode, PACKED)
+    plan = cvx.cvx_conv_plan(d)
+    kind, tc, sk = force.split(",")
+    assert f"tile=3 bm=32 bn=16 tc={tc} splitk={sk}" in plan, plan
+    say(f"16-pixel tile {name} [{plan}]")
+    r = wk.x if L.res_mode else None
+    y, ok = gpu_conv(wk.x, L, r)
+    assert ok, "write outside the output"
+    check(y, oracle_conv(wk.x, L, r), f"16-pixel tile {name} {force}")
 
 
 def _packed_setup(x, L, layout=PACKED):
