@@ -173,6 +173,7 @@ constexpr TileEntry kTileTable[] = {
     {1, 64, 80, 80, 128, 3, 2, 1, 0, 16, 1},    // b      6.21 -> 6.07
     {1, 128, 40, 40, 128, 3, 1, 1, 0, 8, 1},    // d      8.66 -> 8.35
     {1, 128, 40, 40, 256, 3, 2, 1, 3, 8, 1},    // e      7.88 -> 6.85 (16-pixel tile; 32x32 needed a split)
+    {1, 256, 20, 20, 256, 1, 1, 0, 3, 0, 1},    // f      5.55 -> 5.05 (16-pixel tile: 200 workgroups, not 104)
     {1, 256, 20, 20, 256, 3, 1, 1, 3, 0, 1},    // g     10.23 -> 9.31 (16-pixel tile; 32x32 needed a split)
     // batch 8
     {8, 16, 320, 320, 32, 3, 2, 1, 0, 16, 1},   // stem2 40.38 -> 37.07 (when not paired with stem1)

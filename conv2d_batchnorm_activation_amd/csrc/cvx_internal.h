@@ -143,7 +143,12 @@ hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s);
 
 // Packed-weight implicit-GEMM family (k_igemm_packed.hip).  A configuration is
 // a kind (tile of 32 x packed_tile_n(kind) outputs), tc and a split count.
+// floats of the packed weight buffer: two copies of the same weights, in the
+// lane orders of the 32x32x2 (32 x 32*NT tiles, the pointwise, 1x1 GEMM, chain
+// and stem-pair kernels) and 16x16x4 (the 16-pixel tile) matrix instructions;
+// a kernel reads one copy and bounds its weight descriptor to it
 long packed_weight_floats(const ConvGeom& g);
+long packed_copy_floats(const ConvGeom& g);
 int packed_num_kinds();
 int packed_tile_n(int kind);
 int packed_chunks_per_stage(int kind, int k);

@@ -771,7 +771,7 @@ hipError_t launch_chain(const ChainLayerSpec* S, int n, void* ws, hipStream_t s)
         fastdiv_params(a.splits, &a.m_sp, &a.l_sp);
         fastdiv_params(a.nmb, &a.m_nmb, &a.l_nmb);
         fastdiv_params(a.tiles_per_img, &a.m_tpi, &a.l_tpi);
-        a.wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+        a.wp_bytes = (unsigned)(packed_copy_floats(g) * 4);
         a.act = g.act;
         a.res_mode = g.res_mode;
         a.in_dep = sp.in_dep;

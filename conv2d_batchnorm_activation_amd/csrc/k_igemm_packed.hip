@@ -37,15 +37,15 @@
 // consecutive pixels of one output channel: the exchange and the epilogue move
 // them 16 bytes at a time.
 //
-// The 16-pixel tile (NT = 0, 3x3 only) halves a workgroup's work for layers
+// The 16-pixel tile (NT = 0) halves a workgroup's work for layers
 // whose 32-pixel tiles number fewer than the compute units, which would
 // otherwise split the reduction and pay its partial-sum round trip.  It runs
 // on v_mfma_f32_16x16x4_f32 (half the work of the 32x32x2 instruction in half
 // the clocks): consumer wave h takes channels 4h..4h+3 of every chunk (A lane
 // l: pixel l%16, channel 4h + l/16) and issues two instructions per tap, one
 // per half of the 32 output channels (B lane l: channel 16*half + l%16), two
-// chunks to a stage.  Its weights are a second copy of the block in that lane
-// order, stored after the first.
+// chunks to a stage for 3x3 and four for 1x1.  Its weights are a second copy
+// of the block in that lane order, stored after the first.
 //
 // Layouts:
 //   * packed weights: [32-row block][16-channel chunk][pair of channel pairs h
@@ -54,9 +54,10 @@
 //     per pair) in five 16-byte slots; [block][chunk][h][lane][2] for 1x1.
 //     A (block, chunk) is one contiguous run of 20 KB (3x3) or 2 KB (1x1);
 //     consumer wave h reads its quarter straight into registers, already in
-//     the operand's lane order.  3x3 weights then repeat in the 16-pixel
+//     the operand's lane order.  The weights then repeat in the 16-pixel
 //     tile's order: same shape, lane l holding output channel 32*block +
-//     16*half + l%16 and input channel 4h + l/16, its 18 values 9*half + tap.  ("YOLO26N Inference Optimisation", "NHWC
+//     16*half + l%16 and input channel 4h + l/16, its values 9*half + tap
+//     (3x3) or half (1x1).  ("YOLO26N Inference Optimisation", "NHWC
 //     migration", "Weight layout": weights are reordered once for the layout
 //     the kernels read.)
 //   * inputs: 16 bytes per lane when rows are 16-byte aligned (VEC), else 4;
@@ -149,7 +150,7 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
     constexpr int KK = K * K;
     constexpr int G = VEC ? 4 : 1;     // floats per staged element
     constexpr bool H16 = NT == 0;      // the 16-pixel tile
-    static_assert(!H16 || (K == 3 && CPS % 2 == 0), "16-pixel tile: 3x3, chunks in pairs");
+    static_assert(!H16 || CPS % 2 == 0, "16-pixel tile: chunks in pairs");
     constexpr int NB = H16 ? 1 : NT;   // input operands a lane reads per tap
     constexpr int BN = H16 ? 16 : 32 * NT;
     constexpr int PITCH = BN + (NT < 4 ? 4 : 0);  // LDS row pitch of the partial-sum exchange
@@ -432,8 +433,10 @@ __global__ void __launch_bounds__(kThreads) k_igemm_packed(PackedArgs a)
             if constexpr (H16) {
 #pragma unroll
                 for (int tap = 0; tap < KK; ++tap) {
-                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][tap], acc[0], 0, 0, 0);
-                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][9 + tap], acc[1], 0, 0, 0);
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][K == 3 ? tap : 0], acc[0], 0,
+                                                                  0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[tap][0], ac[q][K == 3 ? 9 + tap : 1], acc[1],
+                                                                  0, 0, 0);
                 }
             } else {
                 const int j = q >> 1, pp = q & 1;
@@ -1085,7 +1088,7 @@ __global__ void __launch_bounds__(kThreads) k_igemm_persist(PackedArgs a)
 }
 
 // One-time weight transform, OIHW -> the packed order above; zero where the row,
-// channel or tap does not exist.  3x3: `copy` floats in the 32x32 blocks' lane
+// channel or tap does not exist.  `copy` floats in the 32x32 blocks' lane
 // order, then as many in the 16-pixel tile's.
 __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ w, int cout, int cin,
                                                       int k, int nchunks, long copy, long total,
@@ -1126,8 +1129,13 @@ __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ 
         const long g3 = g >> 2;
         const int chunk = (int)(g3 % nchunks);
         const int blk = (int)(g3 / nchunks);
-        co = blk * 32 + (lane & 31);
-        ci = chunk * kCh + 2 * (2 * h + j) + (lane >> 5);
+        if (h16) {
+            co = blk * 32 + 16 * j + (lane & 15);
+            ci = chunk * kCh + 4 * h + (lane >> 4);
+        } else {
+            co = blk * 32 + (lane & 31);
+            ci = chunk * kCh + 2 * (2 * h + j) + (lane >> 5);
+        }
     }
     float v = 0.0f;
     if (live && co < cout && ci < cin) v = w[((long)co * cin + ci) * (k * k) + tap];
@@ -1136,12 +1144,11 @@ __global__ void __launch_bounds__(256) k_pack_weights(const float* __restrict__ 
 
 // ------------------------------------------------------------------ host side
 // Compiled configurations: NT pixel blocks per wave, and chunks per pipeline
-// stage for 3x3 and 1x1.  The tile is 32 x 32*NT; NT = 0 is the 16-pixel tile
-// (3x3 only).
+// stage for 3x3 and 1x1.  The tile is 32 x 32*NT; NT = 0 is the 16-pixel tile.
 struct PackedKind {
     int nt, cps3, cps1;
 };
-static constexpr PackedKind kPacked[] = {{1, 1, 4}, {2, 1, 4}, {4, 1, 2}, {0, 2, 0}};
+static constexpr PackedKind kPacked[] = {{1, 1, 4}, {2, 1, 4}, {4, 1, 2}, {0, 2, 4}};
 constexpr int kNumPacked = sizeof(kPacked) / sizeof(kPacked[0]);
 
 int packed_num_kinds() { return kNumPacked; }
@@ -1149,14 +1156,14 @@ int packed_chunks_per_stage(int kind, int k) { return k == 3 ? kPacked[kind].cps
 int packed_tile_n(int kind) { return kPacked[kind].nt > 0 ? 32 * kPacked[kind].nt : 16; }
 
 // One copy of the packed weights (one lane order)
-static long packed_copy_floats(const ConvGeom& g)
+long packed_copy_floats(const ConvGeom& g)
 {
     const long blocks = (g.cout + 31) / 32;
     const long nchunks = (g.cin + kCh - 1) / kCh;
     return blocks * nchunks * (g.k == 3 ? kBCFloats3 : kBCFloats1);
 }
 
-long packed_weight_floats(const ConvGeom& g) { return (g.k == 3 ? 2 : 1) * packed_copy_floats(g); }
+long packed_weight_floats(const ConvGeom& g) { return 2 * packed_copy_floats(g); }
 
 hipError_t launch_pack_weights(const ConvGeom& g, const float* w, float* wp, hipStream_t s)
 {
@@ -1272,7 +1279,6 @@ bool packed_tile_fits(const ConvGeom& g, int kind, int tc, size_t* lds_bytes)
 {
     if (kind < 0 || kind >= kNumPacked) return false;
     if (g.groups != 1 || (g.k != 1 && g.k != 3)) return false;
-    if (packed_chunks_per_stage(kind, g.k) == 0) return false;  // the 16-pixel tile: 3x3 only
     const int bn = packed_tile_n(kind);
     if (tc < 0 || (tc > 0 && (tc > bn || bn % tc != 0 || (tc & (tc - 1)) != 0))) return false;
     const long lim = 0x7fffffffL;
@@ -1314,9 +1320,9 @@ size_t packed_workspace_bytes(const ConvGeom& g, int kind, int tc, int splits)
 // two (LDS).
 int packed_occupancy(int kind, int k)
 {
-    static constexpr int kRegs[2][kNumPacked] = {{56, 81, 123, 0},     // 1x1: NT = 1, 2, 4 (no 16-pixel tile)
-                                                 {87, 127, 207, 118}};  // 3x3, and the 16-pixel tile
-    const int regs = std::max(1, kRegs[k == 3 ? 1 : 0][kind]);
+    static constexpr int kRegs[2][kNumPacked] = {{56, 81, 123, 51},    // 1x1: NT = 1, 2, 4, 16-pixel tile
+                                                 {87, 127, 207, 118}};  // 3x3
+    const int regs = kRegs[k == 3 ? 1 : 0][kind];
     const int occ = 512 / regs / 2;
     return occ < 1 ? 1 : occ > 2 ? 2 : occ;
 }
@@ -1384,18 +1390,16 @@ static void launch_packed_kind(bool vec, bool persist, dim3 grid, size_t lds, hi
 {
     constexpr PackedKind t = kPacked[KIND];
     constexpr int cps = K == 3 ? t.cps3 : t.cps1;
-    if constexpr (cps > 0) {
-        if constexpr (t.nt >= 1 && t.nt <= 2) {
-            if (persist) {
-                hipLaunchKernelGGL((k_igemm_persist<K, t.nt, cps>), grid, dim3(kThreads), lds, s, a);
-                return;
-            }
+    if constexpr (t.nt >= 1 && t.nt <= 2) {
+        if (persist) {
+            hipLaunchKernelGGL((k_igemm_persist<K, t.nt, cps>), grid, dim3(kThreads), lds, s, a);
+            return;
         }
-        if (vec)
-            launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
-        else
-            launch_packed_cfg<K, t.nt, cps, 0>(grid, lds, s, a);
     }
+    if (vec)
+        launch_packed_cfg<K, t.nt, cps, 1>(grid, lds, s, a);
+    else
+        launch_packed_cfg<K, t.nt, cps, 0>(grid, lds, s, a);
 }
 
 template <int K>

@@ -677,7 +677,7 @@ static void fill_src(const ConvGeom& g, const PwStage& st, const float* x, const
     sr->S = g.stride;
     sr->CS = st.cs;
     fastdiv_params(st.owd, &sr->m_owd, &sr->l_owd);
-    sr->wp_bytes = (unsigned)(packed_weight_floats(g) * 4);
+    sr->wp_bytes = (unsigned)(packed_copy_floats(g) * 4);
 }
 
 // One layer (g2 null), or a layer and a second 1x1 source summed into the same

@@ -679,7 +679,7 @@ hipError_t launch_stem_pair(const ConvGeom& g1, const float* x, const StemProlog
     fastdiv_params(pg.WR * pg.WCW / 4, &a.m_wc, &a.l_wc);
     fastdiv_params(pg.WCW, &a.m_wcw, &a.l_wcw);
     a.x_bytes = (unsigned)((long)g1.n * g1.cin * g1.h * g1.w * 4);
-    a.wp_bytes = (unsigned)(packed_weight_floats(g2) * 4);
+    a.wp_bytes = (unsigned)(packed_copy_floats(g2) * 4);
     if (pre != nullptr) {
         a.src = pre->src;
         a.src_h = pre->src_h;

@@ -116,7 +116,7 @@ CVX_API size_t cvx_packed_weights_bytes(const cvx_conv_desc *d);
  * w_layout = CVX_W_PACKED.  For the dense 1x1/3x3 kernels the OIHW weights are
  * reordered into the matrix cores' operand order (zero-padded to whole 32-row
  * and 16-channel groups, a 3x3 chunk's 18 taps per lane in five 16-byte slots);
- * 3x3 weights are stored twice, in the two lane orders of the 32x32x2 and the
+ * the weights are stored twice, in the two lane orders of the 32x32x2 and the
  * 16x16x4 matrix instructions (the second copy serves the 16-pixel tile), so
  * every plan of the shape reads the same buffer;
  * for the other kernels the packed form is a copy

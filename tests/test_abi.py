@@ -464,12 +464,12 @@ def test_gemm1x1_plan_on_the_host(monkeypatch):
 
 
 def test_sixteen_pixel_tile_plan_on_the_host(monkeypatch):
-    """The 16-pixel tile (packed kind 3, v_mfma_f32_16x16x4_f32) is a 3x3
-    configuration: the detector's e and g at batch 1 take it without a split
-    (their 32 x 32 tiles number fewer than the compute units), the other layers
-    keep 32-channel x 32-pixel tiles; forcing it on a 1x1 layer leaves the
-    planner's own choice.  3x3 packed weights hold two copies (the 32 x 32
-    tiles' lane order, then the 16-pixel tile's), 1x1 weights one."""
+    """The 16-pixel tile (packed kind 3, v_mfma_f32_16x16x4_f32): the
+    detector's e, f and g at batch 1 take it, e and g without a split (their
+    32 x 32 tiles number fewer than the compute units), the other layers keep
+    32-channel x 32-pixel tiles; it can be forced on 1x1 layers too.  Packed
+    weights hold two copies (the 32 x 32 tiles' lane order, then the 16-pixel
+    tile's)."""
     P = cvx.CVX_W_PACKED
     monkeypatch.delenv("CVX_IGEMM_TILE", raising=False)
     e1 = _desc(n=1, c_in=128, h=40, w=40, c_out=256, stride=2, w_layout=P)
@@ -477,14 +477,15 @@ def test_sixteen_pixel_tile_plan_on_the_host(monkeypatch):
     d1 = _desc(n=1, c_in=128, h=40, w=40, c_out=128, w_layout=P)
     assert " tile=3 bm=32 bn=16 tc=8 splitk=1 kernel=cvx::k_igemm_packed<3, 0, 2, 1>" in cvx.cvx_conv_plan(e1)
     assert " tile=3 bm=32 bn=16 tc=0 splitk=1 " in cvx.cvx_conv_plan(g1)
+    f1 = _desc(n=1, c_in=256, h=20, w=20, c_out=256, k=1, pad=0, w_layout=P)
+    assert " tile=3 bm=32 bn=16 tc=0 splitk=1 kernel=cvx::k_igemm_packed<1, 0, 4, 1>" in cvx.cvx_conv_plan(f1)
     assert " tile=0 bm=32 bn=32 " in cvx.cvx_conv_plan(d1)
     assert " tile=3 " not in cvx.cvx_conv_plan(_desc(n=8, c_in=256, h=20, w=20, c_out=256, w_layout=P))
     # one copy: ceil(c_out/32) blocks x ceil(c_in/16) chunks x 20 KB (3x3) or 2 KB (1x1)
     assert cvx.cvx_packed_weights_bytes(g1) == 2 * 8 * 16 * 5120 * 4
-    f1 = _desc(n=1, c_in=256, h=20, w=20, c_out=256, k=1, pad=0, w_layout=P)
-    assert cvx.cvx_packed_weights_bytes(f1) == 8 * 16 * 512 * 4
+    assert cvx.cvx_packed_weights_bytes(f1) == 2 * 8 * 16 * 512 * 4
     monkeypatch.setenv("CVX_IGEMM_TILE", "3,4,1")
     assert " tile=3 bm=32 bn=16 tc=4 splitk=1 " in cvx.cvx_conv_plan(d1)
-    assert " tile=3 " not in cvx.cvx_conv_plan(f1)
+    assert " tile=3 bm=32 bn=16 tc=4 splitk=1 kernel=cvx::k_igemm_packed<1, 0, 4, 1>" in cvx.cvx_conv_plan(f1)
     monkeypatch.setenv("CVX_IGEMM_TILE", "3,32,1")  # wider than the tile: not a configuration
     assert " tile=3 " not in cvx.cvx_conv_plan(d1)

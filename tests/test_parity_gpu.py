@@ -345,9 +345,9 @@ def test_gap_fc():
 
 def test_packed_weights_layout():
     """The packed form holds every OIHW weight exactly once per copy (the rest
-    is zero padding): one copy for 1x1, two equal halves for 3x3 (the 32x32
-    blocks' lane order, then the 16-pixel tile's), for shapes with ragged row,
-    channel and tap groups."""
+    is zero padding), in two equal halves (the 32x32 blocks' lane order, then
+    the 16-pixel tile's), for 3x3 and 1x1 shapes with ragged row, channel and
+    tap groups."""
     for (cout, cin, k) in [(70, 40, 3), (33, 19, 1), (256, 256, 3), (10, 192, 1)]:
         d = cvx.make_desc(1, cin, 12, 12, cout, k, 1, k // 2, 1, 0, 0, PACKED)
         w = np.random.default_rng(cout).normal(size=(cout, cin, k, k)).astype(np.float32)
@@ -357,9 +357,8 @@ def test_packed_weights_layout():
         torch.cuda.synchronize()
         got = wp.cpu().numpy()
         assert not np.isnan(got).any()
-        copies = 2 if k == 3 else 1
-        assert got.size % copies == 0
-        for part in np.split(got, copies):
+        assert got.size % 2 == 0
+        for part in np.split(got, 2):
             nz = np.sort(part[part != 0.0])
             assert np.array_equal(nz, np.sort(w[w != 0.0].ravel()))
 
@@ -391,7 +390,7 @@ def test_forward_repeat_is_stable():
 
 
 # every compiled tile configuration (kinds 0-2: 32 x 32, 64 and 128 pixels; 3:
-# the 16-pixel tile, 3x3 only), both pixel layouts, with and without a split
+# the 16-pixel tile), both pixel layouts, with and without a split
 # reduction, on shapes with ragged edges in both dimensions
 FORCED = [(kind, tc, sk) for kind in range(4) for tc in (0, 4, 8, 16, 32) for sk in (1, 3)]
 
