@@ -481,7 +481,8 @@ def kernel_sources_hash(kernel: str) -> str:
                "k_direct": "k_direct.hip", "k_stem": "k_direct.hip", "k_depthwise3x3": "k_depthwise.hip",
                "k_dw_planes": "k_depthwise.hip", "k_dw_rows": "k_depthwise.hip", "k_pointwise": "k_pointwise.hip",
                "k_preprocess": "k_preprocess.hip", "k_preprocess_rows": "k_preprocess.hip",
-               "k_stem_pair": "k_stem_pair.hip", "k_conv_nhwc": "k_nhwc.hip", "k_chain": "k_chain.hip"}.get(base)
+               "k_stem_pair": "k_stem_pair.hip", "k_conv_nhwc": "k_nhwc.hip", "k_chain": "k_chain.hip",
+               "k_gemm1x1": "k_gemm1x1.hip"}.get(base)
     h = hashlib.sha256()
     for f in ([srcfile] if srcfile else []) + ["bufio.h", "epilogue.h", "cvx_internal.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
