@@ -980,11 +980,30 @@ def stats(per_step_ms) -> dict:
             "cv": round(float(a.std() / a.mean()), 4) if a.mean() > 0 else None, "n": int(a.size)}
 
 
+def plain_steps(fn, steps: int) -> float:
+    """`steps` back-to-back calls of `fn` on one stream between two events and
+    nothing else: the ms between them.  The host enqueues a forward in about
+    half the time the GPU takes to run it, so this is GPU time."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def timed_steps(fn, steps: int):
     """`steps` back-to-back calls of `fn` on one stream with an event before and
     after each: (total ms between the first and last event, per-call ms list).
     The GPU runs the calls back to back (the host enqueues faster than they
-    run), so a per-call time is that forward's own duration."""
+    run), so a per-call time is that forward's own duration plus the cost of
+    the event between calls (about 4 us on the detector forward): the spread
+    comes from such a pass, the means from `plain_steps`."""
     import torch
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
@@ -1024,8 +1043,14 @@ def cold_forward_us(net, wk, steps: int) -> dict:
         cvx.cvx_forward(net.arr, xj, oj, wj, net.ws_bytes)
     for _ in range(sets):
         one()
-    _, per = timed_steps(one, max(steps, 2 * sets))
+    n = max(steps, 2 * sets)
+    plain_us = plain_steps(one, n) / n * 1e3
+    _, per = timed_steps(one, n)
     st = stats(per)
+    # mean without per-forward events (comparable with the hot figure); the
+    # other statistics from the pass with an event after each forward
+    st["events_mean_us"] = st["mean_us"]
+    st["mean_us"] = round(plain_us, 3)
     st["sets"] = sets
     st["rotated_mbytes"] = round(sets * set_bytes / 1e6, 1)
     del bufs, pool
@@ -1081,8 +1106,8 @@ def other_workloads(layer_reps: int, steps: int):
         x = torch.from_numpy(wk.x).cuda()
         for _ in range(3):
             net(x)
-        total, per = timed_steps(lambda: net(x), steps)
-        ms = total / steps
+        ms = plain_steps(lambda: net(x), steps) / steps
+        _t, per = timed_steps(lambda: net(x), steps)
         ms_graph = forward_time_ms(net, x, steps)
         ms_graph10 = forward_time_ms(net, x, steps, per_graph=10)
         log(f"{name}: {ms * 1e3:.1f} us/forward, {ms_graph * 1e3:.1f} us as a graph replay, "
@@ -1294,18 +1319,20 @@ def main() -> int:
     for _ in range(args.warmup):
         net(x)
     torch.cuda.synchronize()
-    # the timed region: exactly `steps` forwards between two events, with an
-    # event after each forward for the spread
+    # the timed region: exactly `steps` forwards between two events
     t_wall = time.perf_counter()
-    total_ms, per = timed_steps(lambda: net(x), args.steps)
+    total_ms = plain_steps(lambda: net(x), args.steps)
     wall = time.perf_counter() - t_wall
     ms_eager = total_ms / args.steps
-    spread = stats(per)
     # two more reruns of the same timed region (run-to-run spread)
     reruns = [round(ms_eager * 1e3, 3)]
     for _ in range(2):
-        t, _p = timed_steps(lambda: net(x), args.steps)
-        reruns.append(round(t / args.steps * 1e3, 3))
+        reruns.append(round(plain_steps(lambda: net(x), args.steps) / args.steps * 1e3, 3))
+    # the per-forward spread: a separate pass with an event after each forward
+    # (each event adds its own cost, reported as the difference of the means)
+    _t, per = timed_steps(lambda: net(x), args.steps)
+    spread = stats(per)
+    spread["event_cost_us"] = round(spread["mean_us"] - ms_eager * 1e3, 3)
     # graph: the forward captured once, replayed once per step
     ms = forward_time_ms(net, x, args.steps)
     ms10 = forward_time_ms(net, x, args.steps, per_graph=10)
@@ -1336,10 +1363,11 @@ def main() -> int:
         "layer_reps": args.layer_reps,
         "forward_probe": probe,
         "gpu_clocks": {"start": clocks_start, "end": None},
-        "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events, "
-                  "with an event after each forward for the spread (forward_spread: mean, p50, "
-                  "p99, cv of the per-forward times); forward_reruns_us repeats the timed region "
-                  "twice more; ms_per_forward_graph replays a HIP graph of one forward per step, "
+        "timing": "steps back-to-back cvx_forward calls on one stream between two HIP events "
+                  "and nothing else; forward_spread (mean, p50, p99, cv of the per-forward "
+                  "times) comes from a separate pass with an event after each forward, whose "
+                  "mean exceeds the timed region's by event_cost_us (the events' own cost); "
+                  "forward_reruns_us repeats the timed region twice more; ms_per_forward_graph replays a HIP graph of one forward per step, "
                   "whose launch boundary adds about 5 us (ms_per_forward_graph10: graphs of ten "
                   "forwards, which also removes most of the gaps between kernels); forward_cold "
                   "rotates frame, workspace "
