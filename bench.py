@@ -1246,7 +1246,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layer-reps", type=int, default=200)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
