@@ -460,6 +460,41 @@ def test_packed_16_pixel_tile_layers(name, force, monkeypatch):
     check(y, oracle_conv(wk.x, L, r), f"16-pixel tile {name} {force}")
 
 
+def _h16_random_cases(count=14, seed=720):
+    """Seeded shapes for the 16-pixel tile: tiny and odd planes (widths that are
+    not multiples of 4 use 4-byte staging), channel counts below one chunk and
+    between chunks, both strides and kernel sizes, with and without a split,
+    a residual added before the activation."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        k = int(rng.choice([1, 3]))
+        stride = int(rng.choice([1, 2]))
+        cin = int(rng.integers(4, 70))
+        cout = int(rng.integers(1, 70))
+        h, w = int(rng.integers(1, 26)), int(rng.integers(1, 26))
+        tc = int(rng.choice([0, 4, 8, 16]))
+        sk = int(rng.choice([1, 2]))
+        cases.append((seed + i, int(rng.integers(1, 4)), cin, h, w, cout, k, stride, k // 2, tc, sk))
+    return cases
+
+
+@pytest.mark.parametrize("case", _h16_random_cases(), ids=lambda c: f"seed{c[0]}")
+def test_packed_16_pixel_tile_random_shapes(case, monkeypatch):
+    seed, n, cin, h, w, cout, k, s, p, tc, sk = case
+    monkeypatch.setenv("CVX_IGEMM_TILE", f"3,{tc},{sk}")
+    act, rm = wl.ACT_SILU, wl.RES_BEFORE_ACT
+    x, L = wl.random_conv_case(seed, n, cin, h, w, cout, k, s, p, 1, act, rm)
+    d = cvx.make_desc(n, cin, h, w, cout, k, s, p, 1, act, rm, PACKED)
+    plan = cvx.cvx_conv_plan(d)
+    oh, ow = cvx.cvx_conv_out_shape(d)
+    say(f"16-pixel tile random seed {seed}: n={n} {cin}x{h}x{w} -> {cout} k{k} s{s} [{plan}]")
+    r = wl.residual_for(seed, (n, cout, oh, ow))
+    y, ok = gpu_conv(x, L, r)
+    assert ok, "write outside the output"
+    check(y, oracle_conv(x, L, r), f"16-pixel tile random seed {seed}")
+
+
 def _packed_setup(x, L, layout=PACKED):
     n, c, h, w = x.shape
     d = cvx.make_desc(n, c, h, w, L.cout, L.k, L.stride, L.pad, L.groups, L.act, L.res_mode,
