@@ -752,6 +752,8 @@ struct NodePlan {
     bool skipped;        // FC folded into the preceding GAP
     bool merged;         // 1x1 shortcut computed inside its reader's kernel: no output
     int pair;            // the merged shortcut this layer computes with its own product, or -1
+    int dsb_dw;          // pointwise layer run as a block with this depthwise layer (k_dsblock), or -1
+    int dsb_skip;        // ... and with this 1x1 shortcut layer, or -1
     bool stem_next;      // stem whose output only the next layer reads: both run as one kernel there
     bool stem_kept;      // ... whose output still gets a region (a list input may be misaligned at launch)
     bool pre_into_pair;  // prologue whose output only a paired stem reads: the pair resizes the frame itself
@@ -817,6 +819,8 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         NodePlan& np = lp->nodes[i];
         np.last_use = i;
         np.pair = -1;
+        np.dsb_dw = -1;
+        np.dsb_skip = -1;
         if (l.kind < CVX_L_CONV || l.kind > CVX_L_PREPROC) return CVX_ERR_ARG;
         if (l.in < CVX_INPUT || l.in >= i) return CVX_ERR_ARG;
         if (l.kind == CVX_L_PREPROC) {
@@ -942,6 +946,45 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
             }
         }
     }
+    // A depthwise 3x3 layer whose one reader is a 1x1 layer, plus that layer's
+    // shortcut (the block input, or a 1x1 strided convolution of it read only
+    // there): at small batches the block runs as one kernel (k_dsblock) and
+    // neither the depthwise output nor the shortcut's is written.  Measured
+    // on the MNIST net it is slower than the separate kernels at every batch
+    // (b=1: 75 against 46-58 us a forward): with 12-21 workgroups a block, each
+    // recomputing the depthwise layer for its channel group, the workgroups'
+    // serial work outweighs the two launches saved.  Opt-in: CVX_DSBLOCK=1.
+    const char* dsb_env = getenv("CVX_DSBLOCK");
+    if (dsb_env && dsb_env[0] == '1') {
+        for (int i = 0; i < nl; ++i) {
+            const cvx_layer& l = L[i];
+            NodePlan& np = lp->nodes[i];
+            if (l.kind != CVX_L_CONV || l.in < 0 || np.merged || np.pair >= 0 || np.stem_next) continue;
+            const int d = l.in;
+            if (L[d].kind != CVX_L_CONV || readers[d] != 1) continue;
+            NodePlan& dp = lp->nodes[d];
+            if (dp.p.fam != FAM_DEPTHWISE || dp.merged || dp.pair >= 0 || dp.stem_next) continue;
+            if (d > 0 && lp->nodes[d - 1].stem_next) continue;
+            // a shortcut that cannot run inside (an activation, other readers)
+            // is added like any residual tensor
+            int j = -1;
+            if (l.conv.res_mode == CVX_RES_BEFORE_ACT && l.res >= 0 && l.res != L[d].in) {
+                const cvx_layer& sl = L[l.res];
+                const NodePlan& sp = lp->nodes[l.res];
+                if (sl.kind == CVX_L_CONV && sl.in == L[d].in && readers[l.res] == 1 && !sp.merged &&
+                    sp.pair < 0 && !sp.stem_next && dsblock_fits(dp.g, np.g, &sp.g))
+                    j = l.res;
+            }
+            if (j < 0 && !dsblock_fits(dp.g, np.g, nullptr)) continue;
+            dp.merged = true;
+            np.dsb_dw = d;
+            if (j >= 0) {
+                lp->nodes[j].merged = true;
+                np.dsb_skip = j;
+            }
+            if (L[d].in >= 0) lp->nodes[L[d].in].last_use = std::max(lp->nodes[L[d].in].last_use, i);
+        }
+    }
     // Placement of intermediate outputs.  A kernel that writes a buffer another
     // kernel has just read runs markedly slower than one writing memory that
     // was not read since (MNIST conv1's 38.5 MB output: 16.7 against 10.8 us),
@@ -1008,7 +1051,8 @@ cvx_status plan_list(const cvx_layer* L, int nl, ListPlan* lp)
         std::vector<char> ok(nl, 0);
         for (int i = 0; i < nl; ++i) {
             NodePlan& np = lp->nodes[i];
-            if (L[i].kind != CVX_L_CONV || np.merged || np.pair >= 0 || np.p.fam != FAM_IGEMM_PACKED) continue;
+            if (L[i].kind != CVX_L_CONV || np.merged || np.pair >= 0 || np.dsb_dw >= 0 || np.p.fam != FAM_IGEMM_PACKED)
+                continue;
             if (i > 0 && lp->nodes[i - 1].stem_next) continue;  // runs with its stem
             ok[i] = chain_choose(np.g, &np.chain_tc, &np.chain_splits) ? 1 : 0;
         }
@@ -1091,8 +1135,15 @@ cvx_status cvx_forward_plan(const cvx_layer* layers, int n_layers, char* buf, in
             } else if (np.merged) {
                 int into = -1;
                 for (int j = i + 1; j < n_layers; ++j)
-                    if (lp.nodes[j].pair == i) into = j;
+                    if (lp.nodes[j].pair == i || lp.nodes[j].dsb_dw == i || lp.nodes[j].dsb_skip == i) into = j;
                 snprintf(line, sizeof(line), "merged into %d", into);
+            } else if (np.dsb_dw >= 0) {
+                char d[256];
+                dsblock_describe(lp.nodes[np.dsb_dw].g, np.g, np.dsb_skip >= 0, d, sizeof(d));
+                if (np.dsb_skip >= 0)
+                    snprintf(line, sizeof(line), "%s dw=%d shortcut=%d", d, np.dsb_dw, np.dsb_skip);
+                else
+                    snprintf(line, sizeof(line), "%s dw=%d", d, np.dsb_dw);
             } else if (np.pair >= 0) {
                 char d[256];
                 pointwise_describe(np.g, &lp.nodes[np.pair].g, d, sizeof(d));
@@ -1238,6 +1289,46 @@ cvx_status cvx_forward(const cvx_layer* layers, int n_layers, const void* input,
                                   l.std, s);
             break;
         case CVX_L_CONV: {
+            if (np.dsb_dw >= 0) {
+                const cvx_layer& dl = layers[np.dsb_dw];
+                const NodePlan& dn = lp.nodes[np.dsb_dw];
+                auto packed_1x1 = [](const NodePlan& n) {
+                    return n.g.w_layout == CVX_W_PACKED &&
+                           (n.p.fam == FAM_IGEMM_PACKED || n.p.fam == FAM_POINTWISE || n.p.fam == FAM_GEMM1X1);
+                };
+                DsBlockArgs a{};
+                a.x = in_ptr(dl.in);
+                a.dw_w = dl.w;
+                a.dw_scale = dl.scale;
+                a.dw_bias = dl.bias;
+                a.pw_w = l.w;
+                a.pw_scale = l.scale;
+                a.pw_bias = l.bias;
+                if (np.dsb_skip >= 0) {
+                    const cvx_layer& sl = layers[np.dsb_skip];
+                    a.skip_w = sl.w;
+                    a.skip_scale = sl.scale;
+                    a.skip_bias = sl.bias;
+                    a.skip_packed = packed_1x1(lp.nodes[np.dsb_skip]);
+                } else if (l.conv.res_mode != CVX_RES_NONE) {
+                    a.res = in_ptr(l.res);
+                }
+                a.y = out_ptr(i);
+                a.n = dn.g.n;
+                a.cin = dn.g.cin;
+                a.h = dn.g.h;
+                a.w = dn.g.w;
+                a.cout = np.g.cout;
+                a.oh = np.g.oh;
+                a.ow = np.g.ow;
+                a.stride = dn.g.stride;
+                a.dw_act = dn.g.act;
+                a.pw_act = np.g.act;
+                a.res_mode = np.g.res_mode;
+                a.pw_packed = packed_1x1(np);
+                e = launch_dsblock(a, s);
+                break;
+            }
             if (np.pair >= 0) {
                 const cvx_layer& sl = layers[np.pair];
                 e = launch_pointwise_pair(np.g, in_ptr(l.in), l.w, l.scale, l.bias, lp.nodes[np.pair].g,

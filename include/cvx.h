@@ -271,6 +271,13 @@ CVX_API cvx_status cvx_forward_plan(const cvx_layer *layers, int n_layers, char 
  * row counters).  It is off by default, as one launch per layer is faster on
  * the detector workloads.  A wait in it that exceeds its bound poisons the
  * affected outputs with NaN instead of hanging.
+ * With CVX_DSBLOCK=1, a depthwise 3x3 layer (pad 1, no residual) whose only
+ * reader is a 1x1 stride-1 layer runs with that layer, and with its 1x1
+ * shortcut of the block input (BN, no activation, added before the
+ * activation) when it has one, as one kernel at small batches ("Как я свертки
+ * ускорял", "А теперь — хардкор на Metal": one launch for the block); the
+ * depthwise and shortcut outputs are then never written.  Same results; off by
+ * default, as the separate kernels are faster on the MNIST net.
  *   input : device; fp32 NCHW, or u8 NHWC frames when layer 0 is CVX_L_PREPROC.
  *   output: device, shape from cvx_forward_out_shape; must not overlap input/workspace.
  *   workspace: device, >= cvx_forward_workspace_bytes(...) bytes, 256-byte aligned.

@@ -489,3 +489,31 @@ def test_sixteen_pixel_tile_plan_on_the_host(monkeypatch):
     assert " tile=3 bm=32 bn=16 tc=4 splitk=1 kernel=cvx::k_igemm_packed<1, 0, 4, 1>" in cvx.cvx_conv_plan(f1)
     monkeypatch.setenv("CVX_IGEMM_TILE", "3,32,1")  # wider than the tile: not a configuration
     assert " tile=3 " not in cvx.cvx_conv_plan(d1)
+
+
+def test_dsblock_plan_on_the_host(monkeypatch):
+    """At small batches a depthwise layer, the 1x1 layer that alone reads it and
+    that layer's 1x1 shortcut run as one kernel: neither the depthwise output
+    nor the shortcut's takes workspace.  Large batches keep the separate
+    kernels (and the two-source pointwise merge).  The block kernel is opt-in
+    (CVX_DSBLOCK=1): measured slower than the separate kernels."""
+    monkeypatch.setenv("CVX_CHAIN", "0")
+    plan = cvx.cvx_forward_plan(_block_list(8, cvx.CVX_ACT_NONE))
+    assert not any("k_dsblock" in p for p in plan), plan
+    monkeypatch.setenv("CVX_DSBLOCK", "1")
+    n = 8
+    a = 4 * n * 32 * 64            # conv 1x1 output, dw output: 32 x 8 x 8
+    c = 4 * n * 64 * 64            # shortcut output, pw output: 64 x 8 x 8
+    plan = cvx.cvx_forward_plan(_block_list(n, cvx.CVX_ACT_NONE))
+    assert plan[1] == "merged into 3" and plan[2] == "merged into 3", plan
+    assert plan[3].startswith("dsblock dw s1 + pw k1 + shortcut k1 ") and plan[3].endswith(" dw=1 shortcut=2")
+    assert "kernel=cvx::k_dsblock" in plan[3]
+    assert cvx.cvx_forward_workspace_bytes(_block_list(n, cvx.CVX_ACT_NONE)) == a + c
+    # an activation on the shortcut: the depthwise and pointwise layers still
+    # merge, the shortcut runs on its own and is added as a residual tensor
+    plan = cvx.cvx_forward_plan(_block_list(n, cvx.CVX_ACT_RELU))
+    assert plan[1] == "merged into 3" and "merged" not in plan[2], plan
+    assert "kernel=cvx::k_dsblock" in plan[3] and plan[3].endswith(" dw=1"), plan
+    # large batch: more workgroups than the block kernel takes
+    plan = cvx.cvx_forward_plan(_block_list(256, cvx.CVX_ACT_NONE))
+    assert not any("k_dsblock" in p for p in plan), plan
