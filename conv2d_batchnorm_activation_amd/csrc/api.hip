@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "cvx_internal.h"
+#include "dsblock.h"
 
 using namespace cvx;
 

@@ -28,6 +28,7 @@
 
 #include "bufio.h"
 #include "cvx_internal.h"
+#include "dsblock.h"
 #include "epilogue.h"
 
 namespace cvx {
