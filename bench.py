@@ -1119,6 +1119,20 @@ def other_workloads(layer_reps: int, steps: int):
                  "gflops": round(flop / (ms * 1e-3) / 1e9, 1),
                  "gbs": round(byts / (ms * 1e-3) / 1e9, 1), "spread": stats(per),
                  "cold": cold_forward_us(net, wk, steps)}
+        if name == "mnist_b1":
+            # the whole-block kernel (opt-in, CVX_DSBLOCK=1) timed the same way
+            os.environ["CVX_DSBLOCK"] = "1"
+            try:
+                net_b = Net(wk.layers, wk.x.shape)
+                for _ in range(3):
+                    net_b(x)
+                entry["us_per_forward_dsblock"] = round(plain_steps(lambda: net_b(x), steps) / steps * 1e3, 2)
+                entry["us_per_forward_graph10_dsblock"] = round(
+                    forward_time_ms(net_b, x, steps, per_graph=10) * 1e3, 2)
+                log(f"{name}: {entry['us_per_forward_dsblock']:.1f} us/forward with each block as one kernel")
+                del net_b
+            finally:
+                os.environ.pop("CVX_DSBLOCK", None)
         if layers:
             entry["layers"] = per_layer(wk, net, counts, layer_reps)
             # the same roofline position as the headline's, for this workload's
